@@ -1,0 +1,199 @@
+"""Benchmark: packed-weight GB/s of the fused mixed-bit GEMV at batch 1 on one MI355X.
+
+One step = the seven batch-1 GEMVs of one 9B-shaped decoder layer (q, k, v, o
+4096x4096; gate, up 14336x4096; down 4096x14336) in decode order, widths drawn
+i.i.d. per 64-weight group from {1: .69, 2: .16, 4: .10, 8: .05}. Every step
+reads a different copy of the packed layer (copies are rotated so that the
+working set is well beyond the 256 MB Infinity Cache), so the weights come from
+HBM. Throughput = packed bytes streamed (payload + widths + scales + row
+offsets) per second.
+
+Workload shapes: VBQ paper (arXiv 2607.02893) §6, Figure 5 (decode at 131M,
+1.0B and 9B). Synthetic weights and activations (workloads.py).
+
+Prints one JSON line. `--gpus N` with N > 1 exits: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "packed-weight GB/s and % HBM peak for fused mixed-bit GEMV, batch 1"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotate-mb", type=float, default=640.0, help="minimum bytes of distinct weight copies")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp16-baseline", action="store_true")
+    ap.add_argument("--only-timed", action="store_true", help="skip every leg except the timed loop (profiling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on a single GPU; --gpus must be 1 (multi-GPU sharding is design-only)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_gemv_02_amd as V
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = W.config(4)
+
+    # ---- pack once on the host, upload rotated copies
+    hosts, specs = [], cfg.matrices
+    for spec in specs:
+        bits, codes, scales = W.draw_matrix(spec)
+        hosts.append((V.vbq_pack(spec.n, spec.k, bits, codes, scales), bits, codes, scales))
+    layer_bytes = sum(h.total_bytes for h, *_ in hosts)
+    copies = max(2, math.ceil(args.rotate_mb * 1e6 / layer_bytes))
+    dev_layers = [[V.DeviceMatrix(h, dev) for h, *_ in hosts] for _ in range(copies)]
+    xs = {}
+    for spec in specs:
+        key = W.x_seed(spec)
+        if key not in xs:
+            xs[key] = torch.from_numpy(W.draw_x(key, spec.k)[0].view(np.float16)).to(dev)
+    ys = [torch.empty(spec.n, dtype=torch.float32, device=dev) for spec in specs]
+    xin = [xs[W.x_seed(spec)] for spec in specs]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        layer = dev_layers[i % copies]
+        for j in range(len(specs)):
+            V.vbq_gemv(layer[j], xin[j], ys[j], stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+    value = layer_bytes / (ms_per_step * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "layer_9b: q,k,v,o 4096x4096 + gate,up 14336x4096 + down 4096x14336, batch 1, "
+                               "widths i.i.d. per 64-group {1:.69,2:.16,4:.10,8:.05}, fp16 scales and x, fp32 y",
+                   "packed_bytes_per_step": layer_bytes, "weights_per_step": cfg.weights,
+                   "rotated_copies": copies, "launches_per_step": len(specs)},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+    }
+    if args.only_timed:
+        print(json.dumps(result))
+        return
+
+    # ---- per-launch durations (events around each launch on the launch stream)
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in specs]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        layer = dev_layers[i % copies]
+        for j in range(len(specs)):
+            a, b = ev[i][j]
+            a.record(stream)
+            V.vbq_gemv(layer[j], xin[j], ys[j], stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])        # ms [steps, matrices]
+    by_shape = {}
+    for j, spec in enumerate(specs):
+        key = f"{spec.n}x{spec.k}"
+        d = by_shape.setdefault(key, {"bytes": hosts[j][0].total_bytes, "ms": [], "launches": 0})
+        d["ms"].extend(per[:, j].tolist())
+        d["launches"] += 1
+    dom_key = max(by_shape, key=lambda k_: np.sum(by_shape[k_]["ms"]))
+    dom = by_shape[dom_key]
+    avg_ms = float(np.mean(dom["ms"]))
+    achieved = dom["bytes"] / (avg_ms * 1e-3) / 1e9
+    result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                          "kernel": f"vbq_gemv {dom_key}", "avg_launch_us": round(avg_ms * 1e3, 3),
+                          "algorithmic_bytes_per_launch": dom["bytes"]}
+    result["per_shape_us"] = {k_: round(float(np.mean(v["ms"])) * 1e3, 3) for k_, v in by_shape.items()}
+
+    # ---- dense fp16 GEMV of the same shapes (torch matmul on the same stream, rotated copies)
+    if not args.no_fp16_baseline:
+        dense_bytes = sum(2 * s.n * s.k for s in specs)
+        dcopies = max(2, math.ceil(args.rotate_mb * 1e6 / dense_bytes))
+        gen = torch.Generator(device=dev).manual_seed(0)
+        dense = [[torch.randn(s.n, s.k, dtype=torch.float16, device=dev, generator=gen) * 0.02 for s in specs]
+                 for _ in range(dcopies)]
+        outs = [torch.empty(s.n, dtype=torch.float16, device=dev) for s in specs]
+
+        def dstep(i):
+            for j in range(len(specs)):
+                torch.mv(dense[i % dcopies][j], xin[j], out=outs[j])
+
+        for i in range(args.warmup):
+            dstep(i)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            dstep(i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        dms = t0.elapsed_time(t1) / args.steps
+        result["fp16_baseline"] = {"impl": "torch.mv (rocBLAS/hipBLASLt) on dense fp16 W of the same shapes",
+                                   "ms_per_step": round(dms, 5), "dense_bytes_per_step": dense_bytes,
+                                   "dense_GBps": round(dense_bytes / (dms * 1e-3) / 1e9, 2),
+                                   "speedup_vbq_over_fp16": round(dms / ms_per_step, 3)}
+        del dense
+
+    # ---- CPU oracle on the host cores (bounded sample of the same workload)
+    if not args.no_cpu_baseline:
+        import oracle
+        cores = len(os.sched_getaffinity(0))
+        packs = [oracle.pack(s.n, s.k, b, c, sc) for s, (h, b, c, sc) in zip(specs, hosts)]
+        xh = {key: W.draw_x(key, specs[[W.x_seed(s) for s in specs].index(key)].k)[0] for key in
+              {W.x_seed(s) for s in specs}}
+        # calibrate on 1% of the rows, then size the sample to ~cpu_seconds
+        frac = 0.01
+        t = time.perf_counter()
+        for s, p in zip(specs, packs):
+            oracle.gemv_threaded(p, xh[W.x_seed(s)], 0, max(1, int(s.n * frac)), cores)
+        dt = time.perf_counter() - t
+        frac = min(1.0, frac * args.cpu_seconds / max(dt, 1e-6))
+        sampled = 0
+        t = time.perf_counter()
+        for s, p, (h, *_) in zip(specs, packs, hosts):
+            rows = max(1, int(s.n * frac))
+            oracle.gemv_threaded(p, xh[W.x_seed(s)], 0, rows, cores)
+            sampled += int(h.row_offsets[rows]) + 4 * (rows + 1) + (rows * s.k // 64) * 2 + (rows * s.k // 64) // 4
+        dt = time.perf_counter() - t
+        result["cpu_baseline"] = {"value": round(sampled / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+                                  "kind": "oracle",
+                                  "sample": f"first {frac:.2%} of the rows of each of the 7 matrices "
+                                            f"({sampled / 1e6:.1f} MB packed), {dt:.1f} s, {cores} threads"}
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+"""VBQ packed mixed-bit decode on AMD MI355X: Python binding of ``libvbq.so``.
+
+Thin ctypes layer with the C ABI's names (``include/vbq.h``): it only
+marshals pointers, sizes and the HIP stream. Every step of the packed GEMV /
+GEMM runs in the library's HIP kernels; PyTorch supplies device memory and
+streams. There is no fallback: if the compiled library is missing, importing
+the binding raises.
+
+Method: VBQ paper (arXiv 2607.02893), §3.1 Eq. (1) (groups of 64 weights with
+their own width b in {1,2,4,8} and scale s, w_hat = s*q) and §6 (fused
+dequantise-and-multiply decode over packed groups).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch  # import before the library so it binds to the HIP runtime torch has mapped
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libvbq.so")
+ABI_VERSION = 1
+GROUP = 64
+MAX_K = 65536
+MAX_BATCH = 64
+
+OK, ERR_NULL, ERR_SHAPE, ERR_WIDTH, ERR_CODE, ERR_SCALE, ERR_CAPACITY, ERR_OFFSETS, ERR_ALIGN, \
+    ERR_TOO_LARGE, ERR_HIP, ERR_ABI = range(12)
+
+
+class VbqSizes(ctypes.Structure):
+    _fields_ = [("widths_bytes", ctypes.c_uint64), ("scales_bytes", ctypes.c_uint64),
+                ("offsets_bytes", ctypes.c_uint64), ("payload_bytes", ctypes.c_uint64),
+                ("total_bytes", ctypes.c_uint64)]
+
+
+class VbqMatrix(ctypes.Structure):
+    _fields_ = [("abi_version", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
+                ("payload_bytes", ctypes.c_uint32), ("widths", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("row_offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p)]
+
+
+class VbqError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"status {status}: {detail}")
+        self.status = status
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run __graft_entry__.build() (hipcc --offload-arch=gfx950)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    U32 = ctypes.c_uint32
+    lib.vbq_abi_version.restype = U32
+    lib.vbq_abi_version.argtypes = []
+    lib.vbq_status_string.restype = ctypes.c_char_p
+    lib.vbq_status_string.argtypes = [ctypes.c_int]
+    lib.vbq_last_error.restype = ctypes.c_char_p
+    lib.vbq_last_error.argtypes = []
+    lib.vbq_pack_sizes.argtypes = [U32, U32, P, ctypes.POINTER(VbqSizes)]
+    lib.vbq_pack.argtypes = [U32, U32, P, P, P, P, P, P, P, ctypes.c_uint64]
+    lib.vbq_validate_host.argtypes = [ctypes.POINTER(VbqMatrix)]
+    lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
+    lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
+    lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
+    for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemm_smallbatch,
+              lib.vbq_unpack_codes):
+        f.restype = ctypes.c_int
+    if lib.vbq_abi_version() != ABI_VERSION:
+        raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != OK:
+        raise VbqError(status, lib.vbq_last_error().decode())
+
+
+def _np_ptr(a):
+    return None if a is None or a.size == 0 else a.ctypes.data
+
+
+def _stream_handle(stream, device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return int(s.cuda_stream)
+
+
+# ------------------------------------------------------------------ host side
+
+@dataclass
+class HostMatrix:
+    """The four packed arrays in host memory."""
+    n: int
+    k: int
+    widths: np.ndarray       # uint8
+    scales: np.ndarray       # uint16 binary16 bits
+    row_offsets: np.ndarray  # uint32 [n+1]
+    payload: np.ndarray      # uint8
+
+    @property
+    def payload_bytes(self) -> int:
+        return int(self.payload.size)
+
+    @property
+    def total_bytes(self) -> int:
+        return int(self.widths.size + 2 * self.scales.size + 4 * self.row_offsets.size + self.payload.size)
+
+    def view(self) -> VbqMatrix:
+        return VbqMatrix(ABI_VERSION, self.n, self.k, self.payload_bytes, _np_ptr(self.widths),
+                         _np_ptr(self.scales), _np_ptr(self.row_offsets), _np_ptr(self.payload))
+
+
+def vbq_pack_sizes(n: int, k: int, bits: np.ndarray) -> dict:
+    bits = np.ascontiguousarray(bits, dtype=np.uint8).reshape(-1)
+    out = VbqSizes()
+    _check(lib.vbq_pack_sizes(n, k, _np_ptr(bits), ctypes.byref(out)))
+    return {f: int(getattr(out, f)) for f, _ in VbqSizes._fields_}
+
+
+def vbq_pack(n: int, k: int, bits: np.ndarray, codes: np.ndarray, scales: np.ndarray) -> HostMatrix:
+    """Pack int8 codes [n,k], per-group widths [n,k/64] and binary16 scales [n,k/64]."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint8).reshape(-1)
+    codes = np.ascontiguousarray(codes, dtype=np.int8).reshape(-1)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16).reshape(-1)
+    sz = vbq_pack_sizes(n, k, bits)
+    widths = np.zeros(sz["widths_bytes"], np.uint8)
+    sc = np.zeros(sz["scales_bytes"] // 2, np.uint16)
+    offs = np.zeros(n + 1, np.uint32)
+    payload = np.zeros(sz["payload_bytes"], np.uint8)
+    _check(lib.vbq_pack(n, k, _np_ptr(bits), _np_ptr(codes), _np_ptr(scales), _np_ptr(widths), _np_ptr(sc),
+                        offs.ctypes.data, _np_ptr(payload), payload.size))
+    return HostMatrix(n, k, widths, sc, offs, payload)
+
+
+def vbq_validate_host(m: HostMatrix) -> None:
+    v = m.view()
+    _check(lib.vbq_validate_host(ctypes.byref(v)))
+
+
+# ------------------------------------------------------------------ device side
+
+class DeviceMatrix:
+    """Packed matrix resident in device memory (torch tensors own the bytes)."""
+
+    def __init__(self, host: HostMatrix, device="cuda"):
+        self.n, self.k = host.n, host.k
+        self.payload_bytes = host.payload_bytes
+        self.total_bytes = host.total_bytes
+        dev = torch.device(device)
+        self.device = dev
+
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        self._widths = up(host.widths)
+        self._scales = up(host.scales.view(np.int16))
+        self._offsets = up(host.row_offsets.view(np.int32))
+        self._payload = up(host.payload)
+        self.struct = VbqMatrix(ABI_VERSION, self.n, self.k, self.payload_bytes, self._widths.data_ptr(),
+                                self._scales.data_ptr(), self._offsets.data_ptr(), self._payload.data_ptr())
+
+
+def vbq_gemv(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """y[n] (fp32) = W x (x fp16 [k]); enqueued on `stream` (default: torch's current stream)."""
+    assert x.dtype == torch.float16 and y.dtype == torch.float32
+    assert x.is_contiguous() and y.is_contiguous() and x.numel() == w.k and y.numel() >= w.n
+    _check(lib.vbq_gemv(ctypes.byref(w.struct), x.data_ptr(), y.data_ptr(), _stream_handle(stream, w.device)))
+    return y
+
+
+def vbq_gemm_smallbatch(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """y[m][n] (fp32) = x[m][k] (fp16) W^T, m <= 64."""
+    assert x.dtype == torch.float16 and y.dtype == torch.float32 and x.dim() == 2 and x.shape[1] == w.k
+    assert x.is_contiguous() and y.is_contiguous() and y.numel() >= x.shape[0] * w.n
+    _check(lib.vbq_gemm_smallbatch(ctypes.byref(w.struct), x.data_ptr(), x.shape[0], y.data_ptr(),
+                                   _stream_handle(stream, w.device)))
+    return y
+
+
+def vbq_unpack_codes(w: DeviceMatrix, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Decoded int8 codes [n][k] (device)."""
+    assert out.dtype == torch.int8 and out.is_contiguous() and out.numel() >= w.n * w.k
+    _check(lib.vbq_unpack_codes(ctypes.byref(w.struct), out.data_ptr(), _stream_handle(stream, w.device)))
+    return out

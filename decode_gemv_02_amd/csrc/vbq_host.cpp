@@ -1,0 +1,189 @@
+// Host half of the VBQ library: packing, validation and error reporting.
+//
+// Layout and grid: VBQ paper (arXiv 2607.02893) §3.1 Eq. (1) and §6
+// "Granularity is deployment-friendly"; the byte-level choices are spelled out
+// in include/vbq.h. Everything here runs on the host and is deterministic.
+#include "vbq_internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+inline bool valid_width(uint8_t b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+
+inline uint8_t width_code(uint8_t b) { return b == 1 ? 0 : b == 2 ? 1 : b == 4 ? 2 : 3; }
+
+inline bool half_is_finite(uint16_t h) { return ((h >> 10) & 0x1F) != 0x1F; }
+
+// b-bit field for code q (two's complement for b >= 2, sign bit for b = 1)
+inline uint32_t encode_field(int q, uint32_t b) {
+    if (b == 1) return q < 0 ? 1u : 0u;
+    return static_cast<uint32_t>(q) & ((1u << b) - 1u);
+}
+
+inline bool on_grid(int q, uint32_t b) {
+    if (b == 1) return q == 1 || q == -1;
+    const int lim = (1 << (b - 1)) - 1;
+    return q >= -lim && q <= lim;
+}
+
+}  // namespace
+
+namespace vbq {
+
+vbq_status fail(vbq_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+}  // namespace vbq
+
+using vbq::fail;
+
+extern "C" uint32_t vbq_abi_version(void) { return VBQ_ABI_VERSION; }
+
+extern "C" const char *vbq_status_string(vbq_status s) {
+    switch (s) {
+        case VBQ_OK: return "ok";
+        case VBQ_ERR_NULL: return "null pointer";
+        case VBQ_ERR_SHAPE: return "bad shape";
+        case VBQ_ERR_WIDTH: return "width not in {1,2,4,8}";
+        case VBQ_ERR_CODE: return "code off its width's grid";
+        case VBQ_ERR_SCALE: return "non-finite scale";
+        case VBQ_ERR_CAPACITY: return "payload capacity too small";
+        case VBQ_ERR_OFFSETS: return "row offsets inconsistent with widths";
+        case VBQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+        case VBQ_ERR_TOO_LARGE: return "payload exceeds 32-bit offsets";
+        case VBQ_ERR_HIP: return "HIP runtime error";
+        case VBQ_ERR_ABI: return "ABI version mismatch";
+    }
+    return "unknown status";
+}
+
+extern "C" const char *vbq_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" vbq_status vbq_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits, vbq_sizes *out) {
+    vbq::clear_error();
+    if (!out) return fail(VBQ_ERR_NULL, "vbq_pack_sizes: out is NULL");
+    if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_pack_sizes: k=%u is not a multiple of 64", k);
+    const uint64_t groups = uint64_t(n) * (k / VBQ_GROUP);
+    if (groups && !bits) return fail(VBQ_ERR_NULL, "vbq_pack_sizes: bits is NULL");
+    uint64_t payload = 0;
+    for (uint64_t t = 0; t < groups; ++t) {
+        if (!valid_width(bits[t]))
+            return fail(VBQ_ERR_WIDTH, "vbq_pack_sizes: group %llu has width %u", (unsigned long long)t, bits[t]);
+        payload += 8u * bits[t];
+    }
+    if (payload > 0xFFFFFFFFull)
+        return fail(VBQ_ERR_TOO_LARGE, "vbq_pack_sizes: payload %llu B exceeds 32-bit offsets",
+                    (unsigned long long)payload);
+    out->widths_bytes = (groups + 3) / 4;
+    out->scales_bytes = 2 * groups;
+    out->offsets_bytes = 4 * (uint64_t(n) + 1);
+    out->payload_bytes = payload;
+    out->total_bytes = out->widths_bytes + out->scales_bytes + out->offsets_bytes + out->payload_bytes;
+    return VBQ_OK;
+}
+
+extern "C" vbq_status vbq_pack(uint32_t n, uint32_t k, const uint8_t *bits, const int8_t *codes,
+                               const uint16_t *scales, uint8_t *widths_out, uint16_t *scales_out,
+                               uint32_t *row_offsets_out, uint8_t *payload_out, uint64_t payload_capacity) {
+    vbq_sizes sz;
+    vbq_status st = vbq_pack_sizes(n, k, bits, &sz);
+    if (st != VBQ_OK) return st;
+    const uint32_t G = k / VBQ_GROUP;
+    const uint64_t groups = uint64_t(n) * G;
+    if (!row_offsets_out) return fail(VBQ_ERR_NULL, "vbq_pack: row_offsets_out is NULL");
+    if (groups && (!codes || !scales || !widths_out || !scales_out))
+        return fail(VBQ_ERR_NULL, "vbq_pack: codes, scales, widths_out or scales_out is NULL");
+    if (sz.payload_bytes && !payload_out) return fail(VBQ_ERR_NULL, "vbq_pack: payload_out is NULL");
+    if (sz.payload_bytes > payload_capacity)
+        return fail(VBQ_ERR_CAPACITY, "vbq_pack: payload needs %llu B, capacity %llu B",
+                    (unsigned long long)sz.payload_bytes, (unsigned long long)payload_capacity);
+    // validate everything before the first write
+    for (uint64_t t = 0; t < groups; ++t) {
+        if (!half_is_finite(scales[t]))
+            return fail(VBQ_ERR_SCALE, "vbq_pack: scale of group %llu is 0x%04x (not finite)",
+                        (unsigned long long)t, scales[t]);
+        const int8_t *q = codes + t * VBQ_GROUP;
+        for (uint32_t i = 0; i < VBQ_GROUP; ++i)
+            if (!on_grid(q[i], bits[t]))
+                return fail(VBQ_ERR_CODE, "vbq_pack: code %d at group %llu element %u is off the %u-bit grid",
+                            q[i], (unsigned long long)t, i, bits[t]);
+    }
+    std::memset(widths_out, 0, sz.widths_bytes);
+    if (sz.payload_bytes) std::memset(payload_out, 0, sz.payload_bytes);
+    uint64_t pos = 0;
+    row_offsets_out[0] = 0;
+    for (uint32_t r = 0; r < n; ++r) {
+        for (uint32_t j = 0; j < G; ++j) {
+            const uint64_t t = uint64_t(r) * G + j;
+            const uint32_t b = bits[t];
+            widths_out[t >> 2] |= uint8_t(width_code(uint8_t(b)) << (2 * (t & 3)));
+            scales_out[t] = scales[t];
+            const int8_t *q = codes + t * VBQ_GROUP;
+            uint8_t *dst = payload_out + pos;
+            // whole fields never straddle a byte because b divides 8
+            for (uint32_t i = 0; i < VBQ_GROUP; ++i) {
+                const uint32_t bit = b * i;
+                dst[bit >> 3] |= uint8_t(encode_field(q[i], b) << (bit & 7));
+            }
+            pos += 8u * b;
+        }
+        row_offsets_out[r + 1] = uint32_t(pos);
+    }
+    return VBQ_OK;
+}
+
+extern "C" vbq_status vbq_validate_host(const vbq_matrix *w) {
+    vbq::clear_error();
+    if (!w) return fail(VBQ_ERR_NULL, "vbq_validate_host: view is NULL");
+    if (w->abi_version != VBQ_ABI_VERSION)
+        return fail(VBQ_ERR_ABI, "vbq_validate_host: abi_version %u, library %u", w->abi_version, VBQ_ABI_VERSION);
+    if (w->k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_validate_host: k=%u is not a multiple of 64", w->k);
+    const uint32_t G = w->k / VBQ_GROUP;
+    const uint64_t groups = uint64_t(w->n) * G;
+    if (!w->row_offsets) return fail(VBQ_ERR_NULL, "vbq_validate_host: row_offsets is NULL");
+    if (groups && (!w->widths || !w->scales || !w->payload))
+        return fail(VBQ_ERR_NULL, "vbq_validate_host: widths, scales or payload is NULL");
+    if (w->row_offsets[0] != 0) return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: row_offsets[0] != 0");
+    uint64_t pos = 0;
+    for (uint32_t r = 0; r < w->n; ++r) {
+        for (uint32_t j = 0; j < G; ++j) {
+            const uint64_t t = uint64_t(r) * G + j;
+            const uint32_t b = 1u << ((w->widths[t >> 2] >> (2 * (t & 3))) & 3);
+            if (!half_is_finite(w->scales[t]))
+                return fail(VBQ_ERR_SCALE, "vbq_validate_host: scale of group %llu not finite", (unsigned long long)t);
+            if (b >= 2 && pos + 8u * b <= w->payload_bytes) {
+                const uint8_t *src = w->payload + pos;
+                for (uint32_t i = 0; i < VBQ_GROUP; ++i) {
+                    const uint32_t bit = b * i;
+                    const uint32_t f = (src[bit >> 3] >> (bit & 7)) & ((1u << b) - 1u);
+                    if (f == (1u << (b - 1)))
+                        return fail(VBQ_ERR_CODE, "vbq_validate_host: reserved pattern at group %llu element %u",
+                                    (unsigned long long)t, i);
+                }
+            }
+            pos += 8u * b;
+        }
+        if (w->row_offsets[r + 1] != pos)
+            return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: row_offsets[%u]=%u, widths give %llu", r + 1,
+                        w->row_offsets[r + 1], (unsigned long long)pos);
+    }
+    if (pos != w->payload_bytes)
+        return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: payload_bytes=%u, widths give %llu", w->payload_bytes,
+                    (unsigned long long)pos);
+    return VBQ_OK;
+}

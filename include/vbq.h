@@ -1,0 +1,160 @@
+/*
+ * vbq.h - C ABI of the VBQ packed-weight decode library for AMD MI355X (gfx950).
+ *
+ * Method: "Variable Bit-width Quantization: Learning Per-Group Precision for
+ * 'Bigger-but-Smaller' Language Models" (arXiv 2607.02893).
+ *   §3.1, Eq. (1): weights are quantised in contiguous groups of 64 along the
+ *     contracted dimension; group g has a width b_g and a scale s_g, and the
+ *     dequantised weight is s_g * q with q on the symmetric integer grid
+ *     |q| <= 2^(b-1) - 1; the 1-bit case is sign * scale (q in {-1, +1}).
+ *   §6, "Fused kernels over packed weights": decode reads each group's packed
+ *     bytes, expands them in registers with the group's scale and accumulates
+ *     y = W x without writing a dense matrix; "Granularity is
+ *     deployment-friendly": widths come from {1, 2, 4, 8} and groups pack into
+ *     whole bytes.
+ *
+ * Packed layout (what the paper leaves open is fixed here):
+ *   W is n x k, row-major, k % 64 == 0, G = k / 64 groups per row; flat group
+ *   index t = r*G + j covers W[r][64j .. 64j+63].
+ *   widths      uint8 [ceil(n*G/4)]  2-bit code c_t = (widths[t/4] >> 2*(t%4)) & 3,
+ *                                    width b_t = 1 << c_t in {1, 2, 4, 8}.
+ *   scales      uint16 [n*G]         IEEE binary16 bit pattern of s_t.
+ *   row_offsets uint32 [n+1]         exclusive prefix sum of the group payload
+ *                                    sizes 8*b_t, sampled at row starts:
+ *                                    row_offsets[0] = 0, row_offsets[r+1] =
+ *                                    row_offsets[r] + sum_j 8*b_{r,j}.
+ *   payload     uint8 [row_offsets[n]]  group (r, j) occupies 8*b bytes at
+ *                                    row_offsets[r] + sum_{j'<j} 8*b_{r,j'};
+ *                                    element i is the b-bit field at bit b*i of
+ *                                    those bytes, little-endian (byte b*i/8,
+ *                                    bit b*i%8).
+ *   field f -> code q: b = 1: f is a sign bit (0 -> +1, 1 -> -1).
+ *                      b >= 2: two's complement; -2^(b-1) is off the grid and
+ *                      rejected by vbq_pack (kernels read it as -2^(b-1)).
+ *   Result: y[m][r] = sum_j s_{r,j} * sum_i q_{r,j,i} * x[m][64j+i], with
+ *   exact fp16 codes, fp32 products and sums, and the scale applied in fp32
+ *   once per group. y is fp32.
+ *
+ * Conventions for every entry point:
+ *   - All buffers belong to the caller. Host entry points (vbq_pack*,
+ *     vbq_validate_host) take host pointers and run synchronously. Device
+ *     entry points take device pointers inside vbq_matrix and as arguments,
+ *     enqueue work on `stream` (a hipStream_t passed as void*, NULL = the
+ *     null stream) and return without waiting; results are visible after the
+ *     stream is synchronised.
+ *   - A non-VBQ_OK status means nothing was written and nothing was enqueued;
+ *     vbq_last_error() then holds a one-line description (thread-local).
+ *   - Device entry points trust the metadata (use vbq_validate_host on the
+ *     host copy once after packing); they check shapes, pointers, alignment
+ *     and the ABI version.
+ *   - Alignment: x, y and every vbq_matrix array 16-byte aligned (device
+ *     allocators return 256-byte aligned memory).
+ */
+#ifndef VBQ_H
+#define VBQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Only the entry points below are exported from the shared library. */
+#define VBQ_API __attribute__((visibility("default")))
+
+#define VBQ_ABI_VERSION 1u
+#define VBQ_GROUP 64u
+#define VBQ_MAX_K 65536u      /* k limit of the device entry points */
+#define VBQ_MAX_BATCH 64u     /* m limit of vbq_gemm_smallbatch */
+
+typedef enum vbq_status {
+    VBQ_OK = 0,
+    VBQ_ERR_NULL = 1,       /* a required pointer is NULL */
+    VBQ_ERR_SHAPE = 2,      /* k % 64 != 0, k > VBQ_MAX_K (device), m == 0 or m > VBQ_MAX_BATCH */
+    VBQ_ERR_WIDTH = 3,      /* a width is not 1, 2, 4 or 8 */
+    VBQ_ERR_CODE = 4,       /* a code is off its width's grid */
+    VBQ_ERR_SCALE = 5,      /* a scale is inf or NaN */
+    VBQ_ERR_CAPACITY = 6,   /* payload_capacity is smaller than the packed payload */
+    VBQ_ERR_OFFSETS = 7,    /* row_offsets / payload_bytes disagree with the widths */
+    VBQ_ERR_ALIGN = 8,      /* a device pointer is not 16-byte aligned */
+    VBQ_ERR_TOO_LARGE = 9,  /* payload would not fit 32-bit offsets */
+    VBQ_ERR_HIP = 10,       /* the HIP runtime refused a launch */
+    VBQ_ERR_ABI = 11        /* vbq_matrix.abi_version != VBQ_ABI_VERSION */
+} vbq_status;
+
+/* Byte sizes of the four packed arrays. */
+typedef struct vbq_sizes {
+    uint64_t widths_bytes;
+    uint64_t scales_bytes;
+    uint64_t offsets_bytes;
+    uint64_t payload_bytes;
+    uint64_t total_bytes;   /* = sum of the four; the bytes one GEMV must stream for W */
+} vbq_sizes;
+
+/* Non-owning view of one packed matrix. The struct itself lives in host
+ * memory; the array pointers are host pointers for host entry points and
+ * device pointers for device entry points. */
+typedef struct vbq_matrix {
+    uint32_t abi_version;          /* VBQ_ABI_VERSION */
+    uint32_t n;                    /* rows (outputs) */
+    uint32_t k;                    /* columns (inputs), multiple of 64 */
+    uint32_t payload_bytes;        /* == row_offsets[n] */
+    const uint8_t *widths;
+    const uint16_t *scales;
+    const uint32_t *row_offsets;
+    const uint8_t *payload;
+} vbq_matrix;
+
+/* Library ABI version (compare with VBQ_ABI_VERSION). */
+VBQ_API uint32_t vbq_abi_version(void);
+
+/* Sizes of the packed arrays for an n x k matrix with per-group widths
+ * bits[n*(k/64)] (host). Errors: NULL, SHAPE (k % 64), WIDTH, TOO_LARGE.
+ * Layout: §3.1 (groups of 64) and §6 (whole-byte groups of {1,2,4,8} bits). */
+VBQ_API vbq_status vbq_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits, vbq_sizes *out);
+
+/* Pack integer codes into the layout above (host, single-threaded,
+ * deterministic). bits: [n*G] widths; codes: int8 [n][k] on each group's grid
+ * (§3.1 Eq. (1): |q| <= 2^(b-1)-1, b = 1: q = +-1); scales: binary16 [n*G],
+ * finite. Output arrays sized by vbq_pack_sizes; payload_capacity is the size
+ * of payload_out in bytes. Every input is checked before anything is written:
+ * NULL, SHAPE, WIDTH, CODE, SCALE, CAPACITY, TOO_LARGE. */
+VBQ_API vbq_status vbq_pack(uint32_t n, uint32_t k, const uint8_t *bits, const int8_t *codes,
+                    const uint16_t *scales, uint8_t *widths_out, uint16_t *scales_out,
+                    uint32_t *row_offsets_out, uint8_t *payload_out, uint64_t payload_capacity);
+
+/* Check a packed matrix held in host memory: k % 64, row_offsets equal to the
+ * prefix sum of 8*b, payload_bytes == row_offsets[n], every field on its
+ * grid, every scale finite. Errors: NULL, ABI, SHAPE, OFFSETS, CODE, SCALE. */
+VBQ_API vbq_status vbq_validate_host(const vbq_matrix *host_view);
+
+/* y = W x for one fp16 vector (§6 fused decode at batch 1).
+ * w: device view; x: device binary16 [k]; y: device fp32 [n] (overwritten).
+ * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (k > VBQ_MAX_K), ALIGN,
+ * HIP. n == 0 enqueues nothing; k == 0 writes y = 0. */
+VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream);
+
+/* Y = X W^T for m <= VBQ_MAX_BATCH fp16 vectors (small-batch decode).
+ * x: device binary16 [m][k] row-major; y: device fp32 [m][n] row-major
+ * (overwritten). m >= 16 runs on the MFMA matrix cores, smaller m on the
+ * vector units. Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, HIP. */
+VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
+                               void *stream);
+
+/* Decoded integer codes int8 [n][k] of a device matrix, produced with the
+ * same in-register field decoding the GEMV and GEMM kernels use (a test and
+ * inspection hook; §3.1 Eq. (1) grid). Asynchronous. Errors: NULL, ABI,
+ * SHAPE, ALIGN, HIP. */
+VBQ_API vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, void *stream);
+
+/* Static English name of a status. */
+VBQ_API const char *vbq_status_string(vbq_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+VBQ_API const char *vbq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VBQ_H */

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bars (per output vector): relative L2 error <= 1e-3 and max abs error <=
+2e-3 * ||x||_2 * max|scale|; decoded codes bit-exact. Inputs are the seeded
+synthetic draws of workloads.py; the library packs with its own packer, the
+oracle with its own, and the two byte streams are compared too.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.conftest import gpu_available
+from tests.helpers import assert_within_tolerance, make_case, xf64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def V():
+    import torch  # noqa: F401
+    import decode_gemv_02_amd as V
+    return V
+
+
+@pytest.fixture(scope="module")
+def torch_mod():
+    import torch
+    return torch
+
+
+def upload(V, bits, codes, scales):
+    n, k = codes.shape
+    h = V.vbq_pack(n, k, bits, codes, scales)
+    return h, V.DeviceMatrix(h)
+
+
+def gpu_gemm(V, torch, dm, x_bits):
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.float16)).cuda()
+    m = x.shape[0]
+    y = torch.full((m, dm.n), float("nan"), dtype=torch.float32, device="cuda")
+    if m == 1:
+        V.vbq_gemv(dm, x[0], y[0])
+    else:
+        V.vbq_gemm_smallbatch(dm, x, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def print_case(**kw):
+    print("CASE", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+# ------------------------------------------------------------------ runtime sanity
+
+def test_one_hip_runtime_mapped(V, torch_mod):
+    torch_mod.zeros(1, device="cuda")
+    maps = open("/proc/self/maps").read().splitlines()
+    libs = {line.split()[-1] for line in maps if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+    assert any(V.LIB_PATH in line for line in maps)
+
+
+# ------------------------------------------------------------------ decoded codes
+
+@pytest.mark.parametrize("n,k,mix", [(1, 64, W.STD_MIX), (7, 192, W.FIRST_MLP_MIX), (129, 768, W.STD_MIX),
+                                     (33, 4160, {1: 0.25, 2: 0.25, 4: 0.25, 8: 0.25}), (5, 128, {8: 1.0}),
+                                     (5, 128, {1: 1.0})])
+def test_unpack_codes_bit_exact(V, torch_mod, n, k, mix):
+    print_case(test="unpack", n=n, k=k)
+    bits, codes, scales, p = make_case((n, k, 1), n, k, mix)
+    h, dm = upload(V, bits, codes, scales)
+    assert h.payload.tobytes() == p.payload.tobytes()
+    out = torch_mod.full((n, k), 99, dtype=torch_mod.int8, device="cuda")
+    V.vbq_unpack_codes(dm, out)
+    torch_mod.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got, oracle.unpack(p))
+    assert np.array_equal(got, codes)
+
+
+# ------------------------------------------------------------------ GEMV / GEMM, small shapes with ragged tails
+
+SHAPES = [(1, 64), (3, 128), (17, 768), (64, 192), (255, 1024), (1000, 448), (130, 4096 + 64), (9, 14336),
+          (40, 65536)]
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_gemv_matches_oracle(V, torch_mod, n, k):
+    print_case(test="gemv", n=n, k=k)
+    bits, codes, scales, p = make_case((n, k, 2), n, k, W.FIRST_MLP_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x((n, k, 3), k)
+    y = gpu_gemm(V, torch_mod, dm, x)
+    assert_within_tolerance(y, oracle.gemm(p, x), x, scales, f"gemv {n}x{k}")
+
+
+@pytest.mark.parametrize("m", [2, 3, 8, 15, 16, 17, 31, 48, 63, 64])
+def test_gemm_matches_oracle(V, torch_mod, m):
+    n, k = 97, 1088
+    print_case(test="gemm", n=n, k=k, m=m)
+    bits, codes, scales, p = make_case((m, 4), n, k, W.STD_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x((m, 5), k, m)
+    assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"gemm m={m}")
+
+
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+def test_single_width_matrices(V, torch_mod, b):
+    n, k = 77, 960
+    print_case(test="single_width", b=b)
+    bits, codes, scales, p = make_case((b, 6), n, k, {b: 1.0})
+    h, dm = upload(V, bits, codes, scales)
+    for m in (1, 5, 16):
+        x = W.draw_x((b, m, 7), k, m)
+        assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"b={b} m={m}")
+
+
+def test_one_hot_x_returns_dequantised_column(V, torch_mod):
+    # s*q has at most 18 significant bits, so the product with 1.0 and the sum of zeros are exact in fp32
+    n, k = 50, 512
+    bits, codes, scales, p = make_case(8, n, k, W.FIRST_MLP_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    wd = codes.astype(np.float64).reshape(n, k // 64, 64) * xf64(scales)[:, :, None]
+    for col in (0, 37, 64, 511):
+        x = np.zeros((1, k), np.float16)
+        x[0, col] = 1.0
+        y = gpu_gemm(V, torch_mod, dm, x.view(np.uint16))
+        assert np.array_equal(y[0], wd.reshape(n, k)[:, col])
+
+
+def test_edge_values(V, torch_mod):
+    n, k = 60, 640
+    bits, codes, scales = W.draw_random_matrix(9, n, k, W.STD_MIX)
+    scales = scales.copy()
+    scales.reshape(-1)[::7] = 0               # zero scales
+    scales.reshape(-1)[3::11] = 0x0001        # smallest subnormal
+    scales.reshape(-1)[5::13] = 0x03FF        # largest subnormal
+    scales.reshape(-1)[1::17] = 0x7BFF        # largest finite
+    p = oracle.pack(n, k, bits, codes, scales)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x(10, k)
+    xs = x.copy()
+    xs.reshape(-1)[::5] = 0x0003              # subnormal x
+    xs.reshape(-1)[2::9] = 0
+    for xx in (x, xs, np.zeros_like(x)):
+        y = gpu_gemm(V, torch_mod, dm, xx)
+        ref = oracle.gemm(p, xx)
+        if not np.any(ref):
+            assert np.all(y == 0)
+        else:
+            assert_within_tolerance(y, ref, xx, scales, "edge values")
+
+
+def test_empty_shapes(V, torch_mod):
+    torch = torch_mod
+    h, dm = upload(V, np.zeros((0, 2), np.uint8), np.zeros((0, 128), np.int8), np.zeros((0, 2), np.uint16))
+    y = torch.zeros(4, device="cuda")
+    V.vbq_gemv(dm, torch.zeros(128, dtype=torch.float16, device="cuda"), y)
+    h, dm = upload(V, np.zeros((5, 0), np.uint8), np.zeros((5, 0), np.int8), np.zeros((5, 0), np.uint16))
+    y = torch.full((3, 5), 7.0, device="cuda")
+    V.vbq_gemm_smallbatch(dm, torch.zeros((3, 0), dtype=torch.float16, device="cuda"), y)
+    torch.cuda.synchronize()
+    assert torch.all(y == 0)
+
+
+def test_deterministic_and_stream_aware(V, torch_mod):
+    torch = torch_mod
+    n, k = 2048, 4096
+    bits, codes, scales, p = make_case(11, n, k, W.STD_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    x = torch.from_numpy(W.draw_x(12, k)[0].view(np.float16)).cuda()
+    y1 = torch.empty(n, device="cuda")
+    y2 = torch.empty(n, device="cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        V.vbq_gemv(dm, x, y1)
+    V.vbq_gemv(dm, x, y2, stream=s)
+    s.synchronize()
+    assert torch.equal(y1, y2)
+    assert_within_tolerance(y1.cpu().numpy(), oracle.gemv(p, W.draw_x(12, k)), W.draw_x(12, k), scales, "stream")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled rows
+
+def sample_rows(n, count=192):
+    idx = np.unique(np.concatenate([np.arange(min(n, 64)), np.linspace(0, n - 1, count).astype(int),
+                                    np.arange(max(0, n - 64), n)]))
+    return idx
+
+
+def _config_matrices(cid):
+    cfg = W.config(cid)
+    if cid == 2:       # layer 0 (its own MLP mix) and layer 1 cover every shape and mix
+        return cfg, [m for m in cfg.matrices if m.layer in (0, 1)]
+    if cid == 3:       # one layer covers every shape; the rest differ only in seeds
+        return cfg, [m for m in cfg.matrices if m.layer == 0]
+    return cfg, cfg.matrices
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cid", W.ALL_CONFIGS)
+def test_full_size_workloads(V, torch_mod, cid):
+    cfg, mats = _config_matrices(cid)
+    for spec in mats:
+        bits, codes, scales = W.draw_matrix(spec)
+        p = oracle.pack(spec.n, spec.k, bits, codes, scales)
+        h, dm = upload(V, bits, codes, scales)
+        assert h.payload.tobytes() == p.payload.tobytes()
+        rows = sample_rows(spec.n)
+        for m in cfg.batches:
+            print_case(test="full", cfg=cfg.name, mat=spec.name, n=spec.n, k=spec.k, m=m)
+            x = W.draw_x(W.x_seed(spec), spec.k, m)
+            y = gpu_gemm(V, torch_mod, dm, x)
+            ref = np.stack([np.concatenate([oracle.gemm(p, x[i:i + 1], rows=(int(r), int(r) + 1))[0, r:r + 1]
+                                            for r in rows]) for i in range(m)])
+            assert_within_tolerance(y[:, rows], ref, x, scales, f"{cfg.name}/{spec.name} m={m}")
+        out = torch_mod.empty((spec.n, spec.k), dtype=torch_mod.int8, device="cuda")
+        V.vbq_unpack_codes(dm, out)
+        torch_mod.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), codes), f"{cfg.name}/{spec.name} codes"
+        del dm, out

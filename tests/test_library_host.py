@@ -1,0 +1,175 @@
+"""CPU checks of the C-ABI library: exported symbols, host packer and validator.
+
+No device work runs here. The packer is compared byte for byte with the
+oracle's independent packer; the validator and every error path are driven
+from the host.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vbq.h")
+
+
+@pytest.fixture(scope="module")
+def V():
+    import decode_gemv_02_amd as V
+    return V
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"VBQ_API\s+[\w\s\*]*?\b(vbq_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted([
+        "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_validate_host", "vbq_gemv",
+        "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_status_string", "vbq_last_error"])
+
+
+def test_library_exports_every_declared_symbol(V):
+    raw = ctypes.CDLL(V.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+    assert raw.vbq_abi_version() == V.ABI_VERSION
+
+
+def test_library_exports_nothing_else(V):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", V.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines() if " T " in line)
+    assert exported == declared_functions()
+
+
+def test_status_strings(V):
+    for s in range(12):
+        assert V.lib.vbq_status_string(s).decode()
+    assert V.lib.vbq_status_string(0).decode() == "ok"
+
+
+@settings(max_examples=40, deadline=None)
+@given(st.integers(0, 12), st.integers(0, 10).map(lambda g: 64 * g), st.integers(0, 2**31 - 1),
+       st.sampled_from([W.STD_MIX, W.FIRST_MLP_MIX, W.HEAD_MIX, {1: 1.0}, {2: 1.0}, {4: 1.0}, {8: 1.0},
+                        {1: 0.5, 8: 0.5}]))
+def test_pack_is_byte_identical_to_oracle(V, n, k, seed, mix):
+    bits, codes, scales = W.draw_random_matrix(seed, n, k, mix)
+    h = V.vbq_pack(n, k, bits, codes, scales)
+    p = oracle.pack(n, k, bits, codes, scales)
+    assert h.widths.tobytes() == p.widths.tobytes()
+    assert h.scales.tobytes() == p.scales.tobytes()
+    assert h.row_offsets.tobytes() == p.row_offsets.tobytes()
+    assert h.payload.tobytes() == p.payload.tobytes()
+    sz = V.vbq_pack_sizes(n, k, bits)
+    assert sz["total_bytes"] == h.total_bytes == p.total_bytes
+    V.vbq_validate_host(h)
+
+
+def test_pack_rejections(V):
+    bits, codes, scales = W.draw_random_matrix(3, 2, 128)
+    with pytest.raises(V.VbqError) as e:
+        V.vbq_pack_sizes(2, 100, np.ones(4, np.uint8))
+    assert e.value.status == V.ERR_SHAPE
+    b2 = bits.copy()
+    b2[0, 1] = 5
+    with pytest.raises(V.VbqError) as e:
+        V.vbq_pack(2, 128, b2, codes, scales)
+    assert e.value.status == V.ERR_WIDTH
+    for b, bad in ((1, 0), (2, -2), (4, 8), (8, -128)):
+        bb = np.full((1, 1), b, np.uint8)
+        cc = np.ones((1, 64), np.int8)
+        cc[0, 5] = bad
+        with pytest.raises(V.VbqError) as e:
+            V.vbq_pack(1, 64, bb, cc, np.full((1, 1), 0x3C00, np.uint16))
+        assert e.value.status == V.ERR_CODE, (b, bad)
+    s2 = scales.copy()
+    s2[1, 0] = 0x7C00
+    with pytest.raises(V.VbqError) as e:
+        V.vbq_pack(2, 128, bits, codes, s2)
+    assert e.value.status == V.ERR_SCALE
+
+
+def test_pack_capacity_and_null(V):
+    bits, codes, scales = W.draw_random_matrix(4, 3, 128)
+    sz = V.vbq_pack_sizes(3, 128, bits)
+    widths = np.zeros(sz["widths_bytes"], np.uint8)
+    sc = np.zeros(sz["scales_bytes"] // 2, np.uint16)
+    offs = np.zeros(4, np.uint32)
+    payload = np.full(sz["payload_bytes"], 0xAB, np.uint8)
+    b, c, s = (np.ascontiguousarray(a) for a in (bits, codes, scales))
+    st_ = V.lib.vbq_pack(3, 128, b.ctypes.data, c.ctypes.data, s.ctypes.data, widths.ctypes.data, sc.ctypes.data,
+                         offs.ctypes.data, payload.ctypes.data, payload.size - 1)
+    assert st_ == V.ERR_CAPACITY
+    assert np.all(payload == 0xAB) and np.all(offs == 0)      # nothing written
+    st_ = V.lib.vbq_pack(3, 128, b.ctypes.data, None, s.ctypes.data, widths.ctypes.data, sc.ctypes.data,
+                         offs.ctypes.data, payload.ctypes.data, payload.size)
+    assert st_ == V.ERR_NULL
+    assert "NULL" in V.lib.vbq_last_error().decode()
+
+
+def test_validate_host_catches_corruption(V):
+    bits, codes, scales = W.draw_random_matrix(5, 4, 256, W.FIRST_MLP_MIX)
+    h = V.vbq_pack(4, 256, bits, codes, scales)
+    V.vbq_validate_host(h)
+    bad = V.HostMatrix(h.n, h.k, h.widths, h.scales, h.row_offsets.copy(), h.payload)
+    bad.row_offsets[2] += 8
+    with pytest.raises(V.VbqError) as e:
+        V.vbq_validate_host(bad)
+    assert e.value.status == V.ERR_OFFSETS
+    bad = V.HostMatrix(h.n, h.k, h.widths, h.scales.copy(), h.row_offsets, h.payload)
+    bad.scales[3] = 0x7E00
+    with pytest.raises(V.VbqError) as e:
+        V.vbq_validate_host(bad)
+    assert e.value.status == V.ERR_SCALE
+    # plant a reserved 8-bit pattern (0x80) inside an 8-bit group
+    t8 = np.flatnonzero(bits.reshape(-1) == 8)
+    if t8.size:
+        t = int(t8[0])
+        r, j = divmod(t, 4)
+        start = int(h.row_offsets[r]) + int((8 * bits[r, :j].astype(int)).sum())
+        bad = V.HostMatrix(h.n, h.k, h.widths, h.scales, h.row_offsets, h.payload.copy())
+        bad.payload[start + 7] = 0x80
+        with pytest.raises(V.VbqError) as e:
+            V.vbq_validate_host(bad)
+        assert e.value.status == V.ERR_CODE
+    v = h.view()
+    v.abi_version = 99
+    assert V.lib.vbq_validate_host(ctypes.byref(v)) == V.ERR_ABI
+
+
+def test_device_entry_points_reject_bad_arguments_without_launching(V):
+    # every check below fails before any HIP call, so this runs without a GPU
+    h = V.vbq_pack(*(lambda b, c, s: (2, 128, b, c, s))(*W.draw_random_matrix(6, 2, 128)))
+    v = h.view()
+    buf = np.zeros(4096, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    assert V.lib.vbq_gemv(None, base, base, None) == V.ERR_NULL
+    v2 = h.view()
+    v2.abi_version = 2
+    assert V.lib.vbq_gemv(ctypes.byref(v2), base, base, None) == V.ERR_ABI
+    v3 = h.view()
+    v3.k = 100
+    assert V.lib.vbq_gemv(ctypes.byref(v3), base, base, None) == V.ERR_SHAPE
+    v4 = h.view()
+    v4.k = 65536 + 64
+    assert V.lib.vbq_gemv(ctypes.byref(v4), base, base, None) == V.ERR_SHAPE
+    assert V.lib.vbq_gemm_smallbatch(ctypes.byref(v), base, 0, base, None) == V.ERR_SHAPE
+    assert V.lib.vbq_gemm_smallbatch(ctypes.byref(v), base, 65, base, None) == V.ERR_SHAPE
+    aligned = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
+    assert V.lib.vbq_gemv(ctypes.byref(aligned), base + 8, base, None) == V.ERR_ALIGN
+    assert V.lib.vbq_gemv(ctypes.byref(aligned), base, base + 4, None) == V.ERR_ALIGN
+    assert V.lib.vbq_gemv(ctypes.byref(aligned), None, base, None) == V.ERR_NULL
+    mis = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base + 8)
+    assert V.lib.vbq_gemv(ctypes.byref(mis), base, base, None) == V.ERR_ALIGN
+    assert V.lib.vbq_unpack_codes(ctypes.byref(aligned), None, None) == V.ERR_NULL
+    assert V.lib.vbq_unpack_codes(ctypes.byref(aligned), base + 1, None) == V.ERR_ALIGN
+    empty = V.VbqMatrix(1, 0, 128, 0, None, None, None, None)
+    assert V.lib.vbq_gemv(ctypes.byref(empty), None, None, None) == V.OK    # n == 0: nothing to do
