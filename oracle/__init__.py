@@ -76,7 +76,7 @@ class Packed:
     k: int
     widths: np.ndarray       # uint8
     scales: np.ndarray       # uint16 (binary16 bits)
-    row_offsets: np.ndarray  # uint32 [n+1]
+    tile_offsets: np.ndarray  # uint32 [tiles+1]
     payload: np.ndarray      # uint8
 
     @property
@@ -85,7 +85,7 @@ class Packed:
 
     @property
     def total_bytes(self) -> int:
-        return int(self.widths.size + 2 * self.scales.size + 4 * self.row_offsets.size + self.payload.size)
+        return int(self.widths.size + 2 * self.scales.size + 4 * self.tile_offsets.size + self.payload.size)
 
 
 def half_to_double(h: int, lib=None) -> float:
@@ -99,7 +99,7 @@ def pack_sizes(n: int, k: int, bits: np.ndarray, lib=None) -> dict:
     st = lib.oracle_pack_sizes(n, k, _p(bits, _u8p), _p(out, _u64p))
     if st:
         raise OracleError(st, "pack_sizes")
-    return dict(zip(("widths", "scales", "row_offsets", "payload", "total"), (int(v) for v in out)))
+    return dict(zip(("widths", "scales", "tile_offsets", "payload", "total"), (int(v) for v in out)))
 
 
 def pack(n: int, k: int, bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, lib=None) -> Packed:
@@ -110,7 +110,7 @@ def pack(n: int, k: int, bits: np.ndarray, codes: np.ndarray, scales: np.ndarray
     sz = pack_sizes(n, k, bits, lib)
     widths = np.zeros(sz["widths"], dtype=np.uint8)
     sc = np.zeros(sz["scales"] // 2, dtype=np.uint16)
-    offs = np.zeros(n + 1, dtype=np.uint32)
+    offs = np.zeros(sz["tile_offsets"] // 4, dtype=np.uint32)
     payload = np.zeros(sz["payload"], dtype=np.uint8)
     st = lib.oracle_pack(n, k, _p(bits, _u8p), _p(codes, _i8p), _p(scales, _u16p), _p(widths, _u8p),
                          _p(sc, _u16p), _p(offs, _u32p), _p(payload, _u8p), sz["payload"])
@@ -121,13 +121,13 @@ def pack(n: int, k: int, bits: np.ndarray, codes: np.ndarray, scales: np.ndarray
 
 def check_offsets(p: Packed, lib=None) -> int:
     lib = lib or load()
-    return lib.oracle_check_offsets(p.n, p.k, _p(p.widths, _u8p), _p(p.row_offsets, _u32p), p.payload_bytes)
+    return lib.oracle_check_offsets(p.n, p.k, _p(p.widths, _u8p), _p(p.tile_offsets, _u32p), p.payload_bytes)
 
 
 def unpack(p: Packed, lib=None) -> np.ndarray:
     lib = lib or load()
     out = np.zeros((p.n, p.k), dtype=np.int8)
-    st = lib.oracle_unpack(p.n, p.k, _p(p.widths, _u8p), _p(p.row_offsets, _u32p), _p(p.payload, _u8p),
+    st = lib.oracle_unpack(p.n, p.k, _p(p.widths, _u8p), _p(p.tile_offsets, _u32p), _p(p.payload, _u8p),
                            p.payload_bytes, _p(out, _i8p))
     if st:
         raise OracleError(st, "unpack")
@@ -145,7 +145,7 @@ def gemm(p: Packed, x: np.ndarray, rows=None, lib=None) -> np.ndarray:
     m = x.shape[0]
     b, e = rows if rows is not None else (0, p.n)
     y = np.full((m, p.n), np.nan, dtype=np.float64)
-    st = lib.oracle_gemm(p.n, p.k, _p(p.widths, _u8p), _p(p.scales, _u16p), _p(p.row_offsets, _u32p),
+    st = lib.oracle_gemm(p.n, p.k, _p(p.widths, _u8p), _p(p.scales, _u16p), _p(p.tile_offsets, _u32p),
                          _p(p.payload, _u8p), p.payload_bytes, _p(x, _u16p), m, _p(y, _f64p), b, e)
     if st:
         raise OracleError(st, "gemm")
@@ -167,7 +167,7 @@ def gemv_threaded(p: Packed, x: np.ndarray, row_begin: int, row_end: int, thread
     def run(i):
         b, e = int(bounds[i]), int(bounds[i + 1])
         if e > b:
-            st = lib.oracle_gemv(p.n, p.k, _p(p.widths, _u8p), _p(p.scales, _u16p), _p(p.row_offsets, _u32p),
+            st = lib.oracle_gemv(p.n, p.k, _p(p.widths, _u8p), _p(p.scales, _u16p), _p(p.tile_offsets, _u32p),
                                  _p(p.payload, _u8p), p.payload_bytes, _p(x, _u16p), _p(y, _f64p), b, e)
             if st:
                 raise OracleError(st, "gemv")

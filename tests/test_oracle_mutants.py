@@ -21,14 +21,20 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "vectors.json")
 MUTANTS = {
     "one_bit_sign": ("return f ? -1 : 1;", "return f ? 1 : -1;"),
     "twos_complement_threshold": ("if (f >= (1u << (b - 1)))", "if (f > (1u << (b - 1)))"),
-    "field_bit_order_msb_first": ("unsigned f = (payload[p + bitpos / 8] >> (bitpos % 8))",
-                                  "unsigned f = (payload[p + bitpos / 8] >> (8 - b - bitpos % 8))"),
+    "field_bit_order_msb_first": ("unsigned f = (payload[p + bit / 8] >> (bit % 8))",
+                                  "unsigned f = (payload[p + bit / 8] >> (8 - b - bit % 8))"),
+    "two_bit_fields_not_interleaved": ("int e = i % 16, m = e / 2 + 8 * (e % 2);", "int e = i % 16, m = e;"),
+    "four_bit_fields_not_interleaved": ("int e = i % 8, m = e / 2 + 4 * (e % 2);", "int e = i % 8, m = e;"),
     "dropped_scale": ("acc += s * d;", "acc += d;"),
     "dropped_product_terms": ("d += (double)decode_code", "d = (double)decode_code"),
     "x_reversed_in_group": ("xm[(uint64_t)j * 64 + i]", "xm[(uint64_t)j * 64 + (63 - i)]"),
     "width_code_msb_first": ("int c = (widths[t / 4] >> (2 * (t % 4))) & 3;",
                              "int c = (widths[t / 4] >> (2 * (3 - t % 4))) & 3;"),
-    "payload_advance": ("acc += s * d;\n                p += 8u * b;", "acc += s * d;\n                p += 8u;"),
+    "buckets_descending": ("for (int b = 1; b <= 8; b *= 2)", "for (int b = 8; b >= 1; b /= 2)"),
+    "bucket_row_major": ("for (uint32_t j = j0; j < j1; ++j)\n                    for (uint32_t r = r0; r < r1; ++r) {",
+                         "for (uint32_t r = r0; r < r1; ++r)\n                    for (uint32_t j = j0; j < j1; ++j) {"),
+    "tile_rows_32": ("#define TILE_ROWS 64u", "#define TILE_ROWS 32u"),
+    "tile_groups_8": ("#define TILE_GROUPS 4u", "#define TILE_GROUPS 8u"),
     "half_subnormal_exponent": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     "half_bias": ("v = ldexp((double)(1024 + frac), expo - 25);", "v = ldexp((double)(1024 + frac), expo - 24);"),
     "half_implicit_bit": ("v = ldexp((double)(1024 + frac), expo - 25);", "v = ldexp((double)frac, expo - 25);"),
@@ -37,8 +43,8 @@ MUTANTS = {
     "packer_sign": ("f = q < 0 ? 1u : 0u;", "f = q > 0 ? 1u : 0u;"),
     "packer_width_code": ("int c = b == 1 ? 0 : b == 2 ? 1 : b == 4 ? 2 : 3;",
                           "int c = b == 1 ? 0 : b == 2 ? 2 : b == 4 ? 1 : 3;"),
-    "row_offsets_shifted": ("row_offsets_out[r + 1] = (uint32_t)pos;",
-                            "row_offsets_out[r + 1] = (uint32_t)(r + 1 < n ? pos + 8 : pos);"),
+    "tile_offsets_shifted": ("tile_offsets[tile] = (uint32_t)pos;\n            for",
+                             "tile_offsets[tile] = (uint32_t)(tile ? pos + 8 : pos);\n            for"),
     "gemm_output_transposed": ("y[(uint64_t)mm * n + r] = acc;",
                                "y[((uint64_t)r * m + mm) < (uint64_t)m * n ? ((uint64_t)r * m + mm) : 0] = acc;"),
     "grid_too_wide": ("int lim = (1 << (b - 1)) - 1;", "int lim = (1 << (b - 1));"),
@@ -70,7 +76,7 @@ def failed_pins(lib):
         try:
             p = oracle.pack(n, k, bits, codes, scales, lib=lib)
             ok = (p.payload.tobytes().hex() == v["payload_hex"] and p.widths.tobytes().hex() == v["widths_hex"]
-                  and p.row_offsets.tolist() == v["row_offsets"]
+                  and p.tile_offsets.tolist() == v["tile_offsets"]
                   and oracle.gemv(p, np.array(v["x"], np.float16).view(np.uint16), lib=lib).tolist() == v["y"])
         except oracle.OracleError:
             ok = False

@@ -60,7 +60,7 @@ def test_golden_vector(v):
     scales = np.array([int(h, 16) for h in v["scales_hex"]], dtype=np.uint16).reshape(n, k // 64)
     p = oracle.pack(n, k, bits, codes, scales)
     assert p.widths.tobytes().hex() == v["widths_hex"]
-    assert p.row_offsets.tolist() == v["row_offsets"]
+    assert p.tile_offsets.tolist() == v["tile_offsets"]
     assert p.payload.tobytes().hex() == v["payload_hex"]
     assert np.array_equal(oracle.unpack(p), codes)
     x = np.array(v["x"], dtype=np.float16).view(np.uint16)
@@ -84,10 +84,12 @@ def test_pack_size_and_roundtrip(shape, seed, mixname):
     g = n * (k // 64)
     payload = int((8 * bits.astype(np.int64)).sum())
     assert p.payload_bytes == payload
-    assert p.total_bytes == payload + (g + 3) // 4 + 2 * g + 4 * (n + 1)
-    # offsets = exclusive prefix sum of 8*b at row starts
-    row_bytes = (8 * bits.astype(np.int64)).sum(axis=1)
-    assert p.row_offsets.tolist() == np.concatenate([[0], np.cumsum(row_bytes)]).tolist()
+    tiles_r, tiles_c = -(-n // 64), -(-(k // 64) // 4)
+    assert p.total_bytes == payload + (g + 3) // 4 + 2 * g + 4 * (tiles_r * tiles_c + 1)
+    # tile offsets = exclusive prefix sum of the tiles' payload sizes (64 rows x 4 groups per tile)
+    sizes = [int((8 * bits[64 * a:64 * a + 64, 4 * c:4 * c + 4].astype(np.int64)).sum())
+             for a in range(tiles_r) for c in range(tiles_c)]
+    assert p.tile_offsets.tolist() == np.concatenate([[0], np.cumsum(sizes)]).astype(np.int64).tolist()
     assert oracle.check_offsets(p) == 0
     assert np.array_equal(oracle.unpack(p), codes)
     assert np.array_equal(p.scales, scales.reshape(-1))
@@ -97,8 +99,9 @@ def test_all_8bit_is_int8_times_scale():
     n, k = 6, 320
     bits, codes, scales = W.draw_random_matrix(11, n, k, {8: 1.0})
     p = oracle.pack(n, k, bits, codes, scales)
-    # payload bytes are literally the int8 codes, rows in order
-    assert p.payload.tobytes() == codes.tobytes()
+    # every group's 64 payload bytes are literally its int8 codes (compared as a multiset of blocks)
+    blocks = sorted(p.payload.reshape(-1, 64).tobytes()[i * 64:(i + 1) * 64] for i in range(n * k // 64))
+    assert blocks == sorted(codes.reshape(-1, 64)[t].tobytes() for t in range(n * k // 64))
     x = W.draw_x(12, k)
     ref = dense_from_inputs(bits, codes, scales) @ xf(x)[0]
     assert np.allclose(oracle.gemv(p, x), ref, rtol=1e-13, atol=1e-15)
@@ -108,8 +111,10 @@ def test_all_1bit_is_sign_times_scale():
     n, k = 7, 256
     bits, codes, scales = W.draw_random_matrix(13, n, k, {1: 1.0})
     p = oracle.pack(n, k, bits, codes, scales)
-    # one sign bit per weight, LSB first, set for negative weights
-    assert np.array_equal(np.unpackbits(p.payload, bitorder="little").reshape(n, k), (codes < 0).astype(np.uint8))
+    # one sign bit per weight, LSB first, set for negative weights (8-byte blocks, as a multiset)
+    want = sorted(np.packbits((codes.reshape(-1, 64)[t] < 0).astype(np.uint8), bitorder="little").tobytes()
+                  for t in range(n * k // 64))
+    assert sorted(p.payload[8 * t:8 * t + 8].tobytes() for t in range(n * k // 64)) == want
     x = W.draw_x(14, k)
     s = np.repeat(scales.view(np.float16).astype(np.float64), 64, axis=1)
     ref = (np.sign(codes.astype(np.float64)) * s) @ xf(x)[0]
@@ -218,10 +223,10 @@ def test_threaded_matches_serial():
 
 def test_empty_shapes():
     p = oracle.pack(0, 128, np.zeros(0, np.uint8), np.zeros(0, np.int8), np.zeros(0, np.uint16))
-    assert p.payload_bytes == 0 and p.row_offsets.tolist() == [0]
+    assert p.payload_bytes == 0 and p.tile_offsets.tolist() == [0]      # no tiles when n == 0
     assert oracle.gemv(p, W.draw_x(1, 128)).shape == (0,)
     p = oracle.pack(3, 0, np.zeros(0, np.uint8), np.zeros(0, np.int8), np.zeros(0, np.uint16))
-    assert p.row_offsets.tolist() == [0, 0, 0, 0]
+    assert p.tile_offsets.tolist() == [0]      # no tiles when k == 0
     assert np.all(oracle.gemv(p, np.zeros(0, np.uint16)) == 0)
 
 
@@ -269,8 +274,8 @@ def test_rejects_ragged_k():
 def test_rejects_inconsistent_offsets():
     bits, codes, scales = _ok_inputs()
     p = oracle.pack(2, 128, bits, codes, scales)
-    p.row_offsets = p.row_offsets.copy()
-    p.row_offsets[1] += 8
+    p.tile_offsets = p.tile_offsets.copy()
+    p.tile_offsets[1] += 8
     assert oracle.check_offsets(p) == oracle.ERR_OFFSETS
     with pytest.raises(oracle.OracleError):
         oracle.gemv(p, W.draw_x(1, 128))
