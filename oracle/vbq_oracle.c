@@ -21,14 +21,20 @@
  *
  * Packed layout (the pages fix only the items above; every other choice is
  * a stated reading, listed with the design notes):
- *   W is N x K row-major, K % 64 == 0, G = K / 64, flat group t = n*G + j.
- *   widths[ceil(N*G/4)]   width code c_t = (widths[t/4] >> 2*(t%4)) & 3,
- *                         b_t = 1 << c_t.
- *   scales[N*G]           IEEE binary16 bit pattern of s_t.
+ *   W is N x K row-major, K % 64 == 0, G = K / 64; group (n, j) covers
+ *   W[n][64j .. 64j+63].
  *   Tiles                 the groups are cut into tiles of 64 rows x 4
  *                         groups (edge tiles are smaller); tile (a, c)
  *                         holds rows [64a, 64a+64) and groups [4c, 4c+4);
  *                         tiles are numbered a * ceil(G/4) + c.
+ *   metadata index        group (n, j) in tile (a, c) = (n/64, j/4), with
+ *                         R = rows of row tile a and C = groups of tile
+ *                         (a, c), has index t = 64*a*G + R*4*c
+ *                         + (n - 64a)*C + (j - 4c): tiles in order, each
+ *                         tile row-major.
+ *   widths[ceil(N*G/4)]   width code c_t = (widths[t/4] >> 2*(t%4)) & 3,
+ *                         b_t = 1 << c_t.
+ *   scales[N*G]           IEEE binary16 bit pattern of s_t.
  *   tile_offsets[T+1]     exclusive prefix sum of the tiles' payload sizes
  *                         (each the sum of 8*b over the tile's groups).
  *   payload               tile by tile; inside a tile, bucketed by width
@@ -94,6 +100,16 @@ static uint64_t tile_count(uint32_t n, uint32_t G)
     return (uint64_t)((n + TILE_ROWS - 1) / TILE_ROWS) * ((G + TILE_GROUPS - 1) / TILE_GROUPS);
 }
 
+/* Metadata index of group (r, j): tiles in order, each tile row-major. */
+static uint64_t meta_index(uint32_t n, uint32_t G, uint32_t r, uint32_t j)
+{
+    uint32_t a = r / TILE_ROWS, c = j / TILE_GROUPS;
+    uint32_t rows = n - a * TILE_ROWS < TILE_ROWS ? n - a * TILE_ROWS : TILE_ROWS;
+    uint32_t cols = G - c * TILE_GROUPS < TILE_GROUPS ? G - c * TILE_GROUPS : TILE_GROUPS;
+    return (uint64_t)TILE_ROWS * a * G + (uint64_t)rows * TILE_GROUPS * c +
+           (uint64_t)(r - a * TILE_ROWS) * cols + (j - c * TILE_GROUPS);
+}
+
 /* Bit position of element i inside a b-bit group's byte string. */
 static unsigned field_bit(int b, int i)
 {
@@ -139,7 +155,7 @@ static uint64_t locate_groups(uint32_t n, uint32_t G, const uint8_t *bits, uint6
     return pos;
 }
 
-/* width code of flat group t */
+/* width code stored at metadata index t */
 static int group_width(const uint8_t *widths, uint64_t t)
 {
     int c = (widths[t / 4] >> (2 * (t % 4))) & 3;
@@ -161,7 +177,8 @@ static int code_is_on_grid(int b, int q)
 }
 
 /* Sizes in bytes of the four packed arrays; out = {widths, scales,
- * tile_offsets, payload, total}. bits[n*G + j] is the width of group (n, j). */
+ * tile_offsets, payload, total}. bits[n*G + j] is the width of group (n, j)
+ * (packer inputs are in natural row-major group order). */
 int oracle_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits, uint64_t out[5])
 {
     if (!out || (!bits && (uint64_t)n * k != 0))
@@ -223,8 +240,9 @@ int oracle_pack(uint32_t n, uint32_t k, const uint8_t *bits, const int8_t *codes
     for (uint64_t t = 0; t < groups; ++t) {
         int b = bits[t];
         int c = b == 1 ? 0 : b == 2 ? 1 : b == 4 ? 2 : 3;
-        widths_out[t / 4] |= (uint8_t)(c << (2 * (t % 4)));
-        scales_out[t] = scales[t];
+        uint64_t m = meta_index(n, G, (uint32_t)(t / G), (uint32_t)(t % G));
+        widths_out[m / 4] |= (uint8_t)(c << (2 * (m % 4)));
+        scales_out[m] = scales[t];
         for (int i = 0; i < 64; ++i) {
             int q = codes[t * 64 + i];
             unsigned f;
@@ -240,14 +258,23 @@ int oracle_pack(uint32_t n, uint32_t k, const uint8_t *bits, const int8_t *codes
     return OR_OK;
 }
 
-/* Expand the packed width codes into one width per group (caller frees). */
-static uint8_t *expand_widths(const uint8_t *widths, uint64_t groups)
+/* Width of group (r, j) from the packed codes. */
+static int width_of(const uint8_t *widths, uint32_t n, uint32_t G, uint32_t r, uint32_t j)
 {
+    return group_width(widths, meta_index(n, G, r, j));
+}
+
+/* Expand the packed width codes into one width per group, natural order
+ * n*G + j (caller frees). */
+static uint8_t *expand_widths(const uint8_t *widths, uint32_t n, uint32_t G)
+{
+    uint64_t groups = (uint64_t)n * G;
     uint8_t *bits = malloc(groups ? groups : 1);
     if (!bits)
         return NULL;
-    for (uint64_t t = 0; t < groups; ++t)
-        bits[t] = (uint8_t)group_width(widths, t);
+    for (uint32_t r = 0; r < n; ++r)
+        for (uint32_t j = 0; j < G; ++j)
+            bits[(uint64_t)r * G + j] = (uint8_t)width_of(widths, n, G, r, j);
     return bits;
 }
 
@@ -261,8 +288,8 @@ int oracle_check_offsets(uint32_t n, uint32_t k, const uint8_t *widths,
     if (k % 64)
         return OR_ERR_SHAPE;
     uint32_t G = k / 64;
-    uint64_t groups = (uint64_t)n * G, tiles = tile_count(n, G);
-    uint8_t *bits = expand_widths(widths, groups);
+    uint64_t tiles = tile_count(n, G);
+    uint8_t *bits = expand_widths(widths, n, G);
     uint32_t *expect = malloc((tiles + 1) * sizeof *expect);
     int st = OR_OK;
     if (!bits || !expect) {
@@ -300,7 +327,7 @@ static int group_offsets(uint32_t n, uint32_t k, const uint8_t *widths, const ui
     if (st)
         return st;
     uint64_t groups = (uint64_t)n * (k / 64);
-    uint8_t *bits = expand_widths(widths, groups);
+    uint8_t *bits = expand_widths(widths, n, k / 64);
     uint64_t *off = malloc((groups ? groups : 1) * sizeof *off);
     if (!bits || !off) {
         free(bits);
@@ -325,12 +352,14 @@ int oracle_unpack(uint32_t n, uint32_t k, const uint8_t *widths, const uint32_t 
         free(off);
         return OR_ERR_NULL;
     }
-    uint64_t groups = (uint64_t)n * (k / 64);
-    for (uint64_t t = 0; t < groups; ++t) {
-        int b = group_width(widths, t);
-        for (int i = 0; i < 64; ++i)
-            codes_out[t * 64 + i] = (int8_t)decode_code(payload, off[t], b, i);
-    }
+    uint32_t G = k / 64;
+    for (uint32_t r = 0; r < n; ++r)
+        for (uint32_t j = 0; j < G; ++j) {
+            uint64_t t = (uint64_t)r * G + j;
+            int b = width_of(widths, n, G, r, j);
+            for (int i = 0; i < 64; ++i)
+                codes_out[t * 64 + i] = (int8_t)decode_code(payload, off[t], b, i);
+        }
     free(off);
     return OR_OK;
 }
@@ -359,8 +388,8 @@ int oracle_gemm(uint32_t n, uint32_t k, const uint8_t *widths, const uint16_t *s
             double acc = 0.0;
             for (uint32_t j = 0; j < G; ++j) {
                 uint64_t t = (uint64_t)r * G + j;
-                int b = group_width(widths, t);
-                double s = oracle_half_to_double(scales[t]);
+                int b = width_of(widths, n, G, r, j);
+                double s = oracle_half_to_double(scales[meta_index(n, G, r, j)]);
                 double d = 0.0;
                 for (int i = 0; i < 64; ++i)
                     d += (double)decode_code(payload, off[t], b, i) *

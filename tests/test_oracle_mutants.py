@@ -38,8 +38,10 @@ MUTANTS = {
     "half_subnormal_exponent": ("v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     "half_bias": ("v = ldexp((double)(1024 + frac), expo - 25);", "v = ldexp((double)(1024 + frac), expo - 24);"),
     "half_implicit_bit": ("v = ldexp((double)(1024 + frac), expo - 25);", "v = ldexp((double)frac, expo - 25);"),
-    "scale_index_transposed": ("double s = oracle_half_to_double(scales[t]);",
-                               "double s = oracle_half_to_double(scales[(uint64_t)j * n + r < (uint64_t)n * G ? (uint64_t)j * n + r : t]);"),
+    "scale_natural_order": ("double s = oracle_half_to_double(scales[meta_index(n, G, r, j)]);",
+                            "double s = oracle_half_to_double(scales[t]);"),
+    "metadata_natural_order": ("    return (uint64_t)TILE_ROWS * a * G + (uint64_t)rows * TILE_GROUPS * c +",
+                               "    return (uint64_t)r * G + j;\n    return (uint64_t)TILE_ROWS * a * G + (uint64_t)rows * TILE_GROUPS * c +"),
     "packer_sign": ("f = q < 0 ? 1u : 0u;", "f = q > 0 ? 1u : 0u;"),
     "packer_width_code": ("int c = b == 1 ? 0 : b == 2 ? 1 : b == 4 ? 2 : 3;",
                           "int c = b == 1 ? 0 : b == 2 ? 2 : b == 4 ? 1 : 3;"),
@@ -76,6 +78,7 @@ def failed_pins(lib):
         try:
             p = oracle.pack(n, k, bits, codes, scales, lib=lib)
             ok = (p.payload.tobytes().hex() == v["payload_hex"] and p.widths.tobytes().hex() == v["widths_hex"]
+                  and p.scales.tobytes().hex() == v.get("packed_scales_hex", p.scales.tobytes().hex())
                   and p.tile_offsets.tolist() == v["tile_offsets"]
                   and oracle.gemv(p, np.array(v["x"], np.float16).view(np.uint16), lib=lib).tolist() == v["y"])
         except oracle.OracleError:
