@@ -77,10 +77,14 @@ def main():
     xin = [xs[W.x_seed(spec)] for spec in specs]
     stream = torch.cuda.current_stream(dev)
 
+    # decode order with the dependencies of a decoder layer: q,k,v read one input (one launch),
+    # o reads the attention output, gate,up read one input (one launch), down reads silu(gate)*up
+    groups = [[0, 1, 2], [3], [4, 5], [6]]
+
     def step(i):
         layer = dev_layers[i % copies]
-        for j in range(len(specs)):
-            V.vbq_gemv(layer[j], xin[j], ys[j], stream)
+        for g in groups:
+            V.vbq_gemv_multi([layer[j] for j in g], [xin[j] for j in g], [ys[j] for j in g], stream)
 
     for i in range(args.warmup):
         step(i)
@@ -103,7 +107,8 @@ def main():
         "config": {"workload": "layer_9b: q,k,v,o 4096x4096 + gate,up 14336x4096 + down 4096x14336, batch 1, "
                                "widths i.i.d. per 64-group {1:.69,2:.16,4:.10,8:.05}, fp16 scales and x, fp32 y",
                    "packed_bytes_per_step": layer_bytes, "weights_per_step": cfg.weights,
-                   "rotated_copies": copies, "launches_per_step": len(specs)},
+                   "rotated_copies": copies, "launches_per_step": len(groups),
+                   "launch_groups": "q+k+v | o | gate+up | down (vbq_gemv_multi)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
     }
     if args.only_timed:
@@ -111,33 +116,47 @@ def main():
         return
 
     # ---- per-launch durations (events around each launch on the launch stream)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in specs]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in groups]
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         layer = dev_layers[i % copies]
-        for j in range(len(specs)):
-            a, b = ev[i][j]
+        for gi, g in enumerate(groups):
+            a, b = ev[i][gi]
             a.record(stream)
-            V.vbq_gemv(layer[j], xin[j], ys[j], stream)
+            V.vbq_gemv_multi([layer[j] for j in g], [xin[j] for j in g], [ys[j] for j in g], stream)
             b.record(stream)
     torch.cuda.synchronize()
-    per = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])        # ms [steps, matrices]
-    by_shape = {}
-    for j, spec in enumerate(specs):
-        key = f"{spec.n}x{spec.k}"
-        d = by_shape.setdefault(key, {"bytes": hosts[j][0].total_bytes, "ms": [], "launches": 0})
-        d["ms"].extend(per[:, j].tolist())
-        d["launches"] += 1
-    dom_key = max(by_shape, key=lambda k_: np.sum(by_shape[k_]["ms"]))
-    dom = by_shape[dom_key]
-    avg_ms = float(np.mean(dom["ms"]))
-    achieved = dom["bytes"] / (avg_ms * 1e-3) / 1e9
+    per = np.array([[a.elapsed_time(b) for a, b in row] for row in ev])        # ms [steps, groups]
+    gbytes = [sum(hosts[j][0].total_bytes for j in g) for g in groups]
+    names = ["+".join(specs[j].name.split(".")[-1] for j in g) for g in groups]
+    tot = per.sum(axis=0)
+    dom = int(np.argmax(tot))
+    avg_ms = float(np.mean(per[:, dom]))
+    achieved = gbytes[dom] / (avg_ms * 1e-3) / 1e9
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                          "kernel": f"vbq_gemv {dom_key}", "avg_launch_us": round(avg_ms * 1e3, 3),
-                          "algorithmic_bytes_per_launch": dom["bytes"]}
-    result["per_shape_us"] = {k_: round(float(np.mean(v["ms"])) * 1e3, 3) for k_, v in by_shape.items()}
+                          "kernel": f"gemv_tiles ({names[dom]} launch)", "avg_launch_us": round(avg_ms * 1e3, 3),
+                          "algorithmic_bytes_per_launch": gbytes[dom]}
+    result["per_launch_us"] = {nm: round(float(np.mean(per[:, gi])) * 1e3, 3) for gi, nm in enumerate(names)}
+
+    # ---- the same seven GEMVs as a single launch (no decode dependencies) and as seven launches
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for i in range(args.steps):
+            fn(args.warmup + i)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    one = timed(lambda i: V.vbq_gemv_multi(dev_layers[i % copies], xin, ys, stream))
+    sep = timed(lambda i: [V.vbq_gemv(dev_layers[i % copies][j], xin[j], ys[j], stream) for j in range(len(specs))])
+    result["other_launch_shapes"] = {
+        "all_seven_one_launch": {"ms_per_step": round(one, 5), "GBps": round(layer_bytes / (one * 1e-3) / 1e9, 2)},
+        "seven_launches": {"ms_per_step": round(sep, 5), "GBps": round(layer_bytes / (sep * 1e-3) / 1e9, 2)}}
 
     # ---- dense fp16 GEMV of the same shapes (torch matmul on the same stream, rotated copies)
     if not args.no_fp16_baseline:
@@ -174,24 +193,20 @@ def main():
         packs = [oracle.pack(s.n, s.k, b, c, sc) for s, (h, b, c, sc) in zip(specs, hosts)]
         xh = {key: W.draw_x(key, specs[[W.x_seed(s) for s in specs].index(key)].k)[0] for key in
               {W.x_seed(s) for s in specs}}
-        # calibrate on 1% of the rows, then size the sample to ~cpu_seconds
-        frac = 0.01
+        # whole-layer passes repeated until about cpu_seconds of host time have been spent
+        reps = 0
         t = time.perf_counter()
-        for s, p in zip(specs, packs):
-            oracle.gemv_threaded(p, xh[W.x_seed(s)], 0, max(1, int(s.n * frac)), cores)
-        dt = time.perf_counter() - t
-        frac = min(1.0, frac * args.cpu_seconds / max(dt, 1e-6))
-        sampled = 0
-        t = time.perf_counter()
-        for s, p, (h, *_) in zip(specs, packs, hosts):
-            rows = max(1, int(s.n * frac))
-            oracle.gemv_threaded(p, xh[W.x_seed(s)], 0, rows, cores)
-            sampled += int(h.row_offsets[rows]) + 4 * (rows + 1) + (rows * s.k // 64) * 2 + (rows * s.k // 64) // 4
-        dt = time.perf_counter() - t
-        result["cpu_baseline"] = {"value": round(sampled / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+        while True:
+            for s, p in zip(specs, packs):
+                oracle.gemv_threaded(p, xh[W.x_seed(s)], 0, s.n, cores)
+            reps += 1
+            dt = time.perf_counter() - t
+            if dt >= args.cpu_seconds or reps >= 200:
+                break
+        result["cpu_baseline"] = {"value": round(layer_bytes * reps / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
                                   "kind": "oracle",
-                                  "sample": f"first {frac:.2%} of the rows of each of the 7 matrices "
-                                            f"({sampled / 1e6:.1f} MB packed), {dt:.1f} s, {cores} threads"}
+                                  "sample": f"{reps} passes over all 7 matrices of the layer "
+                                            f"({layer_bytes * reps / 1e6:.0f} MB packed), {dt:.1f} s, {cores} threads"}
     print(json.dumps(result))
 
 

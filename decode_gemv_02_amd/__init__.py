@@ -25,6 +25,9 @@ ABI_VERSION = 1
 GROUP = 64
 MAX_K = 65536
 MAX_BATCH = 64
+MAX_MULTI = 16
+TILE_ROWS = 64
+TILE_GROUPS = 4
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WIDTH, ERR_CODE, ERR_SCALE, ERR_CAPACITY, ERR_OFFSETS, ERR_ALIGN, \
     ERR_TOO_LARGE, ERR_HIP, ERR_ABI = range(12)
@@ -39,7 +42,7 @@ class VbqSizes(ctypes.Structure):
 class VbqMatrix(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
                 ("payload_bytes", ctypes.c_uint32), ("widths", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("row_offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p)]
+                ("tile_offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p)]
 
 
 class VbqError(RuntimeError):
@@ -63,11 +66,15 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_pack_sizes.argtypes = [U32, U32, P, ctypes.POINTER(VbqSizes)]
     lib.vbq_pack.argtypes = [U32, U32, P, P, P, P, P, P, P, ctypes.c_uint64]
     lib.vbq_validate_host.argtypes = [ctypes.POINTER(VbqMatrix)]
+    lib.vbq_tile_count.restype = ctypes.c_uint64
+    lib.vbq_tile_count.argtypes = [U32, U32]
+    lib.vbq_gemv_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P), ctypes.POINTER(P),
+                                   U32, P]
     lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
     lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
-    for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemm_smallbatch,
-              lib.vbq_unpack_codes):
+    for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
+              lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -100,7 +107,7 @@ class HostMatrix:
     k: int
     widths: np.ndarray       # uint8
     scales: np.ndarray       # uint16 binary16 bits
-    row_offsets: np.ndarray  # uint32 [n+1]
+    tile_offsets: np.ndarray  # uint32 [tiles+1]
     payload: np.ndarray      # uint8
 
     @property
@@ -109,11 +116,11 @@ class HostMatrix:
 
     @property
     def total_bytes(self) -> int:
-        return int(self.widths.size + 2 * self.scales.size + 4 * self.row_offsets.size + self.payload.size)
+        return int(self.widths.size + 2 * self.scales.size + 4 * self.tile_offsets.size + self.payload.size)
 
     def view(self) -> VbqMatrix:
         return VbqMatrix(ABI_VERSION, self.n, self.k, self.payload_bytes, _np_ptr(self.widths),
-                         _np_ptr(self.scales), _np_ptr(self.row_offsets), _np_ptr(self.payload))
+                         _np_ptr(self.scales), _np_ptr(self.tile_offsets), _np_ptr(self.payload))
 
 
 def vbq_pack_sizes(n: int, k: int, bits: np.ndarray) -> dict:
@@ -131,7 +138,7 @@ def vbq_pack(n: int, k: int, bits: np.ndarray, codes: np.ndarray, scales: np.nda
     sz = vbq_pack_sizes(n, k, bits)
     widths = np.zeros(sz["widths_bytes"], np.uint8)
     sc = np.zeros(sz["scales_bytes"] // 2, np.uint16)
-    offs = np.zeros(n + 1, np.uint32)
+    offs = np.zeros(sz["offsets_bytes"] // 4, np.uint32)
     payload = np.zeros(sz["payload_bytes"], np.uint8)
     _check(lib.vbq_pack(n, k, _np_ptr(bits), _np_ptr(codes), _np_ptr(scales), _np_ptr(widths), _np_ptr(sc),
                         offs.ctypes.data, _np_ptr(payload), payload.size))
@@ -160,7 +167,7 @@ class DeviceMatrix:
 
         self._widths = up(host.widths)
         self._scales = up(host.scales.view(np.int16))
-        self._offsets = up(host.row_offsets.view(np.int32))
+        self._offsets = up(host.tile_offsets.view(np.int32))
         self._payload = up(host.payload)
         self.struct = VbqMatrix(ABI_VERSION, self.n, self.k, self.payload_bytes, self._widths.data_ptr(),
                                 self._scales.data_ptr(), self._offsets.data_ptr(), self._payload.data_ptr())
@@ -172,6 +179,25 @@ def vbq_gemv(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> 
     assert x.is_contiguous() and y.is_contiguous() and x.numel() == w.k and y.numel() >= w.n
     _check(lib.vbq_gemv(ctypes.byref(w.struct), x.data_ptr(), y.data_ptr(), _stream_handle(stream, w.device)))
     return y
+
+
+def vbq_tile_count(n: int, k: int) -> int:
+    return int(lib.vbq_tile_count(n, k))
+
+
+def vbq_gemv_multi(ws, xs, ys, stream=None):
+    """Several independent GEMVs (ys[i] = W_i xs[i]) in one launch; up to 16."""
+    count = len(ws)
+    assert len(xs) == count and len(ys) == count
+    for w, x, y in zip(ws, xs, ys):
+        assert x.dtype == torch.float16 and y.dtype == torch.float32 and x.is_contiguous() and y.is_contiguous()
+        assert x.numel() == w.k and y.numel() >= w.n
+    wa = (ctypes.POINTER(VbqMatrix) * max(count, 1))(*[ctypes.pointer(w.struct) for w in ws])
+    xa = (ctypes.c_void_p * max(count, 1))(*[x.data_ptr() for x in xs])
+    ya = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
+    dev = ws[0].device if count else torch.device("cuda")
+    _check(lib.vbq_gemv_multi(wa, xa, ya, count, _stream_handle(stream, dev)))
+    return ys
 
 
 def vbq_gemm_smallbatch(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:

@@ -1,12 +1,32 @@
-// Device half of the VBQ library (gfx950): argument checks, launches and kernels.
+// Device half of the VBQ library (gfx950): launches and kernels.
 //
 // VBQ paper (arXiv 2607.02893) §6, "Fused kernels over packed weights": each
-// group's packed bytes are read once, expanded to integer codes in registers,
-// combined with the group's fp16 scale and accumulated into y = W x; no dense
-// weight matrix is ever written. Grid and scale: §3.1 Eq. (1).
+// group's packed bytes are read once, expanded in registers and combined with
+// the group's fp16 scale while y = W x accumulates; no dense weight matrix is
+// written. Grid and scale: §3.1 Eq. (1). The payload is the width-bucketed
+// tile stream described in vbq.h.
+//
+// Work decomposition. A wave owns one tile (64 rows x 4 groups) at a time:
+//   1. it stages the tile's 256 activations in LDS, once as fp16 pairs and
+//      once as a 4-bit lookup table (16 partial sums per 4 activations);
+//   2. lane r reads the four width codes and scales of row r and the wave
+//      compacts the tile into one list per width (ballot + mbcnt ranks give
+//      each group its place in the column-major bucket order of the stream);
+//   3. for each width the wave walks its bucket with one group (or a 16-byte
+//      slice of a group) per lane, so every instruction runs a single width's
+//      unpack; the bucket is contiguous, so loads are coalesced;
+//   4. each group's fp32 dot product is scaled once and parked in LDS; rows
+//      are summed in a fixed order, so results are bitwise repeatable.
+// A workgroup of four waves shares one row tile and splits its column tiles;
+// when a row tile is further split across workgroups (small n, large k), the
+// partial sums go to a scratch buffer and the last workgroup to arrive adds
+// them in a fixed order.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
+#include <mutex>
+#include <unordered_map>
 
 #include "vbq_internal.h"
 
@@ -15,82 +35,515 @@ using vbq::fail;
 namespace {
 
 constexpr uint32_t kWave = 64;
+constexpr uint32_t kTileRows = VBQ_TILE_ROWS;     // 64
+constexpr uint32_t kTileGroups = VBQ_TILE_GROUPS; // 4
+constexpr uint32_t kWavesPerBlock = 4;
+constexpr uint32_t kXStride = 36;                 // dwords per staged column (32 used, padded)
+constexpr uint32_t kMagic = 0x64006400u;          // two fp16 1024.0
 
-__device__ __forceinline__ float half_to_float(uint16_t h) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
-// b-bit field -> integer code: b = 1 is a sign bit, b >= 2 two's complement.
-__device__ __forceinline__ int decode_field(uint32_t f, uint32_t b) {
-    if (b == 1) return f ? -1 : 1;
-    const uint32_t sh = 32u - b;
-    return static_cast<int>(f << sh) >> sh;
+__device__ __forceinline__ float half_to_float(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
-// width of flat group t
-__device__ __forceinline__ uint32_t group_bits(const uint8_t *widths, uint64_t t) {
-    return 1u << ((widths[t >> 2] >> (2 * (t & 3))) & 3u);
+// ---------------------------------------------------------------- per-width unpack
+// Each helper turns one little-endian 32-bit word of a group into fp16 pairs
+// (1024 + 2^s * u) where u = q + 2^(b-1) is the offset-binary code; the pairs
+// come out in natural element order (2i, 2i+1) thanks to the in-group field
+// layout, and multiply fp16 activation pairs with v_dot2.
+
+// 8-bit: elements 4w..4w+3 -> pairs (0,1), (2,3); factor 1
+__device__ __forceinline__ void unpack8(uint32_t v, uint32_t &p0, uint32_t &p1) {
+    v ^= 0x80808080u;
+    p0 = __builtin_amdgcn_perm(0x64646464u, v, 0x04010400u);   // bytes {v0, 64, v1, 64}
+    p1 = __builtin_amdgcn_perm(0x64646464u, v, 0x04030402u);   // bytes {v2, 64, v3, 64}
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+// 4-bit: elements 8w..8w+7 -> pairs (0,1) x1, (2,3) x16, (4,5) x1, (6,7) x16
+__device__ __forceinline__ void unpack4(uint32_t v, uint32_t p[4]) {
+    v ^= 0x88888888u;
+    const uint32_t h = v >> 8;
+    p[0] = (v & 0x000F000Fu) | kMagic;
+    p[1] = (v & 0x00F000F0u) | kMagic;
+    p[2] = (h & 0x000F000Fu) | kMagic;
+    p[3] = (h & 0x00F000F0u) | kMagic;
 }
 
-// One wave per row; lane i decodes element i of each group in turn, so the
-// width branch is uniform across the wave. The scale is folded into the code
-// (s*q is exact in fp32: 11 x 7 significant bits) and the product with x is
-// accumulated per lane in fp32, then summed across the wave.
-__global__ __launch_bounds__(256) void gemv_rowwave(const uint8_t *__restrict__ widths,
-                                                    const uint16_t *__restrict__ scales,
-                                                    const uint32_t *__restrict__ row_offsets,
-                                                    const uint8_t *__restrict__ payload,
-                                                    const uint16_t *__restrict__ x, float *__restrict__ y,
-                                                    uint32_t n, uint32_t groups, uint32_t k, uint32_t m) {
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint32_t r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    const uint32_t mm = blockIdx.y;
-    if (r >= n || mm >= m) return;
-    const uint16_t *xm = x + uint64_t(mm) * k;
-    uint32_t off = row_offsets[r];
-    float acc = 0.f;
-    for (uint32_t j = 0; j < groups; ++j) {
-        const uint64_t t = uint64_t(r) * groups + j;
-        const uint32_t b = group_bits(widths, t);
-        const float s = half_to_float(scales[t]);
-        const uint32_t bit = b * lane;
-        const uint32_t f = (payload[off + (bit >> 3)] >> (bit & 7)) & ((1u << b) - 1u);
-        acc += (s * static_cast<float>(decode_field(f, b))) * half_to_float(xm[j * kWave + lane]);
-        off += 8u * b;
+// 2-bit: elements 16w..16w+15 -> pairs m = 0..7 with factors 1,4,16,64,256,1,4,16
+__device__ __forceinline__ void unpack2(uint32_t v, uint32_t p[8]) {
+    v ^= 0xAAAAAAAAu;
+    const uint32_t h = v >> 10;
+    p[0] = (v & 0x00030003u) | kMagic;
+    p[1] = (v & 0x000C000Cu) | kMagic;
+    p[2] = (v & 0x00300030u) | kMagic;
+    p[3] = (v & 0x00C000C0u) | kMagic;
+    p[4] = (v & 0x03000300u) | kMagic;
+    p[5] = (h & 0x00030003u) | kMagic;
+    p[6] = (h & 0x000C000Cu) | kMagic;
+    p[7] = (h & 0x00300030u) | kMagic;
+}
+
+// 1-bit: bit i is the sign of element i; pair k = (2k, 2k+1) as fp16 +-1
+__device__ __forceinline__ uint32_t unpack1_pair(uint32_t lo16, uint32_t hi16) {
+    // lo16/hi16: the two sign bits already in bit positions 15 and 31
+    return ((lo16 & 0x00008000u) | (hi16 & 0x80000000u)) | 0x3C003C00u;
+}
+
+// ---------------------------------------------------------------- tiles and lists
+
+struct MatArgs {
+    const uint8_t *widths;
+    const uint16_t *scales;
+    const uint32_t *tile_offsets;
+    const uint8_t *payload;
+    const uint16_t *x;
+    float *y;
+    float *partial;       // [splits][n] when splits > 1
+    uint32_t *counters;   // [row tiles] arrival counters when splits > 1 (self-resetting)
+    uint32_t n, groups, col_tiles, splits, block_begin, pad;
+};
+
+struct Batch {
+    MatArgs m[VBQ_MAX_MULTI];
+    uint32_t count;
+};
+
+struct alignas(16) WaveLds {
+    float lut[kTileGroups * 16 * 16];        // [column][nibble position][4-bit index]
+    uint32_t xs[kTileGroups * kXStride];     // fp16 activation pairs per column
+    float corr[kTileGroups][4];              // per column: sum x, 2-bit and 4-bit bias terms
+    uint32_t list[4][kTileRows * kTileGroups];
+    float part[kTileGroups][kTileRows];      // scaled group dot products
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+// Inputs of one tile that need no payload: read in one round trip and
+// prefetched one tile ahead.
+struct TileMeta {
+    uint32_t off;     // payload byte offset of the tile (uniform)
+    uint2 xv;         // activations 4k..4k+3 of column lane/16 (k = lane%16)
+    uint32_t codes;   // width codes of row `lane`, groups j0..j0+3
+    uint32_t s01;     // scales of row `lane`, groups j0, j0+1
+    uint32_t s23;     // scales of row `lane`, groups j0+2, j0+3
+};
+
+template <bool kAligned>
+__device__ __forceinline__ TileMeta load_meta(const MatArgs &M, uint32_t a, uint32_t ct, uint32_t lane,
+                                              bool with_x) {
+    TileMeta t;
+    const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
+    const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, M.groups - j0);
+    t.off = M.tile_offsets[a * M.col_tiles + ct];
+    const uint32_t jl = lane >> 4, k = lane & 15;
+    t.xv = make_uint2(0u, 0u);
+    if (with_x && jl < cn) t.xv = *reinterpret_cast<const uint2 *>(M.x + 64u * (j0 + jl) + 4u * k);
+    t.codes = t.s01 = t.s23 = 0u;
+    if (lane < rows) {
+        // the tile's metadata is one contiguous run of rows*cn slots, row-major
+        const uint64_t base = static_cast<uint64_t>(r0) * M.groups + static_cast<uint64_t>(rows) * j0;
+        if (kAligned || cn == kTileGroups) {
+            // base is a multiple of 4: one width byte and one 8-byte scale load per row
+            t.codes = M.widths[(base >> 2) + lane];
+            const uint2 sv = *reinterpret_cast<const uint2 *>(M.scales + base + 4u * lane);
+            t.s01 = sv.x;
+            t.s23 = sv.y;
+        } else {
+            const uint64_t g = base + static_cast<uint64_t>(lane) * cn;
+            const uint64_t wbytes = (static_cast<uint64_t>(M.n) * M.groups + 3) >> 2;
+            uint32_t two = M.widths[g >> 2];
+            if ((g >> 2) + 1 < wbytes) two |= static_cast<uint32_t>(M.widths[(g >> 2) + 1]) << 8;
+            t.codes = (two >> (2 * (g & 3))) & ((1u << (2 * cn)) - 1u);
+            uint32_t sc[4] = {0u, 0u, 0u, 0u};
+            for (uint32_t q = 0; q < cn; ++q) sc[q] = M.scales[g + q];
+            t.s01 = sc[0] | (sc[1] << 16);
+            t.s23 = sc[2] | (sc[3] << 16);
+        }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) y[uint64_t(mm) * n + r] = acc;
+    return t;
 }
 
-__global__ __launch_bounds__(256) void unpack_rowwave(const uint8_t *__restrict__ widths,
-                                                      const uint32_t *__restrict__ row_offsets,
-                                                      const uint8_t *__restrict__ payload, int8_t *__restrict__ codes,
-                                                      uint32_t n, uint32_t groups) {
-    const uint32_t lane = threadIdx.x & (kWave - 1);
-    const uint32_t r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (r >= n) return;
-    uint32_t off = row_offsets[r];
-    int8_t *dst = codes + uint64_t(r) * groups * kWave;
-    for (uint32_t j = 0; j < groups; ++j) {
-        const uint32_t b = group_bits(widths, uint64_t(r) * groups + j);
-        const uint32_t bit = b * lane;
-        const uint32_t f = (payload[off + (bit >> 3)] >> (bit & 7)) & ((1u << b) - 1u);
-        dst[j * kWave + lane] = static_cast<int8_t>(decode_field(f, b));
-        off += 8u * b;
+// Stage the tile's activations: fp16 pairs, the 4-bit lookup table (sums of
+// the activations selected by the set bits of a 4-bit index) and the
+// per-column bias terms of the unpack paths.
+__device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
+    const uint32_t jl = lane >> 4, k = lane & 15;
+    L.xs[jl * kXStride + 2 * k] = xv.x;
+    L.xs[jl * kXStride + 2 * k + 1] = xv.y;
+    const float x0 = half_to_float(xv.x & 0xFFFFu), x1 = half_to_float(xv.x >> 16);
+    const float x2 = half_to_float(xv.y & 0xFFFFu), x3 = half_to_float(xv.y >> 16);
+    const float a01 = x0 + x1, t5 = x2 + x0, t6 = x2 + x1, t7 = x2 + a01;
+    float4 *t = reinterpret_cast<float4 *>(L.lut + lane * 16);
+    t[0] = make_float4(0.f, x0, x1, a01);
+    t[1] = make_float4(x2, t5, t6, t7);
+    t[2] = make_float4(x3, x3 + x0, x3 + x1, x3 + a01);
+    t[3] = make_float4(x3 + x2, x3 + t5, x3 + t6, x3 + t7);
+    // bias terms. 4-bit: element pairs alternate factor 1 / 16 -> weights 1032 / 72.
+    // 2-bit: pair factors 1,4,16,64,256,1,4,16 -> weights 1024/f + 2.
+    const float a23 = x2 + x3;
+    float xsum = a01 + a23;
+    float c4 = 1032.f * a01 + 72.f * a23;
+    const uint32_t km = k & 3;
+    const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
+    const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
+    float c2 = wa * a01 + wb * a23;
+#pragma unroll
+    for (uint32_t o = 8; o > 0; o >>= 1) {
+        xsum += __shfl_xor(xsum, o, kWave);
+        c2 += __shfl_xor(c2, o, kWave);
+        c4 += __shfl_xor(c4, o, kWave);
+    }
+    if (k == 0) {
+        L.corr[jl][0] = xsum;
+        L.corr[jl][1] = c2;
+        L.corr[jl][2] = c4;
+    }
+}
+
+// Lane r = row r of the tile: sort the tile's groups into per-width lists in
+// the stream's order (column-major inside a bucket) and count them. Two
+// ballots give the bit planes of the width codes of one column; a lane's rank
+// among the rows that share its width is one mbcnt over the mask of equal codes.
+__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, uint32_t rows, uint32_t cn,
+                                            uint32_t lane, uint32_t cnt[4]) {
+    const bool valid = lane < rows;
+    const uint64_t live = __ballot(valid);
+    uint64_t packed = 0;   // running counts of the four widths, 16 bits each (a tile has <= 256 groups)
+    for (uint32_t jl = 0; jl < cn; ++jl) {
+        const uint32_t c = (t.codes >> (2 * jl)) & 3u;
+        const uint64_t p0 = __ballot(valid && (c & 1u)), p1 = __ballot(valid && (c & 2u));
+        // rows whose code equals mine: bit planes equal to my bits
+        const uint64_t f0 = (c & 1u) ? p0 : ~p0, f1 = (c & 2u) ? p1 : ~p1;
+        const uint64_t same = f0 & f1 & live;
+        const uint32_t slot = static_cast<uint32_t>((packed >> (16 * c)) & 0xFFFFu) + lane_rank(same);
+        if (valid) {
+            const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
+            L.list[c][slot] = lane | (jl << 8) | (sb << 16);
+        }
+        const uint32_t n3 = static_cast<uint32_t>(__popcll(p0 & p1));
+        const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1 & live));
+        const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1 & live));
+        const uint32_t n0 = static_cast<uint32_t>(__popcll(live)) - n1 - n2 - n3;
+        packed += static_cast<uint64_t>(n0) | (static_cast<uint64_t>(n1) << 16) | (static_cast<uint64_t>(n2) << 32) |
+                  (static_cast<uint64_t>(n3) << 48);
+    }
+    cnt[0] = static_cast<uint32_t>(packed & 0xFFFFu);
+    cnt[1] = static_cast<uint32_t>((packed >> 16) & 0xFFFFu);
+    cnt[2] = static_cast<uint32_t>((packed >> 32) & 0xFFFFu);
+    cnt[3] = static_cast<uint32_t>(packed >> 48);
+}
+
+__device__ __forceinline__ uint2 load8(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+
+// ---- one group (or slice) per lane, per width; results to L.part[column][row]
+
+__device__ __forceinline__ void group1(WaveLds &L, uint32_t info, uint2 v) {
+    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const float *lut = L.lut + jl * 256u;
+    float s = 0.f;
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) s += lut[k * 16u + ((v.x >> (4 * k)) & 15u)];
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) s += lut[(k + 8) * 16u + ((v.y >> (4 * k)) & 15u)];
+    L.part[jl][r] = half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * s);
+}
+
+__device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
+    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
+    const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride);
+    float a1 = 0.f, a4 = 0.f, a16 = 0.f, a64 = 0.f, a256 = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        uint32_t p[8];
+        unpack2(w[q], p);
+        const uint4 xa = xp[2 * q], xb = xp[2 * q + 1];
+        a1 = dot2(p[0], xa.x, a1);
+        a4 = dot2(p[1], xa.y, a4);
+        a16 = dot2(p[2], xa.z, a16);
+        a64 = dot2(p[3], xa.w, a64);
+        a256 = dot2(p[4], xb.x, a256);
+        a1 = dot2(p[5], xb.y, a1);
+        a4 = dot2(p[6], xb.z, a4);
+        a16 = dot2(p[7], xb.w, a16);
+    }
+    const float d = a1 + 0.25f * a4 + 0.0625f * a16 + 0.015625f * a64 + 0.00390625f * a256 - L.corr[jl][1];
+    L.part[jl][r] = half_to_float(info >> 16) * d;
+}
+
+// 4-bit: a 16-byte half group (h = task & 1); lane pairs add their halves
+__device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uint2 va, uint2 vb) {
+    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
+    const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 16u * h);
+    float a1 = 0.f, a16 = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        uint32_t p[4];
+        unpack4(w[q], p);
+        const uint4 xa = xp[q];
+        a1 = dot2(p[0], xa.x, a1);
+        a16 = dot2(p[1], xa.y, a16);
+        a1 = dot2(p[2], xa.z, a1);
+        a16 = dot2(p[3], xa.w, a16);
+    }
+    float part = a1 + 0.0625f * a16;
+    part += __shfl_xor(part, 1, kWave);
+    if (h == 0) L.part[jl][r] = half_to_float(info >> 16) * (part - L.corr[jl][2]);
+}
+
+// 8-bit: a 16-byte quarter group (qd = task & 3); lane quads add their quarters
+__device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, uint2 va, uint2 vb) {
+    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
+    const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 8u * qd);
+    float a = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < 2; ++q) {
+        const uint4 xa = xp[q];
+        uint32_t p0, p1, p2, p3;
+        unpack8(w[2 * q], p0, p1);
+        unpack8(w[2 * q + 1], p2, p3);
+        a = dot2(p0, xa.x, a);
+        a = dot2(p1, xa.y, a);
+        a = dot2(p2, xa.z, a);
+        a = dot2(p3, xa.w, a);
+    }
+    a += __shfl_xor(a, 1, kWave);
+    a += __shfl_xor(a, 2, kWave);
+    if (qd == 0) L.part[jl][r] = half_to_float(info >> 16) * (a - 1152.f * L.corr[jl][0]);
+}
+
+// Payload of the first 256 one-bit groups and of the first 64 slices of
+// each wider bucket, loaded before any of it is used. A tile has at most
+// 256 groups, so only the wider buckets can need more rounds.
+struct Staged {
+    uint32_t i1[4];
+    uint2 p1[4];
+    uint32_t i2, i4, i8;
+    uint2 p2a, p2b, p4a, p4b, p8a, p8b;
+};
+
+__device__ __forceinline__ void stage_payload(const WaveLds &L, const uint8_t *tile, const uint32_t cnt[4],
+                                              uint32_t lane, Staged &S) {
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+        const uint32_t e = lane + kWave * i;
+        if (e < cnt[0]) {
+            S.i1[i] = L.list[0][e];
+            S.p1[i] = load8(tile + 8u * e);
+        }
+    }
+    const uint8_t *b2 = tile + 8u * cnt[0];
+    const uint8_t *b4 = b2 + 16u * cnt[1];
+    const uint8_t *b8 = b4 + 32u * cnt[2];
+    if (lane < cnt[1]) {
+        S.i2 = L.list[1][lane];
+        S.p2a = load8(b2 + 16u * lane);
+        S.p2b = load8(b2 + 16u * lane + 8u);
+    }
+    if (lane < 2u * cnt[2]) {
+        S.i4 = L.list[2][lane >> 1];
+        S.p4a = load8(b4 + 16u * lane);
+        S.p4b = load8(b4 + 16u * lane + 8u);
+    }
+    if (lane < 4u * cnt[3]) {
+        S.i8 = L.list[3][lane >> 2];
+        S.p8a = load8(b8 + 16u * lane);
+        S.p8b = load8(b8 + 16u * lane + 8u);
+    }
+}
+
+__device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const uint8_t *tile, const uint32_t cnt[4],
+                                              uint32_t lane) {
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i)
+        if (lane + kWave * i < cnt[0]) group1(L, S.i1[i], S.p1[i]);
+    const uint8_t *b2 = tile + 8u * cnt[0];
+    const uint8_t *b4 = b2 + 16u * cnt[1];
+    const uint8_t *b8 = b4 + 32u * cnt[2];
+    if (lane < cnt[1]) group2(L, S.i2, S.p2a, S.p2b);
+    for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
+        group2(L, L.list[1][e], load8(b2 + 16u * e), load8(b2 + 16u * e + 8u));
+    if (lane < 2u * cnt[2]) task4(L, S.i4, lane & 1u, S.p4a, S.p4b);
+    for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
+        task4(L, L.list[2][e >> 1], e & 1u, load8(b4 + 16u * e), load8(b4 + 16u * e + 8u));
+    if (lane < 4u * cnt[3]) task8(L, S.i8, lane & 3u, S.p8a, S.p8b);
+    for (uint32_t e = lane + kWave; e < 4u * cnt[3]; e += kWave)
+        task8(L, L.list[3][e >> 2], e & 3u, load8(b8 + 16u * e), load8(b8 + 16u * e + 8u));
+}
+
+template <bool kAligned>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemv_tiles(Batch B) {
+    __shared__ WaveLds lds[kWavesPerBlock];
+    __shared__ float rowsum[kWavesPerBlock][kTileRows];
+    // which matrix, row tile and split this block serves (uniform)
+    uint32_t mi = 0;
+    while (mi + 1 < B.count && blockIdx.x >= B.m[mi + 1].block_begin) ++mi;
+    const MatArgs &M = B.m[mi];
+    const uint32_t local = blockIdx.x - M.block_begin;
+    const uint32_t a = local / M.splits, split = local % M.splits;
+    const uint32_t wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const uint32_t r0 = a * kTileRows;
+    const uint32_t rows = min(kTileRows, M.n - r0);
+    const uint32_t c_lo = (split * M.col_tiles) / M.splits, c_hi = ((split + 1) * M.col_tiles) / M.splits;
+    WaveLds &L = lds[wave];
+    float acc = 0.f;
+    uint32_t ct = c_lo + wave;
+    TileMeta cur{};
+    if (ct < c_hi) cur = load_meta<kAligned>(M, a, ct, lane, true);
+    for (; ct < c_hi; ct += kWavesPerBlock) {
+        const uint32_t cn = min(kTileGroups, M.groups - ct * kTileGroups);
+        stage_x(L, cur.xv, lane);
+        uint32_t cnt[4];
+        build_lists(L, cur, rows, cn, lane, cnt);
+        wave_lds_sync();
+        const uint8_t *tp = M.payload + cur.off;
+        Staged S;
+        stage_payload(L, tp, cnt, lane, S);
+        // the next tile's metadata travels while this tile computes
+        TileMeta nxt{};
+        if (ct + kWavesPerBlock < c_hi) nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock, lane, true);
+        tile_products(L, S, tp, cnt, lane);
+        wave_lds_sync();
+        if (lane < rows)
+            for (uint32_t jl = 0; jl < cn; ++jl) acc += L.part[jl][lane];
+        wave_lds_sync();
+        cur = nxt;
+    }
+    rowsum[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    const float sum = ((rowsum[0][lane] + rowsum[1][lane]) + rowsum[2][lane]) + rowsum[3][lane];
+    if (M.splits == 1) {
+        if (lane < rows) M.y[r0 + lane] = sum;
+        return;
+    }
+    // Split row tile: publish the partial sums with coherent (agent-scope) stores,
+    // wait until they have landed, then count arrivals; the last workgroup adds
+    // the partials in split order and resets the counter for the next call.
+    if (lane < rows)
+        __hip_atomic_store(&M.partial[static_cast<uint64_t>(split) * M.n + r0 + lane], sum, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t arrived = 0;
+    if (lane == 0) arrived = __hip_atomic_fetch_add(&M.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    arrived = __shfl(arrived, 0, kWave);
+    if (arrived != M.splits - 1) return;
+    if (lane < rows) {
+        float tot = 0.f;
+        for (uint32_t s = 0; s < M.splits; ++s)
+            tot += __hip_atomic_load(&M.partial[static_cast<uint64_t>(s) * M.n + r0 + lane], __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        M.y[r0 + lane] = tot;
+    }
+    if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Decoded codes of every group, written at its natural position; the same
+// field decoders as the product kernels (fp16 pairs 1024 + 2^s*u, then exact
+// integer recovery) plus the sign bits of 1-bit groups.
+template <bool kAligned>
+__global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict__ codes) {
+    __shared__ WaveLds L;
+    const uint32_t lane = threadIdx.x;
+    const uint32_t a = blockIdx.x / M.col_tiles, ct = blockIdx.x % M.col_tiles;
+    const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
+    const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, M.groups - j0);
+    const TileMeta t = load_meta<kAligned>(M, a, ct, lane, false);
+    const uint8_t *tp = M.payload + t.off;
+    const uint64_t k = static_cast<uint64_t>(M.groups) * 64u;
+    uint32_t cnt[4];
+    build_lists(L, t, rows, cn, lane, cnt);
+    wave_lds_sync();
+    const uint8_t *base = tp;
+    for (uint32_t wsel = 0; wsel < 4; ++wsel) {
+        const uint32_t b = 1u << wsel;
+        for (uint32_t e = lane; e < cnt[wsel]; e += kWave) {
+            const uint32_t info = L.list[wsel][e];
+            const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+            const uint32_t *src = reinterpret_cast<const uint32_t *>(base + 8u * b * e);
+            uint32_t *dst = reinterpret_cast<uint32_t *>(codes + (r0 + r) * k + 64u * (j0 + jl));
+            for (uint32_t wd = 0; wd < 2 * b; ++wd) {
+                const uint32_t v = src[wd];
+                if (b == 1) {
+                    // 32 sign bits -> 32 codes of +-1
+                    for (uint32_t o = 0; o < 8; ++o) {
+                        uint32_t out = 0;
+                        for (uint32_t i = 0; i < 4; ++i) {
+                            const uint32_t bit = (v >> (4 * o + i)) & 1u;
+                            const uint32_t pair = unpack1_pair(bit << 15, 0u);
+                            const int q = static_cast<int>(half_to_float(pair & 0xFFFFu));
+                            out |= (static_cast<uint32_t>(q) & 0xFFu) << (8 * i);
+                        }
+                        dst[wd * 8 + o] = out;
+                    }
+                } else if (b == 2) {
+                    uint32_t p[8];
+                    unpack2(v, p);
+                    const float f[8] = {1.f, 4.f, 16.f, 64.f, 256.f, 1.f, 4.f, 16.f};
+                    uint32_t outw[4] = {0, 0, 0, 0};
+                    for (uint32_t m = 0; m < 8; ++m) {
+                        const int qa = static_cast<int>((half_to_float(p[m] & 0xFFFFu) - 1024.f) / f[m]) - 2;
+                        const int qb = static_cast<int>((half_to_float(p[m] >> 16) - 1024.f) / f[m]) - 2;
+                        const uint32_t e0 = 2 * m, e1 = 2 * m + 1;
+                        outw[e0 >> 2] |= (static_cast<uint32_t>(qa) & 0xFFu) << (8 * (e0 & 3));
+                        outw[e1 >> 2] |= (static_cast<uint32_t>(qb) & 0xFFu) << (8 * (e1 & 3));
+                    }
+                    for (uint32_t o = 0; o < 4; ++o) dst[wd * 4 + o] = outw[o];
+                } else if (b == 4) {
+                    uint32_t p[4];
+                    unpack4(v, p);
+                    uint32_t outw[2] = {0, 0};
+                    for (uint32_t m = 0; m < 4; ++m) {
+                        const float f = (m & 1) ? 16.f : 1.f;
+                        const int qa = static_cast<int>((half_to_float(p[m] & 0xFFFFu) - 1024.f) / f) - 8;
+                        const int qb = static_cast<int>((half_to_float(p[m] >> 16) - 1024.f) / f) - 8;
+                        const uint32_t e0 = 2 * m, e1 = 2 * m + 1;
+                        outw[e0 >> 2] |= (static_cast<uint32_t>(qa) & 0xFFu) << (8 * (e0 & 3));
+                        outw[e1 >> 2] |= (static_cast<uint32_t>(qb) & 0xFFu) << (8 * (e1 & 3));
+                    }
+                    dst[wd * 2] = outw[0];
+                    dst[wd * 2 + 1] = outw[1];
+                } else {
+                    uint32_t p0, p1;
+                    unpack8(v, p0, p1);
+                    const int q0 = static_cast<int>(half_to_float(p0 & 0xFFFFu)) - 1152;
+                    const int q1 = static_cast<int>(half_to_float(p0 >> 16)) - 1152;
+                    const int q2 = static_cast<int>(half_to_float(p1 & 0xFFFFu)) - 1152;
+                    const int q3 = static_cast<int>(half_to_float(p1 >> 16)) - 1152;
+                    dst[wd] = (static_cast<uint32_t>(q0) & 0xFFu) | ((static_cast<uint32_t>(q1) & 0xFFu) << 8) |
+                              ((static_cast<uint32_t>(q2) & 0xFFu) << 16) | ((static_cast<uint32_t>(q3) & 0xFFu) << 24);
+                }
+            }
+        }
+        base += 8u * b * cnt[wsel];
     }
 }
 
 __global__ void fill_zero(float *__restrict__ y, uint64_t count) {
-    const uint64_t i = uint64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < count) y[i] = 0.f;
 }
 
+// ---------------------------------------------------------------- host side
+
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline uint32_t ceil_div(uint32_t a, uint32_t b) { return (a + b - 1) / b; }
 
 vbq_status check_matrix(const char *who, const vbq_matrix *w) {
     if (!w) return fail(VBQ_ERR_NULL, "%s: matrix view is NULL", who);
@@ -98,12 +551,10 @@ vbq_status check_matrix(const char *who, const vbq_matrix *w) {
         return fail(VBQ_ERR_ABI, "%s: abi_version %u, library %u", who, w->abi_version, VBQ_ABI_VERSION);
     if (w->k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "%s: k=%u is not a multiple of 64", who, w->k);
     if (w->k > VBQ_MAX_K) return fail(VBQ_ERR_SHAPE, "%s: k=%u exceeds %u", who, w->k, VBQ_MAX_K);
-    if (w->n == 0) return VBQ_OK;
-    if (!w->row_offsets) return fail(VBQ_ERR_NULL, "%s: row_offsets is NULL", who);
-    if (w->k && (!w->widths || !w->scales || !w->payload))
-        return fail(VBQ_ERR_NULL, "%s: widths, scales or payload is NULL", who);
-    if (!aligned16(w->row_offsets) || (w->k && (!aligned16(w->widths) || !aligned16(w->scales) ||
-                                                !aligned16(w->payload))))
+    if (w->n == 0 || w->k == 0) return VBQ_OK;
+    if (!w->tile_offsets || !w->widths || !w->scales || !w->payload)
+        return fail(VBQ_ERR_NULL, "%s: widths, scales, tile_offsets or payload is NULL", who);
+    if (!aligned16(w->tile_offsets) || !aligned16(w->widths) || !aligned16(w->scales) || !aligned16(w->payload))
         return fail(VBQ_ERR_ALIGN, "%s: a matrix array is not 16-byte aligned", who);
     return VBQ_OK;
 }
@@ -114,36 +565,180 @@ vbq_status launched(const char *who) {
     return VBQ_OK;
 }
 
-vbq_status run_gemm(const char *who, const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y, void *stream) {
-    vbq::clear_error();
-    vbq_status st = check_matrix(who, w);
-    if (st != VBQ_OK) return st;
-    if (m == 0 || m > VBQ_MAX_BATCH) return fail(VBQ_ERR_SHAPE, "%s: m=%u outside [1, %u]", who, m, VBQ_MAX_BATCH);
+// Scratch for split row tiles: one buffer per (device, stream), grown on demand.
+// The buffer starts with a region that only ever holds arrival counters: it is
+// zeroed when allocated and every counter is reset to zero by the last
+// workgroup of its row tile, so the region is all zeros between calls however
+// the next call lays out its matrices. Partial sums follow it.
+struct Scratch {
+    void *ptr = nullptr;
+    size_t counter_bytes = 0;
+    size_t partial_bytes = 0;
+};
+
+std::mutex g_scratch_mu;
+std::unordered_map<uint64_t, Scratch> g_scratch;
+
+vbq_status scratch_for(const char *who, hipStream_t stream, size_t counters, size_t partials, uint32_t **ctr_out,
+                       char **part_out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: hipGetDevice failed", who);
+    const uint64_t key = (static_cast<uint64_t>(dev) << 56) ^ reinterpret_cast<uintptr_t>(stream);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    Scratch &s = g_scratch[key];
+    if (s.counter_bytes < counters || s.partial_bytes < partials) {
+        if (s.ptr) {
+            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(s.ptr) != hipSuccess)
+                return fail(VBQ_ERR_HIP, "%s: could not release the old scratch buffer", who);
+            s.ptr = nullptr;
+        }
+        const size_t cb = std::max<size_t>(counters, std::max<size_t>(s.counter_bytes, 64u << 10));
+        const size_t pb = std::max<size_t>(partials, std::max<size_t>(s.partial_bytes, 1u << 20));
+        if (hipMalloc(&s.ptr, cb + pb) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch hipMalloc failed", who);
+        if (hipMemset(s.ptr, 0, cb + pb) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch memset failed", who);
+        s.counter_bytes = cb;
+        s.partial_bytes = pb;
+    }
+    *ctr_out = static_cast<uint32_t *>(s.ptr);
+    *part_out = static_cast<char *>(s.ptr) + s.counter_bytes;
+    return VBQ_OK;
+}
+
+inline size_t partial_bytes(uint32_t splits, uint32_t n) {
+    return (static_cast<size_t>(splits) * n * 4 + 255) / 256 * 256;
+}
+
+// One launch for up to VBQ_MAX_MULTI independent GEMVs.
+vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
+                       uint32_t count, hipStream_t stream) {
+    Batch B{};
+    uint32_t blocks = 0, total_row_tiles = 0;
+    bool aligned = true;
+    for (uint32_t i = 0; i < count; ++i) {
+        const vbq_matrix *w = ws[i];
+        if (w->n && w->k) total_row_tiles += ceil_div(w->n, kTileRows);
+    }
+    const uint32_t want_blocks = 768;
+    const uint32_t factor = total_row_tiles ? ceil_div(want_blocks, total_row_tiles) : 1;
+    size_t counter_slots = 0, partial_total = 0;
+    uint32_t used = 0;
+    bool any_launch = false;
+    for (uint32_t i = 0; i < count; ++i) {
+        const vbq_matrix *w = ws[i];
+        if (w->n == 0) continue;
+        if (w->k == 0) {
+            const uint64_t cnt = w->n;
+            hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream, ys[i],
+                               cnt);
+            any_launch = true;
+            continue;
+        }
+        MatArgs &M = B.m[used++];
+        M.widths = w->widths;
+        M.scales = w->scales;
+        M.tile_offsets = w->tile_offsets;
+        M.payload = w->payload;
+        M.x = xs[i];
+        M.y = ys[i];
+        M.n = w->n;
+        M.groups = w->k / VBQ_GROUP;
+        M.col_tiles = ceil_div(M.groups, kTileGroups);
+        const uint32_t row_tiles = ceil_div(M.n, kTileRows);
+        M.splits = std::max(1u, std::min(ceil_div(M.col_tiles, kWavesPerBlock), factor));
+        M.block_begin = blocks;
+        blocks += row_tiles * M.splits;
+        if (M.groups % 4) aligned = false;
+        if (M.splits > 1) {
+            counter_slots += row_tiles;
+            partial_total += partial_bytes(M.splits, M.n);
+        }
+    }
+    B.count = used;
+    if (used == 0) return any_launch ? launched(who) : VBQ_OK;
+    if (counter_slots) {
+        uint32_t *ctr = nullptr;
+        char *part = nullptr;
+        vbq_status st = scratch_for(who, stream, counter_slots * 4, partial_total, &ctr, &part);
+        if (st != VBQ_OK) return st;
+        for (uint32_t i = 0; i < used; ++i) {
+            MatArgs &M = B.m[i];
+            if (M.splits == 1) continue;
+            M.counters = ctr;
+            ctr += ceil_div(M.n, kTileRows);
+            M.partial = reinterpret_cast<float *>(part);
+            part += partial_bytes(M.splits, M.n);
+        }
+    }
+    if (aligned)
+        hipLaunchKernelGGL(gemv_tiles<true>, dim3(blocks), dim3(256), 0, stream, B);
+    else
+        hipLaunchKernelGGL(gemv_tiles<false>, dim3(blocks), dim3(256), 0, stream, B);
+    return launched(who);
+}
+
+vbq_status check_vectors(const char *who, const vbq_matrix *w, const void *x, const void *y) {
     if (w->n == 0) return VBQ_OK;
     if (!y || (w->k && !x)) return fail(VBQ_ERR_NULL, "%s: x or y is NULL", who);
     if (!aligned16(y) || (w->k && !aligned16(x))) return fail(VBQ_ERR_ALIGN, "%s: x or y is not 16-byte aligned", who);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    (void)hipGetLastError();
-    if (w->k == 0) {
-        const uint64_t count = uint64_t(m) * w->n;
-        hipLaunchKernelGGL(fill_zero, dim3(uint32_t((count + 255) / 256)), dim3(256), 0, s, y, count);
-        return launched(who);
-    }
-    const uint32_t groups = w->k / VBQ_GROUP;
-    hipLaunchKernelGGL(gemv_rowwave, dim3((w->n + 3) / 4, m), dim3(256), 0, s, w->widths, w->scales, w->row_offsets,
-                       w->payload, x, y, w->n, groups, w->k, m);
-    return launched(who);
+    return VBQ_OK;
 }
 
 }  // namespace
 
+extern "C" vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
+                                     uint32_t count, void *stream) {
+    vbq::clear_error();
+    const char *who = "vbq_gemv_multi";
+    if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
+    if (count == 0) return VBQ_OK;
+    if (!ws || !xs || !ys) return fail(VBQ_ERR_NULL, "%s: ws, xs or ys is NULL", who);
+    for (uint32_t i = 0; i < count; ++i) {
+        vbq_status st = check_matrix(who, ws[i]);
+        if (st != VBQ_OK) return st;
+        st = check_vectors(who, ws[i], xs[i], ys[i]);
+        if (st != VBQ_OK) return st;
+    }
+    (void)hipGetLastError();
+    return gemv_launch(who, ws, xs, ys, count, static_cast<hipStream_t>(stream));
+}
+
 extern "C" vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream) {
-    return run_gemm("vbq_gemv", w, x, 1, y, stream);
+    vbq::clear_error();
+    const char *who = "vbq_gemv";
+    vbq_status st = check_matrix(who, w);
+    if (st != VBQ_OK) return st;
+    st = check_vectors(who, w, x, y);
+    if (st != VBQ_OK) return st;
+    (void)hipGetLastError();
+    return gemv_launch(who, &w, &x, &y, 1, static_cast<hipStream_t>(stream));
 }
 
 extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                                           void *stream) {
-    return run_gemm("vbq_gemm_smallbatch", w, x, m, y, stream);
+    vbq::clear_error();
+    const char *who = "vbq_gemm_smallbatch";
+    if (m == 0 || m > VBQ_MAX_BATCH) return fail(VBQ_ERR_SHAPE, "%s: m=%u outside [1, %u]", who, m, VBQ_MAX_BATCH);
+    vbq_status st = check_matrix(who, w);
+    if (st != VBQ_OK) return st;
+    st = check_vectors(who, w, x, y);
+    if (st != VBQ_OK) return st;
+    if (w->n == 0) return VBQ_OK;
+    (void)hipGetLastError();
+    // each input row as its own GEMV of one batched launch
+    const vbq_matrix *ws[VBQ_MAX_MULTI];
+    const uint16_t *xs[VBQ_MAX_MULTI];
+    float *ys[VBQ_MAX_MULTI];
+    for (uint32_t m0 = 0; m0 < m; m0 += VBQ_MAX_MULTI) {
+        const uint32_t cnt = std::min(VBQ_MAX_MULTI, m - m0);
+        for (uint32_t i = 0; i < cnt; ++i) {
+            ws[i] = w;
+            xs[i] = x + static_cast<uint64_t>(m0 + i) * w->k;
+            ys[i] = y + static_cast<uint64_t>(m0 + i) * w->n;
+        }
+        st = gemv_launch(who, ws, xs, ys, cnt, static_cast<hipStream_t>(stream));
+        if (st != VBQ_OK) return st;
+    }
+    return VBQ_OK;
 }
 
 extern "C" vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, void *stream) {
@@ -154,7 +749,20 @@ extern "C" vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, v
     if (!codes_out) return fail(VBQ_ERR_NULL, "vbq_unpack_codes: codes_out is NULL");
     if (!aligned16(codes_out)) return fail(VBQ_ERR_ALIGN, "vbq_unpack_codes: codes_out is not 16-byte aligned");
     (void)hipGetLastError();
-    hipLaunchKernelGGL(unpack_rowwave, dim3((w->n + 3) / 4), dim3(256), 0, static_cast<hipStream_t>(stream),
-                       w->widths, w->row_offsets, w->payload, codes_out, w->n, w->k / VBQ_GROUP);
+    MatArgs M{};
+    M.widths = w->widths;
+    M.scales = w->scales;
+    M.tile_offsets = w->tile_offsets;
+    M.payload = w->payload;
+    M.n = w->n;
+    M.groups = w->k / VBQ_GROUP;
+    M.col_tiles = ceil_div(M.groups, kTileGroups);
+    M.splits = 1;
+    const uint32_t tiles = ceil_div(M.n, kTileRows) * M.col_tiles;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (M.groups % 4 == 0)
+        hipLaunchKernelGGL(unpack_tiles<true>, dim3(tiles), dim3(64), 0, s, M, codes_out);
+    else
+        hipLaunchKernelGGL(unpack_tiles<false>, dim3(tiles), dim3(64), 0, s, M, codes_out);
     return launched("vbq_unpack_codes");
 }

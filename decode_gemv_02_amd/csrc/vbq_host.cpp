@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <string>
+#include <vector>
 
 namespace {
 
@@ -63,7 +65,7 @@ extern "C" const char *vbq_status_string(vbq_status s) {
         case VBQ_ERR_CODE: return "code off its width's grid";
         case VBQ_ERR_SCALE: return "non-finite scale";
         case VBQ_ERR_CAPACITY: return "payload capacity too small";
-        case VBQ_ERR_OFFSETS: return "row offsets inconsistent with widths";
+        case VBQ_ERR_OFFSETS: return "tile offsets inconsistent with widths";
         case VBQ_ERR_ALIGN: return "pointer not 16-byte aligned";
         case VBQ_ERR_TOO_LARGE: return "payload exceeds 32-bit offsets";
         case VBQ_ERR_HIP: return "HIP runtime error";
@@ -73,6 +75,73 @@ extern "C" const char *vbq_status_string(vbq_status s) {
 }
 
 extern "C" const char *vbq_last_error(void) { return g_last_error.c_str(); }
+
+namespace {
+
+// bit position of element i inside a b-bit group (see the layout in vbq.h)
+inline uint32_t field_pos(uint32_t b, uint32_t i) {
+    switch (b) {
+        case 1: return i;
+        case 2: { const uint32_t e = i & 15; return 32 * (i >> 4) + 2 * ((e >> 1) | ((e & 1) << 3)); }
+        case 4: { const uint32_t e = i & 7; return 32 * (i >> 3) + 4 * ((e >> 1) | ((e & 1) << 2)); }
+        default: return 8 * i;
+    }
+}
+
+inline uint32_t width_slot(uint32_t b) { return b == 1 ? 0 : b == 2 ? 1 : b == 4 ? 2 : 3; }
+
+uint64_t tiles_of(uint32_t n, uint32_t G) {
+    return uint64_t((n + VBQ_TILE_ROWS - 1) / VBQ_TILE_ROWS) * ((G + VBQ_TILE_GROUPS - 1) / VBQ_TILE_GROUPS);
+}
+
+// Slot of group (r, j) in the width-code and scale arrays: tiles one after the
+// other (row tile major), the groups of a tile row-major inside it. A full
+// row tile holds 64*G slots; a tile of R rows and C groups holds R*C.
+inline uint64_t meta_slot(uint32_t n, uint32_t G, uint32_t r, uint32_t j) {
+    const uint32_t r0 = r / VBQ_TILE_ROWS * VBQ_TILE_ROWS, j0 = j / VBQ_TILE_GROUPS * VBQ_TILE_GROUPS;
+    const uint32_t R = std::min<uint32_t>(VBQ_TILE_ROWS, n - r0), C = std::min<uint32_t>(VBQ_TILE_GROUPS, G - j0);
+    return uint64_t(r0) * G + uint64_t(R) * j0 + uint64_t(r - r0) * C + (j - j0);
+}
+
+// Payload offset of every group, plus the tile offsets, for per-group widths
+// given by width(r, j). Inside a tile the four width buckets follow each other;
+// a group's place in its bucket is its column-major rank among same-width
+// groups of the tile.
+template <class WidthFn>
+uint64_t place_groups(uint32_t n, uint32_t G, WidthFn width, uint64_t *group_off, uint32_t *tile_off) {
+    uint64_t pos = 0, tile = 0;
+    for (uint32_t r0 = 0; r0 < n; r0 += VBQ_TILE_ROWS) {
+        const uint32_t r1 = std::min(n, r0 + VBQ_TILE_ROWS);
+        for (uint32_t j0 = 0; j0 < G; j0 += VBQ_TILE_GROUPS) {
+            const uint32_t j1 = std::min(G, j0 + VBQ_TILE_GROUPS);
+            uint64_t bucket_bytes[4] = {0, 0, 0, 0};
+            for (uint32_t j = j0; j < j1; ++j)
+                for (uint32_t r = r0; r < r1; ++r) {
+                    const uint32_t b = width(r, j);
+                    bucket_bytes[width_slot(b)] += 8u * b;
+                }
+            uint64_t next[4];
+            next[0] = pos;
+            for (int i = 1; i < 4; ++i) next[i] = next[i - 1] + bucket_bytes[i - 1];
+            if (tile_off) tile_off[tile] = uint32_t(pos);
+            for (uint32_t j = j0; j < j1; ++j)
+                for (uint32_t r = r0; r < r1; ++r) {
+                    const uint64_t t = uint64_t(r) * G + j;
+                    const uint32_t b = width(r, j);
+                    if (group_off) group_off[t] = next[width_slot(b)];
+                    next[width_slot(b)] += 8u * b;
+                }
+            pos = next[3];
+            ++tile;
+        }
+    }
+    if (tile_off) tile_off[tile] = uint32_t(pos);
+    return pos;
+}
+
+}  // namespace
+
+extern "C" uint64_t vbq_tile_count(uint32_t n, uint32_t k) { return tiles_of(n, k / VBQ_GROUP); }
 
 extern "C" vbq_status vbq_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits, vbq_sizes *out) {
     vbq::clear_error();
@@ -91,7 +160,7 @@ extern "C" vbq_status vbq_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits
                     (unsigned long long)payload);
     out->widths_bytes = (groups + 3) / 4;
     out->scales_bytes = 2 * groups;
-    out->offsets_bytes = 4 * (uint64_t(n) + 1);
+    out->offsets_bytes = 4 * (tiles_of(n, k / VBQ_GROUP) + 1);
     out->payload_bytes = payload;
     out->total_bytes = out->widths_bytes + out->scales_bytes + out->offsets_bytes + out->payload_bytes;
     return VBQ_OK;
@@ -99,13 +168,13 @@ extern "C" vbq_status vbq_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits
 
 extern "C" vbq_status vbq_pack(uint32_t n, uint32_t k, const uint8_t *bits, const int8_t *codes,
                                const uint16_t *scales, uint8_t *widths_out, uint16_t *scales_out,
-                               uint32_t *row_offsets_out, uint8_t *payload_out, uint64_t payload_capacity) {
+                               uint32_t *tile_offsets_out, uint8_t *payload_out, uint64_t payload_capacity) {
     vbq_sizes sz;
     vbq_status st = vbq_pack_sizes(n, k, bits, &sz);
     if (st != VBQ_OK) return st;
     const uint32_t G = k / VBQ_GROUP;
     const uint64_t groups = uint64_t(n) * G;
-    if (!row_offsets_out) return fail(VBQ_ERR_NULL, "vbq_pack: row_offsets_out is NULL");
+    if (!tile_offsets_out) return fail(VBQ_ERR_NULL, "vbq_pack: tile_offsets_out is NULL");
     if (groups && (!codes || !scales || !widths_out || !scales_out))
         return fail(VBQ_ERR_NULL, "vbq_pack: codes, scales, widths_out or scales_out is NULL");
     if (sz.payload_bytes && !payload_out) return fail(VBQ_ERR_NULL, "vbq_pack: payload_out is NULL");
@@ -123,26 +192,23 @@ extern "C" vbq_status vbq_pack(uint32_t n, uint32_t k, const uint8_t *bits, cons
                 return fail(VBQ_ERR_CODE, "vbq_pack: code %d at group %llu element %u is off the %u-bit grid",
                             q[i], (unsigned long long)t, i, bits[t]);
     }
+    std::vector<uint64_t> off(groups);
+    place_groups(n, G, [&](uint32_t r, uint32_t j) { return uint32_t(bits[uint64_t(r) * G + j]); }, off.data(),
+                 tile_offsets_out);
     std::memset(widths_out, 0, sz.widths_bytes);
     if (sz.payload_bytes) std::memset(payload_out, 0, sz.payload_bytes);
-    uint64_t pos = 0;
-    row_offsets_out[0] = 0;
-    for (uint32_t r = 0; r < n; ++r) {
-        for (uint32_t j = 0; j < G; ++j) {
-            const uint64_t t = uint64_t(r) * G + j;
-            const uint32_t b = bits[t];
-            widths_out[t >> 2] |= uint8_t(width_code(uint8_t(b)) << (2 * (t & 3)));
-            scales_out[t] = scales[t];
-            const int8_t *q = codes + t * VBQ_GROUP;
-            uint8_t *dst = payload_out + pos;
-            // whole fields never straddle a byte because b divides 8
-            for (uint32_t i = 0; i < VBQ_GROUP; ++i) {
-                const uint32_t bit = b * i;
-                dst[bit >> 3] |= uint8_t(encode_field(q[i], b) << (bit & 7));
-            }
-            pos += 8u * b;
+    for (uint64_t t = 0; t < groups; ++t) {
+        const uint32_t b = bits[t];
+        const uint64_t m = meta_slot(n, G, uint32_t(t / G), uint32_t(t % G));
+        widths_out[m >> 2] |= uint8_t(width_code(uint8_t(b)) << (2 * (m & 3)));
+        scales_out[m] = scales[t];
+        const int8_t *q = codes + t * VBQ_GROUP;
+        uint8_t *dst = payload_out + off[t];
+        // fields never straddle a byte: b divides 8 and every field starts at a multiple of b
+        for (uint32_t i = 0; i < VBQ_GROUP; ++i) {
+            const uint32_t bit = field_pos(b, i);
+            dst[bit >> 3] |= uint8_t(encode_field(q[i], b) << (bit & 7));
         }
-        row_offsets_out[r + 1] = uint32_t(pos);
     }
     return VBQ_OK;
 }
@@ -155,35 +221,37 @@ extern "C" vbq_status vbq_validate_host(const vbq_matrix *w) {
     if (w->k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_validate_host: k=%u is not a multiple of 64", w->k);
     const uint32_t G = w->k / VBQ_GROUP;
     const uint64_t groups = uint64_t(w->n) * G;
-    if (!w->row_offsets) return fail(VBQ_ERR_NULL, "vbq_validate_host: row_offsets is NULL");
+    const uint64_t tiles = tiles_of(w->n, G);
+    if (!w->tile_offsets) return fail(VBQ_ERR_NULL, "vbq_validate_host: tile_offsets is NULL");
     if (groups && (!w->widths || !w->scales || !w->payload))
         return fail(VBQ_ERR_NULL, "vbq_validate_host: widths, scales or payload is NULL");
-    if (w->row_offsets[0] != 0) return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: row_offsets[0] != 0");
-    uint64_t pos = 0;
-    for (uint32_t r = 0; r < w->n; ++r) {
-        for (uint32_t j = 0; j < G; ++j) {
-            const uint64_t t = uint64_t(r) * G + j;
-            const uint32_t b = 1u << ((w->widths[t >> 2] >> (2 * (t & 3))) & 3);
-            if (!half_is_finite(w->scales[t]))
-                return fail(VBQ_ERR_SCALE, "vbq_validate_host: scale of group %llu not finite", (unsigned long long)t);
-            if (b >= 2 && pos + 8u * b <= w->payload_bytes) {
-                const uint8_t *src = w->payload + pos;
-                for (uint32_t i = 0; i < VBQ_GROUP; ++i) {
-                    const uint32_t bit = b * i;
-                    const uint32_t f = (src[bit >> 3] >> (bit & 7)) & ((1u << b) - 1u);
-                    if (f == (1u << (b - 1)))
-                        return fail(VBQ_ERR_CODE, "vbq_validate_host: reserved pattern at group %llu element %u",
-                                    (unsigned long long)t, i);
-                }
-            }
-            pos += 8u * b;
-        }
-        if (w->row_offsets[r + 1] != pos)
-            return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: row_offsets[%u]=%u, widths give %llu", r + 1,
-                        w->row_offsets[r + 1], (unsigned long long)pos);
-    }
-    if (pos != w->payload_bytes)
+    auto width = [&](uint32_t r, uint32_t j) {
+        const uint64_t m = meta_slot(w->n, G, r, j);
+        return 1u << ((w->widths[m >> 2] >> (2 * (m & 3))) & 3u);
+    };
+    std::vector<uint64_t> off(groups);
+    std::vector<uint32_t> expect(tiles + 1);
+    const uint64_t total = place_groups(w->n, G, width, off.data(), expect.data());
+    for (uint64_t i = 0; i <= tiles; ++i)
+        if (w->tile_offsets[i] != expect[i])
+            return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: tile_offsets[%llu]=%u, widths give %u",
+                        (unsigned long long)i, w->tile_offsets[i], expect[i]);
+    if (total != w->payload_bytes)
         return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: payload_bytes=%u, widths give %llu", w->payload_bytes,
-                    (unsigned long long)pos);
+                    (unsigned long long)total);
+    for (uint64_t t = 0; t < groups; ++t) {
+        if (!half_is_finite(w->scales[t]))
+            return fail(VBQ_ERR_SCALE, "vbq_validate_host: scale slot %llu not finite", (unsigned long long)t);
+        const uint32_t b = width(uint32_t(t / G), uint32_t(t % G));
+        if (b == 1) continue;
+        const uint8_t *src = w->payload + off[t];
+        for (uint32_t i = 0; i < VBQ_GROUP; ++i) {
+            const uint32_t bit = field_pos(b, i);
+            const uint32_t f = (src[bit >> 3] >> (bit & 7)) & ((1u << b) - 1u);
+            if (f == (1u << (b - 1)))
+                return fail(VBQ_ERR_CODE, "vbq_validate_host: reserved pattern at group %llu element %u",
+                            (unsigned long long)t, i);
+        }
+    }
     return VBQ_OK;
 }

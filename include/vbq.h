@@ -14,26 +14,42 @@
  *     whole bytes.
  *
  * Packed layout (what the paper leaves open is fixed here):
- *   W is n x k, row-major, k % 64 == 0, G = k / 64 groups per row; flat group
- *   index t = r*G + j covers W[r][64j .. 64j+63].
- *   widths      uint8 [ceil(n*G/4)]  2-bit code c_t = (widths[t/4] >> 2*(t%4)) & 3,
- *                                    width b_t = 1 << c_t in {1, 2, 4, 8}.
- *   scales      uint16 [n*G]         IEEE binary16 bit pattern of s_t.
- *   row_offsets uint32 [n+1]         exclusive prefix sum of the group payload
- *                                    sizes 8*b_t, sampled at row starts:
- *                                    row_offsets[0] = 0, row_offsets[r+1] =
- *                                    row_offsets[r] + sum_j 8*b_{r,j}.
- *   payload     uint8 [row_offsets[n]]  group (r, j) occupies 8*b bytes at
- *                                    row_offsets[r] + sum_{j'<j} 8*b_{r,j'};
- *                                    element i is the b-bit field at bit b*i of
- *                                    those bytes, little-endian (byte b*i/8,
- *                                    bit b*i%8).
- *   field f -> code q: b = 1: f is a sign bit (0 -> +1, 1 -> -1).
- *                      b >= 2: two's complement; -2^(b-1) is off the grid and
- *                      rejected by vbq_pack (kernels read it as -2^(b-1)).
- *   Result: y[m][r] = sum_j s_{r,j} * sum_i q_{r,j,i} * x[m][64j+i], with
- *   exact fp16 codes, fp32 products and sums, and the scale applied in fp32
- *   once per group. y is fp32.
+ *   W is n x k, row-major, k % 64 == 0, G = k / 64 groups per row; group
+ *   (r, j) covers W[r][64j .. 64j+63].
+ *   tiles        groups are cut into tiles of VBQ_TILE_ROWS = 64 rows by
+ *                VBQ_TILE_GROUPS = 4 groups (edge tiles are smaller); tile
+ *                (a, c) holds rows [64a, 64a+64) and groups [4c, 4c+4) and is
+ *                numbered a * ceil(G/4) + c.
+ *   metadata slot of group (r, j), in tile order: with r0 = 64a, j0 = 4c and
+ *                the tile's R rows and C groups,
+ *                  m = r0*G + R*j0 + (r - r0)*C + (j - j0),
+ *                i.e. tiles one after the other, each tile row-major, so the
+ *                metadata of one tile is one contiguous run of R*C slots.
+ *   widths       uint8 [ceil(n*G/4)]  2-bit code c = (widths[m/4] >> 2*(m%4)) & 3,
+ *                                     width b = 1 << c in {1, 2, 4, 8}.
+ *   scales       uint16 [n*G]         scales[m] = IEEE binary16 bit pattern of s.
+ *   tile_offsets uint32 [tiles+1]     exclusive prefix sum of the tile payload
+ *                                     sizes (each the sum of 8*b over its
+ *                                     groups); tile_offsets[tiles] = payload size.
+ *   payload      uint8                tile after tile; inside a tile the groups
+ *                                     are bucketed by width (1, 2, 4 then 8
+ *                                     bits) and ordered column-major inside a
+ *                                     bucket (j ascending, then r ascending);
+ *                                     each group holds 8*b bytes, so its offset
+ *                                     is the exclusive prefix sum of 8*b over
+ *                                     the groups stored before it.
+ *   inside a group, element i (weight W[r][64j+i]) is a b-bit field:
+ *     b = 1: bit i (byte i/8, bit i%8) - a sign bit: 0 -> +1, 1 -> -1;
+ *     b = 8: byte i, two's complement;
+ *     b = 2: in little-endian 32-bit word i/16, field m = e/2 + 8*(e%2) with
+ *            e = i%16, bits 2m..2m+1, two's complement;
+ *     b = 4: in little-endian 32-bit word i/8, field m = e/2 + 4*(e%2) with
+ *            e = i%8, bits 4m..4m+3, two's complement.
+ *   The two's complement pattern -2^(b-1) is off the grid: vbq_pack rejects
+ *   it (kernels read it as -2^(b-1)).
+ *   Result: y[m][r] = sum_j s_{r,j} * sum_i q_{r,j,i} * x[m][64j+i]; codes are
+ *   exact in fp16, products and sums are fp32, the scale is applied in fp32
+ *   once per group, y is fp32.
  *
  * Conventions for every entry point:
  *   - All buffers belong to the caller. Host entry points (vbq_pack*,
@@ -64,8 +80,11 @@ extern "C" {
 
 #define VBQ_ABI_VERSION 1u
 #define VBQ_GROUP 64u
+#define VBQ_TILE_ROWS 64u
+#define VBQ_TILE_GROUPS 4u
 #define VBQ_MAX_K 65536u      /* k limit of the device entry points */
 #define VBQ_MAX_BATCH 64u     /* m limit of vbq_gemm_smallbatch */
+#define VBQ_MAX_MULTI 16u     /* matrices per vbq_gemv_multi call */
 
 typedef enum vbq_status {
     VBQ_OK = 0,
@@ -75,7 +94,7 @@ typedef enum vbq_status {
     VBQ_ERR_CODE = 4,       /* a code is off its width's grid */
     VBQ_ERR_SCALE = 5,      /* a scale is inf or NaN */
     VBQ_ERR_CAPACITY = 6,   /* payload_capacity is smaller than the packed payload */
-    VBQ_ERR_OFFSETS = 7,    /* row_offsets / payload_bytes disagree with the widths */
+    VBQ_ERR_OFFSETS = 7,    /* tile_offsets / payload_bytes disagree with the widths */
     VBQ_ERR_ALIGN = 8,      /* a device pointer is not 16-byte aligned */
     VBQ_ERR_TOO_LARGE = 9,  /* payload would not fit 32-bit offsets */
     VBQ_ERR_HIP = 10,       /* the HIP runtime refused a launch */
@@ -86,7 +105,7 @@ typedef enum vbq_status {
 typedef struct vbq_sizes {
     uint64_t widths_bytes;
     uint64_t scales_bytes;
-    uint64_t offsets_bytes;
+    uint64_t offsets_bytes;     /* tile_offsets: 4 * (tiles + 1) */
     uint64_t payload_bytes;
     uint64_t total_bytes;   /* = sum of the four; the bytes one GEMV must stream for W */
 } vbq_sizes;
@@ -98,10 +117,10 @@ typedef struct vbq_matrix {
     uint32_t abi_version;          /* VBQ_ABI_VERSION */
     uint32_t n;                    /* rows (outputs) */
     uint32_t k;                    /* columns (inputs), multiple of 64 */
-    uint32_t payload_bytes;        /* == row_offsets[n] */
+    uint32_t payload_bytes;        /* == tile_offsets[tiles] */
     const uint8_t *widths;
     const uint16_t *scales;
-    const uint32_t *row_offsets;
+    const uint32_t *tile_offsets;
     const uint8_t *payload;
 } vbq_matrix;
 
@@ -114,18 +133,23 @@ VBQ_API uint32_t vbq_abi_version(void);
 VBQ_API vbq_status vbq_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits, vbq_sizes *out);
 
 /* Pack integer codes into the layout above (host, single-threaded,
- * deterministic). bits: [n*G] widths; codes: int8 [n][k] on each group's grid
- * (§3.1 Eq. (1): |q| <= 2^(b-1)-1, b = 1: q = +-1); scales: binary16 [n*G],
- * finite. Output arrays sized by vbq_pack_sizes; payload_capacity is the size
+ * deterministic). Inputs are in natural order, group (r, j) at r*G + j:
+ * bits: [n*G] widths; codes: int8 [n][k] on each group's grid (§3.1 Eq. (1):
+ * |q| <= 2^(b-1)-1, b = 1: q = +-1); scales: binary16 [n*G], finite. Outputs
+ * widths_out and scales_out are in metadata-slot (tile) order. Output arrays sized by vbq_pack_sizes; payload_capacity is the size
  * of payload_out in bytes. Every input is checked before anything is written:
  * NULL, SHAPE, WIDTH, CODE, SCALE, CAPACITY, TOO_LARGE. */
 VBQ_API vbq_status vbq_pack(uint32_t n, uint32_t k, const uint8_t *bits, const int8_t *codes,
                     const uint16_t *scales, uint8_t *widths_out, uint16_t *scales_out,
-                    uint32_t *row_offsets_out, uint8_t *payload_out, uint64_t payload_capacity);
+                    uint32_t *tile_offsets_out, uint8_t *payload_out, uint64_t payload_capacity);
 
-/* Check a packed matrix held in host memory: k % 64, row_offsets equal to the
- * prefix sum of 8*b, payload_bytes == row_offsets[n], every field on its
- * grid, every scale finite. Errors: NULL, ABI, SHAPE, OFFSETS, CODE, SCALE. */
+/* Number of tiles of an n x k matrix: ceil(n/64) * ceil(k/256). */
+VBQ_API uint64_t vbq_tile_count(uint32_t n, uint32_t k);
+
+/* Check a packed matrix held in host memory: k % 64, tile_offsets equal to
+ * the prefix sum of the tile payload sizes, payload_bytes == tile_offsets[tiles],
+ * every field on its grid, every scale finite.
+ * Errors: NULL, ABI, SHAPE, OFFSETS, CODE, SCALE. */
 VBQ_API vbq_status vbq_validate_host(const vbq_matrix *host_view);
 
 /* y = W x for one fp16 vector (§6 fused decode at batch 1).
@@ -133,6 +157,17 @@ VBQ_API vbq_status vbq_validate_host(const vbq_matrix *host_view);
  * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (k > VBQ_MAX_K), ALIGN,
  * HIP. n == 0 enqueues nothing; k == 0 writes y = 0. */
 VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream);
+
+/* Several independent batch-1 GEMVs in one launch: ys[i] = W_i xs[i] for
+ * i < count <= VBQ_MAX_MULTI. ws, xs and ys are host arrays of count entries
+ * (the matrix views and x / y pointers as for vbq_gemv). Matrices that read
+ * the same activation (q/k/v, gate/up) or a whole layer's projections run as
+ * one dispatch. Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (count),
+ * ALIGN, HIP. Scratch: calls with large-k, small-n matrices use a
+ * library-owned device buffer per (device, stream), allocated on first need;
+ * calls that overlap on the same stream handle are not allowed. */
+VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
+                                  uint32_t count, void *stream);
 
 /* Y = X W^T for m <= VBQ_MAX_BATCH fp16 vectors (small-batch decode).
  * x: device binary16 [m][k] row-major; y: device fp32 [m][n] row-major

@@ -185,10 +185,17 @@ def test_deterministic_and_stream_aware(V, torch_mod):
 
 # ------------------------------------------------------------------ full-size workloads, sampled rows
 
-def sample_rows(n, count=192):
-    idx = np.unique(np.concatenate([np.arange(min(n, 64)), np.linspace(0, n - 1, count).astype(int),
-                                    np.arange(max(0, n - 64), n)]))
-    return idx
+def sample_ranges(n, width=96):
+    """First, middle and last row blocks (the last one covers the ragged tail tile)."""
+    mid = max(0, n // 2 - width // 2)
+    spans = [(0, min(n, width)), (mid, min(n, mid + width)), (max(0, n - width), n)]
+    out = []
+    for b, e in sorted(spans):
+        if out and b <= out[-1][1]:
+            out[-1] = (out[-1][0], max(out[-1][1], e))
+        else:
+            out.append((b, e))
+    return out
 
 
 def _config_matrices(cid):
@@ -209,16 +216,58 @@ def test_full_size_workloads(V, torch_mod, cid):
         p = oracle.pack(spec.n, spec.k, bits, codes, scales)
         h, dm = upload(V, bits, codes, scales)
         assert h.payload.tobytes() == p.payload.tobytes()
-        rows = sample_rows(spec.n)
+        ranges = sample_ranges(spec.n)
+        rows = np.concatenate([np.arange(b, e) for b, e in ranges])
         for m in cfg.batches:
             print_case(test="full", cfg=cfg.name, mat=spec.name, n=spec.n, k=spec.k, m=m)
             x = W.draw_x(W.x_seed(spec), spec.k, m)
             y = gpu_gemm(V, torch_mod, dm, x)
-            ref = np.stack([np.concatenate([oracle.gemm(p, x[i:i + 1], rows=(int(r), int(r) + 1))[0, r:r + 1]
-                                            for r in rows]) for i in range(m)])
+            ref = np.concatenate([oracle.gemm(p, x, rows=(b, e))[:, b:e] for b, e in ranges], axis=1)
             assert_within_tolerance(y[:, rows], ref, x, scales, f"{cfg.name}/{spec.name} m={m}")
         out = torch_mod.empty((spec.n, spec.k), dtype=torch_mod.int8, device="cuda")
         V.vbq_unpack_codes(dm, out)
         torch_mod.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), codes), f"{cfg.name}/{spec.name} codes"
         del dm, out
+
+
+def test_gemv_multi_mixed_shapes_one_launch(V, torch_mod):
+    torch = torch_mod
+    shapes = [(300, 768), (64, 4096), (9, 14336), (130, 320), (1, 64), (700, 1024), (65, 4160)]
+    dms, xs, ys, refs = [], [], [], []
+    for i, (n, k) in enumerate(shapes):
+        bits, codes, scales, p = make_case((i, 31), n, k, W.STD_MIX)
+        h, dm = upload(V, bits, codes, scales)
+        x = W.draw_x((i, 32), k)
+        dms.append(dm)
+        xs.append(torch.from_numpy(x[0].view(np.float16)).cuda())
+        ys.append(torch.full((n,), float("nan"), device="cuda"))
+        refs.append((oracle.gemv(p, x), x, scales))
+    print_case(test="gemv_multi", count=len(shapes))
+    V.vbq_gemv_multi(dms, xs, ys)
+    torch.cuda.synchronize()
+    for (n, k), y, (ref, x, scales) in zip(shapes, ys, refs):
+        assert_within_tolerance(y.cpu().numpy(), ref, x, scales, f"multi {n}x{k}")
+    # the same call again gives identical bits (the split path resets its counters)
+    first = [y.clone() for y in ys]
+    V.vbq_gemv_multi(dms, xs, ys)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(first, ys))
+
+
+def test_split_path_repeats_exactly(V, torch_mod):
+    # small n and large k split each row tile across several workgroups
+    torch = torch_mod
+    n, k = 100, 32768
+    bits, codes, scales, p = make_case(41, n, k, W.STD_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x(42, k)
+    xt = torch.from_numpy(x[0].view(np.float16)).cuda()
+    outs = []
+    for _ in range(3):
+        y = torch.empty(n, device="cuda")
+        V.vbq_gemv(dm, xt, y)
+        torch.cuda.synchronize()
+        outs.append(y.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    assert_within_tolerance(outs[0], oracle.gemv(p, x), x, scales, "split")

@@ -32,8 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     assert declared_functions() == sorted([
-        "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_validate_host", "vbq_gemv",
-        "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_status_string", "vbq_last_error"])
+        "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
+        "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_status_string", "vbq_last_error"])
 
 
 def test_library_exports_every_declared_symbol(V):
@@ -66,7 +66,7 @@ def test_pack_is_byte_identical_to_oracle(V, n, k, seed, mix):
     p = oracle.pack(n, k, bits, codes, scales)
     assert h.widths.tobytes() == p.widths.tobytes()
     assert h.scales.tobytes() == p.scales.tobytes()
-    assert h.row_offsets.tobytes() == p.row_offsets.tobytes()
+    assert h.tile_offsets.tobytes() == p.tile_offsets.tobytes()
     assert h.payload.tobytes() == p.payload.tobytes()
     sz = V.vbq_pack_sizes(n, k, bits)
     assert sz["total_bytes"] == h.total_bytes == p.total_bytes
@@ -102,7 +102,7 @@ def test_pack_capacity_and_null(V):
     sz = V.vbq_pack_sizes(3, 128, bits)
     widths = np.zeros(sz["widths_bytes"], np.uint8)
     sc = np.zeros(sz["scales_bytes"] // 2, np.uint16)
-    offs = np.zeros(4, np.uint32)
+    offs = np.zeros(sz["offsets_bytes"] // 4, np.uint32)
     payload = np.full(sz["payload_bytes"], 0xAB, np.uint8)
     b, c, s = (np.ascontiguousarray(a) for a in (bits, codes, scales))
     st_ = V.lib.vbq_pack(3, 128, b.ctypes.data, c.ctypes.data, s.ctypes.data, widths.ctypes.data, sc.ctypes.data,
@@ -119,24 +119,21 @@ def test_validate_host_catches_corruption(V):
     bits, codes, scales = W.draw_random_matrix(5, 4, 256, W.FIRST_MLP_MIX)
     h = V.vbq_pack(4, 256, bits, codes, scales)
     V.vbq_validate_host(h)
-    bad = V.HostMatrix(h.n, h.k, h.widths, h.scales, h.row_offsets.copy(), h.payload)
-    bad.row_offsets[2] += 8
+    bad = V.HostMatrix(h.n, h.k, h.widths, h.scales, h.tile_offsets.copy(), h.payload)
+    bad.tile_offsets[1] += 8
     with pytest.raises(V.VbqError) as e:
         V.vbq_validate_host(bad)
     assert e.value.status == V.ERR_OFFSETS
-    bad = V.HostMatrix(h.n, h.k, h.widths, h.scales.copy(), h.row_offsets, h.payload)
+    bad = V.HostMatrix(h.n, h.k, h.widths, h.scales.copy(), h.tile_offsets, h.payload)
     bad.scales[3] = 0x7E00
     with pytest.raises(V.VbqError) as e:
         V.vbq_validate_host(bad)
     assert e.value.status == V.ERR_SCALE
     # plant a reserved 8-bit pattern (0x80) inside an 8-bit group
-    t8 = np.flatnonzero(bits.reshape(-1) == 8)
-    if t8.size:
-        t = int(t8[0])
-        r, j = divmod(t, 4)
-        start = int(h.row_offsets[r]) + int((8 * bits[r, :j].astype(int)).sum())
-        bad = V.HostMatrix(h.n, h.k, h.widths, h.scales, h.row_offsets, h.payload.copy())
-        bad.payload[start + 7] = 0x80
+    if np.any(bits == 8):
+        # one tile here; the 8-bit bucket closes it, so its last byte belongs to an 8-bit group
+        bad = V.HostMatrix(h.n, h.k, h.widths, h.scales, h.tile_offsets, h.payload.copy())
+        bad.payload[int(h.tile_offsets[1]) - 1] = 0x80
         with pytest.raises(V.VbqError) as e:
             V.vbq_validate_host(bad)
         assert e.value.status == V.ERR_CODE
@@ -173,3 +170,27 @@ def test_device_entry_points_reject_bad_arguments_without_launching(V):
     assert V.lib.vbq_unpack_codes(ctypes.byref(aligned), base + 1, None) == V.ERR_ALIGN
     empty = V.VbqMatrix(1, 0, 128, 0, None, None, None, None)
     assert V.lib.vbq_gemv(ctypes.byref(empty), None, None, None) == V.OK    # n == 0: nothing to do
+
+
+def test_gemv_multi_rejects_bad_arguments_without_launching(V):
+    h = V.vbq_pack(*(lambda b, c, s: (2, 128, b, c, s))(*W.draw_random_matrix(7, 2, 128)))
+    v = h.view()
+    buf = np.zeros(4096, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    W17 = (ctypes.POINTER(V.VbqMatrix) * 17)(*([ctypes.pointer(v)] * 17))
+    P17 = (ctypes.c_void_p * 17)(*([base] * 17))
+    assert V.lib.vbq_gemv_multi(W17, P17, P17, 17, None) == V.ERR_SHAPE
+    assert V.lib.vbq_gemv_multi(None, P17, P17, 2, None) == V.ERR_NULL
+    assert V.lib.vbq_gemv_multi(W17, P17, P17, 0, None) == V.OK
+    bad = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
+    Wb = (ctypes.POINTER(V.VbqMatrix) * 2)(ctypes.pointer(bad), ctypes.pointer(bad))
+    Pm = (ctypes.c_void_p * 2)(base, base + 8)
+    assert V.lib.vbq_gemv_multi(Wb, Pm, (ctypes.c_void_p * 2)(base, base), 2, None) == V.ERR_ALIGN
+
+
+def test_tile_count(V):
+    assert V.vbq_tile_count(64, 256) == 1
+    assert V.vbq_tile_count(65, 256) == 2
+    assert V.vbq_tile_count(64, 320) == 2
+    assert V.vbq_tile_count(4096, 14336) == 64 * 56
+    assert V.vbq_tile_count(0, 256) == 0 and V.vbq_tile_count(5, 0) == 0
