@@ -1,0 +1,161 @@
+"""Per-launch summaries of rocprofv3 runs of bench.py's timed loop.
+
+Writes the short text summaries kept under profiles/ and reads the traffic
+summary back for bench.py. Launches are told apart by dispatch order: every
+step of bench.py issues the same launches in the same order (LAUNCHES).
+
+Kernel durations (`trace`):
+  rocprofv3 --kernel-trace --stats -f csv -d <dir> -o kt -- python bench.py --steps 50 --warmup 10 --only-timed
+  python bench_counters.py trace --csv <dir>/kt_kernel_trace.csv --out profiles/gemv_tiles_layer9b_kernel_trace.txt
+
+HBM traffic (`traffic`), one rocprofv3 run per counter:
+  rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch -- python bench.py --steps 5 --warmup 2 --only-timed
+  rocprofv3 --pmc WRITE_SIZE -d <dir> -o write -- python bench.py --steps 5 --warmup 2 --only-timed
+  rocprofv3 --pmc FETCH_SIZE -d <dir> -o cfetch -- python bench.py --calibrate-copy
+  rocprofv3 --pmc WRITE_SIZE -d <dir> -o cwrite -- python bench.py --calibrate-copy
+  python bench_counters.py traffic --fetch F.db --write W.db --copy-fetch CF.db --copy-write CW.db \
+      --copy-bytes 268435456 --out profiles/gemv_tiles_layer9b_traffic.txt
+
+FETCH_SIZE and WRITE_SIZE are KiB per dispatch as the counters define them.
+Each is scaled by the ratio (bytes the copy kernel moved) / (what the same
+counter reads for that copy), so the reported figure is in true bytes. Both
+summaries record a hash of the kernel source; bench.py reports the traffic
+only while that hash still matches.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import sqlite3
+import statistics
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCE = os.path.join(ROOT, "decode_gemv_02_amd", "csrc", "vbq_device.hip")
+LAUNCHES = ["q+k+v", "o", "gate+up", "down"]     # bench.py's launch order within a step
+GEMV_KERNEL = "gemv_tiles"
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _by_launch(vals: list, what: str) -> dict:
+    if not vals or len(vals) % len(LAUNCHES):
+        raise SystemExit(f"{what}: {len(vals)} GEMV dispatches is not a whole number of steps")
+    return {nm: vals[i::len(LAUNCHES)] for i, nm in enumerate(LAUNCHES)}
+
+
+def _counter_rows(db: str, counter: str):
+    con = sqlite3.connect(db)
+    try:
+        return con.execute("select dispatch_id, kernel_name, value from counters_collection "
+                           "where counter_name = ? order by dispatch_id", (counter,)).fetchall()
+    finally:
+        con.close()
+
+
+def _copy_reading(db: str, counter: str) -> float:
+    """Counter value (KiB) of the largest copy-kernel dispatch (the calibration copy)."""
+    vals = [v for _, name, v in _counter_rows(db, counter) if COPY_KERNEL in name]
+    if not vals:
+        raise SystemExit(f"{db}: no copy kernel dispatch")
+    return max(vals)
+
+
+def traffic_summary(a) -> str:
+    cf, cw = _copy_reading(a.copy_fetch, "FETCH_SIZE"), _copy_reading(a.copy_write, "WRITE_SIZE")
+    fscale, wscale = a.copy_bytes / (cf * 1024.0), a.copy_bytes / (cw * 1024.0)
+    fetch = _by_launch([v for _, nm, v in _counter_rows(a.fetch, "FETCH_SIZE") if GEMV_KERNEL in nm], a.fetch)
+    write = _by_launch([v for _, nm, v in _counter_rows(a.write, "WRITE_SIZE") if GEMV_KERNEL in nm], a.write)
+    lines = [
+        "# HBM traffic per launch of gemv_tiles, layer_9b decode step (q+k+v | o | gate+up | down), batch 1",
+        "# commands (repository root, one rocprofv3 run each):",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch -- python bench.py --steps 5 --warmup 2 --only-timed",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o write -- python bench.py --steps 5 --warmup 2 --only-timed",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <dir> -o cfetch -- python bench.py --calibrate-copy",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir> -o cwrite -- python bench.py --calibrate-copy",
+        "#   python bench_counters.py traffic --fetch ... --write ... --copy-fetch ... --copy-write ... "
+        f"--copy-bytes {a.copy_bytes} --out <this file>",
+        f"kernel_source_sha256: {kernel_source_sha()}",
+        f"copy_calibration: bytes={a.copy_bytes} fetch_kib={cf:.2f} write_kib={cw:.2f} "
+        f"fetch_scale={fscale:.4f} write_scale={wscale:.4f}",
+    ]
+    for nm in LAUNCHES:
+        fk, wk = statistics.fmean(fetch[nm]), statistics.fmean(write[nm])
+        tb = fk * 1024 * fscale + wk * 1024 * wscale
+        lines.append(f"launch {nm}: dispatches={len(fetch[nm])} fetch_kib={fk:.2f} write_kib={wk:.2f} "
+                     f"traffic_bytes={tb:.0f}")
+    return "\n".join(lines) + "\n"
+
+
+def trace_summary(a) -> str:
+    with open(a.csv, newline="") as f:
+        rows = [r for r in csv.DictReader(f) if GEMV_KERNEL in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]    # us
+    per = _by_launch(dur, a.csv)
+    first = rows[0]
+    lines = [
+        "# Kernel durations per launch of gemv_tiles, layer_9b decode step (q+k+v | o | gate+up | down), batch 1",
+        "# command (repository root):",
+        "#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o kt -- python bench.py --steps 50 --warmup 10 "
+        "--only-timed",
+        "#   python bench_counters.py trace --csv <dir>/kt_kernel_trace.csv --out <this file>",
+        f"kernel_source_sha256: {kernel_source_sha()}",
+        f"kernel: {first['Kernel_Name']} vgpr={first['VGPR_Count']} sgpr={first['SGPR_Count']} "
+        f"lds={first['LDS_Block_Size']} scratch={first['Scratch_Size']} workgroup={first['Workgroup_Size_X']}",
+        f"all launches: dispatches={len(dur)} avg_us={statistics.fmean(dur):.3f}",
+    ]
+    for nm in LAUNCHES:
+        v = per[nm]
+        lines.append(f"launch {nm}: dispatches={len(v)} avg_us={statistics.fmean(v):.3f} "
+                     f"median_us={statistics.median(v):.3f} min_us={min(v):.3f} max_us={max(v):.3f}")
+    tot = sum(statistics.fmean(per[nm]) for nm in LAUNCHES)
+    lines.append(f"step: sum_of_launch_avg_us={tot:.3f}")
+    return "\n".join(lines) + "\n"
+
+
+def read_traffic(path: str) -> dict | None:
+    """{launch: traffic bytes} from a traffic summary, or None if absent or taken on another kernel source."""
+    if not os.path.exists(path):
+        return None
+    sha, out = None, {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("kernel_source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            elif line.startswith("launch "):
+                name, rest = line[len("launch "):].split(":", 1)
+                fields = dict(kv.split("=") for kv in rest.split())
+                out[name] = float(fields["traffic_bytes"])
+    if sha != kernel_source_sha():
+        return None
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out", required=True)
+    k = sub.add_parser("trace")
+    k.add_argument("--csv", required=True)
+    k.add_argument("--out", required=True)
+    a = ap.parse_args()
+    text = traffic_summary(a) if a.cmd == "traffic" else trace_summary(a)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text, end="")
+
+
+if __name__ == "__main__":
+    main()

@@ -126,6 +126,14 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
+// Lane index, recomputed at each use: keeping it live across the tile loop
+// would cost a register the loop needs.
+__device__ __forceinline__ uint32_t lane_id() {
+    uint32_t r;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const MatArgs &M = B.m[mi];
     const uint32_t local = blockIdx.x - M.block_begin;
     const uint32_t a = local / M.splits, split = local % M.splits;
-    const uint32_t wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;   // uniform
     const uint32_t r0 = a * kTileRows;
     const uint32_t rows = min(kTileRows, M.n - r0);
     const uint32_t c_lo = (split * M.col_tiles) / M.splits, c_hi = ((split + 1) * M.col_tiles) / M.splits;
@@ -404,26 +412,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     float acc = 0.f;
     uint32_t ct = c_lo + wave;
     TileMeta cur{};
-    if (ct < c_hi) cur = load_meta<kAligned>(M, a, ct, lane, true);
+    if (ct < c_hi) cur = load_meta<kAligned>(M, a, ct, lane_id(), true);
     for (; ct < c_hi; ct += kWavesPerBlock) {
         const uint32_t cn = min(kTileGroups, M.groups - ct * kTileGroups);
-        stage_x(L, cur.xv, lane);
+        stage_x(L, cur.xv, lane_id());
         uint32_t cnt[4];
-        build_lists(L, cur, rows, cn, lane, cnt);
+        build_lists(L, cur, rows, cn, lane_id(), cnt);
         wave_lds_sync();
         const uint8_t *tp = M.payload + cur.off;
         Staged S;
-        stage_payload(L, tp, cnt, lane, S);
+        stage_payload(L, tp, cnt, lane_id(), S);
         // the next tile's metadata travels while this tile computes
         TileMeta nxt{};
-        if (ct + kWavesPerBlock < c_hi) nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock, lane, true);
-        tile_products(L, S, tp, cnt, lane);
+        if (ct + kWavesPerBlock < c_hi) nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock, lane_id(), true);
+        tile_products(L, S, tp, cnt, lane_id());
         wave_lds_sync();
+        const uint32_t lane = lane_id();
         if (lane < rows)
             for (uint32_t jl = 0; jl < cn; ++jl) acc += L.part[jl][lane];
         wave_lds_sync();
         cur = nxt;
     }
+    const uint32_t lane = lane_id();
     rowsum[wave][lane] = acc;
     __syncthreads();
     if (wave != 0) return;
