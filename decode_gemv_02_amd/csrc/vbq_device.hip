@@ -149,8 +149,8 @@ struct TileMeta {
     uint32_t s23;     // scales of row `lane`, groups j0+2, j0+3
 };
 
-template <bool kAligned>
-__device__ __forceinline__ TileMeta load_meta(const MatArgs &M, uint32_t a, uint32_t ct, uint32_t lane,
+template <bool kAligned, class Args>
+__device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_t ct, uint32_t lane,
                                               bool with_x) {
     TileMeta t;
     const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
@@ -549,6 +549,319 @@ __global__ void fill_zero(float *__restrict__ y, uint64_t count) {
     if (i < count) y[i] = 0.f;
 }
 
+// ---------------------------------------------------------------- small batch on the matrix cores
+// Y[m][r] = sum_j s[r,j] * sum_i q[r,j,i] * X[m][64j+i] for 16 <= m <= 64 rows of X
+// (VBQ paper §6 fused decode, batched; grid and scale §3.1 Eq. (1)).
+// A wave owns one tile at a time, two columns per pass: it decodes every
+// group of the two columns into exact fp16 codes in LDS (natural row order,
+// one width per instruction, from the same bucket lists as the GEMV), then
+// multiplies 16-row blocks of codes with 16-row blocks of X on the matrix
+// cores (v_mfma_f32_16x16x32_f16, 32 k per instruction). Each column's fp32
+// product is scaled by the group scale once and added to the accumulators.
+// The four waves of a workgroup take a row tile's column tiles round robin
+// and add their accumulators in a fixed order at the end.
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
+
+constexpr uint32_t kGemmMinBatch = 16;
+constexpr uint32_t kAStride = 136;   // fp16 per staged row: two columns of 64 codes + 8 pad (272 B)
+
+struct GemmArgs {
+    const uint8_t *widths;
+    const uint16_t *scales;
+    const uint32_t *tile_offsets;
+    const uint8_t *payload;
+    const uint16_t *x;    // [m][k] fp16
+    float *y;             // [m][n] fp32
+    float *partial;       // [splits][m][n] when splits > 1
+    uint32_t *counters;   // [row tiles] when splits > 1 (self-resetting)
+    uint32_t n, groups, col_tiles, splits, m, k;
+};
+
+struct alignas(16) GemmWaveLds {
+    uint16_t a[kTileRows * kAStride];            // decoded codes of two columns, exact fp16, row-major
+    float scale[kTileGroups][kTileRows];         // group scales as fp32 [column][row]
+    uint8_t list[4][kTileRows * kTileGroups];    // per width: row | column << 6, in bucket order
+};
+
+__device__ __forceinline__ uint32_t half2_fma(uint32_t v, uint32_t mul, uint32_t add) {
+    const half2_t r = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, v), __builtin_bit_cast(half2_t, mul),
+                                                __builtin_bit_cast(half2_t, add));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// fp16 pair constants: (mul, add) turn 1024 + f*u into u - bias exactly
+constexpr uint32_t h2(uint32_t h) { return h | (h << 16); }
+
+// 1-bit group (8 payload bytes) -> 64 codes +-1 at dst
+__device__ __forceinline__ void decode1(uint2 v, uint16_t *dst) {
+#pragma unroll
+    for (uint32_t t = 0; t < 8; ++t) {
+        const uint32_t w = t < 4 ? v.x : v.y;
+        const uint32_t sel = (t & 3u) | 0x0C000000u | 0x00000C00u | ((t & 3u) << 16);
+        const uint32_t d = __builtin_amdgcn_perm(0u, w, sel);          // {byte t, 0, byte t, 0}
+        uint32_t o[4];
+#pragma unroll
+        for (uint32_t p = 0; p < 4; ++p) {
+            const ushort2_t sh = {static_cast<uint16_t>(15 - 2 * p), static_cast<uint16_t>(14 - 2 * p)};
+            const uint32_t s = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ushort2_t, d) << sh);
+            o[p] = (s & 0x80008000u) | 0x3C003C00u;                    // sign bits 2p, 2p+1 -> fp16 +-1
+        }
+        *reinterpret_cast<uint4 *>(dst + 8 * t) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+}
+
+// 2-bit group (16 payload bytes) -> 64 codes at dst
+__device__ __forceinline__ void decode2(uint4 v, uint16_t *dst) {
+    // offset binary: u = q + 2 in every field
+    const uint32_t w[4] = {v.x ^ 0xAAAAAAAAu, v.y ^ 0xAAAAAAAAu, v.z ^ 0xAAAAAAAAu, v.w ^ 0xAAAAAAAAu};
+    // pair p = fields p, p+8 -> 1024 + 4^p u (p < 5) or, from word >> 10, 1024 + 4^(p-5) u
+    constexpr uint32_t mul[5] = {h2(0x3C00), h2(0x3400), h2(0x2C00), h2(0x2400), h2(0x1C00)};   // 4^-p
+    constexpr uint32_t add[5] = {h2(0xE402), h2(0xDC08), h2(0xD420), h2(0xCC80), h2(0xC600)};   // -(1024/4^p + 2)
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t lo = w[q], hi = w[q] >> 10;
+        uint32_t o[8];
+#pragma unroll
+        for (uint32_t p = 0; p < 8; ++p) {
+            const uint32_t src = p < 5 ? lo : hi, c = p < 5 ? p : p - 5;
+            const uint32_t f = (src & (0x00030003u << (2 * c))) | kMagic;
+            o[p] = half2_fma(f, mul[c], add[c]);
+        }
+        *reinterpret_cast<uint4 *>(dst + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4 *>(dst + 16 * q + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+}
+
+// 16 payload bytes of a 4-bit group (32 elements) -> 32 codes at dst
+__device__ __forceinline__ void decode4(uint4 v, uint16_t *dst) {
+    // offset binary: u = q + 8 in every field
+    const uint32_t w[4] = {v.x ^ 0x88888888u, v.y ^ 0x88888888u, v.z ^ 0x88888888u, v.w ^ 0x88888888u};
+    constexpr uint32_t m1 = h2(0x3C00), a1 = h2(0xE408);    // 1, -(1024 + 8)
+    constexpr uint32_t m16 = h2(0x2C00), a16 = h2(0xD480);  // 1/16, -(64 + 8)
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        const uint32_t lo = w[q], hi = w[q] >> 8;
+        const uint32_t o0 = half2_fma((lo & 0x000F000Fu) | kMagic, m1, a1);
+        const uint32_t o1 = half2_fma((lo & 0x00F000F0u) | kMagic, m16, a16);
+        const uint32_t o2 = half2_fma((hi & 0x000F000Fu) | kMagic, m1, a1);
+        const uint32_t o3 = half2_fma((hi & 0x00F000F0u) | kMagic, m16, a16);
+        *reinterpret_cast<uint4 *>(dst + 8 * q) = make_uint4(o0, o1, o2, o3);
+    }
+}
+
+// 16 payload bytes of an 8-bit group (16 elements) -> 16 codes at dst
+__device__ __forceinline__ void decode8(uint4 v, uint16_t *dst) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    constexpr uint32_t one = h2(0x3C00), a8 = h2(0xE480);   // 1, -(1024 + 128)
+    uint32_t o[8];
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        uint32_t p0, p1;
+        unpack8(w[q], p0, p1);
+        o[2 * q] = half2_fma(p0, one, a8);
+        o[2 * q + 1] = half2_fma(p1, one, a8);
+    }
+    *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+    *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// Per-width lists of one tile (bucket order) and where each column starts in
+// them; scales of the tile to LDS as fp32. colstart[c] packs, 16 bits per
+// width, how many groups of each width precede column c.
+__device__ __forceinline__ void gemm_lists(GemmWaveLds &L, const TileMeta &t, uint32_t rows, uint32_t cn,
+                                           uint64_t colstart[kTileGroups + 1]) {
+    const uint32_t lane = lane_id();
+    const bool valid = lane < rows;
+    const uint64_t live = __ballot(valid);
+    uint64_t packed = 0;
+#pragma unroll
+    for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
+        colstart[jl] = packed;
+        if (jl < cn) {
+            const uint32_t c = (t.codes >> (2 * jl)) & 3u;
+            const uint64_t p0 = __ballot(valid && (c & 1u)), p1 = __ballot(valid && (c & 2u));
+            const uint64_t f0 = (c & 1u) ? p0 : ~p0, f1 = (c & 2u) ? p1 : ~p1;
+            const uint32_t slot = static_cast<uint32_t>((packed >> (16 * c)) & 0xFFFFu) + lane_rank(f0 & f1 & live);
+            if (valid) {
+                L.list[c][slot] = static_cast<uint8_t>(lane | (jl << 6));
+                const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
+                L.scale[jl][lane] = half_to_float(sb);
+            }
+            const uint32_t n3 = static_cast<uint32_t>(__popcll(p0 & p1));
+            const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1 & live));
+            const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1 & live));
+            const uint32_t n0 = static_cast<uint32_t>(__popcll(live)) - n1 - n2 - n3;
+            packed += static_cast<uint64_t>(n0) | (static_cast<uint64_t>(n1) << 16) |
+                      (static_cast<uint64_t>(n2) << 32) | (static_cast<uint64_t>(n3) << 48);
+        }
+    }
+    colstart[kTileGroups] = packed;
+}
+
+// 16 payload bytes at an 8-byte aligned address (buckets start at multiples of 8)
+__device__ __forceinline__ uint4 load16(const uint8_t *p) {
+    const uint2 lo = load8(p), hi = load8(p + 8);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+__device__ __forceinline__ uint32_t field16(uint64_t v, uint32_t w) {
+    return static_cast<uint32_t>((v >> (16 * w)) & 0xFFFFu);
+}
+
+// Decode columns 2*pass and 2*pass+1 of the tile into L.a.
+__device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const uint8_t *tile, const uint64_t colstart[5],
+                                                 uint32_t pass, uint32_t cn) {
+    const uint32_t lane = lane_id();
+    const uint32_t c_end = min(2 * pass + 2, cn);
+    const uint64_t total = colstart[kTileGroups];
+    uint32_t base = 0;    // byte offset of the width's bucket in the tile
+#pragma unroll
+    for (uint32_t wi = 0; wi < 4; ++wi) {
+        const uint32_t b = 1u << wi;
+        const uint32_t e0 = field16(colstart[2 * pass], wi), e1 = field16(colstart[c_end], wi);
+        const uint32_t tpg = wi < 2 ? 1u : (b >> 1);           // tasks per group: 1, 1, 2, 4
+        const uint32_t tasks = (e1 - e0) * tpg;
+        const uint8_t *bucket = tile + base;
+        for (uint32_t t = lane; t < tasks; t += kWave) {
+            const uint32_t e = e0 + t / tpg, sl = t % tpg;
+            const uint32_t info = L.list[wi][e];
+            const uint32_t r = info & 63u, jj = (info >> 6) - 2 * pass;
+            uint16_t *dst = L.a + r * kAStride + 64u * jj;
+            const uint8_t *src = bucket + 8u * b * e;
+            if (wi == 0) {
+                decode1(load8(src), dst);
+            } else if (wi == 1) {
+                decode2(load16(src), dst);
+            } else if (wi == 2) {
+                decode4(load16(src + 16u * sl), dst + 32u * sl);
+            } else {
+                decode8(load16(src + 16u * sl), dst + 16u * sl);
+            }
+        }
+        base += 8u * b * field16(total, wi);
+    }
+}
+
+template <uint32_t MB>
+__global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
+    __shared__ GemmWaveLds lds[kWavesPerBlock];
+    __shared__ uint32_t arrived_s;
+    const uint32_t a = blockIdx.x / G.splits, split = blockIdx.x % G.splits;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
+    const uint32_t r0 = a * kTileRows;
+    const uint32_t rows = min(kTileRows, G.n - r0);
+    const uint32_t c_lo = (split * G.col_tiles) / G.splits, c_hi = ((split + 1) * G.col_tiles) / G.splits;
+    GemmWaveLds &L = lds[wave];
+
+    float4_t acc[4][MB];
+#pragma unroll
+    for (uint32_t rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (uint32_t ct = c_lo + wave; ct < c_hi; ct += kWavesPerBlock) {
+        const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, G.groups - j0);
+        const TileMeta meta = load_meta<false>(G, a, ct, lane_id(), false);
+        uint64_t colstart[kTileGroups + 1];
+        gemm_lists(L, meta, rows, cn, colstart);
+        wave_lds_sync();
+        const uint8_t *tile = G.payload + meta.off;
+        for (uint32_t pass = 0; 2 * pass < cn; ++pass) {
+            // activations of the pass's columns: lane holds X[16mb + lane%16][k .. k+7]
+            const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
+            half8_t bx[2][2][MB];
+#pragma unroll
+            for (uint32_t jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (uint32_t h = 0; h < 2; ++h)
+#pragma unroll
+                    for (uint32_t mb = 0; mb < MB; ++mb) {
+                        const uint32_t m = 16 * mb + mr, jl = 2 * pass + jj;
+                        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                        if (m < G.m && jl < cn)
+                            v = *reinterpret_cast<const uint4 *>(G.x + static_cast<uint64_t>(m) * G.k +
+                                                                 64u * (j0 + jl) + 32u * h + 8u * q);
+                        bx[jj][h][mb] = __builtin_bit_cast(half8_t, v);
+                    }
+            gemm_decode_pass(L, tile, colstart, pass, cn);
+            wave_lds_sync();
+#pragma unroll
+            for (uint32_t jj = 0; jj < 2; ++jj) {
+                const uint32_t jl = 2 * pass + jj;
+                if (jl >= cn) break;
+#pragma unroll
+                for (uint32_t rb = 0; rb < 4; ++rb) {
+                    const uint16_t *arow = L.a + (16 * rb + mr) * kAStride + 64u * jj + 8u * q;
+                    const half8_t a0 = *reinterpret_cast<const half8_t *>(arow);
+                    const half8_t a1 = *reinterpret_cast<const half8_t *>(arow + 32);
+                    float4_t d[MB];
+#pragma unroll
+                    for (uint32_t mb = 0; mb < MB; ++mb)
+                        d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[jj][0][mb], float4_t{0.f, 0.f, 0.f, 0.f},
+                                                                       0, 0, 0);
+#pragma unroll
+                    for (uint32_t mb = 0; mb < MB; ++mb)
+                        d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[jj][1][mb], d[mb], 0, 0, 0);
+                    // rows 16rb + 4q .. +3 of this column
+                    const float4_t s = *reinterpret_cast<const float4_t *>(&L.scale[jl][16 * rb + 4 * q]);
+#pragma unroll
+                    for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] += s * d[mb];
+                }
+            }
+            wave_lds_sync();
+        }
+    }
+
+    // Workgroup sum in wave order: each wave parks its accumulators as fp32 [m][row]
+    {
+        float *red = reinterpret_cast<float *>(L.a);
+        const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
+#pragma unroll
+        for (uint32_t rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (uint32_t mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (uint32_t v = 0; v < 4; ++v) red[(16 * mb + mr) * kTileRows + 16 * rb + 4 * q + v] = acc[rb][mb][v];
+    }
+    __syncthreads();
+    const uint32_t outs = G.m * kTileRows;
+    const float *r0p = reinterpret_cast<const float *>(lds[0].a), *r1p = reinterpret_cast<const float *>(lds[1].a);
+    const float *r2p = reinterpret_cast<const float *>(lds[2].a), *r3p = reinterpret_cast<const float *>(lds[3].a);
+    if (G.splits == 1) {
+        for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
+            const uint32_t m = i / kTileRows, row = i % kTileRows;
+            if (row < rows) G.y[static_cast<uint64_t>(m) * G.n + r0 + row] = ((r0p[i] + r1p[i]) + r2p[i]) + r3p[i];
+        }
+        return;
+    }
+    // split row tile: publish partial sums, count arrivals, the last workgroup adds them in split order
+    for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
+        const uint32_t m = i / kTileRows, row = i % kTileRows;
+        if (row < rows)
+            __hip_atomic_store(&G.partial[(static_cast<uint64_t>(split) * G.m + m) * G.n + r0 + row],
+                               ((r0p[i] + r1p[i]) + r2p[i]) + r3p[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        arrived_s = __hip_atomic_fetch_add(&G.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (arrived_s != G.splits - 1) return;
+    for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
+        const uint32_t m = i / kTileRows, row = i % kTileRows;
+        if (row >= rows) continue;
+        float tot = 0.f;
+        for (uint32_t s = 0; s < G.splits; ++s)
+            tot += __hip_atomic_load(&G.partial[(static_cast<uint64_t>(s) * G.m + m) * G.n + r0 + row],
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        G.y[static_cast<uint64_t>(m) * G.n + r0 + row] = tot;
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&G.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- host side
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -686,6 +999,43 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     return launched(who);
 }
 
+// Small-batch GEMM on the matrix cores: one launch for 16 <= m <= 64.
+vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
+                       hipStream_t stream) {
+    GemmArgs G{};
+    G.widths = w->widths;
+    G.scales = w->scales;
+    G.tile_offsets = w->tile_offsets;
+    G.payload = w->payload;
+    G.x = x;
+    G.y = y;
+    G.n = w->n;
+    G.groups = w->k / VBQ_GROUP;
+    G.col_tiles = ceil_div(G.groups, kTileGroups);
+    G.m = m;
+    G.k = w->k;
+    const uint32_t row_tiles = ceil_div(G.n, kTileRows);
+    const uint32_t want_blocks = 512;
+    G.splits = std::max(1u, std::min(ceil_div(G.col_tiles, kWavesPerBlock), ceil_div(want_blocks, row_tiles)));
+    if (G.splits > 1) {
+        uint32_t *ctr = nullptr;
+        char *part = nullptr;
+        const size_t partials = (static_cast<size_t>(G.splits) * m * G.n * 4 + 255) / 256 * 256;
+        vbq_status st = scratch_for(who, stream, static_cast<size_t>(row_tiles) * 4, partials, &ctr, &part);
+        if (st != VBQ_OK) return st;
+        G.counters = ctr;
+        G.partial = reinterpret_cast<float *>(part);
+    }
+    const dim3 grid(row_tiles * G.splits), block(kWavesPerBlock * kWave);
+    switch (ceil_div(m, 16)) {
+        case 1: hipLaunchKernelGGL(gemm_tiles<1>, grid, block, 0, stream, G); break;
+        case 2: hipLaunchKernelGGL(gemm_tiles<2>, grid, block, 0, stream, G); break;
+        case 3: hipLaunchKernelGGL(gemm_tiles<3>, grid, block, 0, stream, G); break;
+        default: hipLaunchKernelGGL(gemm_tiles<4>, grid, block, 0, stream, G); break;
+    }
+    return launched(who);
+}
+
 vbq_status check_vectors(const char *who, const vbq_matrix *w, const void *x, const void *y) {
     if (w->n == 0) return VBQ_OK;
     if (!y || (w->k && !x)) return fail(VBQ_ERR_NULL, "%s: x or y is NULL", who);
@@ -734,7 +1084,16 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
     if (st != VBQ_OK) return st;
     if (w->n == 0) return VBQ_OK;
     (void)hipGetLastError();
-    // each input row as its own GEMV of one batched launch
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (m >= kGemmMinBatch) {
+        if (w->k == 0) {
+            const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
+            hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s, y, cnt);
+            return launched(who);
+        }
+        return gemm_launch(who, w, x, m, y, s);
+    }
+    // fewer rows than one matrix-core block: each input row as its own GEMV of one batched launch
     const vbq_matrix *ws[VBQ_MAX_MULTI];
     const uint16_t *xs[VBQ_MAX_MULTI];
     float *ys[VBQ_MAX_MULTI];
@@ -745,7 +1104,7 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
             xs[i] = x + static_cast<uint64_t>(m0 + i) * w->k;
             ys[i] = y + static_cast<uint64_t>(m0 + i) * w->n;
         }
-        st = gemv_launch(who, ws, xs, ys, cnt, static_cast<hipStream_t>(stream));
+        st = gemv_launch(who, ws, xs, ys, cnt, s);
         if (st != VBQ_OK) return st;
     }
     return VBQ_OK;

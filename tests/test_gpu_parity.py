@@ -131,6 +131,34 @@ def test_one_hot_x_returns_dequantised_column(V, torch_mod):
         assert np.array_equal(y[0], wd.reshape(n, k)[:, col])
 
 
+@pytest.mark.parametrize("m", [16, 37, 64])
+def test_one_hot_rows_on_matrix_cores(V, torch_mod, m):
+    # row i of X is one-hot at column c_i: Y[i] is that column of s*q, exact in fp32
+    n, k = 130, 1216
+    bits, codes, scales, p = make_case((m, 12), n, k, W.FIRST_MLP_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    wd = (codes.astype(np.float64).reshape(n, k // 64, 64) * xf64(scales)[:, :, None]).reshape(n, k)
+    cols = (np.arange(m) * 97 + 5) % k
+    x = np.zeros((m, k), np.float16)
+    x[np.arange(m), cols] = 1.0
+    print_case(test="one_hot_mfma", n=n, k=k, m=m)
+    y = gpu_gemm(V, torch_mod, dm, x.view(np.uint16))
+    assert np.array_equal(y, wd[:, cols].T)
+
+
+def test_gemm_split_path_repeats_exactly(V, torch_mod):
+    # few row tiles and a long k: each row tile is split across workgroups
+    torch = torch_mod
+    n, k, m = 100, 32768, 32
+    bits, codes, scales, p = make_case(43, n, k, W.STD_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x(44, k, m)
+    print_case(test="gemm_split", n=n, k=k, m=m)
+    outs = [gpu_gemm(V, torch_mod, dm, x) for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
+    assert_within_tolerance(outs[0], oracle.gemm(p, x), x, scales, "gemm split")
+
+
 def test_edge_values(V, torch_mod):
     n, k = 60, 640
     bits, codes, scales = W.draw_random_matrix(9, n, k, W.STD_MIX)
