@@ -47,6 +47,39 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
+// A constant the compiler treats as an unknown register value: lets a mask
+// and an OR constant share one v_bitop3_b32 instead of a literal v_or_b32.
+__device__ __forceinline__ uint32_t opaque(uint32_t c) {
+    uint32_t r;
+    asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(c));
+    return r;
+}
+
+// x ^ c computed where written (not folded into later mask-and-or steps)
+__device__ __forceinline__ uint32_t xor_opaque(uint32_t x, uint32_t c) {
+    uint32_t r;
+    asm("v_xor_b32 %0, %1, %2" : "=v"(r) : "v"(x), "v"(c));
+    return r;
+}
+
+// Cross-lane moves on the VALU (DPP): quad permutes and rotations inside a row of 16 lanes.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// sum over the 16 lanes of a row, in every lane of the row
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<kRowRor8>(v);
+    v += dpp<kRowRor4>(v);
+    v += dpp<kRowRor2>(v);
+    v += dpp<kRowRor1>(v);
+    return v;
+}
+
 __device__ __forceinline__ float half_to_float(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
@@ -64,28 +97,29 @@ __device__ __forceinline__ void unpack8(uint32_t v, uint32_t &p0, uint32_t &p1) 
     p1 = __builtin_amdgcn_perm(0x64646464u, v, 0x04030402u);   // bytes {v2, 64, v3, 64}
 }
 
-// 4-bit: elements 8w..8w+7 -> pairs (0,1) x1, (2,3) x16, (4,5) x1, (6,7) x16
-__device__ __forceinline__ void unpack4(uint32_t v, uint32_t p[4]) {
-    v ^= 0x88888888u;
+// 4-bit: elements 8w..8w+7 -> pairs (0,1) x1, (2,3) x16, (4,5) x1, (6,7) x16.
+// magic holds kMagic in a register so each pair is one mask-and-or.
+__device__ __forceinline__ void unpack4(uint32_t v, uint32_t magic, uint32_t p[4]) {
+    v = xor_opaque(v, 0x88888888u);
     const uint32_t h = v >> 8;
-    p[0] = (v & 0x000F000Fu) | kMagic;
-    p[1] = (v & 0x00F000F0u) | kMagic;
-    p[2] = (h & 0x000F000Fu) | kMagic;
-    p[3] = (h & 0x00F000F0u) | kMagic;
+    p[0] = (v & 0x000F000Fu) | magic;
+    p[1] = (v & 0x00F000F0u) | magic;
+    p[2] = (h & 0x000F000Fu) | magic;
+    p[3] = (h & 0x00F000F0u) | magic;
 }
 
 // 2-bit: elements 16w..16w+15 -> pairs m = 0..7 with factors 1,4,16,64,256,1,4,16
-__device__ __forceinline__ void unpack2(uint32_t v, uint32_t p[8]) {
-    v ^= 0xAAAAAAAAu;
+__device__ __forceinline__ void unpack2(uint32_t v, uint32_t magic, uint32_t p[8]) {
+    v = xor_opaque(v, 0xAAAAAAAAu);
     const uint32_t h = v >> 10;
-    p[0] = (v & 0x00030003u) | kMagic;
-    p[1] = (v & 0x000C000Cu) | kMagic;
-    p[2] = (v & 0x00300030u) | kMagic;
-    p[3] = (v & 0x00C000C0u) | kMagic;
-    p[4] = (v & 0x03000300u) | kMagic;
-    p[5] = (h & 0x00030003u) | kMagic;
-    p[6] = (h & 0x000C000Cu) | kMagic;
-    p[7] = (h & 0x00300030u) | kMagic;
+    p[0] = (v & 0x00030003u) | magic;
+    p[1] = (v & 0x000C000Cu) | magic;
+    p[2] = (v & 0x00300030u) | magic;
+    p[3] = (v & 0x00C000C0u) | magic;
+    p[4] = (v & 0x03000300u) | magic;
+    p[5] = (h & 0x00030003u) | magic;
+    p[6] = (h & 0x000C000Cu) | magic;
+    p[7] = (h & 0x00300030u) | magic;
 }
 
 // 1-bit: bit i is the sign of element i; pair k = (2k, 2k+1) as fp16 +-1
@@ -208,12 +242,9 @@ __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
     const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
     const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
     float c2 = wa * a01 + wb * a23;
-#pragma unroll
-    for (uint32_t o = 8; o > 0; o >>= 1) {
-        xsum += __shfl_xor(xsum, o, kWave);
-        c2 += __shfl_xor(c2, o, kWave);
-        c4 += __shfl_xor(c4, o, kWave);
-    }
+    xsum = row16_sum(xsum);
+    c2 = row16_sum(c2);
+    c4 = row16_sum(c4);
     if (k == 0) {
         L.corr[jl][0] = xsum;
         L.corr[jl][1] = c2;
@@ -260,24 +291,38 @@ __device__ __forceinline__ uint2 load8(const uint8_t *p) { return *reinterpret_c
 
 __device__ __forceinline__ void group1(WaveLds &L, uint32_t info, uint2 v) {
     const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
-    const float *lut = L.lut + jl * 256u;
-    float s = 0.f;
+    // table k (one per 4 activations) starts at byte 64k; the entry for nibble u is at +4u.
+    // Bytes of lo/hi hold 4 * (nibble 2t / 2t+1) of each word.
+    const char *lut = reinterpret_cast<const char *>(L.lut + jl * 256u);
+    const uint32_t w[2] = {v.x, v.y};
+    float acc[4];
 #pragma unroll
-    for (uint32_t k = 0; k < 8; ++k) s += lut[k * 16u + ((v.x >> (4 * k)) & 15u)];
+    for (uint32_t q = 0; q < 2; ++q) {
+        uint32_t lo, hi;
+        asm("v_lshlrev_b32 %0, 2, %1\n\tv_and_b32 %0, 0x3c3c3c3c, %0" : "=&v"(lo) : "v"(w[q]));
+        asm("v_lshrrev_b32 %0, 2, %1\n\tv_and_b32 %0, 0x3c3c3c3c, %0" : "=&v"(hi) : "v"(w[q]));
 #pragma unroll
-    for (uint32_t k = 0; k < 8; ++k) s += lut[(k + 8) * 16u + ((v.y >> (4 * k)) & 15u)];
-    L.part[jl][r] = half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * s);
+        for (uint32_t t = 0; t < 4; ++t) {
+            const uint32_t k = 8 * q + 2 * t;
+            const float a = *reinterpret_cast<const float *>(lut + 64u * k + ((lo >> (8 * t)) & 0xFFu));
+            const float b = *reinterpret_cast<const float *>(lut + 64u * (k + 1) + ((hi >> (8 * t)) & 0xFFu));
+            acc[t] = q == 0 ? a + b : acc[t] + (a + b);
+        }
+    }
+    const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    L.part[jl][r] = half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * sum);
 }
 
 __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
     const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride);
+    const uint32_t magic = opaque(kMagic);
     float a1 = 0.f, a4 = 0.f, a16 = 0.f, a64 = 0.f, a256 = 0.f;
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         uint32_t p[8];
-        unpack2(w[q], p);
+        unpack2(w[q], magic, p);
         const uint4 xa = xp[2 * q], xb = xp[2 * q + 1];
         a1 = dot2(p[0], xa.x, a1);
         a4 = dot2(p[1], xa.y, a4);
@@ -297,11 +342,12 @@ __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uin
     const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 16u * h);
+    const uint32_t magic = opaque(kMagic);
     float a1 = 0.f, a16 = 0.f;
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         uint32_t p[4];
-        unpack4(w[q], p);
+        unpack4(w[q], magic, p);
         const uint4 xa = xp[q];
         a1 = dot2(p[0], xa.x, a1);
         a16 = dot2(p[1], xa.y, a16);
@@ -309,7 +355,7 @@ __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uin
         a16 = dot2(p[3], xa.w, a16);
     }
     float part = a1 + 0.0625f * a16;
-    part += __shfl_xor(part, 1, kWave);
+    part += dpp<kQuadXor1>(part);
     if (h == 0) L.part[jl][r] = half_to_float(info >> 16) * (part - L.corr[jl][2]);
 }
 
@@ -330,8 +376,8 @@ __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, ui
         a = dot2(p2, xa.z, a);
         a = dot2(p3, xa.w, a);
     }
-    a += __shfl_xor(a, 1, kWave);
-    a += __shfl_xor(a, 2, kWave);
+    a += dpp<kQuadXor1>(a);
+    a += dpp<kQuadXor2>(a);
     if (qd == 0) L.part[jl][r] = half_to_float(info >> 16) * (a - 1152.f * L.corr[jl][0]);
 }
 
@@ -503,7 +549,7 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
                     }
                 } else if (b == 2) {
                     uint32_t p[8];
-                    unpack2(v, p);
+                    unpack2(v, opaque(kMagic), p);
                     const float f[8] = {1.f, 4.f, 16.f, 64.f, 256.f, 1.f, 4.f, 16.f};
                     uint32_t outw[4] = {0, 0, 0, 0};
                     for (uint32_t m = 0; m < 8; ++m) {
@@ -516,7 +562,7 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
                     for (uint32_t o = 0; o < 4; ++o) dst[wd * 4 + o] = outw[o];
                 } else if (b == 4) {
                     uint32_t p[4];
-                    unpack4(v, p);
+                    unpack4(v, opaque(kMagic), p);
                     uint32_t outw[2] = {0, 0};
                     for (uint32_t m = 0; m < 4; ++m) {
                         const float f = (m & 1) ? 16.f : 1.f;
@@ -597,6 +643,7 @@ constexpr uint32_t h2(uint32_t h) { return h | (h << 16); }
 
 // 1-bit group (8 payload bytes) -> 64 codes +-1 at dst
 __device__ __forceinline__ void decode1(uint2 v, uint16_t *dst) {
+    const uint32_t ones = opaque(0x3C003C00u);
 #pragma unroll
     for (uint32_t t = 0; t < 8; ++t) {
         const uint32_t w = t < 4 ? v.x : v.y;
@@ -607,7 +654,7 @@ __device__ __forceinline__ void decode1(uint2 v, uint16_t *dst) {
         for (uint32_t p = 0; p < 4; ++p) {
             const ushort2_t sh = {static_cast<uint16_t>(15 - 2 * p), static_cast<uint16_t>(14 - 2 * p)};
             const uint32_t s = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ushort2_t, d) << sh);
-            o[p] = (s & 0x80008000u) | 0x3C003C00u;                    // sign bits 2p, 2p+1 -> fp16 +-1
+            o[p] = (s & 0x80008000u) | ones;                           // sign bits 2p, 2p+1 -> fp16 +-1
         }
         *reinterpret_cast<uint4 *>(dst + 8 * t) = make_uint4(o[0], o[1], o[2], o[3]);
     }
@@ -616,7 +663,9 @@ __device__ __forceinline__ void decode1(uint2 v, uint16_t *dst) {
 // 2-bit group (16 payload bytes) -> 64 codes at dst
 __device__ __forceinline__ void decode2(uint4 v, uint16_t *dst) {
     // offset binary: u = q + 2 in every field
-    const uint32_t w[4] = {v.x ^ 0xAAAAAAAAu, v.y ^ 0xAAAAAAAAu, v.z ^ 0xAAAAAAAAu, v.w ^ 0xAAAAAAAAu};
+    const uint32_t w[4] = {xor_opaque(v.x, 0xAAAAAAAAu), xor_opaque(v.y, 0xAAAAAAAAu), xor_opaque(v.z, 0xAAAAAAAAu),
+                           xor_opaque(v.w, 0xAAAAAAAAu)};
+    const uint32_t magic = opaque(kMagic);
     // pair p = fields p, p+8 -> 1024 + 4^p u (p < 5) or, from word >> 10, 1024 + 4^(p-5) u
     constexpr uint32_t mul[5] = {h2(0x3C00), h2(0x3400), h2(0x2C00), h2(0x2400), h2(0x1C00)};   // 4^-p
     constexpr uint32_t add[5] = {h2(0xE402), h2(0xDC08), h2(0xD420), h2(0xCC80), h2(0xC600)};   // -(1024/4^p + 2)
@@ -627,7 +676,7 @@ __device__ __forceinline__ void decode2(uint4 v, uint16_t *dst) {
 #pragma unroll
         for (uint32_t p = 0; p < 8; ++p) {
             const uint32_t src = p < 5 ? lo : hi, c = p < 5 ? p : p - 5;
-            const uint32_t f = (src & (0x00030003u << (2 * c))) | kMagic;
+            const uint32_t f = (src & (0x00030003u << (2 * c))) | magic;
             o[p] = half2_fma(f, mul[c], add[c]);
         }
         *reinterpret_cast<uint4 *>(dst + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -638,16 +687,18 @@ __device__ __forceinline__ void decode2(uint4 v, uint16_t *dst) {
 // 16 payload bytes of a 4-bit group (32 elements) -> 32 codes at dst
 __device__ __forceinline__ void decode4(uint4 v, uint16_t *dst) {
     // offset binary: u = q + 8 in every field
-    const uint32_t w[4] = {v.x ^ 0x88888888u, v.y ^ 0x88888888u, v.z ^ 0x88888888u, v.w ^ 0x88888888u};
+    const uint32_t w[4] = {xor_opaque(v.x, 0x88888888u), xor_opaque(v.y, 0x88888888u), xor_opaque(v.z, 0x88888888u),
+                           xor_opaque(v.w, 0x88888888u)};
+    const uint32_t magic = opaque(kMagic);
     constexpr uint32_t m1 = h2(0x3C00), a1 = h2(0xE408);    // 1, -(1024 + 8)
     constexpr uint32_t m16 = h2(0x2C00), a16 = h2(0xD480);  // 1/16, -(64 + 8)
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         const uint32_t lo = w[q], hi = w[q] >> 8;
-        const uint32_t o0 = half2_fma((lo & 0x000F000Fu) | kMagic, m1, a1);
-        const uint32_t o1 = half2_fma((lo & 0x00F000F0u) | kMagic, m16, a16);
-        const uint32_t o2 = half2_fma((hi & 0x000F000Fu) | kMagic, m1, a1);
-        const uint32_t o3 = half2_fma((hi & 0x00F000F0u) | kMagic, m16, a16);
+        const uint32_t o0 = half2_fma((lo & 0x000F000Fu) | magic, m1, a1);
+        const uint32_t o1 = half2_fma((lo & 0x00F000F0u) | magic, m16, a16);
+        const uint32_t o2 = half2_fma((hi & 0x000F000Fu) | magic, m1, a1);
+        const uint32_t o3 = half2_fma((hi & 0x00F000F0u) | magic, m16, a16);
         *reinterpret_cast<uint4 *>(dst + 8 * q) = make_uint4(o0, o1, o2, o3);
     }
 }
@@ -711,37 +762,125 @@ __device__ __forceinline__ uint32_t field16(uint64_t v, uint32_t w) {
     return static_cast<uint32_t>((v >> (16 * w)) & 0xFFFFu);
 }
 
-// Decode columns 2*pass and 2*pass+1 of the tile into L.a.
-__device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const uint8_t *tile, const uint64_t colstart[5],
-                                                 uint32_t pass, uint32_t cn) {
-    const uint32_t lane = lane_id();
+// Payload of one pass (two columns of a tile): the first 128 one-bit groups
+// and the first 64 tasks of each wider width, loaded before any is decoded.
+struct PassStage {
+    uint2 p1[2];
+    uint4 p2, p4, p8;
+};
+
+// List range [e0, e1) of width wi for the columns of `pass`, and the byte
+// offset of that width's bucket in the tile.
+__device__ __forceinline__ void pass_range(const uint64_t colstart[kTileGroups + 1], uint32_t pass, uint32_t cn,
+                                           uint32_t wi, uint32_t &e0, uint32_t &e1, uint32_t &base) {
     const uint32_t c_end = min(2 * pass + 2, cn);
+    e0 = field16(colstart[2 * pass], wi);
+    e1 = field16(colstart[c_end], wi);
     const uint64_t total = colstart[kTileGroups];
-    uint32_t base = 0;    // byte offset of the width's bucket in the tile
+    base = 0;
+    for (uint32_t w = 0; w < wi; ++w) base += (8u << w) * field16(total, w);
+}
+
+__device__ __forceinline__ PassStage gemm_stage_pass(const uint8_t *tile, const uint64_t colstart[kTileGroups + 1],
+                                                     uint32_t pass, uint32_t cn) {
+    const uint32_t lane = lane_id();
+    PassStage S;
+    S.p1[0] = S.p1[1] = make_uint2(0u, 0u);
+    S.p2 = S.p4 = S.p8 = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t e0, e1, base;
+    pass_range(colstart, pass, cn, 0, e0, e1, base);
+    if (lane < e1 - e0) S.p1[0] = load8(tile + base + 8u * (e0 + lane));
+    if (lane + kWave < e1 - e0) S.p1[1] = load8(tile + base + 8u * (e0 + lane + kWave));
+    pass_range(colstart, pass, cn, 1, e0, e1, base);
+    if (lane < e1 - e0) S.p2 = load16(tile + base + 16u * (e0 + lane));
+    pass_range(colstart, pass, cn, 2, e0, e1, base);
+    if (lane < 2 * (e1 - e0)) S.p4 = load16(tile + base + 32u * e0 + 16u * lane);
+    pass_range(colstart, pass, cn, 3, e0, e1, base);
+    if (lane < 4 * (e1 - e0)) S.p8 = load16(tile + base + 64u * e0 + 16u * lane);
+    return S;
+}
+
+// Decode columns 2*pass and 2*pass+1 of the tile into L.a; tasks past the
+// staged ones load their bytes here.
+__device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const PassStage &S, const uint8_t *tile,
+                                                 const uint64_t colstart[kTileGroups + 1], uint32_t pass, uint32_t cn) {
+    const uint32_t lane = lane_id();
 #pragma unroll
     for (uint32_t wi = 0; wi < 4; ++wi) {
         const uint32_t b = 1u << wi;
-        const uint32_t e0 = field16(colstart[2 * pass], wi), e1 = field16(colstart[c_end], wi);
+        uint32_t e0, e1, base;
+        pass_range(colstart, pass, cn, wi, e0, e1, base);
         const uint32_t tpg = wi < 2 ? 1u : (b >> 1);           // tasks per group: 1, 1, 2, 4
         const uint32_t tasks = (e1 - e0) * tpg;
         const uint8_t *bucket = tile + base;
-        for (uint32_t t = lane; t < tasks; t += kWave) {
+        uint32_t round = 0;
+        for (uint32_t t = lane; t < tasks; t += kWave, ++round) {
             const uint32_t e = e0 + t / tpg, sl = t % tpg;
             const uint32_t info = L.list[wi][e];
             const uint32_t r = info & 63u, jj = (info >> 6) - 2 * pass;
             uint16_t *dst = L.a + r * kAStride + 64u * jj;
             const uint8_t *src = bucket + 8u * b * e;
             if (wi == 0) {
-                decode1(load8(src), dst);
+                decode1(round == 0 ? S.p1[0] : round == 1 ? S.p1[1] : load8(src), dst);
             } else if (wi == 1) {
-                decode2(load16(src), dst);
+                decode2(round == 0 ? S.p2 : load16(src), dst);
             } else if (wi == 2) {
-                decode4(load16(src + 16u * sl), dst + 32u * sl);
+                decode4(round == 0 ? S.p4 : load16(src + 16u * sl), dst + 32u * sl);
             } else {
-                decode8(load16(src + 16u * sl), dst + 16u * sl);
+                decode8(round == 0 ? S.p8 : load16(src + 16u * sl), dst + 16u * sl);
             }
         }
-        base += 8u * b * field16(total, wi);
+    }
+}
+
+// Activations of one pass: lane holds X[16mb + lane%16][k .. k+7] for each
+// column jj and half h of the pass (zeros past m or past the last column).
+template <uint32_t MB>
+__device__ __forceinline__ void load_bx(const GemmArgs &G, uint32_t j0, uint32_t pass, uint32_t cn,
+                                        half8_t bx[2][2][MB]) {
+    const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
+#pragma unroll
+    for (uint32_t jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h)
+#pragma unroll
+            for (uint32_t mb = 0; mb < MB; ++mb) {
+                const uint32_t m = 16 * mb + mr, jl = 2 * pass + jj;
+                uint4 v = make_uint4(0u, 0u, 0u, 0u);
+                if (m < G.m && jl < cn)
+                    v = *reinterpret_cast<const uint4 *>(G.x + static_cast<uint64_t>(m) * G.k + 64u * (j0 + jl) +
+                                                         32u * h + 8u * q);
+                bx[jj][h][mb] = __builtin_bit_cast(half8_t, v);
+            }
+}
+
+// Codes of the pass (L.a) times activations, scaled per group, into acc.
+template <uint32_t MB>
+__device__ __forceinline__ void mfma_pass(const GemmWaveLds &L, const half8_t bx[2][2][MB], uint32_t pass,
+                                          uint32_t cn, float4_t acc[4][MB]) {
+    const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
+#pragma unroll
+    for (uint32_t jj = 0; jj < 2; ++jj) {
+        const uint32_t jl = 2 * pass + jj;
+        if (jl >= cn) break;
+#pragma unroll
+        for (uint32_t rb = 0; rb < 4; ++rb) {
+            const uint16_t *arow = L.a + (16 * rb + mr) * kAStride + 64u * jj + 8u * q;
+            const half8_t a0 = *reinterpret_cast<const half8_t *>(arow);
+            const half8_t a1 = *reinterpret_cast<const half8_t *>(arow + 32);
+            float4_t d[MB];
+#pragma unroll
+            for (uint32_t mb = 0; mb < MB; ++mb)
+                d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[jj][0][mb], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                               0);
+#pragma unroll
+            for (uint32_t mb = 0; mb < MB; ++mb)
+                d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[jj][1][mb], d[mb], 0, 0, 0);
+            // rows 16rb + 4q .. +3 of this column
+            const float4_t sc = *reinterpret_cast<const float4_t *>(&L.scale[jl][16 * rb + 4 * q]);
+#pragma unroll
+            for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] += sc * d[mb];
+        }
     }
 }
 
@@ -762,57 +901,36 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
 #pragma unroll
         for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    for (uint32_t ct = c_lo + wave; ct < c_hi; ct += kWavesPerBlock) {
+    uint32_t ct = c_lo + wave;
+    TileMeta cur{};
+    if (ct < c_hi) cur = load_meta<false>(G, a, ct, lane_id(), false);
+    for (; ct < c_hi; ct += kWavesPerBlock) {
         const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, G.groups - j0);
-        const TileMeta meta = load_meta<false>(G, a, ct, lane_id(), false);
         uint64_t colstart[kTileGroups + 1];
-        gemm_lists(L, meta, rows, cn, colstart);
+        gemm_lists(L, cur, rows, cn, colstart);
         wave_lds_sync();
-        const uint8_t *tile = G.payload + meta.off;
-        for (uint32_t pass = 0; 2 * pass < cn; ++pass) {
-            // activations of the pass's columns: lane holds X[16mb + lane%16][k .. k+7]
-            const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
-            half8_t bx[2][2][MB];
-#pragma unroll
-            for (uint32_t jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (uint32_t h = 0; h < 2; ++h)
-#pragma unroll
-                    for (uint32_t mb = 0; mb < MB; ++mb) {
-                        const uint32_t m = 16 * mb + mr, jl = 2 * pass + jj;
-                        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                        if (m < G.m && jl < cn)
-                            v = *reinterpret_cast<const uint4 *>(G.x + static_cast<uint64_t>(m) * G.k +
-                                                                 64u * (j0 + jl) + 32u * h + 8u * q);
-                        bx[jj][h][mb] = __builtin_bit_cast(half8_t, v);
-                    }
-            gemm_decode_pass(L, tile, colstart, pass, cn);
+        const uint8_t *tile = G.payload + cur.off;
+        // every payload byte of the tile is requested before the first decode
+        const PassStage s0 = gemm_stage_pass(tile, colstart, 0, cn);
+        PassStage s1{};
+        if (cn > 2) s1 = gemm_stage_pass(tile, colstart, 1, cn);
+        half8_t bx[2][2][MB];
+        load_bx<MB>(G, j0, 0, cn, bx);
+        // the next tile's metadata travels while this tile computes
+        TileMeta nxt{};
+        if (ct + kWavesPerBlock < c_hi) nxt = load_meta<false>(G, a, ct + kWavesPerBlock, lane_id(), false);
+        gemm_decode_pass(L, s0, tile, colstart, 0, cn);
+        wave_lds_sync();
+        mfma_pass<MB>(L, bx, 0, cn, acc);
+        if (cn > 2) {
+            load_bx<MB>(G, j0, 1, cn, bx);
             wave_lds_sync();
-#pragma unroll
-            for (uint32_t jj = 0; jj < 2; ++jj) {
-                const uint32_t jl = 2 * pass + jj;
-                if (jl >= cn) break;
-#pragma unroll
-                for (uint32_t rb = 0; rb < 4; ++rb) {
-                    const uint16_t *arow = L.a + (16 * rb + mr) * kAStride + 64u * jj + 8u * q;
-                    const half8_t a0 = *reinterpret_cast<const half8_t *>(arow);
-                    const half8_t a1 = *reinterpret_cast<const half8_t *>(arow + 32);
-                    float4_t d[MB];
-#pragma unroll
-                    for (uint32_t mb = 0; mb < MB; ++mb)
-                        d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[jj][0][mb], float4_t{0.f, 0.f, 0.f, 0.f},
-                                                                       0, 0, 0);
-#pragma unroll
-                    for (uint32_t mb = 0; mb < MB; ++mb)
-                        d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[jj][1][mb], d[mb], 0, 0, 0);
-                    // rows 16rb + 4q .. +3 of this column
-                    const float4_t s = *reinterpret_cast<const float4_t *>(&L.scale[jl][16 * rb + 4 * q]);
-#pragma unroll
-                    for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] += s * d[mb];
-                }
-            }
+            gemm_decode_pass(L, s1, tile, colstart, 1, cn);
             wave_lds_sync();
+            mfma_pass<MB>(L, bx, 1, cn, acc);
         }
+        wave_lds_sync();
+        cur = nxt;
     }
 
     // Workgroup sum in wave order: each wave parks its accumulators as fp32 [m][row]
@@ -918,7 +1036,12 @@ vbq_status scratch_for(const char *who, hipStream_t stream, size_t counters, siz
         const size_t cb = std::max<size_t>(counters, std::max<size_t>(s.counter_bytes, 64u << 10));
         const size_t pb = std::max<size_t>(partials, std::max<size_t>(s.partial_bytes, 1u << 20));
         if (hipMalloc(&s.ptr, cb + pb) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch hipMalloc failed", who);
-        if (hipMemset(s.ptr, 0, cb + pb) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch memset failed", who);
+        // zero the counter region on the caller's stream, ahead of the launches that use it (a memset on
+        // the null stream is not ordered with non-blocking streams)
+        const uint64_t words = cb / 4;
+        hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<float *>(s.ptr), words);
+        if (hipGetLastError() != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch clear failed", who);
         s.counter_bytes = cb;
         s.partial_bytes = pb;
     }
