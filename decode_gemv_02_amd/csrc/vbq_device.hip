@@ -252,37 +252,65 @@ __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
     }
 }
 
-// Lane r = row r of the tile: sort the tile's groups into per-width lists in
-// the stream's order (column-major inside a bucket) and count them. Two
-// ballots give the bit planes of the width codes of one column; a lane's rank
-// among the rows that share its width is one mbcnt over the mask of equal codes.
-__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, uint32_t rows, uint32_t cn,
-                                            uint32_t lane, uint32_t cnt[4]) {
+// Width-code bit planes of a tile, one ballot pair per column: bit r of
+// plane0[jl] / plane1[jl] is bit 0 / bit 1 of row r's code in column jl.
+struct TilePlanes {
+    uint64_t plane0[kTileGroups], plane1[kTileGroups], live;
+};
+
+__device__ __forceinline__ TilePlanes tile_planes(const TileMeta &t, uint32_t rows, uint32_t cn, uint32_t lane,
+                                                  uint32_t cnt[4]) {
+    TilePlanes P;
     const bool valid = lane < rows;
-    const uint64_t live = __ballot(valid);
-    uint64_t packed = 0;   // running counts of the four widths, 16 bits each (a tile has <= 256 groups)
-    for (uint32_t jl = 0; jl < cn; ++jl) {
+    P.live = __ballot(valid);
+    const uint32_t nlive = static_cast<uint32_t>(__popcll(P.live));
+    cnt[0] = cnt[1] = cnt[2] = cnt[3] = 0;
+#pragma unroll
+    for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
         const uint32_t c = (t.codes >> (2 * jl)) & 3u;
         const uint64_t p0 = __ballot(valid && (c & 1u)), p1 = __ballot(valid && (c & 2u));
-        // rows whose code equals mine: bit planes equal to my bits
+        P.plane0[jl] = p0;
+        P.plane1[jl] = p1;
+        if (jl < cn) {
+            const uint32_t n3 = static_cast<uint32_t>(__popcll(p0 & p1));
+            const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1));
+            const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1));
+            cnt[0] += nlive - n1 - n2 - n3;
+            cnt[1] += n1;
+            cnt[2] += n2;
+            cnt[3] += n3;
+        }
+    }
+    return P;
+}
+
+// Lane r = row r of the tile: sort the tile's groups into per-width lists in
+// the stream's order (column-major inside a bucket). A lane's rank among the
+// rows that share its width is one mbcnt over the mask of equal codes.
+__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const TilePlanes &P, uint32_t rows,
+                                            uint32_t cn, uint32_t lane) {
+    const bool valid = lane < rows;
+    uint32_t before[4] = {0u, 0u, 0u, 0u};   // groups of each width in earlier columns
+#pragma unroll
+    for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
+        if (jl >= cn) break;
+        const uint32_t c = (t.codes >> (2 * jl)) & 3u;
+        const uint64_t p0 = P.plane0[jl], p1 = P.plane1[jl];
         const uint64_t f0 = (c & 1u) ? p0 : ~p0, f1 = (c & 2u) ? p1 : ~p1;
-        const uint64_t same = f0 & f1 & live;
-        const uint32_t slot = static_cast<uint32_t>((packed >> (16 * c)) & 0xFFFFu) + lane_rank(same);
+        const uint32_t rank = lane_rank(f0 & f1 & P.live);
+        const uint32_t base = c == 0 ? before[0] : c == 1 ? before[1] : c == 2 ? before[2] : before[3];
         if (valid) {
             const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
-            L.list[c][slot] = lane | (jl << 8) | (sb << 16);
+            L.list[c][base + rank] = lane | (jl << 8) | (sb << 16);
         }
         const uint32_t n3 = static_cast<uint32_t>(__popcll(p0 & p1));
-        const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1 & live));
-        const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1 & live));
-        const uint32_t n0 = static_cast<uint32_t>(__popcll(live)) - n1 - n2 - n3;
-        packed += static_cast<uint64_t>(n0) | (static_cast<uint64_t>(n1) << 16) | (static_cast<uint64_t>(n2) << 32) |
-                  (static_cast<uint64_t>(n3) << 48);
+        const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1));
+        const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1));
+        before[0] += static_cast<uint32_t>(__popcll(P.live)) - n1 - n2 - n3;
+        before[1] += n1;
+        before[2] += n2;
+        before[3] += n3;
     }
-    cnt[0] = static_cast<uint32_t>(packed & 0xFFFFu);
-    cnt[1] = static_cast<uint32_t>((packed >> 16) & 0xFFFFu);
-    cnt[2] = static_cast<uint32_t>((packed >> 32) & 0xFFFFu);
-    cnt[3] = static_cast<uint32_t>(packed >> 48);
 }
 
 __device__ __forceinline__ uint2 load8(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
@@ -383,39 +411,31 @@ __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, ui
 
 // Payload of the first 256 one-bit groups and of the first 64 slices of
 // each wider bucket, loaded before any of it is used. A tile has at most
-// 256 groups, so only the wider buckets can need more rounds.
+// 256 groups, so only the wider buckets can need more rounds. The addresses
+// need only the per-width counts, so the loads leave before the lists exist.
 struct Staged {
-    uint32_t i1[4];
     uint2 p1[4];
-    uint32_t i2, i4, i8;
     uint2 p2a, p2b, p4a, p4b, p8a, p8b;
 };
 
-__device__ __forceinline__ void stage_payload(const WaveLds &L, const uint8_t *tile, const uint32_t cnt[4],
-                                              uint32_t lane, Staged &S) {
+__device__ __forceinline__ void stage_payload(const uint8_t *tile, const uint32_t cnt[4], uint32_t lane, Staged &S) {
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i) {
         const uint32_t e = lane + kWave * i;
-        if (e < cnt[0]) {
-            S.i1[i] = L.list[0][e];
-            S.p1[i] = load8(tile + 8u * e);
-        }
+        if (e < cnt[0]) S.p1[i] = load8(tile + 8u * e);
     }
     const uint8_t *b2 = tile + 8u * cnt[0];
     const uint8_t *b4 = b2 + 16u * cnt[1];
     const uint8_t *b8 = b4 + 32u * cnt[2];
     if (lane < cnt[1]) {
-        S.i2 = L.list[1][lane];
         S.p2a = load8(b2 + 16u * lane);
         S.p2b = load8(b2 + 16u * lane + 8u);
     }
     if (lane < 2u * cnt[2]) {
-        S.i4 = L.list[2][lane >> 1];
         S.p4a = load8(b4 + 16u * lane);
         S.p4b = load8(b4 + 16u * lane + 8u);
     }
     if (lane < 4u * cnt[3]) {
-        S.i8 = L.list[3][lane >> 2];
         S.p8a = load8(b8 + 16u * lane);
         S.p8b = load8(b8 + 16u * lane + 8u);
     }
@@ -425,17 +445,17 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
                                               uint32_t lane) {
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i)
-        if (lane + kWave * i < cnt[0]) group1(L, S.i1[i], S.p1[i]);
+        if (lane + kWave * i < cnt[0]) group1(L, L.list[0][lane + kWave * i], S.p1[i]);
     const uint8_t *b2 = tile + 8u * cnt[0];
     const uint8_t *b4 = b2 + 16u * cnt[1];
     const uint8_t *b8 = b4 + 32u * cnt[2];
-    if (lane < cnt[1]) group2(L, S.i2, S.p2a, S.p2b);
+    if (lane < cnt[1]) group2(L, L.list[1][lane], S.p2a, S.p2b);
     for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
         group2(L, L.list[1][e], load8(b2 + 16u * e), load8(b2 + 16u * e + 8u));
-    if (lane < 2u * cnt[2]) task4(L, S.i4, lane & 1u, S.p4a, S.p4b);
+    if (lane < 2u * cnt[2]) task4(L, L.list[2][lane >> 1], lane & 1u, S.p4a, S.p4b);
     for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
         task4(L, L.list[2][e >> 1], e & 1u, load8(b4 + 16u * e), load8(b4 + 16u * e + 8u));
-    if (lane < 4u * cnt[3]) task8(L, S.i8, lane & 3u, S.p8a, S.p8b);
+    if (lane < 4u * cnt[3]) task8(L, L.list[3][lane >> 2], lane & 3u, S.p8a, S.p8b);
     for (uint32_t e = lane + kWave; e < 4u * cnt[3]; e += kWave)
         task8(L, L.list[3][e >> 2], e & 3u, load8(b8 + 16u * e), load8(b8 + 16u * e + 8u));
 }
@@ -461,16 +481,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     if (ct < c_hi) cur = load_meta<kAligned>(M, a, ct, lane_id(), true);
     for (; ct < c_hi; ct += kWavesPerBlock) {
         const uint32_t cn = min(kTileGroups, M.groups - ct * kTileGroups);
-        stage_x(L, cur.xv, lane_id());
+        // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
-        build_lists(L, cur, rows, cn, lane_id(), cnt);
-        wave_lds_sync();
+        const TilePlanes P = tile_planes(cur, rows, cn, lane_id(), cnt);
         const uint8_t *tp = M.payload + cur.off;
         Staged S;
-        stage_payload(L, tp, cnt, lane_id(), S);
+        stage_payload(tp, cnt, lane_id(), S);
         // the next tile's metadata travels while this tile computes
         TileMeta nxt{};
         if (ct + kWavesPerBlock < c_hi) nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock, lane_id(), true);
+        stage_x(L, cur.xv, lane_id());
+        build_lists(L, cur, P, rows, cn, lane_id());
+        wave_lds_sync();
         tile_products(L, S, tp, cnt, lane_id());
         wave_lds_sync();
         const uint32_t lane = lane_id();
@@ -523,7 +545,8 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
     const uint8_t *tp = M.payload + t.off;
     const uint64_t k = static_cast<uint64_t>(M.groups) * 64u;
     uint32_t cnt[4];
-    build_lists(L, t, rows, cn, lane, cnt);
+    const TilePlanes P = tile_planes(t, rows, cn, lane, cnt);
+    build_lists(L, t, P, rows, cn, lane);
     wave_lds_sync();
     const uint8_t *base = tp;
     for (uint32_t wsel = 0; wsel < 4; ++wsel) {
