@@ -190,21 +190,25 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
     const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
     const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, M.groups - j0);
     t.off = M.tile_offsets[a * M.col_tiles + ct];
-    const uint32_t jl = lane >> 4, k = lane & 15;
+    // Loads are unconditional (lanes past the tile read a valid neighbour and
+    // their values are never used), so the compiler can count them and wait
+    // for exactly these, not for loads issued after them.
+    const uint32_t jl = min(lane >> 4, cn - 1), k = lane & 15;
     t.xv = make_uint2(0u, 0u);
-    if (with_x && jl < cn) t.xv = *reinterpret_cast<const uint2 *>(M.x + 64u * (j0 + jl) + 4u * k);
+    if (with_x) t.xv = *reinterpret_cast<const uint2 *>(M.x + 64u * (j0 + jl) + 4u * k);
     t.codes = t.s01 = t.s23 = 0u;
-    if (lane < rows) {
+    {
         // the tile's metadata is one contiguous run of rows*cn slots, row-major
         const uint64_t base = static_cast<uint64_t>(r0) * M.groups + static_cast<uint64_t>(rows) * j0;
+        const uint32_t lr = min(lane, rows - 1);
         if (kAligned || cn == kTileGroups) {
             // base is a multiple of 4: one width byte and one 8-byte scale load per row
-            t.codes = M.widths[(base >> 2) + lane];
-            const uint2 sv = *reinterpret_cast<const uint2 *>(M.scales + base + 4u * lane);
+            t.codes = M.widths[(base >> 2) + lr];
+            const uint2 sv = *reinterpret_cast<const uint2 *>(M.scales + base + 4u * lr);
             t.s01 = sv.x;
             t.s23 = sv.y;
         } else {
-            const uint64_t g = base + static_cast<uint64_t>(lane) * cn;
+            const uint64_t g = base + static_cast<uint64_t>(lr) * cn;
             const uint64_t wbytes = (static_cast<uint64_t>(M.n) * M.groups + 3) >> 2;
             uint32_t two = M.widths[g >> 2];
             if ((g >> 2) + 1 < wbytes) two |= static_cast<uint32_t>(M.widths[(g >> 2) + 1]) << 8;
@@ -252,64 +256,72 @@ __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
     }
 }
 
-// Width-code bit planes of a tile, one ballot pair per column: bit r of
-// plane0[jl] / plane1[jl] is bit 0 / bit 1 of row r's code in column jl.
-struct TilePlanes {
-    uint64_t plane0[kTileGroups], plane1[kTileGroups], live;
+// Inclusive prefix sum over the 64 lanes (DPP: row shifts, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+    v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x111, 0xF, 0xF, true));  // row_shr:1
+    v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x112, 0xF, 0xF, true));  // row_shr:2
+    v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x114, 0xF, 0xF, true));  // row_shr:4
+    v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x118, 0xF, 0xF, true));  // row_shr:8
+    v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x142, 0xA, 0xF, false)); // row_bcast:15
+    v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x143, 0xC, 0xF, false)); // row_bcast:31
+    return v;
+}
+
+// Per column, each lane's width code as a one-hot byte counter (byte c = 1
+// for code c) and its inclusive prefix sum over the rows: byte c of the
+// exclusive sum is the row's rank among the rows of its width in that column,
+// byte c of lane 63's sum is the column's count of width c.
+struct TileScan {
+    uint32_t incl[kTileGroups];   // per lane
+    uint32_t cols[kTileGroups];   // column counts, four bytes (uniform)
 };
 
-__device__ __forceinline__ TilePlanes tile_planes(const TileMeta &t, uint32_t rows, uint32_t cn, uint32_t lane,
-                                                  uint32_t cnt[4]) {
-    TilePlanes P;
+__device__ __forceinline__ TileScan tile_scan(const TileMeta &t, uint32_t rows, uint32_t cn, uint32_t lane,
+                                              uint32_t cnt[4]) {
+    TileScan T;
     const bool valid = lane < rows;
-    P.live = __ballot(valid);
-    const uint32_t nlive = static_cast<uint32_t>(__popcll(P.live));
-    cnt[0] = cnt[1] = cnt[2] = cnt[3] = 0;
 #pragma unroll
     for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
         const uint32_t c = (t.codes >> (2 * jl)) & 3u;
-        const uint64_t p0 = __ballot(valid && (c & 1u)), p1 = __ballot(valid && (c & 2u));
-        P.plane0[jl] = p0;
-        P.plane1[jl] = p1;
-        if (jl < cn) {
-            const uint32_t n3 = static_cast<uint32_t>(__popcll(p0 & p1));
-            const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1));
-            const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1));
-            cnt[0] += nlive - n1 - n2 - n3;
-            cnt[1] += n1;
-            cnt[2] += n2;
-            cnt[3] += n3;
-        }
+        const uint32_t one = (valid && jl < cn) ? 1u << (8 * c) : 0u;
+        T.incl[jl] = wave_scan(one);
+        T.cols[jl] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(T.incl[jl]), kWave - 1));
     }
-    return P;
+    // tile totals per width (up to 256: summed outside the byte fields)
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+#pragma unroll
+    for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
+        c0 += T.cols[jl] & 0xFFu;
+        c1 += (T.cols[jl] >> 8) & 0xFFu;
+        c2 += (T.cols[jl] >> 16) & 0xFFu;
+        c3 += T.cols[jl] >> 24;
+    }
+    cnt[0] = c0;
+    cnt[1] = c1;
+    cnt[2] = c2;
+    cnt[3] = c3;
+    return T;
 }
 
-// Lane r = row r of the tile: sort the tile's groups into per-width lists in
-// the stream's order (column-major inside a bucket). A lane's rank among the
-// rows that share its width is one mbcnt over the mask of equal codes.
-__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const TilePlanes &P, uint32_t rows,
+// Lane r = row r of the tile: put each of its groups into its width's list
+// at its place in the stream's order (column-major inside a bucket).
+__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const TileScan &T, uint32_t rows,
                                             uint32_t cn, uint32_t lane) {
     const bool valid = lane < rows;
-    uint32_t before[4] = {0u, 0u, 0u, 0u};   // groups of each width in earlier columns
+    uint64_t before = 0;   // groups of each width in earlier columns, 16 bits per width (uniform)
 #pragma unroll
     for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
         if (jl >= cn) break;
         const uint32_t c = (t.codes >> (2 * jl)) & 3u;
-        const uint64_t p0 = P.plane0[jl], p1 = P.plane1[jl];
-        const uint64_t f0 = (c & 1u) ? p0 : ~p0, f1 = (c & 2u) ? p1 : ~p1;
-        const uint32_t rank = lane_rank(f0 & f1 & P.live);
-        const uint32_t base = c == 0 ? before[0] : c == 1 ? before[1] : c == 2 ? before[2] : before[3];
+        const uint32_t excl = T.incl[jl] - (1u << (8 * c));
+        const uint32_t slot = static_cast<uint32_t>((before >> (16 * c)) & 0xFFFFu) + ((excl >> (8 * c)) & 0xFFu);
         if (valid) {
             const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
-            L.list[c][base + rank] = lane | (jl << 8) | (sb << 16);
+            L.list[c][slot] = lane | (jl << 8) | (sb << 16);
         }
-        const uint32_t n3 = static_cast<uint32_t>(__popcll(p0 & p1));
-        const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1));
-        const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1));
-        before[0] += static_cast<uint32_t>(__popcll(P.live)) - n1 - n2 - n3;
-        before[1] += n1;
-        before[2] += n2;
-        before[3] += n3;
+        const uint32_t cc = T.cols[jl];
+        before += static_cast<uint64_t>(cc & 0xFFu) | (static_cast<uint64_t>((cc >> 8) & 0xFFu) << 16) |
+                  (static_cast<uint64_t>((cc >> 16) & 0xFFu) << 32) | (static_cast<uint64_t>(cc >> 24) << 48);
     }
 }
 
@@ -418,29 +430,30 @@ struct Staged {
     uint2 p2a, p2b, p4a, p4b, p8a, p8b;
 };
 
+// Every staged load is issued unconditionally: a lane without a task reads
+// the tile's first bytes (always inside the payload) and ignores them. With
+// a fixed number of loads the compiler waits for exactly these and not for
+// the next tile's metadata issued after them.
 __device__ __forceinline__ void stage_payload(const uint8_t *tile, const uint32_t cnt[4], uint32_t lane, Staged &S) {
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i) {
         const uint32_t e = lane + kWave * i;
-        if (e < cnt[0]) S.p1[i] = load8(tile + 8u * e);
+        S.p1[i] = load8(tile + (e < cnt[0] ? 8u * e : 0u));
     }
-    const uint8_t *b2 = tile + 8u * cnt[0];
-    const uint8_t *b4 = b2 + 16u * cnt[1];
-    const uint8_t *b8 = b4 + 32u * cnt[2];
-    if (lane < cnt[1]) {
-        S.p2a = load8(b2 + 16u * lane);
-        S.p2b = load8(b2 + 16u * lane + 8u);
-    }
-    if (lane < 2u * cnt[2]) {
-        S.p4a = load8(b4 + 16u * lane);
-        S.p4b = load8(b4 + 16u * lane + 8u);
-    }
-    if (lane < 4u * cnt[3]) {
-        S.p8a = load8(b8 + 16u * lane);
-        S.p8b = load8(b8 + 16u * lane + 8u);
-    }
+    const uint32_t o2 = 8u * cnt[0], o4 = o2 + 16u * cnt[1], o8 = o4 + 32u * cnt[2];
+    // (a lane without a task reads bytes 0..7 twice: a tile may be only 8 bytes long)
+    const bool t2 = lane < cnt[1], t4 = lane < 2u * cnt[2], t8 = lane < 4u * cnt[3];
+    const uint32_t a2 = o2 + 16u * lane, a4 = o4 + 16u * lane, a8 = o8 + 16u * lane;
+    S.p2a = load8(tile + (t2 ? a2 : 0u));
+    S.p2b = load8(tile + (t2 ? a2 + 8u : 0u));
+    S.p4a = load8(tile + (t4 ? a4 : 0u));
+    S.p4b = load8(tile + (t4 ? a4 + 8u : 0u));
+    S.p8a = load8(tile + (t8 ? a8 : 0u));
+    S.p8b = load8(tile + (t8 ? a8 + 8u : 0u));
 }
 
+// Staged work first, then the rounds that load their own bytes (rare: more
+// than 64 two-bit groups or 64 slices of a wider width in one tile).
 __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const uint8_t *tile, const uint32_t cnt[4],
                                               uint32_t lane) {
 #pragma unroll
@@ -450,12 +463,12 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
     const uint8_t *b4 = b2 + 16u * cnt[1];
     const uint8_t *b8 = b4 + 32u * cnt[2];
     if (lane < cnt[1]) group2(L, L.list[1][lane], S.p2a, S.p2b);
+    if (lane < 2u * cnt[2]) task4(L, L.list[2][lane >> 1], lane & 1u, S.p4a, S.p4b);
+    if (lane < 4u * cnt[3]) task8(L, L.list[3][lane >> 2], lane & 3u, S.p8a, S.p8b);
     for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
         group2(L, L.list[1][e], load8(b2 + 16u * e), load8(b2 + 16u * e + 8u));
-    if (lane < 2u * cnt[2]) task4(L, L.list[2][lane >> 1], lane & 1u, S.p4a, S.p4b);
     for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
         task4(L, L.list[2][e >> 1], e & 1u, load8(b4 + 16u * e), load8(b4 + 16u * e + 8u));
-    if (lane < 4u * cnt[3]) task8(L, L.list[3][lane >> 2], lane & 3u, S.p8a, S.p8b);
     for (uint32_t e = lane + kWave; e < 4u * cnt[3]; e += kWave)
         task8(L, L.list[3][e >> 2], e & 3u, load8(b8 + 16u * e), load8(b8 + 16u * e + 8u));
 }
@@ -477,19 +490,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     WaveLds &L = lds[wave];
     float acc = 0.f;
     uint32_t ct = c_lo + wave;
-    TileMeta cur{};
-    if (ct < c_hi) cur = load_meta<kAligned>(M, a, ct, lane_id(), true);
+    // metadata loads are unconditional (a wave without a next tile reloads its
+    // own): a conditional load would make its result a branch merge, and the
+    // merge copy would wait for the load
+    TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, lane_id(), true);
     for (; ct < c_hi; ct += kWavesPerBlock) {
         const uint32_t cn = min(kTileGroups, M.groups - ct * kTileGroups);
         // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
-        const TilePlanes P = tile_planes(cur, rows, cn, lane_id(), cnt);
+        const TileScan P = tile_scan(cur, rows, cn, lane_id(), cnt);
         const uint8_t *tp = M.payload + cur.off;
         Staged S;
         stage_payload(tp, cnt, lane_id(), S);
         // the next tile's metadata travels while this tile computes
-        TileMeta nxt{};
-        if (ct + kWavesPerBlock < c_hi) nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock, lane_id(), true);
+        const TileMeta nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock < c_hi ? ct + kWavesPerBlock : ct,
+                                                 lane_id(), true);
         stage_x(L, cur.xv, lane_id());
         build_lists(L, cur, P, rows, cn, lane_id());
         wave_lds_sync();
@@ -545,7 +560,7 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
     const uint8_t *tp = M.payload + t.off;
     const uint64_t k = static_cast<uint64_t>(M.groups) * 64u;
     uint32_t cnt[4];
-    const TilePlanes P = tile_planes(t, rows, cn, lane, cnt);
+    const TileScan P = tile_scan(t, rows, cn, lane, cnt);
     build_lists(L, t, P, rows, cn, lane);
     wave_lds_sync();
     const uint8_t *base = tp;
