@@ -160,17 +160,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
+__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
 // Lane index, recomputed at each use: keeping it live across the tile loop
 // would cost a register the loop needs.
 __device__ __forceinline__ uint32_t lane_id() {
     uint32_t r;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
     return r;
-}
-
-__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
 }
 
 // Inputs of one tile that need no payload: read in one round trip and
@@ -326,6 +326,25 @@ __device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const
 }
 
 __device__ __forceinline__ uint2 load8(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
+
+// Sum of the split partials p[0], p[stride], ... in split order. The coherent
+// loads go out eight at a time (clamped addresses, no branches) so their round
+// trips overlap instead of following one another.
+__device__ __forceinline__ float sum_partials(const float *p, uint64_t stride, uint32_t splits) {
+    float tot = 0.f;
+    for (uint32_t s0 = 0; s0 < splits; s0 += 8) {
+        float v[8];
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i) {
+            const uint32_t s = min(s0 + i, splits - 1);
+            v[i] = __hip_atomic_load(p + s * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i)
+            if (s0 + i < splits) tot += v[i];
+    }
+    return tot;
+}
 
 // ---- one group (or slice) per lane, per width; results to L.part[column][row]
 
@@ -536,13 +555,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     if (lane == 0) arrived = __hip_atomic_fetch_add(&M.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     arrived = __shfl(arrived, 0, kWave);
     if (arrived != M.splits - 1) return;
-    if (lane < rows) {
-        float tot = 0.f;
-        for (uint32_t s = 0; s < M.splits; ++s)
-            tot += __hip_atomic_load(&M.partial[static_cast<uint64_t>(s) * M.n + r0 + lane], __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        M.y[r0 + lane] = tot;
-    }
+    if (lane < rows) M.y[r0 + lane] = sum_partials(M.partial + r0 + lane, M.n, M.splits);
     if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -872,7 +885,10 @@ __device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const PassStage
 }
 
 // Activations of one pass: lane holds X[16mb + lane%16][k .. k+7] for each
-// column jj and half h of the pass (zeros past m or past the last column).
+// column jj and half h of the pass. Rows past m and columns past the tile
+// load a valid neighbour instead: the products they feed are never stored
+// (a matrix-core output column depends on its own input column only) or
+// never computed, and branch-free loads are waited for exactly.
 template <uint32_t MB>
 __device__ __forceinline__ void load_bx(const GemmArgs &G, uint32_t j0, uint32_t pass, uint32_t cn,
                                         half8_t bx[2][2][MB]) {
@@ -883,11 +899,9 @@ __device__ __forceinline__ void load_bx(const GemmArgs &G, uint32_t j0, uint32_t
         for (uint32_t h = 0; h < 2; ++h)
 #pragma unroll
             for (uint32_t mb = 0; mb < MB; ++mb) {
-                const uint32_t m = 16 * mb + mr, jl = 2 * pass + jj;
-                uint4 v = make_uint4(0u, 0u, 0u, 0u);
-                if (m < G.m && jl < cn)
-                    v = *reinterpret_cast<const uint4 *>(G.x + static_cast<uint64_t>(m) * G.k + 64u * (j0 + jl) +
-                                                         32u * h + 8u * q);
+                const uint32_t m = min(16 * mb + mr, G.m - 1), jl = min(2 * pass + jj, cn - 1);
+                const uint4 v = *reinterpret_cast<const uint4 *>(G.x + static_cast<uint64_t>(m) * G.k +
+                                                                 64u * (j0 + jl) + 32u * h + 8u * q);
                 bx[jj][h][mb] = __builtin_bit_cast(half8_t, v);
             }
 }
@@ -940,8 +954,7 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
         for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
     uint32_t ct = c_lo + wave;
-    TileMeta cur{};
-    if (ct < c_hi) cur = load_meta<false>(G, a, ct, lane_id(), false);
+    TileMeta cur = load_meta<false>(G, a, ct < c_hi ? ct : c_lo, lane_id(), false);
     for (; ct < c_hi; ct += kWavesPerBlock) {
         const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, G.groups - j0);
         uint64_t colstart[kTileGroups + 1];
@@ -952,20 +965,21 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
         const PassStage s0 = gemm_stage_pass(tile, colstart, 0, cn);
         PassStage s1{};
         if (cn > 2) s1 = gemm_stage_pass(tile, colstart, 1, cn);
-        half8_t bx[2][2][MB];
+        half8_t bx[2][2][MB], bx1[2][2][MB];
         load_bx<MB>(G, j0, 0, cn, bx);
+        if (MB <= 2) load_bx<MB>(G, j0, cn > 2 ? 1 : 0, cn, bx1);   // both passes' activations up front
         // the next tile's metadata travels while this tile computes
-        TileMeta nxt{};
-        if (ct + kWavesPerBlock < c_hi) nxt = load_meta<false>(G, a, ct + kWavesPerBlock, lane_id(), false);
+        const TileMeta nxt = load_meta<false>(G, a, ct + kWavesPerBlock < c_hi ? ct + kWavesPerBlock : ct,
+                                              lane_id(), false);
         gemm_decode_pass(L, s0, tile, colstart, 0, cn);
         wave_lds_sync();
         mfma_pass<MB>(L, bx, 0, cn, acc);
         if (cn > 2) {
-            load_bx<MB>(G, j0, 1, cn, bx);
+            if (MB > 2) load_bx<MB>(G, j0, 1, cn, bx1);
             wave_lds_sync();
             gemm_decode_pass(L, s1, tile, colstart, 1, cn);
             wave_lds_sync();
-            mfma_pass<MB>(L, bx, 1, cn, acc);
+            mfma_pass<MB>(L, bx1, 1, cn, acc);
         }
         wave_lds_sync();
         cur = nxt;
@@ -1007,13 +1021,10 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
     __syncthreads();
     if (arrived_s != G.splits - 1) return;
     for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
-        const uint32_t m = i / kTileRows, row = i % kTileRows;
-        if (row >= rows) continue;
-        float tot = 0.f;
-        for (uint32_t s = 0; s < G.splits; ++s)
-            tot += __hip_atomic_load(&G.partial[(static_cast<uint64_t>(s) * G.m + m) * G.n + r0 + row],
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        G.y[static_cast<uint64_t>(m) * G.n + r0 + row] = tot;
+        const uint32_t m = i / kTileRows, row = min(i % kTileRows, rows - 1);
+        const float tot = sum_partials(G.partial + static_cast<uint64_t>(m) * G.n + r0 + row,
+                                       static_cast<uint64_t>(G.m) * G.n, G.splits);
+        if (i % kTileRows < rows) G.y[static_cast<uint64_t>(m) * G.n + r0 + row] = tot;
     }
     if (threadIdx.x == 0) __hip_atomic_store(&G.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
