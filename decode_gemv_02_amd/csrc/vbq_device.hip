@@ -499,7 +499,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     // which matrix, row tile and split this block serves (uniform)
     uint32_t mi = 0;
     while (mi + 1 < B.count && blockIdx.x >= B.m[mi + 1].block_begin) ++mi;
-    const MatArgs &M = B.m[mi];
+    const MatArgs M = B.m[mi];   // by value: loaded into scalar registers once
     const uint32_t local = blockIdx.x - M.block_begin;
     const uint32_t a = local / M.splits, split = local % M.splits;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;   // uniform
