@@ -142,9 +142,11 @@ struct MatArgs {
     uint32_t n, groups, col_tiles, splits, block_begin, pad;
 };
 
+// The block ranges come first, in one 64-byte run, so a block finds its
+// matrix with one scalar load before it loads that matrix's arguments.
 struct Batch {
+    uint32_t first_block[VBQ_MAX_MULTI];   // first block of matrix i; unused entries hold UINT32_MAX
     MatArgs m[VBQ_MAX_MULTI];
-    uint32_t count;
 };
 
 struct alignas(16) WaveLds {
@@ -498,7 +500,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     __shared__ float rowsum[kWavesPerBlock][kTileRows];
     // which matrix, row tile and split this block serves (uniform)
     uint32_t mi = 0;
-    while (mi + 1 < B.count && blockIdx.x >= B.m[mi + 1].block_begin) ++mi;
+#pragma unroll
+    for (uint32_t i = 1; i < VBQ_MAX_MULTI; ++i) mi += blockIdx.x >= B.first_block[i] ? 1u : 0u;
     const MatArgs M = B.m[mi];   // by value: loaded into scalar registers once
     const uint32_t local = blockIdx.x - M.block_begin;
     const uint32_t a = local / M.splits, split = local % M.splits;
@@ -1148,7 +1151,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
             partial_total += partial_bytes(M.splits, M.n);
         }
     }
-    B.count = used;
+    for (uint32_t i = 0; i < VBQ_MAX_MULTI; ++i) B.first_block[i] = i < used ? B.m[i].block_begin : UINT32_MAX;
     if (used == 0) return any_launch ? launched(who) : VBQ_OK;
     if (counter_slots) {
         uint32_t *ctr = nullptr;
