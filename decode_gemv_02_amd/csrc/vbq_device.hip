@@ -139,13 +139,12 @@ struct MatArgs {
     float *y;
     float *partial;       // [splits][n] when splits > 1
     uint32_t *counters;   // [row tiles] arrival counters when splits > 1 (self-resetting)
-    uint32_t n, groups, col_tiles, splits, block_begin, pad;
+    uint32_t n, groups, col_tiles, splits, blocks, pad;   // blocks = row tiles x splits
 };
 
-// The block ranges come first, in one 64-byte run, so a block finds its
-// matrix with one scalar load before it loads that matrix's arguments.
+// Launched as a 2D grid: blockIdx.y picks the matrix, so a block loads its
+// matrix's arguments with one scalar load and no search.
 struct Batch {
-    uint32_t first_block[VBQ_MAX_MULTI];   // first block of matrix i; unused entries hold UINT32_MAX
     MatArgs m[VBQ_MAX_MULTI];
 };
 
@@ -499,12 +498,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     __shared__ WaveLds lds[kWavesPerBlock];
     __shared__ float rowsum[kWavesPerBlock][kTileRows];
     // which matrix, row tile and split this block serves (uniform)
-    uint32_t mi = 0;
-#pragma unroll
-    for (uint32_t i = 1; i < VBQ_MAX_MULTI; ++i) mi += blockIdx.x >= B.first_block[i] ? 1u : 0u;
-    const MatArgs M = B.m[mi];   // by value: loaded into scalar registers once
-    const uint32_t local = blockIdx.x - M.block_begin;
-    const uint32_t a = local / M.splits, split = local % M.splits;
+    const MatArgs M = B.m[blockIdx.y];   // by value: loaded into scalar registers once
+    // The grid is as wide as the largest matrix of the launch. A block past
+    // its matrix's end repeats the matrix's last block and stores nothing:
+    // testing first would put a dependent load ahead of the others.
+    const bool spare = blockIdx.x >= M.blocks;
+    const uint32_t bx = spare ? M.blocks - 1 : blockIdx.x;
+    const uint32_t a = bx / M.splits, split = bx % M.splits;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;   // uniform
     const uint32_t r0 = a * kTileRows;
     const uint32_t rows = min(kTileRows, M.n - r0);
@@ -541,7 +541,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     const uint32_t lane = lane_id();
     rowsum[wave][lane] = acc;
     __syncthreads();
-    if (wave != 0) return;
+    if (wave != 0 || spare) return;
     const float sum = ((rowsum[0][lane] + rowsum[1][lane]) + rowsum[2][lane]) + rowsum[3][lane];
     if (M.splits == 1) {
         if (lane < rows) M.y[r0 + lane] = sum;
@@ -1143,15 +1143,14 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.col_tiles = ceil_div(M.groups, kTileGroups);
         const uint32_t row_tiles = ceil_div(M.n, kTileRows);
         M.splits = std::max(1u, std::min(ceil_div(M.col_tiles, kWavesPerBlock), factor));
-        M.block_begin = blocks;
-        blocks += row_tiles * M.splits;
+        M.blocks = row_tiles * M.splits;
+        blocks = std::max(blocks, M.blocks);
         if (M.groups % 4) aligned = false;
         if (M.splits > 1) {
             counter_slots += row_tiles;
             partial_total += partial_bytes(M.splits, M.n);
         }
     }
-    for (uint32_t i = 0; i < VBQ_MAX_MULTI; ++i) B.first_block[i] = i < used ? B.m[i].block_begin : UINT32_MAX;
     if (used == 0) return any_launch ? launched(who) : VBQ_OK;
     if (counter_slots) {
         uint32_t *ctr = nullptr;
@@ -1168,9 +1167,9 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         }
     }
     if (aligned)
-        hipLaunchKernelGGL(gemv_tiles<true>, dim3(blocks), dim3(256), 0, stream, B);
+        hipLaunchKernelGGL(gemv_tiles<true>, dim3(blocks, used), dim3(256), 0, stream, B);
     else
-        hipLaunchKernelGGL(gemv_tiles<false>, dim3(blocks), dim3(256), 0, stream, B);
+        hipLaunchKernelGGL(gemv_tiles<false>, dim3(blocks, used), dim3(256), 0, stream, B);
     return launched(who);
 }
 
