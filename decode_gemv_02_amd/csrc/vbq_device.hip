@@ -161,11 +161,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-__device__ __forceinline__ uint32_t lane_rank(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
-}
-
 // Lane index, recomputed at each use: keeping it live across the tile loop
 // would cost a register the loop needs.
 __device__ __forceinline__ uint32_t lane_id() {
@@ -773,37 +768,42 @@ __device__ __forceinline__ void decode8(uint4 v, uint16_t *dst) {
     *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// Per-width lists of one tile (bucket order) and where each column starts in
-// them; scales of the tile to LDS as fp32. colstart[c] packs, 16 bits per
-// width, how many groups of each width precede column c.
-__device__ __forceinline__ void gemm_lists(GemmWaveLds &L, const TileMeta &t, uint32_t rows, uint32_t cn,
-                                           uint64_t colstart[kTileGroups + 1]) {
-    const uint32_t lane = lane_id();
-    const bool valid = lane < rows;
-    const uint64_t live = __ballot(valid);
-    uint64_t packed = 0;
+// How many groups of each width come before each column (16 bits per width),
+// from the per-column counts of the tile scan; entry 4 holds the tile totals.
+__device__ __forceinline__ void column_starts(const TileScan &T, uint64_t colstart[kTileGroups + 1]) {
+    uint64_t before = 0;
 #pragma unroll
     for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
-        colstart[jl] = packed;
-        if (jl < cn) {
-            const uint32_t c = (t.codes >> (2 * jl)) & 3u;
-            const uint64_t p0 = __ballot(valid && (c & 1u)), p1 = __ballot(valid && (c & 2u));
-            const uint64_t f0 = (c & 1u) ? p0 : ~p0, f1 = (c & 2u) ? p1 : ~p1;
-            const uint32_t slot = static_cast<uint32_t>((packed >> (16 * c)) & 0xFFFFu) + lane_rank(f0 & f1 & live);
-            if (valid) {
-                L.list[c][slot] = static_cast<uint8_t>(lane | (jl << 6));
-                const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
-                L.scale[jl][lane] = half_to_float(sb);
-            }
-            const uint32_t n3 = static_cast<uint32_t>(__popcll(p0 & p1));
-            const uint32_t n1 = static_cast<uint32_t>(__popcll(p0 & ~p1 & live));
-            const uint32_t n2 = static_cast<uint32_t>(__popcll(~p0 & p1 & live));
-            const uint32_t n0 = static_cast<uint32_t>(__popcll(live)) - n1 - n2 - n3;
-            packed += static_cast<uint64_t>(n0) | (static_cast<uint64_t>(n1) << 16) |
-                      (static_cast<uint64_t>(n2) << 32) | (static_cast<uint64_t>(n3) << 48);
+        colstart[jl] = before;
+        const uint32_t cc = T.cols[jl];
+        before += static_cast<uint64_t>(cc & 0xFFu) | (static_cast<uint64_t>((cc >> 8) & 0xFFu) << 16) |
+                  (static_cast<uint64_t>((cc >> 16) & 0xFFu) << 32) | (static_cast<uint64_t>(cc >> 24) << 48);
+    }
+    colstart[kTileGroups] = before;
+}
+
+__device__ __forceinline__ uint32_t field16(uint64_t v, uint32_t w) {
+    return static_cast<uint32_t>((v >> (16 * w)) & 0xFFFFu);
+}
+
+// Per-width lists of one tile (bucket order) from the tile scan, and the
+// scales of the tile as fp32.
+__device__ __forceinline__ void gemm_lists(GemmWaveLds &L, const TileMeta &t, const TileScan &T,
+                                           const uint64_t colstart[kTileGroups + 1], uint32_t rows, uint32_t cn,
+                                           uint32_t lane) {
+    const bool valid = lane < rows;
+#pragma unroll
+    for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
+        if (jl >= cn) break;
+        const uint32_t c = (t.codes >> (2 * jl)) & 3u;
+        const uint32_t excl = T.incl[jl] - (1u << (8 * c));
+        const uint32_t slot = field16(colstart[jl], c) + ((excl >> (8 * c)) & 0xFFu);
+        if (valid) {
+            L.list[c][slot] = static_cast<uint8_t>(lane | (jl << 6));
+            const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
+            L.scale[jl][lane] = half_to_float(sb);
         }
     }
-    colstart[kTileGroups] = packed;
 }
 
 // 16 payload bytes at an 8-byte aligned address (buckets start at multiples of 8)
@@ -812,9 +812,6 @@ __device__ __forceinline__ uint4 load16(const uint8_t *p) {
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-__device__ __forceinline__ uint32_t field16(uint64_t v, uint32_t w) {
-    return static_cast<uint32_t>((v >> (16 * w)) & 0xFFFFu);
-}
 
 // Payload of one pass (two columns of a tile): the first 128 one-bit groups
 // and the first 64 tasks of each wider width, loaded before any is decoded.
@@ -838,19 +835,35 @@ __device__ __forceinline__ void pass_range(const uint64_t colstart[kTileGroups +
 __device__ __forceinline__ PassStage gemm_stage_pass(const uint8_t *tile, const uint64_t colstart[kTileGroups + 1],
                                                      uint32_t pass, uint32_t cn) {
     const uint32_t lane = lane_id();
+    // unconditional loads (a lane without a task reads the tile's first bytes
+    // twice: a tile may be only 8 bytes long), so the compiler counts them
     PassStage S;
-    S.p1[0] = S.p1[1] = make_uint2(0u, 0u);
-    S.p2 = S.p4 = S.p8 = make_uint4(0u, 0u, 0u, 0u);
     uint32_t e0, e1, base;
     pass_range(colstart, pass, cn, 0, e0, e1, base);
-    if (lane < e1 - e0) S.p1[0] = load8(tile + base + 8u * (e0 + lane));
-    if (lane + kWave < e1 - e0) S.p1[1] = load8(tile + base + 8u * (e0 + lane + kWave));
+    S.p1[0] = load8(tile + (lane < e1 - e0 ? base + 8u * (e0 + lane) : 0u));
+    S.p1[1] = load8(tile + (lane + kWave < e1 - e0 ? base + 8u * (e0 + lane + kWave) : 0u));
     pass_range(colstart, pass, cn, 1, e0, e1, base);
-    if (lane < e1 - e0) S.p2 = load16(tile + base + 16u * (e0 + lane));
+    const bool t2 = lane < e1 - e0;
+    const uint32_t a2 = base + 16u * (e0 + lane);
+    S.p2 = make_uint4(0u, 0u, 0u, 0u);
+    {
+        const uint2 lo = load8(tile + (t2 ? a2 : 0u)), hi = load8(tile + (t2 ? a2 + 8u : 0u));
+        S.p2 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
     pass_range(colstart, pass, cn, 2, e0, e1, base);
-    if (lane < 2 * (e1 - e0)) S.p4 = load16(tile + base + 32u * e0 + 16u * lane);
+    const bool t4 = lane < 2 * (e1 - e0);
+    const uint32_t a4 = base + 32u * e0 + 16u * lane;
+    {
+        const uint2 lo = load8(tile + (t4 ? a4 : 0u)), hi = load8(tile + (t4 ? a4 + 8u : 0u));
+        S.p4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
     pass_range(colstart, pass, cn, 3, e0, e1, base);
-    if (lane < 4 * (e1 - e0)) S.p8 = load16(tile + base + 64u * e0 + 16u * lane);
+    const bool t8 = lane < 4 * (e1 - e0);
+    const uint32_t a8 = base + 64u * e0 + 16u * lane;
+    {
+        const uint2 lo = load8(tile + (t8 ? a8 : 0u)), hi = load8(tile + (t8 ? a8 + 8u : 0u));
+        S.p8 = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
     return S;
 }
 
@@ -960,20 +973,22 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
     TileMeta cur = load_meta<false>(G, a, ct < c_hi ? ct : c_lo, lane_id(), false);
     for (; ct < c_hi; ct += kWavesPerBlock) {
         const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, G.groups - j0);
+        // counts first: every payload byte of the tile is requested before the lists are built
+        uint32_t cnt[4];
+        const TileScan T = tile_scan(cur, rows, cn, lane_id(), cnt);
         uint64_t colstart[kTileGroups + 1];
-        gemm_lists(L, cur, rows, cn, colstart);
-        wave_lds_sync();
+        column_starts(T, colstart);
         const uint8_t *tile = G.payload + cur.off;
-        // every payload byte of the tile is requested before the first decode
         const PassStage s0 = gemm_stage_pass(tile, colstart, 0, cn);
-        PassStage s1{};
-        if (cn > 2) s1 = gemm_stage_pass(tile, colstart, 1, cn);
+        const PassStage s1 = gemm_stage_pass(tile, colstart, cn > 2 ? 1 : 0, cn);
         half8_t bx[2][2][MB], bx1[2][2][MB];
         load_bx<MB>(G, j0, 0, cn, bx);
         if (MB <= 2) load_bx<MB>(G, j0, cn > 2 ? 1 : 0, cn, bx1);   // both passes' activations up front
         // the next tile's metadata travels while this tile computes
         const TileMeta nxt = load_meta<false>(G, a, ct + kWavesPerBlock < c_hi ? ct + kWavesPerBlock : ct,
                                               lane_id(), false);
+        gemm_lists(L, cur, T, colstart, rows, cn, lane_id());
+        wave_lds_sync();
         gemm_decode_pass(L, s0, tile, colstart, 0, cn);
         wave_lds_sync();
         mfma_pass<MB>(L, bx, 0, cn, acc);
@@ -1000,9 +1015,11 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
                 for (uint32_t v = 0; v < 4; ++v) red[(16 * mb + mr) * kTileRows + 16 * rb + 4 * q + v] = acc[rb][mb][v];
     }
     __syncthreads();
+    // output i = m * 64 + row; thread t owns outputs t, t + 256, ... (at most 16)
     const uint32_t outs = G.m * kTileRows;
     const float *r0p = reinterpret_cast<const float *>(lds[0].a), *r1p = reinterpret_cast<const float *>(lds[1].a);
     const float *r2p = reinterpret_cast<const float *>(lds[2].a), *r3p = reinterpret_cast<const float *>(lds[3].a);
+    constexpr uint32_t kPerThread = (VBQ_MAX_BATCH * kTileRows) / (kWavesPerBlock * kWave);   // 16
     if (G.splits == 1) {
         for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
             const uint32_t m = i / kTileRows, row = i % kTileRows;
@@ -1023,11 +1040,34 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
         arrived_s = __hip_atomic_fetch_add(&G.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (arrived_s != G.splits - 1) return;
-    for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
-        const uint32_t m = i / kTileRows, row = min(i % kTileRows, rows - 1);
-        const float tot = sum_partials(G.partial + static_cast<uint64_t>(m) * G.n + r0 + row,
-                                       static_cast<uint64_t>(G.m) * G.n, G.splits);
-        if (i % kTileRows < rows) G.y[static_cast<uint64_t>(m) * G.n + r0 + row] = tot;
+    // every output's partials are requested before any is added (clamped
+    // addresses for outputs past m x rows, which are not stored)
+    const uint64_t stride = static_cast<uint64_t>(G.m) * G.n;
+    for (uint32_t s0 = 0; s0 < G.splits; s0 += 2) {
+        float v[kPerThread][2];
+#pragma unroll
+        for (uint32_t j = 0; j < kPerThread; ++j) {
+            const uint32_t i = min(threadIdx.x + j * blockDim.x, outs - 1);
+            const uint32_t m = i / kTileRows, row = min(i % kTileRows, rows - 1);
+            const float *p = G.partial + static_cast<uint64_t>(m) * G.n + r0 + row;
+#pragma unroll
+            for (uint32_t h = 0; h < 2; ++h)
+                v[j][h] = __hip_atomic_load(p + min(s0 + h, G.splits - 1) * stride, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (uint32_t j = 0; j < kPerThread; ++j) {
+            const uint32_t i = threadIdx.x + j * blockDim.x;
+            if (i >= outs) break;
+            const uint32_t m = i / kTileRows, row = i % kTileRows;
+            float *y = G.y + static_cast<uint64_t>(m) * G.n + r0 + row;
+            if (row < rows) {
+                float t = s0 == 0 ? 0.f : *y;
+                t += v[j][0];
+                if (s0 + 1 < G.splits) t += v[j][1];
+                *y = t;
+            }
+        }
     }
     if (threadIdx.x == 0) __hip_atomic_store(&G.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1189,8 +1229,10 @@ vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, 
     G.m = m;
     G.k = w->k;
     const uint32_t row_tiles = ceil_div(G.n, kTileRows);
+    // two workgroups per CU are resident (LDS): split the column tiles only
+    // while the row tiles alone leave CUs idle
     const uint32_t want_blocks = 512;
-    G.splits = std::max(1u, std::min(ceil_div(G.col_tiles, kWavesPerBlock), ceil_div(want_blocks, row_tiles)));
+    G.splits = std::max(1u, std::min(ceil_div(G.col_tiles, kWavesPerBlock), want_blocks / row_tiles));
     if (G.splits > 1) {
         uint32_t *ctr = nullptr;
         char *part = nullptr;
