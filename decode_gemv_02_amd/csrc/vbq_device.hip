@@ -660,7 +660,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kGemmMinBatch = 16;
+constexpr uint32_t kGemmMinBatch = 4;   // from 4 rows the matrix cores beat one GEMV per row (measured)
 constexpr uint32_t kAStride = 136;   // fp16 per staged row: two columns of 64 codes + 8 pad (272 B)
 
 struct GemmArgs {

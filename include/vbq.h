@@ -171,8 +171,10 @@ VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *c
 
 /* Y = X W^T for m <= VBQ_MAX_BATCH fp16 vectors (small-batch decode).
  * x: device binary16 [m][k] row-major; y: device fp32 [m][n] row-major
- * (overwritten). m >= 16 runs on the MFMA matrix cores, smaller m on the
- * vector units. Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, HIP. */
+ * (overwritten). m >= 4 runs on the matrix cores (each group's codes decoded
+ * once, 16x16x32 fp16 products, fp32 accumulation), m < 4 as one batch-1 GEMV
+ * per row of X on the vector units. Scratch as for vbq_gemv_multi.
+ * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, HIP. */
 VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                                void *stream);
 

@@ -97,7 +97,7 @@ def test_gemv_matches_oracle(V, torch_mod, n, k):
     assert_within_tolerance(y, oracle.gemm(p, x), x, scales, f"gemv {n}x{k}")
 
 
-@pytest.mark.parametrize("m", [2, 3, 8, 15, 16, 17, 31, 48, 63, 64])
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 8, 15, 16, 17, 31, 48, 63, 64])
 def test_gemm_matches_oracle(V, torch_mod, m):
     n, k = 97, 1088
     print_case(test="gemm", n=n, k=k, m=m)
