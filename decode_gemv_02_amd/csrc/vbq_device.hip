@@ -152,7 +152,7 @@ struct alignas(16) WaveLds {
     float lut[kTileGroups * 16 * 16];        // [column][nibble position][4-bit index]
     uint32_t xs[kTileGroups * kXStride];     // fp16 activation pairs per column
     float corr[kTileGroups][4];              // per column: sum x, 2-bit and 4-bit bias terms
-    uint32_t list[4][kTileRows * kTileGroups];
+    uint32_t list[kTileRows * kTileGroups];  // the tile's groups in stream order: 1-bit bucket first
     float part[kTileGroups][kTileRows];      // scaled group dot products
 };
 
@@ -299,12 +299,14 @@ __device__ __forceinline__ TileScan tile_scan(const TileMeta &t, uint32_t rows, 
     return T;
 }
 
-// Lane r = row r of the tile: put each of its groups into its width's list
-// at its place in the stream's order (column-major inside a bucket).
-__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const TileScan &T, uint32_t rows,
-                                            uint32_t cn, uint32_t lane) {
+// Lane r = row r of the tile: put each of its groups into the list at its
+// place in the stream's order (buckets by width, column-major inside a bucket).
+__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const TileScan &T, const uint32_t cnt[4],
+                                            uint32_t rows, uint32_t cn, uint32_t lane) {
     const bool valid = lane < rows;
-    uint64_t before = 0;   // groups of each width in earlier columns, 16 bits per width (uniform)
+    // bucket starts, then the groups of each width in earlier columns, 16 bits per width (uniform)
+    uint64_t before = (static_cast<uint64_t>(cnt[0]) << 16) | (static_cast<uint64_t>(cnt[0] + cnt[1]) << 32) |
+                      (static_cast<uint64_t>(cnt[0] + cnt[1] + cnt[2]) << 48);
 #pragma unroll
     for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
         if (jl >= cn) break;
@@ -313,7 +315,7 @@ __device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const
         const uint32_t slot = static_cast<uint32_t>((before >> (16 * c)) & 0xFFFFu) + ((excl >> (8 * c)) & 0xFFu);
         if (valid) {
             const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
-            L.list[c][slot] = lane | (jl << 8) | (sb << 16);
+            L.list[slot] = lane | (jl << 8) | (sb << 16);
         }
         const uint32_t cc = T.cols[jl];
         before += static_cast<uint64_t>(cc & 0xFFu) | (static_cast<uint64_t>((cc >> 8) & 0xFFu) << 16) |
@@ -473,19 +475,20 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
                                               uint32_t lane) {
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i)
-        if (lane + kWave * i < cnt[0]) group1(L, L.list[0][lane + kWave * i], S.p1[i]);
+        if (lane + kWave * i < cnt[0]) group1(L, L.list[lane + kWave * i], S.p1[i]);
     const uint8_t *b2 = tile + 8u * cnt[0];
     const uint8_t *b4 = b2 + 16u * cnt[1];
     const uint8_t *b8 = b4 + 32u * cnt[2];
-    if (lane < cnt[1]) group2(L, L.list[1][lane], S.p2a, S.p2b);
-    if (lane < 2u * cnt[2]) task4(L, L.list[2][lane >> 1], lane & 1u, S.p4a, S.p4b);
-    if (lane < 4u * cnt[3]) task8(L, L.list[3][lane >> 2], lane & 3u, S.p8a, S.p8b);
+    const uint32_t *l2 = L.list + cnt[0], *l4 = l2 + cnt[1], *l8 = l4 + cnt[2];
+    if (lane < cnt[1]) group2(L, l2[lane], S.p2a, S.p2b);
+    if (lane < 2u * cnt[2]) task4(L, l4[lane >> 1], lane & 1u, S.p4a, S.p4b);
+    if (lane < 4u * cnt[3]) task8(L, l8[lane >> 2], lane & 3u, S.p8a, S.p8b);
     for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
-        group2(L, L.list[1][e], load8(b2 + 16u * e), load8(b2 + 16u * e + 8u));
+        group2(L, l2[e], load8(b2 + 16u * e), load8(b2 + 16u * e + 8u));
     for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
-        task4(L, L.list[2][e >> 1], e & 1u, load8(b4 + 16u * e), load8(b4 + 16u * e + 8u));
+        task4(L, l4[e >> 1], e & 1u, load8(b4 + 16u * e), load8(b4 + 16u * e + 8u));
     for (uint32_t e = lane + kWave; e < 4u * cnt[3]; e += kWave)
-        task8(L, L.list[3][e >> 2], e & 3u, load8(b8 + 16u * e), load8(b8 + 16u * e + 8u));
+        task8(L, l8[e >> 2], e & 3u, load8(b8 + 16u * e), load8(b8 + 16u * e + 8u));
 }
 
 template <bool kAligned>
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         const TileMeta nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock < c_hi ? ct + kWavesPerBlock : ct,
                                                  lane_id(), true);
         stage_x(L, cur.xv, lane_id());
-        build_lists(L, cur, P, rows, cn, lane_id());
+        build_lists(L, cur, P, cnt, rows, cn, lane_id());
         wave_lds_sync();
         tile_products(L, S, tp, cnt, lane_id());
         wave_lds_sync();
@@ -572,13 +575,14 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
     const uint64_t k = static_cast<uint64_t>(M.groups) * 64u;
     uint32_t cnt[4];
     const TileScan P = tile_scan(t, rows, cn, lane, cnt);
-    build_lists(L, t, P, rows, cn, lane);
+    build_lists(L, t, P, cnt, rows, cn, lane);
     wave_lds_sync();
     const uint8_t *base = tp;
+    uint32_t first = 0;   // list index of the bucket's first group
     for (uint32_t wsel = 0; wsel < 4; ++wsel) {
         const uint32_t b = 1u << wsel;
         for (uint32_t e = lane; e < cnt[wsel]; e += kWave) {
-            const uint32_t info = L.list[wsel][e];
+            const uint32_t info = L.list[first + e];
             const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
             const uint32_t *src = reinterpret_cast<const uint32_t *>(base + 8u * b * e);
             uint32_t *dst = reinterpret_cast<uint32_t *>(codes + (r0 + r) * k + 64u * (j0 + jl));
@@ -636,6 +640,7 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
             }
         }
         base += 8u * b * cnt[wsel];
+        first += cnt[wsel];
     }
 }
 
