@@ -185,7 +185,11 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
     TileMeta t;
     const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
     const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, M.groups - j0);
-    t.off = M.tile_offsets[a * M.col_tiles + ct];
+    // The tile offset is uniform: a scalar load (constant address space), so
+    // moving it into a scalar register waits on the scalar counter only and
+    // not on the payload loads issued before it.
+    typedef const __attribute__((address_space(4))) uint32_t *const_u32p;
+    t.off = ((const_u32p)(reinterpret_cast<uintptr_t>(M.tile_offsets)))[a * M.col_tiles + ct];
     // Loads are unconditional (lanes past the tile read a valid neighbour and
     // their values are never used), so the compiler can count them and wait
     // for exactly these, not for loads issued after them.
