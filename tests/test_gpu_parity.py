@@ -131,8 +131,8 @@ def test_one_hot_x_returns_dequantised_column(V, torch_mod):
         assert np.array_equal(y[0], wd.reshape(n, k)[:, col])
 
 
-@pytest.mark.parametrize("m", [16, 37, 64])
-def test_one_hot_rows_on_matrix_cores(V, torch_mod, m):
+@pytest.mark.parametrize("m", [2, 3, 16, 37, 64])
+def test_one_hot_rows_exact(V, torch_mod, m):
     # row i of X is one-hot at column c_i: Y[i] is that column of s*q, exact in fp32
     n, k = 130, 1216
     bits, codes, scales, p = make_case((m, 12), n, k, W.FIRST_MLP_MIX)
@@ -141,7 +141,7 @@ def test_one_hot_rows_on_matrix_cores(V, torch_mod, m):
     cols = (np.arange(m) * 97 + 5) % k
     x = np.zeros((m, k), np.float16)
     x[np.arange(m), cols] = 1.0
-    print_case(test="one_hot_mfma", n=n, k=k, m=m)
+    print_case(test="one_hot_rows", n=n, k=k, m=m)
     y = gpu_gemm(V, torch_mod, dm, x.view(np.uint16))
     assert np.array_equal(y, wd[:, cols].T)
 
