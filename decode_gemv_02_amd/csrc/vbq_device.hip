@@ -193,18 +193,23 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
     // Loads are unconditional (lanes past the tile read a valid neighbour and
     // their values are never used), so the compiler can count them and wait
     // for exactly these, not for loads issued after them.
+    // Byte offsets are 32-bit: a matrix has fewer than 2^29 groups (each group
+    // has at least 8 payload bytes and the payload fits 32-bit offsets, which
+    // the launch checks), so they address from a scalar base register.
     const uint32_t jl = min(lane >> 4, cn - 1), k = lane & 15;
     t.xv = make_uint2(0u, 0u);
-    if (with_x) t.xv = *reinterpret_cast<const uint2 *>(M.x + 64u * (j0 + jl) + 4u * k);
+    const uint32_t xoff = 128u * (j0 + jl) + 8u * k;
+    if (with_x) t.xv = *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(M.x) + xoff);
     t.codes = t.s01 = t.s23 = 0u;
     {
         // the tile's metadata is one contiguous run of rows*cn slots, row-major
-        const uint64_t base = static_cast<uint64_t>(r0) * M.groups + static_cast<uint64_t>(rows) * j0;
+        const uint32_t base = r0 * M.groups + rows * j0;
         const uint32_t lr = min(lane, rows - 1);
         if (kAligned || cn == kTileGroups) {
             // base is a multiple of 4: one width byte and one 8-byte scale load per row
             t.codes = M.widths[(base >> 2) + lr];
-            const uint2 sv = *reinterpret_cast<const uint2 *>(M.scales + base + 4u * lr);
+            const uint2 sv =
+                *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(M.scales) + 2u * (base + 4u * lr));
             t.s01 = sv.x;
             t.s23 = sv.y;
         } else {
@@ -319,7 +324,7 @@ __device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const
         const uint32_t slot = static_cast<uint32_t>((before >> (16 * c)) & 0xFFFFu) + ((excl >> (8 * c)) & 0xFFu);
         if (valid) {
             const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
-            L.list[slot] = lane | (jl << 8) | (sb << 16);
+            L.list[slot] = (jl * sizeof(L.part[0]) + 4u * lane) | (sb << 16);
         }
         const uint32_t cc = T.cols[jl];
         before += static_cast<uint64_t>(cc & 0xFFu) | (static_cast<uint64_t>((cc >> 8) & 0xFFu) << 16) |
@@ -349,9 +354,16 @@ __device__ __forceinline__ float sum_partials(const float *p, uint64_t stride, u
 }
 
 // ---- one group (or slice) per lane, per width; results to L.part[column][row]
+// A list entry holds the byte offset of the group's L.part slot (column *
+// 256 + row * 4, so the column is bits 8-9) and the group's fp16 scale in the
+// high half.
+
+__device__ __forceinline__ void store_part(WaveLds &L, uint32_t info, float v) {
+    *reinterpret_cast<float *>(reinterpret_cast<char *>(&L.part[0][0]) + (info & 0xFFFFu)) = v;
+}
 
 __device__ __forceinline__ void group1(WaveLds &L, uint32_t info, uint2 v) {
-    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = (info >> 8) & 0xFFu;
     // table k (one per 4 activations) starts at byte 64k; the entry for nibble u is at +4u.
     // Bytes of lo/hi hold 4 * (nibble 2t / 2t+1) of each word.
     const char *lut = reinterpret_cast<const char *>(L.lut + jl * 256u);
@@ -371,11 +383,11 @@ __device__ __forceinline__ void group1(WaveLds &L, uint32_t info, uint2 v) {
         }
     }
     const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    L.part[jl][r] = half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * sum);
+    store_part(L, info, half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * sum));
 }
 
 __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
-    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = (info >> 8) & 0xFFu;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride);
     const uint32_t magic = opaque(kMagic);
@@ -395,12 +407,12 @@ __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint
         a16 = dot2(p[7], xb.w, a16);
     }
     const float d = a1 + 0.25f * a4 + 0.0625f * a16 + 0.015625f * a64 + 0.00390625f * a256 - L.corr[jl][1];
-    L.part[jl][r] = half_to_float(info >> 16) * d;
+    store_part(L, info, half_to_float(info >> 16) * d);
 }
 
 // 4-bit: a 16-byte half group (h = task & 1); lane pairs add their halves
 __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uint2 va, uint2 vb) {
-    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = (info >> 8) & 0xFFu;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 16u * h);
     const uint32_t magic = opaque(kMagic);
@@ -417,12 +429,12 @@ __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uin
     }
     float part = a1 + 0.0625f * a16;
     part += dpp<kQuadXor1>(part);
-    if (h == 0) L.part[jl][r] = half_to_float(info >> 16) * (part - L.corr[jl][2]);
+    if (h == 0) store_part(L, info, half_to_float(info >> 16) * (part - L.corr[jl][2]));
 }
 
 // 8-bit: a 16-byte quarter group (qd = task & 3); lane quads add their quarters
 __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, uint2 va, uint2 vb) {
-    const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = (info >> 8) & 0xFFu;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 8u * qd);
     float a = 0.f;
@@ -439,7 +451,7 @@ __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, ui
     }
     a += dpp<kQuadXor1>(a);
     a += dpp<kQuadXor2>(a);
-    if (qd == 0) L.part[jl][r] = half_to_float(info >> 16) * (a - 1152.f * L.corr[jl][0]);
+    if (qd == 0) store_part(L, info, half_to_float(info >> 16) * (a - 1152.f * L.corr[jl][0]));
 }
 
 // Payload of the first 256 one-bit groups and of the first 64 slices of
@@ -587,7 +599,7 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
         const uint32_t b = 1u << wsel;
         for (uint32_t e = lane; e < cnt[wsel]; e += kWave) {
             const uint32_t info = L.list[first + e];
-            const uint32_t r = info & 0xFFu, jl = (info >> 8) & 0xFFu;
+            const uint32_t r = (info & 0xFFu) >> 2, jl = (info >> 8) & 0xFFu;
             const uint32_t *src = reinterpret_cast<const uint32_t *>(base + 8u * b * e);
             uint32_t *dst = reinterpret_cast<uint32_t *>(codes + (r0 + r) * k + 64u * (j0 + jl));
             for (uint32_t wd = 0; wd < 2 * b; ++wd) {
@@ -1094,6 +1106,10 @@ vbq_status check_matrix(const char *who, const vbq_matrix *w) {
     if (w->k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "%s: k=%u is not a multiple of 64", who, w->k);
     if (w->k > VBQ_MAX_K) return fail(VBQ_ERR_SHAPE, "%s: k=%u exceeds %u", who, w->k, VBQ_MAX_K);
     if (w->n == 0 || w->k == 0) return VBQ_OK;
+    // every group has at least 8 payload bytes; the kernels rely on it for 32-bit metadata offsets
+    if (static_cast<uint64_t>(w->n) * (w->k / VBQ_GROUP) * 8u > w->payload_bytes)
+        return fail(VBQ_ERR_OFFSETS, "%s: payload_bytes=%u is below 8 bytes per group (n=%u, k=%u)", who,
+                    w->payload_bytes, w->n, w->k);
     if (!w->tile_offsets || !w->widths || !w->scales || !w->payload)
         return fail(VBQ_ERR_NULL, "%s: widths, scales, tile_offsets or payload is NULL", who);
     if (!aligned16(w->tile_offsets) || !aligned16(w->widths) || !aligned16(w->scales) || !aligned16(w->payload))
