@@ -155,7 +155,9 @@ VBQ_API vbq_status vbq_validate_host(const vbq_matrix *host_view);
 /* y = W x for one fp16 vector (§6 fused decode at batch 1).
  * w: device view; x: device binary16 [k]; y: device fp32 [n] (overwritten).
  * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (k > VBQ_MAX_K), ALIGN,
- * HIP. n == 0 enqueues nothing; k == 0 writes y = 0. */
+ * OFFSETS (payload_bytes below 8 per group: no packed matrix has that; the
+ * device views are not otherwise re-validated), HIP. n == 0 enqueues
+ * nothing; k == 0 writes y = 0. */
 VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream);
 
 /* Several independent batch-1 GEMVs in one launch: ys[i] = W_i xs[i] for
@@ -163,7 +165,7 @@ VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, vo
  * (the matrix views and x / y pointers as for vbq_gemv). Matrices that read
  * the same activation (q/k/v, gate/up) or a whole layer's projections run as
  * one dispatch. Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (count),
- * ALIGN, HIP. Scratch: calls with large-k, small-n matrices use a
+ * ALIGN, OFFSETS, HIP. Scratch: calls with large-k, small-n matrices use a
  * library-owned device buffer per (device, stream), allocated on first need;
  * calls that overlap on the same stream handle are not allowed. */
 VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
@@ -174,14 +176,14 @@ VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *c
  * (overwritten). m >= 4 runs on the matrix cores (each group's codes decoded
  * once, 16x16x32 fp16 products, fp32 accumulation), m < 4 as one batch-1 GEMV
  * per row of X on the vector units. Scratch as for vbq_gemv_multi.
- * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, HIP. */
+ * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                                void *stream);
 
 /* Decoded integer codes int8 [n][k] of a device matrix, produced with the
  * same in-register field decoding the GEMV and GEMM kernels use (a test and
  * inspection hook; §3.1 Eq. (1) grid). Asynchronous. Errors: NULL, ABI,
- * SHAPE, ALIGN, HIP. */
+ * SHAPE, ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, void *stream);
 
 /* Static English name of a status. */

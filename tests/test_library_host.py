@@ -170,6 +170,11 @@ def test_device_entry_points_reject_bad_arguments_without_launching(V):
     assert V.lib.vbq_unpack_codes(ctypes.byref(aligned), base + 1, None) == V.ERR_ALIGN
     empty = V.VbqMatrix(1, 0, 128, 0, None, None, None, None)
     assert V.lib.vbq_gemv(ctypes.byref(empty), None, None, None) == V.OK    # n == 0: nothing to do
+    # every group has at least 8 payload bytes (2 x 2 groups here: 32 bytes at least)
+    short = V.VbqMatrix(1, 2, 128, 31, base, base, base, base)
+    assert V.lib.vbq_gemv(ctypes.byref(short), base, base, None) == V.ERR_OFFSETS
+    assert V.lib.vbq_gemm_smallbatch(ctypes.byref(short), base, 16, base, None) == V.ERR_OFFSETS
+    assert V.lib.vbq_unpack_codes(ctypes.byref(short), base, None) == V.ERR_OFFSETS
 
 
 def test_gemv_multi_rejects_bad_arguments_without_launching(V):
