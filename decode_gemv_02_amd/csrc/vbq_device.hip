@@ -681,7 +681,14 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
 
-constexpr uint32_t kGemmMinBatch = 4;   // from 4 rows the matrix cores beat one GEMV per row (measured)
+// When the matrix cores run a small batch (measured on MI355X): the matrix-core
+// kernel runs one wave per tile, so a matrix of few tiles leaves most SIMDs
+// idle, while m GEMVs in one launch fill the chip. It wins from 4 rows when
+// rows x tiles reach about 5120 (LM head 32000x4096 at m = 8: 29 vs 66 us;
+// 4096x4096 at m = 8: 12.6 vs 14.9 us; 2048x2048 at m = 16: 11.4 vs 9.7 us),
+// and always beyond the 16 rows one GEMV launch takes.
+constexpr uint32_t kGemmMinBatch = 4;
+constexpr uint64_t kGemmMinWork = 5120;   // rows of X times tiles of W
 constexpr uint32_t kAStride = 136;   // fp16 per staged row: two columns of 64 codes + 8 pad (272 B)
 
 struct GemmArgs {
@@ -1326,7 +1333,8 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
     if (w->n == 0) return VBQ_OK;
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (m >= kGemmMinBatch) {
+    const uint64_t tiles = static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
+    if (m > VBQ_MAX_MULTI || (m >= kGemmMinBatch && m * tiles >= kGemmMinWork)) {
         if (w->k == 0) {
             const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
             hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s, y, cnt);
@@ -1334,7 +1342,7 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
         }
         return gemm_launch(who, w, x, m, y, s);
     }
-    // fewer rows than one matrix-core block: each input row as its own GEMV of one batched launch
+    // each input row as its own GEMV of one batched launch
     const vbq_matrix *ws[VBQ_MAX_MULTI];
     const uint16_t *xs[VBQ_MAX_MULTI];
     float *ys[VBQ_MAX_MULTI];

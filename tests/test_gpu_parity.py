@@ -107,13 +107,25 @@ def test_gemm_matches_oracle(V, torch_mod, m):
     assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"gemm m={m}")
 
 
+@pytest.mark.parametrize("m", [4, 8, 16])
+def test_gemm_both_paths_below_17_rows(V, torch_mod, m):
+    # 1280x8192 has 640 tiles: m = 8 and 16 reach the matrix cores (m * tiles >= 5120),
+    # m = 4 runs as one GEMV per row; 97x1088 (10 tiles) stays on the GEMVs
+    for n, k in ((1280, 8192), (97, 1088)):
+        print_case(test="gemm_paths", n=n, k=k, m=m)
+        bits, codes, scales, p = make_case((m, n, k, 31), n, k, W.STD_MIX)
+        h, dm = upload(V, bits, codes, scales)
+        x = W.draw_x((m, n, k, 32), k, m)
+        assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"paths {n}x{k} m={m}")
+
+
 @pytest.mark.parametrize("b", [1, 2, 4, 8])
 def test_single_width_matrices(V, torch_mod, b):
     n, k = 77, 960
     print_case(test="single_width", b=b)
     bits, codes, scales, p = make_case((b, 6), n, k, {b: 1.0})
     h, dm = upload(V, bits, codes, scales)
-    for m in (1, 5, 16):
+    for m in (1, 5, 16, 17):
         x = W.draw_x((b, m, 7), k, m)
         assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"b={b} m={m}")
 
