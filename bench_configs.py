@@ -12,6 +12,9 @@ stream around passes replayed from a HIP graph (one graph holds one pass per
 copy, at most --graph-launches launches), so the figure is the GPU's and not
 the Python launch rate; eager_us_per_pass times the same passes launched one
 by one from Python (for workloads of small matrices that rate is the bound).
+Beside each line, the same pass on dense fp16 weights of the same shapes
+(torch F.linear, i.e. rocBLAS/hipBLASLt; random values, timed the same way)
+gives fp16_us_per_pass and speedup_vs_fp16.
 
   python bench_configs.py [--configs 1,2,3,4,5] [--passes 50] [--warmup 10]
 """
@@ -35,6 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate-mb", type=float, default=640.0)
     ap.add_argument("--graph-launches", type=int, default=4096)
+    ap.add_argument("--no-fp16", action="store_true")
     return ap.parse_args()
 
 
@@ -51,6 +55,25 @@ def launch_groups(specs):
     if cur:
         groups.append(cur)
     return groups
+
+
+def graph_time(torch, stream, one_pass, passes_per_graph, passes):
+    """Microseconds per pass: passes_per_graph passes captured once, replayed on `stream`."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for i in range(passes_per_graph):
+            one_pass(i)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(passes / passes_per_graph))
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return t0.elapsed_time(t1) * 1e3 / (reps * passes_per_graph)
 
 
 def main():
@@ -103,20 +126,7 @@ def main():
                 # one graph: one pass per copy (the scratch buffers exist already, so nothing allocates)
                 launches = len(groups) if m == 1 else len(specs)
                 per_graph = max(1, min(copies, args.graph_launches // launches))
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g, stream=stream):
-                    for i in range(per_graph):
-                        one_pass(i)
-                g.replay()
-                torch.cuda.synchronize()
-                reps = max(1, math.ceil(args.passes / per_graph))
-                t0.record(stream)
-                for _ in range(reps):
-                    g.replay()
-                t1.record(stream)
-                torch.cuda.synchronize()
-                us = t0.elapsed_time(t1) * 1e3 / (reps * per_graph)
-                del g
+                us = graph_time(torch, stream, one_pass, per_graph, args.passes)
             gbps = packed / (us * 1e-6) / 1e9
             line = {"workload": cfg.name, "batch": m, "matrices": len(specs), "packed_bytes": packed,
                     "weights": cfg.weights, "us_per_pass": round(us, 3), "GBps": round(gbps, 2),
@@ -126,6 +136,28 @@ def main():
                     "entry": "vbq_gemv_multi" if m == 1 else "vbq_gemm_smallbatch"}
             if m > 1:
                 line["TFLOPs"] = round(2.0 * m * cfg.weights / (us * 1e-6) / 1e12, 2)
+            if not args.no_fp16:
+                dense_bytes = 2 * cfg.weights
+                dcopies = max(1, math.ceil(args.rotate_mb * 1e6 / dense_bytes))
+                dense = [[(torch.randn(s.n, s.k, device=dev) * 0.02).half() for s in specs] for _ in range(dcopies)]
+                xd = [xi.view(m, -1) for xi in xin]
+                yd = [torch.empty((m, s.n), dtype=torch.float16, device=dev) for s in specs]
+
+                def dense_pass(i):
+                    d = dense[i % dcopies]
+                    for j in range(len(specs)):
+                        torch.nn.functional.linear(xd[j], d[j], out=yd[j])
+
+                with torch.cuda.stream(stream):
+                    for i in range(args.warmup):
+                        dense_pass(i)
+                    torch.cuda.synchronize()
+                    fp16_us = graph_time(torch, stream, dense_pass, max(1, min(dcopies, args.graph_launches // len(specs))),
+                                         args.passes)
+                line["fp16_us_per_pass"] = round(fp16_us, 3)
+                line["fp16_dense_GBps"] = round(dense_bytes / (fp16_us * 1e-6) / 1e9, 2)
+                line["speedup_vs_fp16"] = round(fp16_us / us, 3)
+                del dense
             print(json.dumps(line), flush=True)
         del layers
 
