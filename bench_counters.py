@@ -8,6 +8,10 @@ Kernel durations (`trace`):
   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o kt -- python bench.py --steps 50 --warmup 10 --only-timed
   python bench_counters.py trace --csv <dir>/kt_kernel_trace.csv --out profiles/gemv_tiles_layer9b_kernel_trace.txt
 
+Kernel durations by kernel name (`kernels`), for any run, e.g. the LM head:
+  rocprofv3 --kernel-trace --stats -f csv -d <dir> -o kt5 -- python bench_configs.py --configs 5 --no-fp16
+  python bench_counters.py kernels --csv <dir>/kt5_kernel_trace.csv --title "..." --command "..." --out <file>
+
 HBM traffic (`traffic`), one rocprofv3 run per counter:
   rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch -- python bench.py --steps 5 --warmup 2 --only-timed
   rocprofv3 --pmc WRITE_SIZE -d <dir> -o write -- python bench.py --steps 5 --warmup 2 --only-timed
@@ -119,6 +123,28 @@ def trace_summary(a) -> str:
     return "\n".join(lines) + "\n"
 
 
+def kernels_summary(a) -> str:
+    """Dispatch count and duration statistics per kernel name (VBQ kernels only)."""
+    per, meta = {}, {}
+    with open(a.csv) as f:
+        for row in csv.DictReader(f):
+            name = row["Kernel_Name"]
+            if "gemv_tiles" not in name and "gemm_tiles" not in name and "unpack_tiles" not in name:
+                continue
+            per.setdefault(name, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0)
+            meta.setdefault(name, row)
+    lines = [f"# Kernel durations by kernel, {a.title}", "# command (repository root):", f"#   {a.command}",
+             f"#   python bench_counters.py kernels --csv <dir>/<name>_kernel_trace.csv --out <this file>",
+             f"kernel_source_sha256: {kernel_source_sha()}"]
+    for name, d in per.items():
+        r = meta[name]
+        lines.append(f"kernel: {name} vgpr={r['VGPR_Count']} sgpr={r['SGPR_Count']} lds={r['LDS_Block_Size']} "
+                     f"scratch={r['Scratch_Size']} grid={r['Grid_Size_X']}x{r['Grid_Size_Y']}")
+        lines.append(f"  dispatches={len(d)} avg_us={statistics.fmean(d):.3f} median_us={statistics.median(d):.3f} "
+                     f"min_us={min(d):.3f} max_us={max(d):.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path: str) -> dict | None:
     """{launch: traffic bytes} from a traffic summary, or None if absent or taken on another kernel source."""
     if not os.path.exists(path):
@@ -150,8 +176,13 @@ def main():
     k = sub.add_parser("trace")
     k.add_argument("--csv", required=True)
     k.add_argument("--out", required=True)
+    n = sub.add_parser("kernels")
+    n.add_argument("--csv", required=True)
+    n.add_argument("--title", required=True)
+    n.add_argument("--command", required=True)
+    n.add_argument("--out", required=True)
     a = ap.parse_args()
-    text = traffic_summary(a) if a.cmd == "traffic" else trace_summary(a)
+    text = {"traffic": traffic_summary, "trace": trace_summary, "kernels": kernels_summary}[a.cmd](a)
     with open(a.out, "w") as f:
         f.write(text)
     print(text, end="")
