@@ -7,11 +7,14 @@
 // tile stream described in vbq.h.
 //
 // Work decomposition. A wave owns one tile (64 rows x 4 groups) at a time:
-//   1. it stages the tile's 256 activations in LDS, once as fp16 pairs and
-//      once as a 4-bit lookup table (16 partial sums per 4 activations);
-//   2. lane r reads the four width codes and scales of row r and the wave
-//      compacts the tile into one list per width (ballot + mbcnt ranks give
-//      each group its place in the column-major bucket order of the stream);
+//   1. lane r reads the four width codes and scales of row r; per column a
+//      DPP prefix sum of one-hot width counters gives each row its rank
+//      among the rows of its width and the per-width counts, which fix where
+//      each width's bucket starts, so the payload loads are issued now;
+//   2. while they travel, it stages the tile's 256 activations in LDS, once
+//      as fp16 pairs and once as a 4-bit lookup table (16 partial sums per 4
+//      activations), and writes one list of the tile's groups in the
+//      stream's order (buckets by width, column-major inside a bucket);
 //   3. for each width the wave walks its bucket with one group (or a 16-byte
 //      slice of a group) per lane, so every instruction runs a single width's
 //      unpack; the bucket is contiguous, so loads are coalesced;
@@ -666,7 +669,7 @@ __global__ void fill_zero(float *__restrict__ y, uint64_t count) {
 }
 
 // ---------------------------------------------------------------- small batch on the matrix cores
-// Y[m][r] = sum_j s[r,j] * sum_i q[r,j,i] * X[m][64j+i] for 16 <= m <= 64 rows of X
+// Y[m][r] = sum_j s[r,j] * sum_i q[r,j,i] * X[m][64j+i] for up to 64 rows of X
 // (VBQ paper §6 fused decode, batched; grid and scale §3.1 Eq. (1)).
 // A wave owns one tile at a time, two columns per pass: it decodes every
 // group of the two columns into exact fp16 codes in LDS (natural row order,
@@ -1245,7 +1248,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     return launched(who);
 }
 
-// Small-batch GEMM on the matrix cores: one launch for 16 <= m <= 64.
+// Small-batch GEMM on the matrix cores: one launch for up to 64 rows of X.
 vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                        hipStream_t stream) {
     GemmArgs G{};
