@@ -33,3 +33,37 @@ def test_traffic_summary_is_read_only_for_the_current_kernel(tmp_path):
 def test_launches_are_split_by_dispatch_order():
     per = bench_counters._by_launch(list(range(8)), "test")
     assert per == {"q+k+v": [0, 4], "o": [1, 5], "gate+up": [2, 6], "down": [3, 7]}
+
+
+def test_workload_passes_follow_decode_order():
+    import bench_configs
+    import workloads as W
+    # 9B layer: q+k+v | o | gate+up | down
+    assert bench_configs.launch_groups(W.config(4).matrices) == [[0, 1, 2], [3], [4, 5], [6]]
+    # 131M set: no gate, so up and down launch alone; 12 layers x 4 launches
+    g = bench_configs.launch_groups(W.config(2).matrices)
+    assert len(g) == 48 and g[:4] == [[0, 1, 2], [3], [4], [5]]
+    # every matrix exactly once, in order
+    for cid in W.ALL_CONFIGS:
+        flat = [i for grp in bench_configs.launch_groups(W.config(cid).matrices) for i in grp]
+        assert flat == list(range(len(W.config(cid).matrices)))
+
+
+def test_kernel_summary_groups_dispatches_by_kernel(tmp_path):
+    cols = ["Kind", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size", "Scratch_Size",
+            "VGPR_Count", "SGPR_Count", "Grid_Size_X", "Grid_Size_Y"]
+    rows = [["KERNEL_DISPATCH", "gemv_tiles<true>(Batch)", "1000", "3000", "28160", "0", "48", "112", "256", "1"],
+            ["KERNEL_DISPATCH", "gemv_tiles<true>(Batch)", "5000", "9000", "28160", "0", "48", "112", "256", "1"],
+            ["KERNEL_DISPATCH", "copyBuffer", "0", "100", "0", "0", "8", "32", "1", "1"],
+            ["KERNEL_DISPATCH", "gemm_tiles<1u>(GemmArgs)", "0", "10000", "78336", "0", "88", "112", "128", "1"]]
+    p = tmp_path / "kt.csv"
+    p.write_text("\n".join(",".join(f'"{v}"' for v in r) for r in [cols] + rows) + "\n")
+
+    class A:
+        csv = str(p)
+        title = "t"
+        command = "c"
+    text = bench_counters.kernels_summary(A)
+    assert "copyBuffer" not in text
+    assert "dispatches=2 avg_us=3.000 median_us=3.000 min_us=2.000 max_us=4.000" in text
+    assert "dispatches=1 avg_us=10.000" in text
