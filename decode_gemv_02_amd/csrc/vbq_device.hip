@@ -151,12 +151,15 @@ struct Batch {
     MatArgs m[VBQ_MAX_MULTI];
 };
 
+// 5760 bytes per wave, so seven four-wave workgroups fit one CU's 160 KiB.
 struct alignas(16) WaveLds {
-    float lut[kTileGroups * 16 * 16];        // [column][nibble position][4-bit index]
+    union {
+        float lut[kTileGroups * 16 * 16];     // [column][nibble position][4-bit index]
+        float part[kTileGroups][kTileRows];   // scaled group dot products, once the 1-bit groups are done
+    };
     uint32_t xs[kTileGroups * kXStride];     // fp16 activation pairs per column
     float corr[kTileGroups][4];              // per column: sum x, 2-bit and 4-bit bias terms
     uint32_t list[kTileRows * kTileGroups];  // the tile's groups in stream order: 1-bit bucket first
-    float part[kTileGroups][kTileRows];      // scaled group dot products
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -365,7 +368,9 @@ __device__ __forceinline__ void store_part(WaveLds &L, uint32_t info, float v) {
     *reinterpret_cast<float *>(reinterpret_cast<char *>(&L.part[0][0]) + (info & 0xFFFFu)) = v;
 }
 
-__device__ __forceinline__ void group1(WaveLds &L, uint32_t info, uint2 v) {
+// returns the scaled product: L.part shares its bytes with the lookup table,
+// so it is stored once every 1-bit group of the tile is done
+__device__ __forceinline__ float group1(WaveLds &L, uint32_t info, uint2 v) {
     const uint32_t jl = (info >> 8) & 0xFFu;
     // table k (one per 4 activations) starts at byte 64k; the entry for nibble u is at +4u.
     // Bytes of lo/hi hold 4 * (nibble 2t / 2t+1) of each word.
@@ -386,7 +391,7 @@ __device__ __forceinline__ void group1(WaveLds &L, uint32_t info, uint2 v) {
         }
     }
     const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    store_part(L, info, half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * sum));
+    return half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * sum);
 }
 
 __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
@@ -492,9 +497,21 @@ __device__ __forceinline__ void stage_payload(const uint8_t *tile, const uint32_
 // than 64 two-bit groups or 64 slices of a wider width in one tile).
 __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const uint8_t *tile, const uint32_t cnt[4],
                                               uint32_t lane) {
+    // A lane without a group in a round parks its (unused) result in a spare
+    // slot past L.part, so the deferred stores need no branches.
+    uint32_t info1[4];
+    float v1[4];
 #pragma unroll
-    for (uint32_t i = 0; i < 4; ++i)
-        if (lane + kWave * i < cnt[0]) group1(L, L.list[lane + kWave * i], S.p1[i]);
+    for (uint32_t i = 0; i < 4; ++i) {
+        const bool on = lane + kWave * i < cnt[0];
+        const uint32_t e = L.list[lane + kWave * i];
+        info1[i] = on ? e : static_cast<uint32_t>(sizeof(L.part)) + 4u * lane;
+        v1[i] = 0.f;
+        if (on) v1[i] = group1(L, e, S.p1[i]);
+    }
+    // the lookup table is dead from here: its bytes take the products
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) store_part(L, info1[i], v1[i]);
     const uint8_t *b2 = tile + 8u * cnt[0];
     const uint8_t *b4 = b2 + 16u * cnt[1];
     const uint8_t *b8 = b4 + 32u * cnt[2];
@@ -511,9 +528,8 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
 }
 
 template <bool kAligned>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void gemv_tiles(Batch B) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) void gemv_tiles(Batch B) {
     __shared__ WaveLds lds[kWavesPerBlock];
-    __shared__ float rowsum[kWavesPerBlock][kTileRows];
     // which matrix, row tile and split this block serves (uniform)
     const MatArgs M = B.m[blockIdx.y];   // by value: loaded into scalar registers once
     // The grid is as wide as the largest matrix of the launch. A block past
@@ -556,10 +572,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
         cur = nxt;
     }
     const uint32_t lane = lane_id();
-    rowsum[wave][lane] = acc;
+    L.part[0][lane] = acc;   // the wave's row sums, in its own (now idle) LDS
     __syncthreads();
     if (wave != 0 || spare) return;
-    const float sum = ((rowsum[0][lane] + rowsum[1][lane]) + rowsum[2][lane]) + rowsum[3][lane];
+    const float sum = ((lds[0].part[0][lane] + lds[1].part[0][lane]) + lds[2].part[0][lane]) + lds[3].part[0][lane];
     if (M.splits == 1) {
         if (lane < rows) M.y[r0 + lane] = sum;
         return;
@@ -1191,7 +1207,8 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         const vbq_matrix *w = ws[i];
         if (w->n && w->k) total_row_tiles += ceil_div(w->n, kTileRows);
     }
-    const uint32_t want_blocks = 768;
+    // enough workgroups for every CU's seven resident ones (LDS bound: 22.5 KiB each)
+    const uint32_t want_blocks = 7 * 256;
     const uint32_t factor = total_row_tiles ? ceil_div(want_blocks, total_row_tiles) : 1;
     size_t counter_slots = 0, partial_total = 0;
     uint32_t used = 0;
