@@ -2,7 +2,9 @@
 
 Writes the short text summaries kept under profiles/ and reads the traffic
 summary back for bench.py. Launches are told apart by dispatch order: every
-step of bench.py issues the same launches in the same order (LAUNCHES).
+step of bench.py issues the same launches in the same order (LAUNCHES), and
+after the steps bench.py runs its dominant launch alone, back to back, once
+per step (the roofline leg).
 
 Kernel durations (`trace`):
   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o kt -- python bench.py --steps 50 --warmup 10 --only-timed
@@ -47,10 +49,12 @@ def kernel_source_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def _by_launch(vals: list, what: str) -> dict:
-    if not vals or len(vals) % len(LAUNCHES):
-        raise SystemExit(f"{what}: {len(vals)} GEMV dispatches is not a whole number of steps")
-    return {nm: vals[i::len(LAUNCHES)] for i, nm in enumerate(LAUNCHES)}
+def _by_launch(vals: list, warmup: int, steps: int, what: str) -> tuple[dict, list]:
+    """Step dispatches per launch name, and the dominant launch's back-to-back dispatches that follow them."""
+    n_step = len(LAUNCHES) * (warmup + steps)
+    if len(vals) != n_step + steps:
+        raise SystemExit(f"{what}: {len(vals)} GEMV dispatches, expected {n_step} in the steps and {steps} after")
+    return {nm: vals[i:n_step:len(LAUNCHES)] for i, nm in enumerate(LAUNCHES)}, vals[n_step:]
 
 
 def _counter_rows(db: str, counter: str):
@@ -73,8 +77,10 @@ def _copy_reading(db: str, counter: str) -> float:
 def traffic_summary(a) -> str:
     cf, cw = _copy_reading(a.copy_fetch, "FETCH_SIZE"), _copy_reading(a.copy_write, "WRITE_SIZE")
     fscale, wscale = a.copy_bytes / (cf * 1024.0), a.copy_bytes / (cw * 1024.0)
-    fetch = _by_launch([v for _, nm, v in _counter_rows(a.fetch, "FETCH_SIZE") if GEMV_KERNEL in nm], a.fetch)
-    write = _by_launch([v for _, nm, v in _counter_rows(a.write, "WRITE_SIZE") if GEMV_KERNEL in nm], a.write)
+    fetch, _ = _by_launch([v for _, nm, v in _counter_rows(a.fetch, "FETCH_SIZE") if GEMV_KERNEL in nm],
+                          a.warmup, a.steps, a.fetch)
+    write, _ = _by_launch([v for _, nm, v in _counter_rows(a.write, "WRITE_SIZE") if GEMV_KERNEL in nm],
+                          a.warmup, a.steps, a.write)
     lines = [
         "# HBM traffic per launch of gemv_tiles, layer_9b decode step (q+k+v | o | gate+up | down), batch 1",
         "# commands (repository root, one rocprofv3 run each):",
@@ -101,8 +107,11 @@ def trace_summary(a) -> str:
         rows = [r for r in csv.DictReader(f) if GEMV_KERNEL in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Dispatch_Id"]))
     dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]    # us
-    per = _by_launch(dur, a.csv)
-    first = rows[0]
+    per, b2b = _by_launch(dur, a.warmup, a.steps, a.csv)
+    first = {nm: rows[i] for i, nm in enumerate(LAUNCHES)}   # each launch's first dispatch: its kernel and shape
+    last = rows[-1]
+    dom = [nm for nm in LAUNCHES if (first[nm]["Kernel_Name"], first[nm]["Grid_Size_X"], first[nm]["Grid_Size_Y"])
+           == (last["Kernel_Name"], last["Grid_Size_X"], last["Grid_Size_Y"])]
     lines = [
         "# Kernel durations per launch of gemv_tiles, layer_9b decode step (q+k+v | o | gate+up | down), batch 1",
         "# command (repository root):",
@@ -110,16 +119,20 @@ def trace_summary(a) -> str:
         "--only-timed",
         "#   python bench_counters.py trace --csv <dir>/kt_kernel_trace.csv --out <this file>",
         f"kernel_source_sha256: {kernel_source_sha()}",
-        f"kernel: {first['Kernel_Name']} vgpr={first['VGPR_Count']} sgpr={first['SGPR_Count']} "
-        f"lds={first['LDS_Block_Size']} scratch={first['Scratch_Size']} workgroup={first['Workgroup_Size_X']}",
         f"all launches: dispatches={len(dur)} avg_us={statistics.fmean(dur):.3f}",
     ]
     for nm in LAUNCHES:
-        v = per[nm]
+        v, r = per[nm], first[nm]
         lines.append(f"launch {nm}: dispatches={len(v)} avg_us={statistics.fmean(v):.3f} "
                      f"median_us={statistics.median(v):.3f} min_us={min(v):.3f} max_us={max(v):.3f}")
+        lines.append(f"  kernel: {r['Kernel_Name']} workgroup={r['Workgroup_Size_X']} "
+                     f"grid={r['Grid_Size_X']}x{r['Grid_Size_Y']} vgpr={r['VGPR_Count']} sgpr={r['SGPR_Count']} "
+                     f"lds={r['LDS_Block_Size']} scratch={r['Scratch_Size']}")
     tot = sum(statistics.fmean(per[nm]) for nm in LAUNCHES)
     lines.append(f"step: sum_of_launch_avg_us={tot:.3f}")
+    lines.append(f"roofline leg ({'+'.join(dom) or '?'} alone, back to back): dispatches={len(b2b)} "
+                 f"avg_us={statistics.fmean(b2b):.3f} median_us={statistics.median(b2b):.3f} "
+                 f"min_us={min(b2b):.3f} max_us={max(b2b):.3f}")
     return "\n".join(lines) + "\n"
 
 
@@ -172,9 +185,13 @@ def main():
     t.add_argument("--copy-fetch", required=True)
     t.add_argument("--copy-write", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--steps", type=int, default=5)
+    t.add_argument("--warmup", type=int, default=2)
     t.add_argument("--out", required=True)
     k = sub.add_parser("trace")
     k.add_argument("--csv", required=True)
+    k.add_argument("--steps", type=int, default=50)
+    k.add_argument("--warmup", type=int, default=10)
     k.add_argument("--out", required=True)
     n = sub.add_parser("kernels")
     n.add_argument("--csv", required=True)

@@ -20,13 +20,15 @@
 //      unpack; the bucket is contiguous, so loads are coalesced;
 //   4. each group's fp32 dot product is scaled once and parked in LDS; rows
 //      are summed in a fixed order, so results are bitwise repeatable.
-// A workgroup of four waves shares one row tile and splits its column tiles;
-// when a row tile is further split across workgroups (small n, large k), the
-// partial sums go to a scratch buffer and the last workgroup to arrive adds
-// them in a fixed order.
+// A workgroup of 4, 8 or 16 waves shares one row tile and splits its column
+// tiles; when a row tile is further split across workgroups (small n, large
+// k), the partial sums go to a scratch buffer and the last workgroup to
+// arrive adds them in a fixed order. The host picks the workgroup size and
+// the split count per launch from a cost model (gemv_plan).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <mutex>
 #include <unordered_map>
@@ -527,9 +529,12 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
         task8(L, l8[e >> 2], e & 3u, load8(b8 + 16u * e), load8(b8 + 16u * e + 8u));
 }
 
-template <bool kAligned>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) void gemv_tiles(Batch B) {
-    __shared__ WaveLds lds[kWavesPerBlock];
+// kWaves waves per workgroup (4, 8 or 16) share one row tile; the LDS
+// (5760 B per wave) allows 7, 3 or 1 such workgroups per CU.
+template <bool kAligned, uint32_t kWaves>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(kWaves == 4 ? 7 : kWaves == 8 ? 6 : 4, 8)))
+void gemv_tiles(Batch B) {
+    __shared__ WaveLds lds[kWaves];
     // which matrix, row tile and split this block serves (uniform)
     const MatArgs M = B.m[blockIdx.y];   // by value: loaded into scalar registers once
     // The grid is as wide as the largest matrix of the launch. A block past
@@ -549,7 +554,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) voi
     // own): a conditional load would make its result a branch merge, and the
     // merge copy would wait for the load
     TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, lane_id(), true);
-    for (; ct < c_hi; ct += kWavesPerBlock) {
+    for (; ct < c_hi; ct += kWaves) {
         const uint32_t cn = min(kTileGroups, M.groups - ct * kTileGroups);
         // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
@@ -558,8 +563,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) voi
         Staged S;
         stage_payload(tp, cnt, lane_id(), S);
         // the next tile's metadata travels while this tile computes
-        const TileMeta nxt = load_meta<kAligned>(M, a, ct + kWavesPerBlock < c_hi ? ct + kWavesPerBlock : ct,
-                                                 lane_id(), true);
+        const TileMeta nxt = load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, lane_id(), true);
         stage_x(L, cur.xv, lane_id());
         build_lists(L, cur, P, cnt, rows, cn, lane_id());
         wave_lds_sync();
@@ -575,7 +579,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(7, 8))) voi
     L.part[0][lane] = acc;   // the wave's row sums, in its own (now idle) LDS
     __syncthreads();
     if (wave != 0 || spare) return;
-    const float sum = ((lds[0].part[0][lane] + lds[1].part[0][lane]) + lds[2].part[0][lane]) + lds[3].part[0][lane];
+    float sum = lds[0].part[0][lane];
+#pragma unroll
+    for (uint32_t w = 1; w < kWaves; ++w) sum += lds[w].part[0][lane];   // in wave order
     if (M.splits == 1) {
         if (lane < rows) M.y[r0 + lane] = sum;
         return;
@@ -1197,19 +1203,66 @@ inline size_t partial_bytes(uint32_t splits, uint32_t n) {
     return (static_cast<size_t>(splits) * n * 4 + 255) / 256 * 256;
 }
 
+// Launch shape of one batched GEMV launch: waves per workgroup and splits
+// per row tile. The cost model was fitted to graph-replayed launch times on
+// MI355X over the shapes of every decode workload (4096- to 14336-wide
+// layers, the 1.0B and 131M sets, the 32000-row head; 12 shapes, every
+// waves/splits choice): time ~ 1.1 per tile slot of a SIMD (tiles per wave x
+// waves per SIMD, averaged over the CUs a launch occupies) + 2.5 per tile a
+// wave handles after its first and per extra round of workgroups + the split
+// tail (1.4 + 0.23 per split: partial stores, the arrival count and the last
+// arriver's sum, three dependent round trips to memory). For each of the 12
+// it picks the fastest measured shape or one within 1% of it.
+struct GemvPlan {
+    uint32_t waves, splits;
+};
+
+GemvPlan gemv_plan(uint32_t row_tiles, uint32_t col_tiles) {
+    constexpr uint32_t kCUs = 256;
+    const uint32_t waves[3] = {4, 8, 16}, per_cu[3] = {7, 3, 1};   // resident workgroups per CU (LDS bound)
+    GemvPlan best{4, 1};
+    double best_cost = 1e300;
+    for (uint32_t w = 0; w < 3; ++w) {
+        const uint32_t gw = waves[w];
+        for (uint32_t s = 1; s <= ceil_div(col_tiles, gw); ++s) {
+            const double wgs = static_cast<double>(row_tiles) * s;
+            const uint32_t ct_per = ceil_div(col_tiles, s);              // column tiles of a workgroup (at most)
+            const uint32_t active = std::min(gw, ct_per);                // waves with a tile
+            const uint32_t tpw = ceil_div(ct_per, gw);                   // tiles per wave (at most)
+            const double cu_load = std::max(1.0, wgs / kCUs);            // workgroups per occupied CU
+            const double rounds = std::ceil(cu_load / per_cu[w]);
+            const double slots = tpw * (active / 4.0) * cu_load;
+            const double cost = 1.1 * slots + 2.5 * ((tpw - 1) + (rounds - 1)) + (s > 1 ? 1.4 + 0.23 * s : 0.0);
+            if (cost < best_cost) {
+                best_cost = cost;
+                best = GemvPlan{gw, s};
+            }
+        }
+    }
+    return best;
+}
+
+template <uint32_t kWaves>
+void gemv_dispatch(bool aligned, uint32_t blocks, uint32_t used, const Batch &B, hipStream_t stream) {
+    if (aligned)
+        hipLaunchKernelGGL((gemv_tiles<true, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0, stream, B);
+    else
+        hipLaunchKernelGGL((gemv_tiles<false, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0, stream, B);
+}
+
 // One launch for up to VBQ_MAX_MULTI independent GEMVs.
 vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                        uint32_t count, hipStream_t stream) {
     Batch B{};
-    uint32_t blocks = 0, total_row_tiles = 0;
+    uint32_t blocks = 0, total_row_tiles = 0, max_col_tiles = 0;
     bool aligned = true;
     for (uint32_t i = 0; i < count; ++i) {
         const vbq_matrix *w = ws[i];
-        if (w->n && w->k) total_row_tiles += ceil_div(w->n, kTileRows);
+        if (w->n == 0 || w->k == 0) continue;
+        total_row_tiles += ceil_div(w->n, kTileRows);
+        max_col_tiles = std::max(max_col_tiles, ceil_div(w->k / VBQ_GROUP, kTileGroups));
     }
-    // enough workgroups for every CU's seven resident ones (LDS bound: 22.5 KiB each)
-    const uint32_t want_blocks = 7 * 256;
-    const uint32_t factor = total_row_tiles ? ceil_div(want_blocks, total_row_tiles) : 1;
+    const GemvPlan plan = total_row_tiles ? gemv_plan(total_row_tiles, max_col_tiles) : GemvPlan{4, 1};
     size_t counter_slots = 0, partial_total = 0;
     uint32_t used = 0;
     bool any_launch = false;
@@ -1234,7 +1287,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.groups = w->k / VBQ_GROUP;
         M.col_tiles = ceil_div(M.groups, kTileGroups);
         const uint32_t row_tiles = ceil_div(M.n, kTileRows);
-        M.splits = std::max(1u, std::min(ceil_div(M.col_tiles, kWavesPerBlock), factor));
+        M.splits = std::max(1u, std::min(ceil_div(M.col_tiles, plan.waves), plan.splits));
         M.blocks = row_tiles * M.splits;
         blocks = std::max(blocks, M.blocks);
         if (M.groups % 4) aligned = false;
@@ -1258,10 +1311,12 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
             part += partial_bytes(M.splits, M.n);
         }
     }
-    if (aligned)
-        hipLaunchKernelGGL(gemv_tiles<true>, dim3(blocks, used), dim3(256), 0, stream, B);
+    if (plan.waves == 16)
+        gemv_dispatch<16>(aligned, blocks, used, B, stream);
+    else if (plan.waves == 8)
+        gemv_dispatch<8>(aligned, blocks, used, B, stream);
     else
-        hipLaunchKernelGGL(gemv_tiles<false>, dim3(blocks, used), dim3(256), 0, stream, B);
+        gemv_dispatch<4>(aligned, blocks, used, B, stream);
     return launched(who);
 }
 

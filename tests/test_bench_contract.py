@@ -31,8 +31,16 @@ def test_traffic_summary_is_read_only_for_the_current_kernel(tmp_path):
 
 
 def test_launches_are_split_by_dispatch_order():
-    per = bench_counters._by_launch(list(range(8)), "test")
+    # one warmup step and one timed step (8 dispatches), then the roofline leg (one dispatch per timed step)
+    per, tail = bench_counters._by_launch(list(range(9)), 1, 1, "test")
     assert per == {"q+k+v": [0, 4], "o": [1, 5], "gate+up": [2, 6], "down": [3, 7]}
+    assert tail == [8]
+    try:
+        bench_counters._by_launch(list(range(8)), 1, 1, "test")
+    except SystemExit:
+        pass
+    else:
+        raise AssertionError("a trace without the roofline leg must be rejected")
 
 
 def test_workload_passes_follow_decode_order():

@@ -97,6 +97,20 @@ def test_gemv_matches_oracle(V, torch_mod, n, k):
     assert_within_tolerance(y, oracle.gemm(p, x), x, scales, f"gemv {n}x{k}")
 
 
+# Shapes that take each GEMV launch shape the host picks: 16-wave workgroups
+# with no split (12288 x 4096 / 4032), 8-wave with no split (6144 x 1984),
+# 16-wave split four ways (4000 x 14272), 8-wave split four ways (3000 x 6400);
+# k = 4032, 1984 and 14272 leave the last column tile with three groups.
+@pytest.mark.parametrize("n,k", [(12288, 4096), (12288, 4032), (6144, 1984), (4000, 14272), (3000, 6400)])
+def test_gemv_launch_shapes(V, torch_mod, n, k):
+    print_case(test="gemv_shapes", n=n, k=k)
+    bits, codes, scales, p = make_case((n, k, 5), n, k, W.STD_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x((n, k, 6), k)
+    y = gpu_gemm(V, torch_mod, dm, x)
+    assert_within_tolerance(y, oracle.gemm(p, x), x, scales, f"gemv {n}x{k}")
+
+
 @pytest.mark.parametrize("m", [2, 3, 4, 5, 8, 15, 16, 17, 31, 48, 63, 64])
 def test_gemm_matches_oracle(V, torch_mod, m):
     n, k = 97, 1088
