@@ -153,15 +153,18 @@ struct Batch {
     MatArgs m[VBQ_MAX_MULTI];
 };
 
-// 5760 bytes per wave, so seven four-wave workgroups fit one CU's 160 KiB.
+// 4992 bytes per wave: eight 4-wave, four 8-wave or two 16-wave workgroups
+// fit one CU's 160 KiB.
 struct alignas(16) WaveLds {
     union {
         float lut[kTileGroups * 16 * 16];     // [column][nibble position][4-bit index]
-        float part[kTileGroups][kTileRows];   // scaled group dot products, once the 1-bit groups are done
+        float part[kTileGroups * kTileRows];  // group dot products (unscaled) at column * 64 + row, once
+                                              // the 1-bit groups are done
     };
     uint32_t xs[kTileGroups * kXStride];     // fp16 activation pairs per column
     float corr[kTileGroups][4];              // per column: sum x, 2-bit and 4-bit bias terms
-    uint32_t list[kTileRows * kTileGroups];  // the tile's groups in stream order: 1-bit bucket first
+    uint8_t list[kTileRows * kTileGroups];   // the tile's groups in stream order, 1-bit bucket first:
+                                             // column * 64 + row
 };
 
 __device__ __forceinline__ void wave_lds_sync() {
@@ -192,7 +195,8 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
                                               bool with_x) {
     TileMeta t;
     const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
-    const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, M.groups - j0);
+    // kAligned: the group count is a multiple of 4, so every tile has four columns
+    const uint32_t j0 = ct * kTileGroups, cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - j0);
     // The tile offset is uniform: a scalar load (constant address space), so
     // moving it into a scalar register waits on the scalar counter only and
     // not on the payload loads issued before it.
@@ -330,10 +334,7 @@ __device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const
         const uint32_t c = (t.codes >> (2 * jl)) & 3u;
         const uint32_t excl = T.incl[jl] - (1u << (8 * c));
         const uint32_t slot = static_cast<uint32_t>((before >> (16 * c)) & 0xFFFFu) + ((excl >> (8 * c)) & 0xFFu);
-        if (valid) {
-            const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
-            L.list[slot] = (jl * sizeof(L.part[0]) + 4u * lane) | (sb << 16);
-        }
+        if (valid) L.list[slot] = static_cast<uint8_t>(jl * kTileRows + lane);
         const uint32_t cc = T.cols[jl];
         before += static_cast<uint64_t>(cc & 0xFFu) | (static_cast<uint64_t>((cc >> 8) & 0xFFu) << 16) |
                   (static_cast<uint64_t>((cc >> 16) & 0xFFu) << 32) | (static_cast<uint64_t>(cc >> 24) << 48);
@@ -361,19 +362,16 @@ __device__ __forceinline__ float sum_partials(const float *p, uint64_t stride, u
     return tot;
 }
 
-// ---- one group (or slice) per lane, per width; results to L.part[column][row]
-// A list entry holds the byte offset of the group's L.part slot (column *
-// 256 + row * 4, so the column is bits 8-9) and the group's fp16 scale in the
-// high half.
+// ---- one group (or slice) per lane, per width; results to L.part[column * 64 + row]
+// A list entry is that index (so the column is bits 6-7). The products are
+// stored unscaled: the row's lane applies its own scales when it adds them.
 
-__device__ __forceinline__ void store_part(WaveLds &L, uint32_t info, float v) {
-    *reinterpret_cast<float *>(reinterpret_cast<char *>(&L.part[0][0]) + (info & 0xFFFFu)) = v;
-}
+__device__ __forceinline__ void store_part(WaveLds &L, uint32_t info, float v) { L.part[info] = v; }
 
-// returns the scaled product: L.part shares its bytes with the lookup table,
-// so it is stored once every 1-bit group of the tile is done
+// returns the product: L.part shares its bytes with the lookup table, so it
+// is stored once every 1-bit group of the tile is done
 __device__ __forceinline__ float group1(WaveLds &L, uint32_t info, uint2 v) {
-    const uint32_t jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = info >> 6;
     // table k (one per 4 activations) starts at byte 64k; the entry for nibble u is at +4u.
     // Bytes of lo/hi hold 4 * (nibble 2t / 2t+1) of each word.
     const char *lut = reinterpret_cast<const char *>(L.lut + jl * 256u);
@@ -393,11 +391,11 @@ __device__ __forceinline__ float group1(WaveLds &L, uint32_t info, uint2 v) {
         }
     }
     const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    return half_to_float(info >> 16) * (L.corr[jl][0] - 2.f * sum);
+    return L.corr[jl][0] - 2.f * sum;
 }
 
 __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
-    const uint32_t jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = info >> 6;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride);
     const uint32_t magic = opaque(kMagic);
@@ -417,12 +415,12 @@ __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint
         a16 = dot2(p[7], xb.w, a16);
     }
     const float d = a1 + 0.25f * a4 + 0.0625f * a16 + 0.015625f * a64 + 0.00390625f * a256 - L.corr[jl][1];
-    store_part(L, info, half_to_float(info >> 16) * d);
+    store_part(L, info, d);
 }
 
 // 4-bit: a 16-byte half group (h = task & 1); lane pairs add their halves
 __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uint2 va, uint2 vb) {
-    const uint32_t jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = info >> 6;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 16u * h);
     const uint32_t magic = opaque(kMagic);
@@ -439,12 +437,12 @@ __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uin
     }
     float part = a1 + 0.0625f * a16;
     part += dpp<kQuadXor1>(part);
-    if (h == 0) store_part(L, info, half_to_float(info >> 16) * (part - L.corr[jl][2]));
+    if (h == 0) store_part(L, info, part - L.corr[jl][2]);
 }
 
 // 8-bit: a 16-byte quarter group (qd = task & 3); lane quads add their quarters
 __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, uint2 va, uint2 vb) {
-    const uint32_t jl = (info >> 8) & 0xFFu;
+    const uint32_t jl = info >> 6;
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 8u * qd);
     float a = 0.f;
@@ -461,7 +459,7 @@ __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, ui
     }
     a += dpp<kQuadXor1>(a);
     a += dpp<kQuadXor2>(a);
-    if (qd == 0) store_part(L, info, half_to_float(info >> 16) * (a - 1152.f * L.corr[jl][0]));
+    if (qd == 0) store_part(L, info, a - 1152.f * L.corr[jl][0]);
 }
 
 // Payload of the first 256 one-bit groups and of the first 64 slices of
@@ -507,7 +505,7 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
     for (uint32_t i = 0; i < 4; ++i) {
         const bool on = lane + kWave * i < cnt[0];
         const uint32_t e = L.list[lane + kWave * i];
-        info1[i] = on ? e : static_cast<uint32_t>(sizeof(L.part)) + 4u * lane;
+        info1[i] = on ? e : kTileGroups * kTileRows + lane;
         v1[i] = 0.f;
         if (on) v1[i] = group1(L, e, S.p1[i]);
     }
@@ -517,7 +515,7 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
     const uint8_t *b2 = tile + 8u * cnt[0];
     const uint8_t *b4 = b2 + 16u * cnt[1];
     const uint8_t *b8 = b4 + 32u * cnt[2];
-    const uint32_t *l2 = L.list + cnt[0], *l4 = l2 + cnt[1], *l8 = l4 + cnt[2];
+    const uint8_t *l2 = L.list + cnt[0], *l4 = l2 + cnt[1], *l8 = l4 + cnt[2];
     if (lane < cnt[1]) group2(L, l2[lane], S.p2a, S.p2b);
     if (lane < 2u * cnt[2]) task4(L, l4[lane >> 1], lane & 1u, S.p4a, S.p4b);
     if (lane < 4u * cnt[3]) task8(L, l8[lane >> 2], lane & 3u, S.p8a, S.p8b);
@@ -530,10 +528,10 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
 }
 
 // kWaves waves per workgroup (4, 8 or 16) share one row tile; the LDS
-// (5760 B per wave) allows 7, 3 or 1 such workgroups per CU.
+// (4992 B per wave) allows 8, 4 or 2 such workgroups per CU, eight waves
+// per SIMD, and the registers are held to the 64 that allow the same.
 template <bool kAligned, uint32_t kWaves>
-__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(kWaves == 4 ? 7 : kWaves == 8 ? 6 : 4, 8)))
-void gemv_tiles(Batch B) {
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void gemv_tiles(Batch B) {
     __shared__ WaveLds lds[kWaves];
     // which matrix, row tile and split this block serves (uniform)
     const MatArgs M = B.m[blockIdx.y];   // by value: loaded into scalar registers once
@@ -555,7 +553,7 @@ void gemv_tiles(Batch B) {
     // merge copy would wait for the load
     TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, lane_id(), true);
     for (; ct < c_hi; ct += kWaves) {
-        const uint32_t cn = min(kTileGroups, M.groups - ct * kTileGroups);
+        const uint32_t cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - ct * kTileGroups);
         // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
         const TileScan P = tile_scan(cur, rows, cn, lane_id(), cnt);
@@ -571,17 +569,20 @@ void gemv_tiles(Batch B) {
         wave_lds_sync();
         const uint32_t lane = lane_id();
         if (lane < rows)
-            for (uint32_t jl = 0; jl < cn; ++jl) acc += L.part[jl][lane];
+            for (uint32_t jl = 0; jl < cn; ++jl) {
+                const uint32_t sb = (jl < 2 ? cur.s01 >> (16 * jl) : cur.s23 >> (16 * (jl - 2))) & 0xFFFFu;
+                acc += half_to_float(sb) * L.part[jl * kTileRows + lane];
+            }
         wave_lds_sync();
         cur = nxt;
     }
     const uint32_t lane = lane_id();
-    L.part[0][lane] = acc;   // the wave's row sums, in its own (now idle) LDS
+    L.part[lane] = acc;   // the wave's row sums, in its own (now idle) LDS
     __syncthreads();
     if (wave != 0 || spare) return;
-    float sum = lds[0].part[0][lane];
+    float sum = lds[0].part[lane];
 #pragma unroll
-    for (uint32_t w = 1; w < kWaves; ++w) sum += lds[w].part[0][lane];   // in wave order
+    for (uint32_t w = 1; w < kWaves; ++w) sum += lds[w].part[lane];   // in wave order
     if (M.splits == 1) {
         if (lane < rows) M.y[r0 + lane] = sum;
         return;
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
         const uint32_t b = 1u << wsel;
         for (uint32_t e = lane; e < cnt[wsel]; e += kWave) {
             const uint32_t info = L.list[first + e];
-            const uint32_t r = (info & 0xFFu) >> 2, jl = (info >> 8) & 0xFFu;
+            const uint32_t r = info % kTileRows, jl = info / kTileRows;
             const uint32_t *src = reinterpret_cast<const uint32_t *>(base + 8u * b * e);
             uint32_t *dst = reinterpret_cast<uint32_t *>(codes + (r0 + r) * k + 64u * (j0 + jl));
             for (uint32_t wd = 0; wd < 2 * b; ++wd) {
@@ -1206,20 +1207,20 @@ inline size_t partial_bytes(uint32_t splits, uint32_t n) {
 // Launch shape of one batched GEMV launch: waves per workgroup and splits
 // per row tile. The cost model was fitted to graph-replayed launch times on
 // MI355X over the shapes of every decode workload (4096- to 14336-wide
-// layers, the 1.0B and 131M sets, the 32000-row head; 12 shapes, every
-// waves/splits choice): time ~ 1.1 per tile slot of a SIMD (tiles per wave x
-// waves per SIMD, averaged over the CUs a launch occupies) + 2.5 per tile a
-// wave handles after its first and per extra round of workgroups + the split
-// tail (1.4 + 0.23 per split: partial stores, the arrival count and the last
-// arriver's sum, three dependent round trips to memory). For each of the 12
-// it picks the fastest measured shape or one within 1% of it.
+// layers, the 1.0B and 131M sets, the 32000-row head) and a 131072x4096
+// matrix, 13 shapes, every waves/splits choice: time ~ 1.1 per tile slot of
+// a SIMD (tiles per wave x waves per SIMD, averaged over the CUs a launch
+// occupies) + 2.5 per tile a wave handles after its first and per extra
+// round of workgroups + the split tail (1.4 + 0.23 per split: partial
+// stores, the arrival count and the last arriver's sum, three dependent
+// round trips to memory). It picks the fastest measured shape for all 13.
 struct GemvPlan {
     uint32_t waves, splits;
 };
 
 GemvPlan gemv_plan(uint32_t row_tiles, uint32_t col_tiles) {
     constexpr uint32_t kCUs = 256;
-    const uint32_t waves[3] = {4, 8, 16}, per_cu[3] = {7, 3, 1};   // resident workgroups per CU (LDS bound)
+    const uint32_t waves[3] = {4, 8, 16}, per_cu[3] = {8, 4, 2};   // resident workgroups per CU (LDS bound)
     GemvPlan best{4, 1};
     double best_cost = 1e300;
     for (uint32_t w = 0; w < 3; ++w) {
