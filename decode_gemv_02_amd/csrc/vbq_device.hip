@@ -89,6 +89,20 @@ __device__ __forceinline__ float half_to_float(uint32_t h) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
 }
 
+// Buffer descriptors (raw, 32-bit data format). The hardware checks every
+// read against the descriptor's byte count and returns zeros past it, so a
+// lane with nothing to read needs no clamped address and a read can never
+// leave the array.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0));
+}
+
 // ---------------------------------------------------------------- per-width unpack
 // Each helper turns one little-endian 32-bit word of a group into fp16 pairs
 // (1024 + 2^s * u) where u = q + 2^(b-1) is the offset-binary code; the pairs
@@ -144,8 +158,10 @@ struct MatArgs {
     float *y;
     float *partial;       // [splits][n] when splits > 1
     uint32_t *counters;   // [row tiles] arrival counters when splits > 1 (self-resetting)
-    uint32_t n, groups, col_tiles, splits, blocks, pad;   // blocks = row tiles x splits
+    uint32_t n, groups, col_tiles, splits, blocks;   // blocks = row tiles x splits
+    uint32_t payload_bytes;
 };
+
 
 // Launched as a 2D grid: blockIdx.y picks the matrix, so a block loads its
 // matrix's arguments with one scalar load and no search.
@@ -471,31 +487,26 @@ struct Staged {
     uint2 p2a, p2b, p4a, p4b, p8a, p8b;
 };
 
-// Every staged load is issued unconditionally: a lane without a task reads
-// the tile's first bytes (always inside the payload) and ignores them. With
-// a fixed number of loads the compiler waits for exactly these and not for
-// the next tile's metadata issued after them.
-__device__ __forceinline__ void stage_payload(const uint8_t *tile, const uint32_t cnt[4], uint32_t lane, Staged &S) {
+// Every staged load is issued unconditionally through the tile's descriptor
+// (base at the tile, bytes to the payload's end): a lane without a task
+// reads later buckets or tiles, or zeros past the payload, and ignores them.
+// With a fixed number of loads the compiler waits for exactly these and not
+// for the next tile's metadata issued after them.
+__device__ __forceinline__ void stage_payload(rsrc_t tile, const uint32_t cnt[4], uint32_t lane, Staged &S) {
 #pragma unroll
-    for (uint32_t i = 0; i < 4; ++i) {
-        const uint32_t e = lane + kWave * i;
-        S.p1[i] = load8(tile + (e < cnt[0] ? 8u * e : 0u));
-    }
+    for (uint32_t i = 0; i < 4; ++i) S.p1[i] = buf_load8(tile, 8u * lane + 8u * kWave * i);
     const uint32_t o2 = 8u * cnt[0], o4 = o2 + 16u * cnt[1], o8 = o4 + 32u * cnt[2];
-    // (a lane without a task reads bytes 0..7 twice: a tile may be only 8 bytes long)
-    const bool t2 = lane < cnt[1], t4 = lane < 2u * cnt[2], t8 = lane < 4u * cnt[3];
-    const uint32_t a2 = o2 + 16u * lane, a4 = o4 + 16u * lane, a8 = o8 + 16u * lane;
-    S.p2a = load8(tile + (t2 ? a2 : 0u));
-    S.p2b = load8(tile + (t2 ? a2 + 8u : 0u));
-    S.p4a = load8(tile + (t4 ? a4 : 0u));
-    S.p4b = load8(tile + (t4 ? a4 + 8u : 0u));
-    S.p8a = load8(tile + (t8 ? a8 : 0u));
-    S.p8b = load8(tile + (t8 ? a8 + 8u : 0u));
+    S.p2a = buf_load8(tile, o2 + 16u * lane);
+    S.p2b = buf_load8(tile, o2 + 16u * lane + 8u);
+    S.p4a = buf_load8(tile, o4 + 16u * lane);
+    S.p4b = buf_load8(tile, o4 + 16u * lane + 8u);
+    S.p8a = buf_load8(tile, o8 + 16u * lane);
+    S.p8b = buf_load8(tile, o8 + 16u * lane + 8u);
 }
 
 // Staged work first, then the rounds that load their own bytes (rare: more
 // than 64 two-bit groups or 64 slices of a wider width in one tile).
-__device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const uint8_t *tile, const uint32_t cnt[4],
+__device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, rsrc_t tile, const uint32_t cnt[4],
                                               uint32_t lane) {
     // A lane without a group in a round parks its (unused) result in a spare
     // slot past L.part, so the deferred stores need no branches.
@@ -512,19 +523,17 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, const
     // the lookup table is dead from here: its bytes take the products
 #pragma unroll
     for (uint32_t i = 0; i < 4; ++i) store_part(L, info1[i], v1[i]);
-    const uint8_t *b2 = tile + 8u * cnt[0];
-    const uint8_t *b4 = b2 + 16u * cnt[1];
-    const uint8_t *b8 = b4 + 32u * cnt[2];
+    const uint32_t o2 = 8u * cnt[0], o4 = o2 + 16u * cnt[1], o8 = o4 + 32u * cnt[2];
     const uint8_t *l2 = L.list + cnt[0], *l4 = l2 + cnt[1], *l8 = l4 + cnt[2];
     if (lane < cnt[1]) group2(L, l2[lane], S.p2a, S.p2b);
     if (lane < 2u * cnt[2]) task4(L, l4[lane >> 1], lane & 1u, S.p4a, S.p4b);
     if (lane < 4u * cnt[3]) task8(L, l8[lane >> 2], lane & 3u, S.p8a, S.p8b);
     for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
-        group2(L, l2[e], load8(b2 + 16u * e), load8(b2 + 16u * e + 8u));
+        group2(L, l2[e], buf_load8(tile, o2 + 16u * e), buf_load8(tile, o2 + 16u * e + 8u));
     for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
-        task4(L, l4[e >> 1], e & 1u, load8(b4 + 16u * e), load8(b4 + 16u * e + 8u));
+        task4(L, l4[e >> 1], e & 1u, buf_load8(tile, o4 + 16u * e), buf_load8(tile, o4 + 16u * e + 8u));
     for (uint32_t e = lane + kWave; e < 4u * cnt[3]; e += kWave)
-        task8(L, l8[e >> 2], e & 3u, load8(b8 + 16u * e), load8(b8 + 16u * e + 8u));
+        task8(L, l8[e >> 2], e & 3u, buf_load8(tile, o8 + 16u * e), buf_load8(tile, o8 + 16u * e + 8u));
 }
 
 // kWaves waves per workgroup (4, 8 or 16) share one row tile; the LDS
@@ -557,7 +566,10 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
         const TileScan P = tile_scan(cur, rows, cn, lane_id(), cnt);
-        const uint8_t *tp = M.payload + cur.off;
+        // the tile's descriptor: from its first byte to the payload's end (none if the offset is past it;
+        // the saturating subtract is a vector instruction, so its result is moved back to a scalar register)
+        const uint32_t left = __builtin_amdgcn_readfirstlane(M.payload_bytes - min(cur.off, M.payload_bytes));
+        const rsrc_t tp = make_rsrc(M.payload + cur.off, left);
         Staged S;
         stage_payload(tp, cnt, lane_id(), S);
         // the next tile's metadata travels while this tile computes
@@ -1282,6 +1294,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.scales = w->scales;
         M.tile_offsets = w->tile_offsets;
         M.payload = w->payload;
+        M.payload_bytes = w->payload_bytes;
         M.x = xs[i];
         M.y = ys[i];
         M.n = w->n;
