@@ -719,14 +719,18 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
 
-// When the matrix cores run a small batch (measured on MI355X): the matrix-core
-// kernel runs one wave per tile, so a matrix of few tiles leaves most SIMDs
-// idle, while m GEMVs in one launch fill the chip. It wins from 4 rows when
-// rows x tiles reach about 5120 (LM head 32000x4096 at m = 8: 29 vs 66 us;
-// 4096x4096 at m = 8: 12.6 vs 14.9 us; 2048x2048 at m = 16: 11.4 vs 9.7 us),
-// and always beyond the 16 rows one GEMV launch takes.
+// When the matrix cores run a small batch (measured on MI355X, graph-replayed):
+// the matrix-core kernel costs about the same for any m up to 16, while m
+// GEMVs in one launch cost more with every row, less so on small matrices
+// whose launches leave the chip idle. The crossover row count falls with the
+// tile count roughly as 1/sqrt(tiles): the matrix cores win from m = 4 rows
+// when m^2 x tiles reaches 85000 (LM head 32000x4096, 8000 tiles: m = 3 24.9
+// vs 27.6 us as GEMVs, m = 4 27.4 vs 31.3 on the matrix cores; 14336x4096:
+// m = 4 19.2 vs 20.0 as GEMVs, m = 6 20.4 vs 25.7; 4096x4096: m = 8 11.1 vs
+// 12.2 as GEMVs, m = 12 12.7 vs 15.6), and always beyond the 16 rows one GEMV
+// launch takes.
 constexpr uint32_t kGemmMinBatch = 4;
-constexpr uint64_t kGemmMinWork = 5120;   // rows of X times tiles of W
+constexpr uint64_t kGemmMinWork = 85000;   // rows of X squared times tiles of W
 constexpr uint32_t kAStride = 136;   // fp16 per staged row: two columns of 64 codes + 8 pad (272 B)
 
 struct GemmArgs {
@@ -1423,7 +1427,7 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
     (void)hipGetLastError();
     hipStream_t s = static_cast<hipStream_t>(stream);
     const uint64_t tiles = static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
-    if (m > VBQ_MAX_MULTI || (m >= kGemmMinBatch && m * tiles >= kGemmMinWork)) {
+    if (m > VBQ_MAX_MULTI || (m >= kGemmMinBatch && static_cast<uint64_t>(m) * m * tiles >= kGemmMinWork)) {
         if (w->k == 0) {
             const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
             hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s, y, cnt);

@@ -175,8 +175,8 @@ VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *c
  * x: device binary16 [m][k] row-major; y: device fp32 [m][n] row-major
  * (overwritten). Runs on the matrix cores (each group's codes decoded once,
  * 16x16x32 fp16 products, fp32 accumulation) when m > 16, or when m >= 4 and
- * m times the matrix's tile count (64x256 weights per tile) is at least 5120;
- * otherwise as one batch-1 GEMV per row of X in one launch on the vector
+ * m * m times the matrix's tile count (64x256 weights per tile) is at least
+ * 85000; otherwise as one batch-1 GEMV per row of X in one launch on the vector
  * units (the faster choice, measured). Scratch as for vbq_gemv_multi.
  * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,

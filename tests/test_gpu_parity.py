@@ -121,10 +121,10 @@ def test_gemm_matches_oracle(V, torch_mod, m):
     assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"gemm m={m}")
 
 
-@pytest.mark.parametrize("m", [4, 8, 16])
+@pytest.mark.parametrize("m", [4, 8, 12, 16])
 def test_gemm_both_paths_below_17_rows(V, torch_mod, m):
-    # 1280x8192 has 640 tiles: m = 8 and 16 reach the matrix cores (m * tiles >= 5120),
-    # m = 4 runs as one GEMV per row; 97x1088 (10 tiles) stays on the GEMVs
+    # 1280x8192 has 640 tiles: m = 12 and 16 reach the matrix cores (m * m * tiles >= 85000),
+    # m = 4 and 8 run as one GEMV per row; 97x1088 (10 tiles) stays on the GEMVs
     for n, k in ((1280, 8192), (97, 1088)):
         print_case(test="gemm_paths", n=n, k=k, m=m)
         bits, codes, scales, p = make_case((m, n, k, 31), n, k, W.STD_MIX)
