@@ -1023,7 +1023,7 @@ __device__ __forceinline__ void mfma_pass(const GemmWaveLds &L, const half8_t bx
 }
 
 template <uint32_t MB>
-__global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB <= 2 ? 2 : 1, 8))) void gemm_tiles(GemmArgs G) {
     __shared__ GemmWaveLds lds[kWavesPerBlock];
     __shared__ uint32_t arrived_s;
     const uint32_t a = blockIdx.x / G.splits, split = blockIdx.x % G.splits;
@@ -1063,9 +1063,10 @@ __global__ __launch_bounds__(256) void gemm_tiles(GemmArgs G) {
         wave_lds_sync();
         mfma_pass<MB>(L, bx, 0, cn, acc);
         if (cn > 2) {
-            if (MB > 2) load_bx<MB>(G, j0, 1, cn, bx1);
             wave_lds_sync();
             gemm_decode_pass(L, s1, tile, colstart, 1, cn);
+            // (issued after the decode: its own loads of later rounds would otherwise wait for these)
+            if (MB > 2) load_bx<MB>(G, j0, 1, cn, bx1);
             wave_lds_sync();
             mfma_pass<MB>(L, bx1, 1, cn, acc);
         }
