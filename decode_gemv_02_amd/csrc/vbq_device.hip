@@ -17,9 +17,11 @@
 //      stream's order (buckets by width, column-major inside a bucket);
 //   3. for each width the wave walks its bucket with one group (or a 16-byte
 //      slice of a group) per lane, so every instruction runs a single width's
-//      unpack; the bucket is contiguous, so loads are coalesced;
-//   4. each group's fp32 dot product is scaled once and parked in LDS; rows
-//      are summed in a fixed order, so results are bitwise repeatable.
+//      unpack; the bucket is contiguous, so loads are coalesced (and go
+//      through a buffer descriptor: the hardware bounds-checks them);
+//   4. each group's fp32 dot product is parked in LDS; each row's lane
+//      scales its groups once and sums them in a fixed order, so results are
+//      bitwise repeatable.
 // A workgroup of 4, 8 or 16 waves shares one row tile and splits its column
 // tiles; when a row tile is further split across workgroups (small n, large
 // k), the partial sums go to a scratch buffer and the last workgroup to
