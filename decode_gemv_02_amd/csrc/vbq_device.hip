@@ -260,7 +260,7 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
 // Stage the tile's activations: fp16 pairs, the 4-bit lookup table (sums of
 // the activations selected by the set bits of a 4-bit index) and the
 // per-column bias terms of the unpack paths.
-__device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
+__device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane, float wa, float wb) {
     const uint32_t jl = lane >> 4, k = lane & 15;
     L.xs[jl * kXStride + 2 * k] = xv.x;
     L.xs[jl * kXStride + 2 * k + 1] = xv.y;
@@ -277,9 +277,6 @@ __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
     const float a23 = x2 + x3;
     float xsum = a01 + a23;
     float c4 = 1032.f * a01 + 72.f * a23;
-    const uint32_t km = k & 3;
-    const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
-    const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
     float c2 = wa * a01 + wb * a23;
     xsum = row16_sum(xsum);
     c2 = row16_sum(c2);
@@ -558,6 +555,10 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     const uint32_t c_lo = (split * M.col_tiles) / M.splits, c_hi = ((split + 1) * M.col_tiles) / M.splits;
     WaveLds &L = lds[wave];
     float acc = 0.f;
+    // 2-bit bias weights of this lane's activation pairs (pair factors 1,4,16,64,256,1,4,16: 1024/f + 2)
+    const uint32_t km = lane_id() & 3u;
+    const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
+    const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
     uint32_t ct = c_lo + wave;
     // metadata loads are unconditional (a wave without a next tile reloads its
     // own): a conditional load would make its result a branch merge, and the
@@ -576,7 +577,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         stage_payload(tp, cnt, lane_id(), S);
         // the next tile's metadata travels while this tile computes
         const TileMeta nxt = load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, lane_id(), true);
-        stage_x(L, cur.xv, lane_id());
+        stage_x(L, cur.xv, lane_id(), wa, wb);
         build_lists(L, cur, P, cnt, rows, cn, lane_id());
         wave_lds_sync();
         tile_products(L, S, tp, cnt, lane_id());
