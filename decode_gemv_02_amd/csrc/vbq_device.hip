@@ -190,11 +190,21 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// Lane index, recomputed at each use: keeping it live across the tile loop
-// would cost a register the loop needs.
+// Lane index, recomputed at each use: kept live across a tile loop, every
+// value derived from it would be hoisted too and the loop would run out of
+// registers.
 __device__ __forceinline__ uint32_t lane_id() {
     uint32_t r;
     asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(r));
+    return r;
+}
+
+// A copy of a kept lane index that the compiler cannot see through: one
+// move per use instead of two instructions, and still nothing derived from
+// it is hoisted.
+__device__ __forceinline__ uint32_t relane(uint32_t lane) {
+    uint32_t r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(lane));
     return r;
 }
 
@@ -555,34 +565,36 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     const uint32_t c_lo = (split * M.col_tiles) / M.splits, c_hi = ((split + 1) * M.col_tiles) / M.splits;
     WaveLds &L = lds[wave];
     float acc = 0.f;
+    const uint32_t lane0 = lane_id();
     // 2-bit bias weights of this lane's activation pairs (pair factors 1,4,16,64,256,1,4,16: 1024/f + 2)
-    const uint32_t km = lane_id() & 3u;
+    const uint32_t km = lane0 & 3u;
     const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
     const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
     uint32_t ct = c_lo + wave;
     // metadata loads are unconditional (a wave without a next tile reloads its
     // own): a conditional load would make its result a branch merge, and the
     // merge copy would wait for the load
-    TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, lane_id(), true);
+    TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, relane(lane0), true);
     for (; ct < c_hi; ct += kWaves) {
         const uint32_t cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - ct * kTileGroups);
         // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
-        const TileScan P = tile_scan(cur, rows, cn, lane_id(), cnt);
+        const TileScan P = tile_scan(cur, rows, cn, relane(lane0), cnt);
         // the tile's descriptor: from its first byte to the payload's end (none if the offset is past it;
         // the saturating subtract is a vector instruction, so its result is moved back to a scalar register)
         const uint32_t left = __builtin_amdgcn_readfirstlane(M.payload_bytes - min(cur.off, M.payload_bytes));
         const rsrc_t tp = make_rsrc(M.payload + cur.off, left);
         Staged S;
-        stage_payload(tp, cnt, lane_id(), S);
+        stage_payload(tp, cnt, relane(lane0), S);
         // the next tile's metadata travels while this tile computes
-        const TileMeta nxt = load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, lane_id(), true);
-        stage_x(L, cur.xv, lane_id(), wa, wb);
-        build_lists(L, cur, P, cnt, rows, cn, lane_id());
+        const TileMeta nxt =
+            load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, relane(lane0), true);
+        stage_x(L, cur.xv, relane(lane0), wa, wb);
+        build_lists(L, cur, P, cnt, rows, cn, relane(lane0));
         wave_lds_sync();
-        tile_products(L, S, tp, cnt, lane_id());
+        tile_products(L, S, tp, cnt, relane(lane0));
         wave_lds_sync();
-        const uint32_t lane = lane_id();
+        const uint32_t lane = relane(lane0);
         if (lane < rows)
             for (uint32_t jl = 0; jl < cn; ++jl) {
                 const uint32_t sb = (jl < 2 ? cur.s01 >> (16 * jl) : cur.s23 >> (16 * (jl - 2))) & 0xFFFFu;
@@ -591,7 +603,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         wave_lds_sync();
         cur = nxt;
     }
-    const uint32_t lane = lane_id();
+    const uint32_t lane = relane(lane0);
     L.part[lane] = acc;   // the wave's row sums, in its own (now idle) LDS
     __syncthreads();
     if (wave != 0 || spare) return;
