@@ -104,6 +104,17 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0));
 }
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+    return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+
+// A tile's payload: from its first byte to the payload's end (nothing if the
+// offset is past it; the saturating subtract is a vector instruction, so its
+// result is moved back to a scalar register).
+__device__ __forceinline__ rsrc_t tile_rsrc(const uint8_t *payload, uint32_t payload_bytes, uint32_t off) {
+    const uint32_t left = __builtin_amdgcn_readfirstlane(payload_bytes - min(off, payload_bytes));
+    return make_rsrc(payload + off, left);
+}
 
 // ---------------------------------------------------------------- per-width unpack
 // Each helper turns one little-endian 32-bit word of a group into fp16 pairs
@@ -366,7 +377,6 @@ __device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const
     }
 }
 
-__device__ __forceinline__ uint2 load8(const uint8_t *p) { return *reinterpret_cast<const uint2 *>(p); }
 
 // Sum of the split partials p[0], p[stride], ... in split order. The coherent
 // loads go out eight at a time (clamped addresses, no branches) so their round
@@ -580,10 +590,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
         const TileScan P = tile_scan(cur, rows, cn, relane(lane0), cnt);
-        // the tile's descriptor: from its first byte to the payload's end (none if the offset is past it;
-        // the saturating subtract is a vector instruction, so its result is moved back to a scalar register)
-        const uint32_t left = __builtin_amdgcn_readfirstlane(M.payload_bytes - min(cur.off, M.payload_bytes));
-        const rsrc_t tp = make_rsrc(M.payload + cur.off, left);
+        const rsrc_t tp = tile_rsrc(M.payload, M.payload_bytes, cur.off);
         Staged S;
         stage_payload(tp, cnt, relane(lane0), S);
         // the next tile's metadata travels while this tile computes
@@ -640,23 +647,23 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
     const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
     const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, M.groups - j0);
     const TileMeta t = load_meta<kAligned>(M, a, ct, lane, false);
-    const uint8_t *tp = M.payload + t.off;
+    const rsrc_t tp = tile_rsrc(M.payload, M.payload_bytes, t.off);
     const uint64_t k = static_cast<uint64_t>(M.groups) * 64u;
     uint32_t cnt[4];
     const TileScan P = tile_scan(t, rows, cn, lane, cnt);
     build_lists(L, t, P, cnt, rows, cn, lane);
     wave_lds_sync();
-    const uint8_t *base = tp;
+    uint32_t base = 0;    // byte offset of the bucket in the tile
     uint32_t first = 0;   // list index of the bucket's first group
     for (uint32_t wsel = 0; wsel < 4; ++wsel) {
         const uint32_t b = 1u << wsel;
         for (uint32_t e = lane; e < cnt[wsel]; e += kWave) {
             const uint32_t info = L.list[first + e];
             const uint32_t r = info % kTileRows, jl = info / kTileRows;
-            const uint32_t *src = reinterpret_cast<const uint32_t *>(base + 8u * b * e);
+            const uint32_t src = base + 8u * b * e;
             uint32_t *dst = reinterpret_cast<uint32_t *>(codes + (r0 + r) * k + 64u * (j0 + jl));
             for (uint32_t wd = 0; wd < 2 * b; ++wd) {
-                const uint32_t v = src[wd];
+                const uint32_t v = buf_load4(tp, src + 4u * wd);
                 if (b == 1) {
                     // 32 sign bits -> 32 codes of +-1
                     for (uint32_t o = 0; o < 8; ++o) {
@@ -758,6 +765,7 @@ struct GemmArgs {
     float *partial;       // [splits][m][n] when splits > 1
     uint32_t *counters;   // [row tiles] when splits > 1 (self-resetting)
     uint32_t n, groups, col_tiles, splits, m, k;
+    uint32_t payload_bytes;
 };
 
 struct alignas(16) GemmWaveLds {
@@ -891,9 +899,9 @@ __device__ __forceinline__ void gemm_lists(GemmWaveLds &L, const TileMeta &t, co
     }
 }
 
-// 16 payload bytes at an 8-byte aligned address (buckets start at multiples of 8)
-__device__ __forceinline__ uint4 load16(const uint8_t *p) {
-    const uint2 lo = load8(p), hi = load8(p + 8);
+// 16 payload bytes at an 8-byte aligned offset (buckets start at multiples of 8)
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+    const uint2 lo = buf_load8(r, off), hi = buf_load8(r, off + 8u);
     return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
@@ -917,44 +925,29 @@ __device__ __forceinline__ void pass_range(const uint64_t colstart[kTileGroups +
     for (uint32_t w = 0; w < wi; ++w) base += (8u << w) * field16(total, w);
 }
 
-__device__ __forceinline__ PassStage gemm_stage_pass(const uint8_t *tile, const uint64_t colstart[kTileGroups + 1],
+__device__ __forceinline__ PassStage gemm_stage_pass(rsrc_t tile, const uint64_t colstart[kTileGroups + 1],
                                                      uint32_t pass, uint32_t cn) {
     const uint32_t lane = lane_id();
-    // unconditional loads (a lane without a task reads the tile's first bytes
-    // twice: a tile may be only 8 bytes long), so the compiler counts them
+    // unconditional loads through the tile's descriptor (a lane without a task
+    // reads later bytes, or zeros past the payload, and ignores them), so the
+    // compiler counts them
     PassStage S;
     uint32_t e0, e1, base;
     pass_range(colstart, pass, cn, 0, e0, e1, base);
-    S.p1[0] = load8(tile + (lane < e1 - e0 ? base + 8u * (e0 + lane) : 0u));
-    S.p1[1] = load8(tile + (lane + kWave < e1 - e0 ? base + 8u * (e0 + lane + kWave) : 0u));
+    S.p1[0] = buf_load8(tile, base + 8u * (e0 + lane));
+    S.p1[1] = buf_load8(tile, base + 8u * (e0 + lane + kWave));
     pass_range(colstart, pass, cn, 1, e0, e1, base);
-    const bool t2 = lane < e1 - e0;
-    const uint32_t a2 = base + 16u * (e0 + lane);
-    S.p2 = make_uint4(0u, 0u, 0u, 0u);
-    {
-        const uint2 lo = load8(tile + (t2 ? a2 : 0u)), hi = load8(tile + (t2 ? a2 + 8u : 0u));
-        S.p2 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    }
+    S.p2 = buf_load16(tile, base + 16u * (e0 + lane));
     pass_range(colstart, pass, cn, 2, e0, e1, base);
-    const bool t4 = lane < 2 * (e1 - e0);
-    const uint32_t a4 = base + 32u * e0 + 16u * lane;
-    {
-        const uint2 lo = load8(tile + (t4 ? a4 : 0u)), hi = load8(tile + (t4 ? a4 + 8u : 0u));
-        S.p4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    }
+    S.p4 = buf_load16(tile, base + 32u * e0 + 16u * lane);
     pass_range(colstart, pass, cn, 3, e0, e1, base);
-    const bool t8 = lane < 4 * (e1 - e0);
-    const uint32_t a8 = base + 64u * e0 + 16u * lane;
-    {
-        const uint2 lo = load8(tile + (t8 ? a8 : 0u)), hi = load8(tile + (t8 ? a8 + 8u : 0u));
-        S.p8 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-    }
+    S.p8 = buf_load16(tile, base + 64u * e0 + 16u * lane);
     return S;
 }
 
 // Decode columns 2*pass and 2*pass+1 of the tile into L.a; tasks past the
 // staged ones load their bytes here.
-__device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const PassStage &S, const uint8_t *tile,
+__device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const PassStage &S, rsrc_t tile,
                                                  const uint64_t colstart[kTileGroups + 1], uint32_t pass, uint32_t cn) {
     const uint32_t lane = lane_id();
 #pragma unroll
@@ -964,22 +957,21 @@ __device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const PassStage
         pass_range(colstart, pass, cn, wi, e0, e1, base);
         const uint32_t tpg = wi < 2 ? 1u : (b >> 1);           // tasks per group: 1, 1, 2, 4
         const uint32_t tasks = (e1 - e0) * tpg;
-        const uint8_t *bucket = tile + base;
         uint32_t round = 0;
         for (uint32_t t = lane; t < tasks; t += kWave, ++round) {
             const uint32_t e = e0 + t / tpg, sl = t % tpg;
             const uint32_t info = L.list[wi][e];
             const uint32_t r = info & 63u, jj = (info >> 6) - 2 * pass;
             uint16_t *dst = L.a + r * kAStride + 64u * jj;
-            const uint8_t *src = bucket + 8u * b * e;
+            const uint32_t src = base + 8u * b * e;   // the group's byte offset in the tile
             if (wi == 0) {
-                decode1(round == 0 ? S.p1[0] : round == 1 ? S.p1[1] : load8(src), dst);
+                decode1(round == 0 ? S.p1[0] : round == 1 ? S.p1[1] : buf_load8(tile, src), dst);
             } else if (wi == 1) {
-                decode2(round == 0 ? S.p2 : load16(src), dst);
+                decode2(round == 0 ? S.p2 : buf_load16(tile, src), dst);
             } else if (wi == 2) {
-                decode4(round == 0 ? S.p4 : load16(src + 16u * sl), dst + 32u * sl);
+                decode4(round == 0 ? S.p4 : buf_load16(tile, src + 16u * sl), dst + 32u * sl);
             } else {
-                decode8(round == 0 ? S.p8 : load16(src + 16u * sl), dst + 16u * sl);
+                decode8(round == 0 ? S.p8 : buf_load16(tile, src + 16u * sl), dst + 16u * sl);
             }
         }
     }
@@ -1063,7 +1055,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB <= 2 ? 2
         const TileScan T = tile_scan(cur, rows, cn, lane_id(), cnt);
         uint64_t colstart[kTileGroups + 1];
         column_starts(T, colstart);
-        const uint8_t *tile = G.payload + cur.off;
+        const rsrc_t tile = tile_rsrc(G.payload, G.payload_bytes, cur.off);
         const PassStage s0 = gemm_stage_pass(tile, colstart, 0, cn);
         const PassStage s1 = gemm_stage_pass(tile, colstart, cn > 2 ? 1 : 0, cn);
         half8_t bx[2][2][MB], bx1[2][2][MB];
@@ -1362,6 +1354,7 @@ vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, 
     G.scales = w->scales;
     G.tile_offsets = w->tile_offsets;
     G.payload = w->payload;
+    G.payload_bytes = w->payload_bytes;
     G.x = x;
     G.y = y;
     G.n = w->n;
@@ -1477,6 +1470,7 @@ extern "C" vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, v
     if (!aligned16(codes_out)) return fail(VBQ_ERR_ALIGN, "vbq_unpack_codes: codes_out is not 16-byte aligned");
     (void)hipGetLastError();
     MatArgs M{};
+    M.payload_bytes = w->payload_bytes;
     M.widths = w->widths;
     M.scales = w->scales;
     M.tile_offsets = w->tile_offsets;
