@@ -112,7 +112,9 @@ typedef struct vbq_sizes {
 
 /* Non-owning view of one packed matrix. The struct itself lives in host
  * memory; the array pointers are host pointers for host entry points and
- * device pointers for device entry points. */
+ * device pointers for device entry points. Device kernels read the payload
+ * through bounds-checked buffer descriptors: no read leaves
+ * [payload, payload + payload_bytes), even with a corrupt tile_offsets. */
 typedef struct vbq_matrix {
     uint32_t abi_version;          /* VBQ_ABI_VERSION */
     uint32_t n;                    /* rows (outputs) */
