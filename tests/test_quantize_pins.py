@@ -1,0 +1,156 @@
+"""Pins for the CPU reference of the per-group quantizer and the fixed recipe.
+
+VBQ paper (arXiv 2607.02893) §3.1 Eq. (1) (absmax scale over 2^(b-1) - 1,
+round and clip; 1-bit sign with the mean magnitude as scale) and §3.4 (the
+recipe: 4-bit first-block MLP, 2-bit projections, frequency-tiered head at a
+mean of 1.18 bits). Each test checks the reference against something it does
+not share code with: a brute-force search over the code grid, the nearest
+binary16 value found by scanning all 65536 patterns, hand-built groups with
+known answers, and the head mean the pages print.
+"""
+import numpy as np
+import pytest
+
+from oracle import quantize as Q
+
+ALL_HALVES = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+FINITE_HALVES = ALL_HALVES[np.isfinite(ALL_HALVES)].astype(np.float64)
+
+
+def nearest_half(v: float) -> float:
+    """Nearest finite binary16 value to v by scanning every pattern (ties to the even mantissa)."""
+    d = np.abs(FINITE_HALVES - v)
+    cand = FINITE_HALVES[d == d.min()]
+    if cand.size == 1:
+        return float(cand[0])
+    pats = cand.astype(np.float16).view(np.uint16)
+    return float(cand[(pats & 1) == 0][0])
+
+
+def one_group(values, b):
+    w = np.zeros((1, 64), np.float32)
+    w[0, :len(values)] = values
+    codes, scales = Q.quantize(w, np.array([[b]], np.uint8))
+    return codes[0], float(scales.view(np.float16)[0, 0])
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_codes_are_the_nearest_grid_point_of_the_stored_scale(b):
+    # brute force: every code minimises |w - s q| over the whole grid for the stored scale
+    rng = np.random.default_rng(b)
+    w = (rng.standard_normal((40, 64 * 8)) * 0.02).astype(np.float32)
+    bits = np.full((40, 8), b, np.uint8)
+    codes, scales = Q.quantize(w, bits)
+    qmax = 2 ** (b - 1) - 1
+    grid = np.arange(-qmax, qmax + 1, dtype=np.float64)
+    s = scales.view(np.float16).astype(np.float64)
+    for r in range(40):
+        for j in range(8):
+            wg = w[r, 64 * j:64 * j + 64].astype(np.float64)
+            err = np.abs(wg[:, None] - s[r, j] * grid[None, :])
+            best = grid[err.argmin(axis=1)]
+            tie = np.sort(err, axis=1)[:, 1] - err.min(axis=1) < 1e-12
+            assert np.array_equal(codes[r, 64 * j:64 * j + 64][~tie], best[~tie])
+            # the largest magnitude lands on the end of the grid
+            i = np.abs(wg).argmax()
+            assert abs(int(codes[r, 64 * j + i])) == qmax
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_scale_is_the_nearest_half_of_max_over_grid_end(b):
+    rng = np.random.default_rng(10 + b)
+    for _ in range(20):
+        vals = (rng.standard_normal(64) * rng.choice([1e-3, 0.02, 3.0])).astype(np.float32)
+        _, s = one_group(vals, b)
+        s32 = np.float32(np.abs(vals).max()) / np.float32(2 ** (b - 1) - 1)
+        assert s == nearest_half(float(s32))
+
+
+def test_one_bit_is_sign_and_mean_magnitude():
+    vals = np.array([0.5, -0.25, 0.0, -0.0, 1.0, -2.0] + [0.25] * 58, np.float32)
+    codes, s = one_group(vals, 1)
+    assert list(codes[:6]) == [1, -1, 1, 1, 1, -1]   # sign(0) = +1, also for -0.0
+    assert np.all(codes[6:] == 1)
+    assert s == nearest_half(float(np.abs(vals.astype(np.float64)).sum() / 64))
+    # equal magnitudes: the mean is that magnitude exactly
+    codes, s = one_group(np.array([0.75, -0.75] * 32, np.float32), 1)
+    assert s == 0.75 and list(codes[:4]) == [1, -1, 1, -1]
+
+
+def test_ties_round_away_from_zero():
+    # b = 4: largest magnitude 7 gives scale 1, so every ratio is the weight itself
+    codes, s = one_group([7, 2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 3.5, -3.5, 0.49], 4)
+    assert s == 1.0
+    assert list(codes[:10]) == [7, 3, -3, 1, -1, 2, -2, 4, -4, 0]
+
+
+def test_codes_use_the_stored_half_scale():
+    # max/127 = 1 + 3 * 2^-13 rounds to the half 1.0; 100.52 / 1.0 rounds to 101,
+    # whereas 100.52 over the unrounded scale would round to 100
+    amax = np.float32(127) * np.float32(1 + 3 * 2 ** -13)
+    codes, s = one_group([amax, 100.52], 8)
+    assert s == 1.0
+    assert codes[0] == 127 and codes[1] == 101
+
+
+def test_zero_group_and_tiny_and_huge_scales():
+    for b in (2, 4, 8):
+        codes, s = one_group([], b)
+        assert s == 0.0 and np.all(codes == 0)
+        codes, s = one_group([1e-10, -1e-10], b)   # the scale underflows fp16
+        assert s == 0.0 and np.all(codes == 0)
+        codes, s = one_group([1e9, -3e8, 2.0], b)   # the scale saturates at the largest finite half
+        qmax = 2 ** (b - 1) - 1
+        assert s == 65504.0
+        assert codes[0] == qmax and codes[2] == 0
+        assert codes[1] == -min(qmax, int(np.floor(3e8 / 65504 + 0.5)))
+    codes, s = one_group([], 1)
+    assert s == 0.0 and np.all(codes == 1)
+
+
+def test_mixed_widths_pick_each_groups_rule():
+    rng = np.random.default_rng(7)
+    w = (rng.standard_normal((3, 256)) * 0.05).astype(np.float32)
+    bits = np.array([[1, 2, 4, 8], [8, 4, 2, 1], [2, 2, 1, 8]], np.uint8)
+    codes, scales = Q.quantize(w, bits)
+    for r in range(3):
+        for j in range(4):
+            c, s = one_group(w[r, 64 * j:64 * j + 64], int(bits[r, j]))
+            assert np.array_equal(codes[r, 64 * j:64 * j + 64], c)
+            assert float(scales.view(np.float16)[r, j]) == s
+
+
+def test_head_recipe_mean_is_the_pages_1_18_bits():
+    rows = 32000
+    freq = np.random.default_rng(3).permutation(rows) + 1   # distinct frequencies
+    bits = Q.head_bits(freq)
+    counts = {b: int((bits == b).sum()) for b in (8, 4, 2, 1)}
+    assert counts == {8: 160, 4: 480, 2: 3200, 1: 28160}
+    assert bits.astype(np.float64).mean() == pytest.approx(1.18, abs=1e-12)
+    # the most frequent rows get the most bits, monotonically
+    order = np.argsort(-freq, kind="stable")
+    assert np.all(np.diff(bits[order].astype(int)) <= 0)
+    assert bits[freq.argmax()] == 8 and bits[freq.argmin()] == 1
+
+
+def test_head_recipe_ties_go_to_the_lower_row():
+    bits = Q.head_bits(np.zeros(1000))   # all tied: rank = row index
+    assert list(bits[:5]) == [8] * 5 and bits[5] == 4 and bits[19] == 4 and bits[20] == 2
+    assert bits[119] == 2 and bits[120] == 1
+
+
+def test_projection_recipe():
+    assert Q.projection_bits(True) == 4 and Q.projection_bits(False) == 2
+
+
+def test_dequantize_error_bound():
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((8, 512)) * 0.02).astype(np.float32)
+    bits = rng.choice(np.array([2, 4, 8], np.uint8), size=(8, 8))
+    codes, scales = Q.quantize(w, bits)
+    wh = Q.dequantize(codes, scales)
+    s = np.repeat(scales.view(np.float16).astype(np.float64), 64, axis=1)
+    # inside the grid the error is at most half a step; the clipped end is the largest magnitude
+    qmax = np.repeat((2 ** (bits.astype(int) - 1) - 1), 64, axis=1)
+    inside = np.abs(codes) < qmax
+    assert np.all(np.abs(w - wh)[inside] <= s[inside] / 2 * (1 + 1e-6))
