@@ -46,8 +46,10 @@ def _stored_scale(s32: np.ndarray) -> np.ndarray:
 
 
 def _round_half_away(r: np.ndarray) -> np.ndarray:
-    """Q3 on fp32 ratios (|r| + 0.5 is exact for the magnitudes a clipped code can reach)."""
-    return np.where(r >= 0, np.floor(r + np.float32(0.5)), -np.floor(-r + np.float32(0.5)))
+    """Q3 on fp32 ratios: |r| + 0.5 taken in fp64, where it is exact for every fp32 |r| < 2^28
+    (in fp32 the sum would round 0.5 - 2^-25 up to 1); larger ratios are clipped anyway."""
+    a = np.abs(r).astype(np.float64)
+    return np.sign(r) * np.floor(a + 0.5)
 
 
 def quantize(w: np.ndarray, bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:

@@ -84,6 +84,17 @@ def test_ties_round_away_from_zero():
     assert list(codes[:10]) == [7, 3, -3, 1, -1, 2, -2, 4, -4, 0]
 
 
+def test_rounding_just_below_a_half():
+    # scale 1 (b = 8, largest magnitude 127): each code is round-half-away of the weight itself
+    below_half = np.nextafter(np.float32(0.5), np.float32(0))          # 0.5 - 2^-25
+    below_1_5 = np.nextafter(np.float32(1.5), np.float32(0))
+    above_half = np.nextafter(np.float32(0.5), np.float32(1))
+    vals = [127, below_half, -below_half, 0.5, -0.5, below_1_5, -below_1_5, above_half, 126.5, -126.5]
+    codes, s = one_group(np.array(vals, np.float32), 8)
+    assert s == 1.0
+    assert list(codes[:10]) == [127, 0, 0, 1, -1, 1, -1, 1, 127, -127]
+
+
 def test_codes_use_the_stored_half_scale():
     # max/127 = 1 + 3 * 2^-13 rounds to the half 1.0; 100.52 / 1.0 rounds to 101,
     # whereas 100.52 over the unrounded scale would round to 100
