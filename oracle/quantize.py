@@ -18,10 +18,11 @@ VBQ paper (arXiv 2607.02893):
 Readings (the pages leave these open):
   Q1 precision: magnitudes, the largest magnitude, the b >= 2 scale s and
      the ratios w / s are fp32 (IEEE, correctly rounded division); the
-     1-bit mean magnitude is summed in fp64, divided by 64, rounded to fp32.
+     1-bit mean magnitude is summed in fp64 (exact here) and divided by 64.
   Q2 the stored scale is the fp16 rounding (to nearest, ties to even) of
-     that fp32 value, and the codes are computed with the stored scale, so
-     s * q is exactly what decode multiplies.
+     that value: of the fp32 quotient at b >= 2, of the fp64 mean at 1 bit
+     (one rounding, no fp32 step in between); the codes are computed with
+     the stored scale, so s * q is exactly what decode multiplies.
   Q3 round half away from zero; sign(0) = +1, also for -0.0.
   Q4 a stored scale of 0 (an all-zero group, or a largest magnitude too
      small for fp16) gives codes 0 at b >= 2 (+1 at 1 bit); a scale beyond
@@ -38,10 +39,10 @@ import numpy as np
 FP16_MAX = np.float16(65504.0)
 
 
-def _stored_scale(s32: np.ndarray) -> np.ndarray:
-    """fp32 scales -> fp16 (nearest even), saturated at the largest finite value (Q2, Q4)."""
+def _stored_scale(s: np.ndarray) -> np.ndarray:
+    """fp32 or fp64 scales -> fp16 in one rounding (nearest even), saturated at the largest finite value (Q2, Q4)."""
     with np.errstate(over="ignore"):
-        s16 = s32.astype(np.float16)
+        s16 = s.astype(np.float16)
     return np.where(np.isinf(s16), FP16_MAX, s16)
 
 
@@ -68,7 +69,7 @@ def quantize(w: np.ndarray, bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     mag = np.abs(g)
     one = b == 1
     if one.any():
-        mean = (mag[one].astype(np.float64).sum(axis=1) / 64.0).astype(np.float32)   # Q1
+        mean = mag[one].astype(np.float64).sum(axis=1) / 64.0                         # Q1
         scales[one] = _stored_scale(mean)
         codes[one] = np.where(g[one] < 0, -1, 1)                                      # Q3
     for width in (2, 4, 8):

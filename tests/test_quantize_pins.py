@@ -77,6 +77,18 @@ def test_one_bit_is_sign_and_mean_magnitude():
     assert s == 0.75 and list(codes[:4]) == [1, -1, 1, -1]
 
 
+def test_one_bit_scale_is_rounded_once_from_the_mean():
+    # M is the midpoint of two adjacent halves; 63 weights at M and one an fp32 ulp below
+    # give a mean of M - 2^-36: nearest half is the lower one, whereas rounding the mean
+    # to fp32 first lands on M and then ties to the even (upper) half
+    lo, hi = np.array([0x237F, 0x2380], np.uint16).view(np.float16).astype(np.float64)
+    mid = (lo + hi) / 2
+    vals = np.array([mid] * 63 + [mid - 2.0 ** -30], np.float32)
+    assert float(vals[0]) == mid and float(vals[63]) == mid - 2.0 ** -30
+    _, s = one_group(vals, 1)
+    assert s == lo == nearest_half(float(np.abs(vals.astype(np.float64)).sum() / 64))
+
+
 def test_ties_round_away_from_zero():
     # b = 4: largest magnitude 7 gives scale 1, so every ratio is the weight itself
     codes, s = one_group([7, 2.5, -2.5, 0.5, -0.5, 1.5, -1.5, 3.5, -3.5, 0.49], 4)
