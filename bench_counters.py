@@ -13,6 +13,8 @@ Kernel durations (`trace`):
 Kernel durations by kernel name (`kernels`), for any run, e.g. the LM head:
   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o kt5 -- python bench_configs.py --configs 5 --no-fp16
   python bench_counters.py kernels --csv <dir>/kt5_kernel_trace.csv --title "..." --command "..." --out <file>
+or the quantizer:
+  rocprofv3 --kernel-trace --stats -f csv -d <dir> -o qt -- python bench_quantize.py --passes 20 --warmup 3 --no-cpu-baseline
 
 HBM traffic (`traffic`), one rocprofv3 run per counter:
   rocprofv3 --pmc FETCH_SIZE -d <dir> -o fetch -- python bench.py --steps 5 --warmup 2 --only-timed
@@ -39,13 +41,14 @@ import statistics
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCE = os.path.join(ROOT, "decode_gemv_02_amd", "csrc", "vbq_device.hip")
+QUANTIZE_SOURCE = os.path.join(ROOT, "decode_gemv_02_amd", "csrc", "vbq_quantize.hip")
 LAUNCHES = ["q+k+v", "o", "gate+up", "down"]     # bench.py's launch order within a step
 GEMV_KERNEL = "gemv_tiles"
 COPY_KERNEL = "copyBuffer"
 
 
-def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -137,24 +140,34 @@ def trace_summary(a) -> str:
 
 
 def kernels_summary(a) -> str:
-    """Dispatch count and duration statistics per kernel name (VBQ kernels only)."""
+    """Dispatch count and duration statistics per kernel name and grid (VBQ kernels only).
+
+    For the quantizer every grid is one matrix shape: a workgroup of 256 lanes covers 64 groups of
+    64 weights, and each weight costs 5 + 3/64 algorithmic bytes (fp32 read, int8 code written, one
+    width byte read and one binary16 scale written per group), which gives alg_GBps."""
     per, meta = {}, {}
     with open(a.csv) as f:
         for row in csv.DictReader(f):
             name = row["Kernel_Name"]
-            if "gemv_tiles" not in name and "gemm_tiles" not in name and "unpack_tiles" not in name:
+            if not any(k in name for k in ("gemv_tiles", "gemm_tiles", "unpack_tiles", "quantize_groups")):
                 continue
-            per.setdefault(name, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0)
-            meta.setdefault(name, row)
-    lines = [f"# Kernel durations by kernel, {a.title}", "# command (repository root):", f"#   {a.command}",
+            key = (name, row["Grid_Size_X"], row["Grid_Size_Y"])
+            per.setdefault(key, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0)
+            meta.setdefault(key, row)
+    lines = [f"# Kernel durations by kernel and grid, {a.title}", "# command (repository root):", f"#   {a.command}",
              f"#   python bench_counters.py kernels --csv <dir>/<name>_kernel_trace.csv --out <this file>",
-             f"kernel_source_sha256: {kernel_source_sha()}"]
-    for name, d in per.items():
-        r = meta[name]
+             f"kernel_source_sha256: {kernel_source_sha()}",
+             f"quantize_source_sha256: {kernel_source_sha(QUANTIZE_SOURCE)}"]
+    for key, d in per.items():
+        name, r = key[0], meta[key]
         lines.append(f"kernel: {name} vgpr={r['VGPR_Count']} sgpr={r['SGPR_Count']} lds={r['LDS_Block_Size']} "
                      f"scratch={r['Scratch_Size']} grid={r['Grid_Size_X']}x{r['Grid_Size_Y']}")
+        extra = ""
+        if "quantize_groups" in name:
+            weights = int(r["Grid_Size_X"]) // 256 * 64 * 64
+            extra = f" weights={weights} alg_GBps={weights * (5 + 3 / 64) / (statistics.fmean(d) * 1e3):.1f}"
         lines.append(f"  dispatches={len(d)} avg_us={statistics.fmean(d):.3f} median_us={statistics.median(d):.3f} "
-                     f"min_us={min(d):.3f} max_us={max(d):.3f}")
+                     f"min_us={min(d):.3f} max_us={max(d):.3f}{extra}")
     return "\n".join(lines) + "\n"
 
 

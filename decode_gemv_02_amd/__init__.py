@@ -73,8 +73,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
     lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
+    lib.vbq_quantize.argtypes = [U32, U32, P, P, P, P, P]
+    lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
     for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
-              lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes):
+              lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -213,4 +215,26 @@ def vbq_unpack_codes(w: DeviceMatrix, out: torch.Tensor, stream=None) -> torch.T
     """Decoded int8 codes [n][k] (device)."""
     assert out.dtype == torch.int8 and out.is_contiguous() and out.numel() >= w.n * w.k
     _check(lib.vbq_unpack_codes(ctypes.byref(w.struct), out.data_ptr(), _stream_handle(stream, w.device)))
+    return out
+
+
+def vbq_quantize(w: torch.Tensor, bits: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
+                 stream=None):
+    """Eq. (1) per group on the device: w fp32 [n][k], bits uint8 [n][k/64] -> codes int8 [n][k]
+    and scales (int16 tensor holding binary16 bit patterns) [n][k/64]."""
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous()
+    n, k = w.shape
+    assert bits.dtype == torch.uint8 and bits.is_contiguous() and bits.numel() == n * (k // GROUP)
+    assert codes.dtype == torch.int8 and codes.is_contiguous() and codes.numel() >= n * k
+    assert scales.dtype == torch.int16 and scales.is_contiguous() and scales.numel() >= n * (k // GROUP)
+    _check(lib.vbq_quantize(n, k, w.data_ptr(), bits.data_ptr(), codes.data_ptr(), scales.data_ptr(),
+                            _stream_handle(stream, w.device)))
+    return codes, scales
+
+
+def vbq_recipe_head_bits(freq: np.ndarray) -> np.ndarray:
+    """Per-row widths of the frequency-tiered head (host, uint8 [rows])."""
+    freq = np.ascontiguousarray(freq, dtype=np.uint64).reshape(-1)
+    out = np.zeros(freq.size, np.uint8)
+    _check(lib.vbq_recipe_head_bits(freq.size, _np_ptr(freq), _np_ptr(out)))
     return out

@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libvbq.so")
-SOURCES = ["vbq_host.cpp", "vbq_device.hip"]
+SOURCES = ["vbq_host.cpp", "vbq_device.hip", "vbq_quantize.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

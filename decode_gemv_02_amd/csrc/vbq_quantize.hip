@@ -1,0 +1,145 @@
+// Per-group quantizer of the VBQ library (gfx950): fp32 weights -> the int8
+// codes and binary16 scales that vbq_pack takes.
+//
+// VBQ paper (arXiv 2607.02893) §3.1 Eq. (1): a group of 64 weights at b >= 2
+// bits has scale s = max|w| / (2^(b-1) - 1) and codes clip(round(w / s),
+// -(2^(b-1) - 1), 2^(b-1) - 1); at 1 bit a weight keeps its sign and the scale
+// is the group's mean magnitude. Where the pages leave a step open:
+//   - max|w|, the b >= 2 scale and the ratios are fp32 with correctly rounded
+//     division; the 1-bit magnitudes are summed in fp64 (exact for any
+//     realistic spread of magnitudes, so the order of the sum does not show)
+//     and divided by 64;
+//   - the stored scale is that value rounded once to binary16 (nearest even;
+//     the fp64 mean goes straight to binary16, with no fp32 step), saturated
+//     at 65504, and the codes are computed with the stored scale;
+//   - ties round away from zero; sign(0) = +1 (also -0.0); a stored scale of 0
+//     gives codes 0 at b >= 2.
+//
+// Work decomposition: a team of 16 lanes holds one group, four weights a
+// lane, so one wave reads four groups (1 KiB) per load; each team has four
+// groups' loads in flight before it reduces the first. The group's largest
+// magnitude or magnitude sum is reduced across its 16 lanes with
+// butterflies, so every lane ends with the same value and the same scale.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "vbq_internal.h"
+
+using vbq::fail;
+
+namespace {
+
+constexpr uint32_t kLanesPerGroup = 16;
+constexpr uint32_t kBlock = 256;
+constexpr uint32_t kTeams = kBlock / kLanesPerGroup;          // 16-lane teams per workgroup
+constexpr uint32_t kGroupsPerTeam = 4;                          // loads a team keeps in flight
+constexpr uint32_t kGroupsPerBlock = kTeams * kGroupsPerTeam;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// binary16 bits of a non-negative value, one rounding to nearest even, saturated at the largest finite half
+template <typename T>
+__device__ __forceinline__ uint16_t stored_scale(T s) {
+    const _Float16 h = static_cast<_Float16>(s);
+    const uint16_t bits = __builtin_bit_cast(uint16_t, h);
+    return (bits & 0x7FFFu) >= 0x7C00u ? 0x7BFFu : bits;
+}
+
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+    for (uint32_t d = 1; d < kLanesPerGroup; d <<= 1) v = fmaxf(v, __shfl_xor(v, d, kLanesPerGroup));
+    return v;
+}
+
+__device__ __forceinline__ double group_sum(double v) {
+#pragma unroll
+    for (uint32_t d = 1; d < kLanesPerGroup; d <<= 1) v += __shfl_xor(v, d, kLanesPerGroup);
+    return v;
+}
+
+// b >= 2: the code of w for stored scale s (binary16 value as fp32)
+__device__ __forceinline__ uint32_t code_of(float w, float s, float qmax) {
+    if (s == 0.f) return 0u;
+    const float q = fminf(fmaxf(roundf(__fdiv_rn(w, s)), -qmax), qmax);   // roundf: ties away from zero
+    return static_cast<uint32_t>(static_cast<int32_t>(q)) & 0xFFu;
+}
+
+// One lane's four weights of a group of width b: the packed int8 codes, and the group's scale in *s16
+// (every lane of the team computes the same scale).
+__device__ __forceinline__ uint32_t quantize_quad(float4 v, uint32_t b, uint16_t *s16) {
+    const float m0 = fabsf(v.x), m1 = fabsf(v.y), m2 = fabsf(v.z), m3 = fabsf(v.w);
+    if (b == 1) {
+        const double sum = group_sum(((static_cast<double>(m0) + m1) + m2) + m3);
+        *s16 = stored_scale(sum * (1.0 / 64.0));   // fp64 -> binary16 directly
+        // sign(w) as an int8 code, +1 for w >= 0 (and -0.0)
+        return (v.x < 0.f ? 0xFFu : 1u) | ((v.y < 0.f ? 0xFFu : 1u) << 8) | ((v.z < 0.f ? 0xFFu : 1u) << 16) |
+               ((v.w < 0.f ? 0xFFu : 1u) << 24);
+    }
+    if (b == 2 || b == 4 || b == 8) {
+        const float amax = group_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+        const float qmax = static_cast<float>((1u << (b - 1)) - 1u);
+        *s16 = stored_scale(__fdiv_rn(amax, qmax));
+        const float s = static_cast<float>(__builtin_bit_cast(_Float16, *s16));
+        return code_of(v.x, s, qmax) | (code_of(v.y, s, qmax) << 8) | (code_of(v.z, s, qmax) << 16) |
+               (code_of(v.w, s, qmax) << 24);
+    }
+    *s16 = 0;   // another width value leaves scale 0 and codes 0
+    return 0u;
+}
+
+// Workgroup x covers groups [x * kGroupsPerBlock, (x + 1) * kGroupsPerBlock): pass j hands group
+// x * kGroupsPerBlock + j * kTeams + team to a team, so each pass reads 4 KiB contiguous. All of a
+// team's loads are issued before the first reduction.
+__global__ __launch_bounds__(kBlock) void quantize_groups(const float4 *__restrict__ w, const uint8_t *__restrict__ bits,
+                                                         uint32_t *__restrict__ codes, uint16_t *__restrict__ scales,
+                                                         uint64_t groups) {
+    const uint32_t team = threadIdx.x / kLanesPerGroup, lane = threadIdx.x % kLanesPerGroup;
+    const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kGroupsPerBlock + team;
+    float4 v[kGroupsPerTeam];
+    uint32_t b[kGroupsPerTeam];
+#pragma unroll
+    for (uint32_t j = 0; j < kGroupsPerTeam; ++j) {
+        const uint64_t g = first + j * kTeams;   // team-uniform, so whole teams take each branch
+        if (g < groups) {
+            // each weight is read once: a non-temporal load keeps the stream out of the caches
+            const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(w) + g * kLanesPerGroup + lane);
+            v[j] = make_float4(t.x, t.y, t.z, t.w);
+            b[j] = bits[g];
+        }
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kGroupsPerTeam; ++j) {
+        const uint64_t g = first + j * kTeams;
+        if (g < groups) {
+            uint16_t s16;
+            codes[g * kLanesPerGroup + lane] = quantize_quad(v[j], b[j], &s16);
+            if (lane == 0) scales[g] = s16;
+        }
+    }
+}
+
+inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const uint8_t *bits, int8_t *codes_out,
+                                   uint16_t *scales_out, void *stream) {
+    vbq::clear_error();
+    if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_quantize: k=%u is not a multiple of 64", k);
+    if (n == 0 || k == 0) return VBQ_OK;
+    if (!w || !bits || !codes_out || !scales_out) return fail(VBQ_ERR_NULL, "vbq_quantize: a pointer is NULL");
+    if (!aligned(w, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 2))
+        return fail(VBQ_ERR_ALIGN, "vbq_quantize: w must be 16-byte, codes 4-byte and scales 2-byte aligned");
+    const uint64_t groups = static_cast<uint64_t>(n) * (k / VBQ_GROUP);
+    const uint64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+    if (blocks > 0x7FFFFFFFull) return fail(VBQ_ERR_SHAPE, "vbq_quantize: %llu groups exceed one launch",
+                                            static_cast<unsigned long long>(groups));
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(quantize_groups, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(w), bits,
+                       reinterpret_cast<uint32_t *>(codes_out), scales_out, groups);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_quantize: launch failed: %s", hipGetErrorString(e));
+    return VBQ_OK;
+}

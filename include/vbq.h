@@ -190,6 +190,34 @@ VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, u
  * SHAPE, ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, void *stream);
 
+/* Quantize fp32 weights group by group into the codes and scales vbq_pack
+ * takes (VBQ §3.1 Eq. (1); device, asynchronous on `stream`).
+ * w: device fp32 [n][k] row-major, 16-byte aligned, finite.
+ * bits: device uint8 [n*(k/64)], each group's width in {1, 2, 4, 8} (a group
+ *   with any other value gets scale 0 and codes 0).
+ * codes_out: device int8 [n][k] (4-byte aligned); scales_out: device
+ *   binary16 bit patterns [n*(k/64)] (2-byte aligned).
+ * b >= 2: s = max|w| / (2^(b-1) - 1) in fp32, stored as binary16 (nearest
+ *   even, saturated at 65504); q = clip(round(w / s), +-(2^(b-1) - 1)) with
+ *   the stored s, ties away from zero, and q = 0 if the stored s is 0.
+ * b = 1: s = the mean of |w| (summed in fp64, rounded once to binary16);
+ *   q = -1 for w < 0, else +1.
+ * The caller owns every buffer. Errors: SHAPE (k % 64, or more groups than
+ * one launch takes), NULL, ALIGN, HIP. */
+VBQ_API vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const uint8_t *bits, int8_t *codes_out,
+                                uint16_t *scales_out, void *stream);
+
+/* The fixed recipe's head widths (VBQ §3.4, host): one width per vocabulary
+ * row from its token frequency freq[rows]. Rows are ranked by descending
+ * frequency (ties: lower row first); with N rows, the first round(0.005 N)
+ * ranks get 8 bits, ranks up to round(0.02 N) 4 bits, up to round(0.12 N)
+ * 2 bits, the rest 1 bit (round = half up; a 32000-row head averages 1.18
+ * bits). Every group of row r then has width bits_out[r]. The projection
+ * recipe of the same section needs no call: first-block MLP projections
+ * (gate, up, down) at 4 bits, all other attention and MLP projections at 2.
+ * Errors: NULL (rows > 0 and a NULL pointer). */
+VBQ_API vbq_status vbq_recipe_head_bits(uint32_t rows, const uint64_t *freq, uint8_t *bits_out);
+
 /* Static English name of a status. */
 VBQ_API const char *vbq_status_string(vbq_status s);
 

@@ -1,4 +1,4 @@
-"""The GEMV kernels keep every live value in registers.
+"""The GEMV, unpack and quantizer kernels keep every live value in registers.
 
 A register spill puts a per-lane private segment in HBM: every wave then
 writes and re-reads it, which shows up as extra memory traffic of a few KiB
@@ -14,18 +14,20 @@ import pytest
 from decode_gemv_02_amd import build as B
 
 
-@pytest.fixture(scope="module")
-def assembly(tmp_path_factory):
-    out = tmp_path_factory.mktemp("asm") / "vbq_device.s"
-    src = os.path.join(B.CSRC, "vbq_device.hip")
+def _assembly(tmp_path_factory, name):
+    out = tmp_path_factory.mktemp("asm") / (name + ".s")
+    src = os.path.join(B.CSRC, name)
     flags = [f for f in B.FLAGS if f not in ("-shared", "-fPIC")]
     subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", src, "-o", str(out)], check=True,
                    stderr=subprocess.DEVNULL)
     return out.read_text()
 
 
-def test_kernels_do_not_spill(assembly):
+@pytest.mark.parametrize("source, kernel_names", [("vbq_device.hip", ("gemv_tiles", "unpack_tiles")),
+                                                  ("vbq_quantize.hip", ("quantize_groups",))])
+def test_kernels_do_not_spill(tmp_path_factory, source, kernel_names):
+    assembly = _assembly(tmp_path_factory, source)
     sizes = dict(re.findall(r"\.set (\S+)\.private_seg_size, (\d+)", assembly))
-    kernels = {k: int(v) for k, v in sizes.items() if "gemv_tiles" in k or "unpack_tiles" in k}
+    kernels = {k: int(v) for k, v in sizes.items() if any(n in k for n in kernel_names)}
     assert kernels, "no kernels found in the assembly"
     assert all(v == 0 for v in kernels.values()), kernels

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
-        "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_status_string", "vbq_last_error"])
+        "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize", "vbq_recipe_head_bits",
+        "vbq_status_string", "vbq_last_error"])
 
 
 def test_library_exports_every_declared_symbol(V):
@@ -199,3 +200,27 @@ def test_tile_count(V):
     assert V.vbq_tile_count(64, 320) == 2
     assert V.vbq_tile_count(4096, 14336) == 64 * 56
     assert V.vbq_tile_count(0, 256) == 0 and V.vbq_tile_count(5, 0) == 0
+
+
+def test_quantize_rejects_bad_arguments_without_launching(V):
+    buf = np.zeros(4096, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    assert V.lib.vbq_quantize(2, 100, base, base, base, base, None) == V.ERR_SHAPE
+    assert "multiple of 64" in V.lib.vbq_last_error().decode()
+    assert V.lib.vbq_quantize(0, 128, None, None, None, None, None) == V.OK     # nothing to do
+    assert V.lib.vbq_quantize(2, 0, None, None, None, None, None) == V.OK
+    assert V.lib.vbq_quantize(2, 128, None, base, base, base, None) == V.ERR_NULL
+    assert V.lib.vbq_quantize(2, 128, base, None, base, base, None) == V.ERR_NULL
+    assert V.lib.vbq_quantize(2, 128, base + 8, base, base, base, None) == V.ERR_ALIGN
+    assert V.lib.vbq_quantize(2, 128, base, base, base + 2, base, None) == V.ERR_ALIGN
+    assert V.lib.vbq_quantize(2, 128, base, base, base, base + 1, None) == V.ERR_ALIGN
+
+
+@pytest.mark.parametrize("rows", [0, 1, 7, 199, 200, 1000, 32000, 151936])
+def test_recipe_head_bits_matches_the_reference(V, rows):
+    from oracle import quantize as Q
+    rng = np.random.default_rng(rows)
+    # Zipf-like counts with many ties, so the tie rule decides tier edges
+    freq = np.minimum(rng.zipf(1.3, rows), 10 ** 6).astype(np.uint64)
+    assert np.array_equal(V.vbq_recipe_head_bits(freq), Q.head_bits(freq))
+    assert V.lib.vbq_recipe_head_bits(3, None, None) == V.ERR_NULL

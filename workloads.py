@@ -140,6 +140,17 @@ def draw_random_matrix(seed, n: int, k: int, mix=None):
     return draw_matrix(MatrixSpec("t", n, k, mix or STD_MIX, tuple(np.atleast_1d(seed).tolist())))
 
 
+def draw_weights(seed, n: int, k: int, sigma: float = 0.02, outlier_frac: float = 0.002) -> np.ndarray:
+    """fp32 weights [n, k] for the quantizer: N(0, sigma), with a small fraction of
+    entries scaled up 10-50x (the heavy tail trained projections show, which
+    is what sets a group's absmax)."""
+    rng = np.random.default_rng(np.random.SeedSequence(tuple(np.atleast_1d(seed).tolist()) + (104729,)))
+    w = rng.standard_normal((n, k), dtype=np.float32) * np.float32(sigma)
+    hit = rng.random((n, k), dtype=np.float32) < outlier_frac
+    w[hit] *= rng.uniform(10.0, 50.0, size=int(hit.sum())).astype(np.float32)
+    return w
+
+
 def draw_x(seed, k: int, m: int = 1) -> np.ndarray:
     """fp16 N(0,1) activations as uint16 bit patterns, shape [m, k]."""
     rng = np.random.default_rng(np.random.SeedSequence(tuple(np.atleast_1d(seed).tolist()) + (7919,)))
