@@ -30,7 +30,8 @@ TILE_ROWS = 64
 TILE_GROUPS = 4
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WIDTH, ERR_CODE, ERR_SCALE, ERR_CAPACITY, ERR_OFFSETS, ERR_ALIGN, \
-    ERR_TOO_LARGE, ERR_HIP, ERR_ABI = range(12)
+    ERR_TOO_LARGE, ERR_HIP, ERR_ABI, ERR_PADDING, ERR_FORMAT = range(14)
+CONTAINER_HEADER = 128
 
 
 class VbqSizes(ctypes.Structure):
@@ -75,8 +76,13 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
     lib.vbq_quantize.argtypes = [U32, U32, P, P, P, P, P]
     lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
+    lib.vbq_check_padding.argtypes = [ctypes.POINTER(VbqMatrix), U32, U32, U32]
+    lib.vbq_container_size.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(ctypes.c_uint64)]
+    lib.vbq_container_write.argtypes = [ctypes.POINTER(VbqMatrix), P, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
+    lib.vbq_container_open.argtypes = [P, ctypes.c_uint64, ctypes.POINTER(VbqMatrix)]
     for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
-              lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits):
+              lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
+              lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -238,3 +244,47 @@ def vbq_recipe_head_bits(freq: np.ndarray) -> np.ndarray:
     out = np.zeros(freq.size, np.uint8)
     _check(lib.vbq_recipe_head_bits(freq.size, _np_ptr(freq), _np_ptr(out)))
     return out
+
+
+def vbq_check_padding(m: HostMatrix, n_real: int, k_real: int, k_multiple: int = 512) -> None:
+    """Raises VbqError unless every padded row/column of m dequantizes to zero and k % k_multiple == 0."""
+    v = m.view()
+    _check(lib.vbq_check_padding(ctypes.byref(v), n_real, k_real, k_multiple))
+
+
+def vbq_container_bytes(m: HostMatrix) -> np.ndarray:
+    """The container image of m (uint8 array)."""
+    v = m.view()
+    size = ctypes.c_uint64()
+    _check(lib.vbq_container_size(ctypes.byref(v), ctypes.byref(size)))
+    out = np.zeros(size.value, np.uint8)
+    written = ctypes.c_uint64()
+    _check(lib.vbq_container_write(ctypes.byref(v), out.ctypes.data, out.size, ctypes.byref(written)))
+    return out
+
+
+def vbq_container_open(image: np.ndarray) -> HostMatrix:
+    """HostMatrix whose arrays are views into image (checked by the library first)."""
+    image = np.ascontiguousarray(image, dtype=np.uint8).reshape(-1)
+    v = VbqMatrix()
+    _check(lib.vbq_container_open(image.ctypes.data, image.size, ctypes.byref(v)))
+    base = image.ctypes.data
+    groups = v.n * (v.k // GROUP)
+
+    def part(ptr, count, dtype):
+        if not ptr or count == 0:
+            return np.zeros(0, dtype)
+        start = ptr - base
+        return image[start:start + count * np.dtype(dtype).itemsize].view(dtype)
+
+    tiles = vbq_tile_count(v.n, v.k)
+    return HostMatrix(v.n, v.k, part(v.widths, (groups + 3) // 4, np.uint8), part(v.scales, groups, np.uint16),
+                      part(v.tile_offsets, tiles + 1, np.uint32), part(v.payload, v.payload_bytes, np.uint8))
+
+
+def vbq_save(path: str, m: HostMatrix) -> None:
+    vbq_container_bytes(m).tofile(path)
+
+
+def vbq_load(path: str) -> HostMatrix:
+    return vbq_container_open(np.fromfile(path, dtype=np.uint8))

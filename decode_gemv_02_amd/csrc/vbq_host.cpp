@@ -70,6 +70,8 @@ extern "C" const char *vbq_status_string(vbq_status s) {
         case VBQ_ERR_TOO_LARGE: return "payload exceeds 32-bit offsets";
         case VBQ_ERR_HIP: return "HIP runtime error";
         case VBQ_ERR_ABI: return "ABI version mismatch";
+        case VBQ_ERR_PADDING: return "padding not inert";
+        case VBQ_ERR_FORMAT: return "bad container";
     }
     return "unknown status";
 }
@@ -270,5 +272,184 @@ extern "C" vbq_status vbq_recipe_head_bits(uint32_t rows, const uint64_t *freq, 
                    cut2 = (120ull * rows + 500) / 1000;
     for (uint64_t rank = 0; rank < rows; ++rank)
         bits_out[order[rank]] = rank < cut8 ? 8 : rank < cut4 ? 4 : rank < cut2 ? 2 : 1;
+    return VBQ_OK;
+}
+
+namespace {
+
+// Code of element i of a group from its packed bytes: b = 1 gives +-1, b >= 2 two's complement.
+int32_t packed_code(uint32_t b, const uint8_t *src, uint32_t i) {
+    const uint32_t bit = field_pos(b, i);
+    const uint32_t f = (src[bit >> 3] >> (bit & 7)) & ((1u << b) - 1u);
+    if (b == 1) return f ? -1 : 1;
+    return f >= (1u << (b - 1)) ? int32_t(f) - int32_t(1u << b) : int32_t(f);
+}
+
+}  // namespace
+
+// VBQ §6, "Granularity is deployment-friendly": padded MLP channels must be
+// inert, i.e. every padded weight dequantizes to exactly zero.
+extern "C" vbq_status vbq_check_padding(const vbq_matrix *w, uint32_t n_real, uint32_t k_real, uint32_t k_multiple) {
+    const vbq_status st = vbq_validate_host(w);
+    if (st != VBQ_OK) return st;
+    if (k_multiple == 0) return fail(VBQ_ERR_SHAPE, "vbq_check_padding: k_multiple is 0");
+    if (w->k % k_multiple)
+        return fail(VBQ_ERR_SHAPE, "vbq_check_padding: k=%u is not a multiple of %u", w->k, k_multiple);
+    if (n_real > w->n || k_real > w->k)
+        return fail(VBQ_ERR_SHAPE, "vbq_check_padding: real %ux%u exceeds the packed %ux%u", n_real, k_real, w->n,
+                    w->k);
+    const uint32_t G = w->k / VBQ_GROUP;
+    std::vector<uint64_t> off(uint64_t(w->n) * G);
+    auto width = [&](uint32_t r, uint32_t j) {
+        const uint64_t m = meta_slot(w->n, G, r, j);
+        return 1u << ((w->widths[m >> 2] >> (2 * (m & 3))) & 3u);
+    };
+    place_groups(w->n, G, width, off.data(), nullptr);
+    for (uint32_t r = 0; r < w->n; ++r)
+        for (uint32_t j = 0; j < G; ++j) {
+            if (r < n_real && (j + 1) * VBQ_GROUP <= k_real) continue;   // no padded weight in this group
+            const uint64_t m = meta_slot(w->n, G, r, j);
+            if ((w->scales[m] & 0x7FFFu) == 0) continue;                   // scale +-0: the whole group is zero
+            const uint32_t b = width(r, j);
+            for (uint32_t i = 0; i < VBQ_GROUP; ++i) {
+                const uint32_t c = j * VBQ_GROUP + i;
+                if (r < n_real && c < k_real) continue;
+                if (packed_code(b, w->payload + off[uint64_t(r) * G + j], i) != 0)
+                    return fail(VBQ_ERR_PADDING, "vbq_check_padding: weight (%u, %u) is padding but not zero", r, c);
+            }
+        }
+    return VBQ_OK;
+}
+
+// ------------------------------------------------------------------ container
+
+namespace {
+
+constexpr char kMagic[8] = {'V', 'B', 'Q', 'P', 'A', 'C', 'K', '\0'};
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// CRC-32 of IEEE 802.3 (reflected polynomial 0xEDB88320, initial and final complement).
+uint32_t crc32(const uint8_t *p, uint64_t len) {
+    static uint32_t table[256];
+    static const bool ready = [] {
+        for (uint32_t i = 0; i < 256; ++i) {
+            uint32_t c = i;
+            for (int k = 0; k < 8; ++k) c = (c & 1) ? 0xEDB88320u ^ (c >> 1) : c >> 1;
+            table[i] = c;
+        }
+        return true;
+    }();
+    (void)ready;
+    uint32_t c = 0xFFFFFFFFu;
+    for (uint64_t i = 0; i < len; ++i) c = table[(c ^ p[i]) & 0xFFu] ^ (c >> 8);
+    return c ^ 0xFFFFFFFFu;
+}
+
+struct Layout {
+    uint64_t widths, scales, offsets, payload, total;   // offsets into the image
+    uint64_t widths_bytes, scales_bytes, offsets_bytes, payload_bytes;
+};
+
+Layout layout_of(uint32_t n, uint32_t k, uint64_t payload_bytes) {
+    const uint64_t groups = uint64_t(n) * (k / VBQ_GROUP);
+    Layout L{};
+    L.widths_bytes = (groups + 3) / 4;
+    L.scales_bytes = 2 * groups;
+    L.offsets_bytes = 4 * (tiles_of(n, k / VBQ_GROUP) + 1);
+    L.payload_bytes = payload_bytes;
+    L.widths = align_up(VBQ_CONTAINER_HEADER);
+    L.scales = align_up(L.widths + L.widths_bytes);
+    L.offsets = align_up(L.scales + L.scales_bytes);
+    L.payload = align_up(L.offsets + L.offsets_bytes);
+    L.total = L.payload + L.payload_bytes;
+    return L;
+}
+
+template <class T> void put(uint8_t *h, uint32_t at, T v) { std::memcpy(h + at, &v, sizeof v); }
+template <class T> T get(const uint8_t *h, uint32_t at) { T v; std::memcpy(&v, h + at, sizeof v); return v; }
+
+}  // namespace
+
+extern "C" vbq_status vbq_container_size(const vbq_matrix *w, uint64_t *bytes_out) {
+    vbq::clear_error();
+    if (!w || !bytes_out) return fail(VBQ_ERR_NULL, "vbq_container_size: a pointer is NULL");
+    if (w->abi_version != VBQ_ABI_VERSION)
+        return fail(VBQ_ERR_ABI, "vbq_container_size: abi_version %u, library %u", w->abi_version, VBQ_ABI_VERSION);
+    if (w->k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_container_size: k=%u is not a multiple of 64", w->k);
+    *bytes_out = layout_of(w->n, w->k, w->payload_bytes).total;
+    return VBQ_OK;
+}
+
+extern "C" vbq_status vbq_container_write(const vbq_matrix *w, uint8_t *out, uint64_t capacity, uint64_t *written) {
+    const vbq_status st = vbq_validate_host(w);
+    if (st != VBQ_OK) return st;
+    if (!out || !written) return fail(VBQ_ERR_NULL, "vbq_container_write: a pointer is NULL");
+    const Layout L = layout_of(w->n, w->k, w->payload_bytes);
+    if (capacity < L.total)
+        return fail(VBQ_ERR_CAPACITY, "vbq_container_write: needs %llu bytes, capacity %llu",
+                    (unsigned long long)L.total, (unsigned long long)capacity);
+    std::memset(out, 0, L.total);
+    std::memcpy(out, kMagic, 8);
+    put<uint32_t>(out, 8, VBQ_CONTAINER_VERSION);
+    put<uint32_t>(out, 12, VBQ_CONTAINER_HEADER);
+    put<uint32_t>(out, 16, w->n);
+    put<uint32_t>(out, 20, w->k);
+    put<uint32_t>(out, 24, VBQ_GROUP);
+    put<uint32_t>(out, 28, VBQ_TILE_ROWS);
+    put<uint32_t>(out, 32, VBQ_TILE_GROUPS);
+    put<uint32_t>(out, 36, w->payload_bytes);
+    put<uint64_t>(out, 40, L.widths);
+    put<uint64_t>(out, 48, L.scales);
+    put<uint64_t>(out, 56, L.offsets);
+    put<uint64_t>(out, 64, L.payload);
+    put<uint64_t>(out, 72, L.total);
+    if (L.widths_bytes) std::memcpy(out + L.widths, w->widths, L.widths_bytes);
+    if (L.scales_bytes) std::memcpy(out + L.scales, w->scales, L.scales_bytes);
+    std::memcpy(out + L.offsets, w->tile_offsets, L.offsets_bytes);
+    if (L.payload_bytes) std::memcpy(out + L.payload, w->payload, L.payload_bytes);
+    put<uint32_t>(out, 80, crc32(out + VBQ_CONTAINER_HEADER, L.total - VBQ_CONTAINER_HEADER));
+    put<uint32_t>(out, 84, crc32(out, 84));
+    *written = L.total;
+    return VBQ_OK;
+}
+
+extern "C" vbq_status vbq_container_open(const uint8_t *buf, uint64_t len, vbq_matrix *view) {
+    vbq::clear_error();
+    if (!buf || !view) return fail(VBQ_ERR_NULL, "vbq_container_open: a pointer is NULL");
+    if (len < VBQ_CONTAINER_HEADER)
+        return fail(VBQ_ERR_FORMAT, "vbq_container_open: %llu bytes, shorter than the header",
+                    (unsigned long long)len);
+    if (std::memcmp(buf, kMagic, 8) != 0) return fail(VBQ_ERR_FORMAT, "vbq_container_open: bad magic");
+    if (crc32(buf, 84) != get<uint32_t>(buf, 84)) return fail(VBQ_ERR_FORMAT, "vbq_container_open: header checksum");
+    if (get<uint32_t>(buf, 8) != VBQ_CONTAINER_VERSION)
+        return fail(VBQ_ERR_FORMAT, "vbq_container_open: format version %u, library reads %u", get<uint32_t>(buf, 8),
+                    VBQ_CONTAINER_VERSION);
+    const uint32_t n = get<uint32_t>(buf, 16), k = get<uint32_t>(buf, 20);
+    if (get<uint32_t>(buf, 12) != VBQ_CONTAINER_HEADER || get<uint32_t>(buf, 24) != VBQ_GROUP ||
+        get<uint32_t>(buf, 28) != VBQ_TILE_ROWS || get<uint32_t>(buf, 32) != VBQ_TILE_GROUPS || k % VBQ_GROUP)
+        return fail(VBQ_ERR_FORMAT, "vbq_container_open: layout constants or k=%u differ from the library's", k);
+    const Layout L = layout_of(n, k, get<uint32_t>(buf, 36));
+    if (get<uint64_t>(buf, 40) != L.widths || get<uint64_t>(buf, 48) != L.scales ||
+        get<uint64_t>(buf, 56) != L.offsets || get<uint64_t>(buf, 64) != L.payload || get<uint64_t>(buf, 72) != L.total)
+        return fail(VBQ_ERR_FORMAT, "vbq_container_open: array offsets disagree with n=%u, k=%u", n, k);
+    if (L.total > len)
+        return fail(VBQ_ERR_FORMAT, "vbq_container_open: needs %llu bytes, image has %llu",
+                    (unsigned long long)L.total, (unsigned long long)len);
+    if (crc32(buf + VBQ_CONTAINER_HEADER, L.total - VBQ_CONTAINER_HEADER) != get<uint32_t>(buf, 80))
+        return fail(VBQ_ERR_FORMAT, "vbq_container_open: body checksum");
+    vbq_matrix v{};
+    v.abi_version = VBQ_ABI_VERSION;
+    v.n = n;
+    v.k = k;
+    v.payload_bytes = uint32_t(L.payload_bytes);
+    v.widths = L.widths_bytes ? buf + L.widths : nullptr;
+    v.scales = L.scales_bytes ? reinterpret_cast<const uint16_t *>(buf + L.scales) : nullptr;
+    v.tile_offsets = reinterpret_cast<const uint32_t *>(buf + L.offsets);
+    v.payload = L.payload_bytes ? buf + L.payload : nullptr;
+    const vbq_status st = vbq_validate_host(&v);
+    if (st != VBQ_OK) return st;
+    *view = v;
     return VBQ_OK;
 }

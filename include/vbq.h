@@ -98,7 +98,9 @@ typedef enum vbq_status {
     VBQ_ERR_ALIGN = 8,      /* a device pointer is not 16-byte aligned */
     VBQ_ERR_TOO_LARGE = 9,  /* payload would not fit 32-bit offsets */
     VBQ_ERR_HIP = 10,       /* the HIP runtime refused a launch */
-    VBQ_ERR_ABI = 11        /* vbq_matrix.abi_version != VBQ_ABI_VERSION */
+    VBQ_ERR_ABI = 11,       /* vbq_matrix.abi_version != VBQ_ABI_VERSION */
+    VBQ_ERR_PADDING = 12,   /* a padded row or column does not dequantize to zero */
+    VBQ_ERR_FORMAT = 13     /* a container's header, sizes or checksum is wrong */
 } vbq_status;
 
 /* Byte sizes of the four packed arrays. */
@@ -217,6 +219,55 @@ VBQ_API vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const ui
  * (gate, up, down) at 4 bits, all other attention and MLP projections at 2.
  * Errors: NULL (rows > 0 and a NULL pointer). */
 VBQ_API vbq_status vbq_recipe_head_bits(uint32_t rows, const uint64_t *freq, uint8_t *bits_out);
+
+/* Export-time check of the padding contract (VBQ §6, "Granularity is
+ * deployment-friendly": MLP intermediates are zero-padded so the contracted
+ * dimension is a multiple of 512; padded channels are inert because
+ * silu(0) * u = 0). Host pointers. Passes when the matrix validates
+ * (vbq_validate_host), k is a multiple of k_multiple, n_real <= n,
+ * k_real <= k, and every weight in a padded row (r >= n_real) or padded
+ * column (c >= k_real) dequantizes to exactly zero: its group's scale is
+ * +-0, or its code is 0 (so a 1-bit group touching the padding needs scale
+ * 0). Errors: those of vbq_validate_host; SHAPE (k_multiple == 0, k not a
+ * multiple of it, n_real > n or k_real > k); PADDING (the first non-zero
+ * padded weight is named by vbq_last_error). */
+VBQ_API vbq_status vbq_check_padding(const vbq_matrix *host_view, uint32_t n_real, uint32_t k_real,
+                                     uint32_t k_multiple);
+
+/* Versioned container: one packed matrix as one byte image (a file's
+ * contents), little-endian.
+ *   bytes 0-7    magic "VBQPACK" and a zero byte
+ *   8  u32 format version (VBQ_CONTAINER_VERSION)
+ *   12 u32 header bytes (128)
+ *   16 u32 n, 20 u32 k, 24 u32 group size (64), 28 u32 tile rows (64),
+ *   32 u32 tile groups (4), 36 u32 payload_bytes
+ *   40 u64 widths offset, 48 u64 scales offset, 56 u64 tile_offsets offset,
+ *   64 u64 payload offset, 72 u64 total bytes
+ *   80 u32 CRC-32 (IEEE 802.3) of bytes [128, total), 84 u32 CRC-32 of
+ *   bytes [0, 84); the rest of the header is zero.
+ * The four arrays follow at 256-byte aligned offsets, in that order, with
+ * zero bytes between them, so one contiguous upload keeps every array
+ * aligned for the device entry points. */
+#define VBQ_CONTAINER_VERSION 1u
+#define VBQ_CONTAINER_HEADER 128u
+
+/* Bytes the container of w takes. Host pointers are not read. Errors: NULL,
+ * ABI, SHAPE (k % 64). */
+VBQ_API vbq_status vbq_container_size(const vbq_matrix *host_view, uint64_t *bytes_out);
+
+/* Write w (host pointers, validated first) into out[0, capacity); the
+ * caller owns out. *written = the container size. Errors: those of
+ * vbq_validate_host; NULL; CAPACITY (capacity below the container size). */
+VBQ_API vbq_status vbq_container_write(const vbq_matrix *host_view, uint8_t *out, uint64_t capacity,
+                                       uint64_t *written);
+
+/* Check a container image buf[0, len) and fill *view_out with pointers into
+ * buf (no copy; buf must outlive the view). Checks the magic, version,
+ * layout constants, that every array lies inside buf at its aligned offset
+ * with the sizes n and k give, both checksums, and then runs
+ * vbq_validate_host on the view. Errors: NULL; FORMAT (header, sizes or
+ * checksum); those of vbq_validate_host. */
+VBQ_API vbq_status vbq_container_open(const uint8_t *buf, uint64_t len, vbq_matrix *view_out);
 
 /* Static English name of a status. */
 VBQ_API const char *vbq_status_string(vbq_status s);

@@ -142,3 +142,34 @@ def test_quantize_pack_gemv_end_to_end(V):
     rc, rs = Q.quantize(w, Q.head_bits(freq)[:, None].repeat(k // 64, axis=1))
     y_ref = oracle.gemv(oracle.pack(n, k, bits, rc, rs), x[0])
     assert_within_tolerance(y.cpu().numpy()[None], y_ref[None], x, rs, "quantize-pack-gemv")
+
+
+def test_padded_and_container_matrices_on_device(V):
+    # a down projection with an awkward intermediate (8960) zero-padded to a multiple of 512 (9216):
+    # the padded columns meet zero activations, so y matches the unpadded product
+    import torch
+    n, k_real, k = 1536, 8960, 9216
+    print_case(test="padded_down", n=n, k_real=k_real, k=k)
+    w = np.zeros((n, k), np.float32)
+    w[:, :k_real] = W.draw_weights((51,), n, k_real)
+    bits = np.full((n, k // 64), 2, np.uint8)
+    codes, scales = gpu_quantize(V, w, bits)
+    hp = V.vbq_pack(n, k, bits, codes, scales)
+    V.vbq_check_padding(hp, n, k_real, 512)
+    hr = V.vbq_pack(n, k_real, bits[:, :k_real // 64], np.ascontiguousarray(codes[:, :k_real]),
+                    np.ascontiguousarray(scales[:, :k_real // 64]))
+    x = np.zeros((1, k), np.uint16)
+    x[:, :k_real] = W.draw_x((52,), k_real)
+    ys = []
+    for h, kk in ((hp, k), (hr, k_real), (V.vbq_container_open(V.vbq_container_bytes(hp)), k)):
+        dm = V.DeviceMatrix(h)
+        xt = torch.from_numpy(np.ascontiguousarray(x[:, :kk]).view(np.float16)).cuda()
+        y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        V.vbq_gemv(dm, xt[0], y)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    rc, rs = Q.quantize(w[:, :k_real], bits[:, :k_real // 64])
+    y_ref = oracle.gemv(oracle.pack(n, k_real, bits[:, :k_real // 64], rc, rs), x[0, :k_real])
+    assert_within_tolerance(ys[0][None], y_ref[None], x, rs, "padded")
+    assert_within_tolerance(ys[1][None], y_ref[None], x, rs, "unpadded")
+    assert np.array_equal(ys[0], ys[2])      # a matrix read back from its container runs identically
