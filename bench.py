@@ -192,6 +192,39 @@ def main():
         "all_seven_one_launch": {"ms_per_step": round(one, 5), "GBps": round(layer_bytes / (one * 1e-3) / 1e9, 2)},
         "seven_launches": {"ms_per_step": round(sep, 5), "GBps": round(layer_bytes / (sep * 1e-3) / 1e9, 2)}}
 
+    # ---- the same step with the gated-MLP epilogue fused: gate+up write h = fp16(silu(g) * u) in their
+    # launch and down reads h, so the step's data flow is the decoder layer's own
+    gi_gate = [s.name.split(".")[-1] for s in specs].index("gate")
+    gi_up, gi_down = gi_gate + 1, gi_gate + 2
+    hbuf = torch.empty(specs[gi_gate].n, dtype=torch.float16, device=dev)
+
+    def fused_step(i):
+        layer = dev_layers[i % copies]
+        V.vbq_gemv_multi(layer[0:3], xin[0:3], ys[0:3], stream)
+        V.vbq_gemv(layer[3], xin[3], ys[3], stream)
+        V.vbq_gemv_swiglu(layer[gi_gate], layer[gi_up], xin[gi_gate], hbuf, stream)
+        V.vbq_gemv(layer[gi_down], hbuf, ys[gi_down], stream)
+
+    def torch_epilogue_step(i):
+        layer = dev_layers[i % copies]
+        V.vbq_gemv_multi(layer[0:3], xin[0:3], ys[0:3], stream)
+        V.vbq_gemv(layer[3], xin[3], ys[3], stream)
+        V.vbq_gemv_multi([layer[gi_gate], layer[gi_up]], [xin[gi_gate]] * 2, [ys[gi_gate], ys[gi_up]], stream)
+        torch.mul(torch.nn.functional.silu(ys[gi_gate]), ys[gi_up], out=hbuf32)
+        hbuf.copy_(hbuf32)
+        V.vbq_gemv(layer[gi_down], hbuf, ys[gi_down], stream)
+
+    hbuf32 = torch.empty(specs[gi_gate].n, dtype=torch.float32, device=dev)
+    fused = timed(fused_step)
+    unfused = timed(torch_epilogue_step)
+    gu = timed(lambda i: V.vbq_gemv_swiglu(dev_layers[i % copies][gi_gate], dev_layers[i % copies][gi_up],
+                                           xin[gi_gate], hbuf, stream))
+    result["fused_mlp_step"] = {
+        "launches": "q+k+v | o | gate+up -> h = fp16(silu(g)*u) (vbq_gemv_swiglu) | down(h)",
+        "ms_per_step": round(fused, 5), "GBps": round(layer_bytes / (fused * 1e-3) / 1e9, 2),
+        "gate_up_swiglu_alone_us": round(gu * 1e3, 3),
+        "with_torch_epilogue_ms_per_step": round(unfused, 5)}
+
     # ---- dense fp16 GEMV of the same shapes (torch matmul on the same stream, rotated copies)
     if not args.no_fp16_baseline:
         dense_bytes = sum(2 * s.n * s.k for s in specs)

@@ -72,6 +72,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_gemv_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P), ctypes.POINTER(P),
                                    U32, P]
     lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
+    lib.vbq_gemv_swiglu.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(VbqMatrix), P, P, P]
     lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
     lib.vbq_quantize.argtypes = [U32, U32, P, P, P, P, P]
@@ -82,7 +83,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_container_open.argtypes = [P, ctypes.c_uint64, ctypes.POINTER(VbqMatrix)]
     for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
-              lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open):
+              lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
+              lib.vbq_gemv_swiglu):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -187,6 +189,16 @@ def vbq_gemv(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> 
     assert x.is_contiguous() and y.is_contiguous() and x.numel() == w.k and y.numel() >= w.n
     _check(lib.vbq_gemv(ctypes.byref(w.struct), x.data_ptr(), y.data_ptr(), _stream_handle(stream, w.device)))
     return y
+
+
+def vbq_gemv_swiglu(gate: DeviceMatrix, up: DeviceMatrix, x: torch.Tensor, h: torch.Tensor,
+                    stream=None) -> torch.Tensor:
+    """h[n] (fp16) = silu(gate x) * (up x), x fp16 [k]; one launch."""
+    assert x.dtype == torch.float16 and h.dtype == torch.float16 and x.is_contiguous() and h.is_contiguous()
+    assert x.numel() == gate.k and h.numel() >= gate.n
+    _check(lib.vbq_gemv_swiglu(ctypes.byref(gate.struct), ctypes.byref(up.struct), x.data_ptr(), h.data_ptr(),
+                               _stream_handle(stream, gate.device)))
+    return h
 
 
 def vbq_tile_count(n: int, k: int) -> int:

@@ -180,6 +180,11 @@ struct MatArgs {
 // matrix's arguments with one scalar load and no search.
 struct Batch {
     MatArgs m[VBQ_MAX_MULTI];
+    // Gated-MLP epilogue, when h is set: matrix 0 is gate and matrix 1 is up
+    // (same n), and instead of y the launch writes h = fp16(silu(g) * u).
+    uint16_t *h;
+    float *pair;              // [2][n]: each row tile's finished g and u values
+    uint32_t *pair_counters;  // [row tiles] arrival counters (self-resetting)
 };
 
 // 4992 bytes per wave: eight 4-wave, four 8-wave or two 16-wave workgroups
@@ -555,6 +560,34 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, rsrc_
         task8(L, l8[e >> 2], e & 3u, buf_load8(tile, o8 + 16u * e), buf_load8(tile, o8 + 16u * e + 8u));
 }
 
+// fp16 bits of silu(g) * u = g * u / (1 + e^-g), rounded to nearest even (beyond the fp16 range: +-inf)
+__device__ __forceinline__ uint16_t swiglu_half(float g, float u) {
+    const float v = g * u / (1.f + expf(-g));
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+
+// Gated-MLP epilogue of one finished row tile (wave 0 of the tile's last
+// workgroup; which = 0 for gate, 1 for up): publish the tile's values, count
+// arrivals per row tile; the second of the two tiles reads the other's values
+// and writes h, then resets the counter. Same publication protocol as the
+// split-K partial sums.
+__device__ __forceinline__ void swiglu_pair(const Batch &B, uint32_t which, uint32_t a, uint32_t row, bool live,
+                                            uint32_t n, uint32_t lane, float v) {
+    if (live) __hip_atomic_store(&B.pair[static_cast<uint64_t>(which) * n + row], v, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    uint32_t arrived = 0;
+    if (lane == 0) arrived = __hip_atomic_fetch_add(&B.pair_counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    arrived = __shfl(arrived, 0, kWave);
+    if (arrived != 1) return;
+    if (live) {
+        const float o = __hip_atomic_load(&B.pair[static_cast<uint64_t>(1 - which) * n + row], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        B.h[row] = which == 0 ? swiglu_half(v, o) : swiglu_half(o, v);
+    }
+    if (lane == 0) __hip_atomic_store(&B.pair_counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // kWaves waves per workgroup (4, 8 or 16) share one row tile; the LDS
 // (4992 B per wave) allows 8, 4 or 2 such workgroups per CU, eight waves
 // per SIMD, and the registers are held to the 64 that allow the same.
@@ -617,23 +650,27 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     float sum = lds[0].part[lane];
 #pragma unroll
     for (uint32_t w = 1; w < kWaves; ++w) sum += lds[w].part[lane];   // in wave order
-    if (M.splits == 1) {
+    if (M.splits > 1) {
+        // Split row tile: publish the partial sums with coherent (agent-scope) stores,
+        // wait until they have landed, then count arrivals; the last workgroup adds
+        // the partials in split order and resets the counter for the next call.
+        if (lane < rows)
+            __hip_atomic_store(&M.partial[static_cast<uint64_t>(split) * M.n + r0 + lane], sum, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t arrived = 0;
+        if (lane == 0)
+            arrived = __hip_atomic_fetch_add(&M.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __shfl(arrived, 0, kWave);
+        if (arrived != M.splits - 1) return;
+        if (lane < rows) sum = sum_partials(M.partial + r0 + lane, M.n, M.splits);
+        if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!B.h) {
         if (lane < rows) M.y[r0 + lane] = sum;
         return;
     }
-    // Split row tile: publish the partial sums with coherent (agent-scope) stores,
-    // wait until they have landed, then count arrivals; the last workgroup adds
-    // the partials in split order and resets the counter for the next call.
-    if (lane < rows)
-        __hip_atomic_store(&M.partial[static_cast<uint64_t>(split) * M.n + r0 + lane], sum, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    uint32_t arrived = 0;
-    if (lane == 0) arrived = __hip_atomic_fetch_add(&M.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    arrived = __shfl(arrived, 0, kWave);
-    if (arrived != M.splits - 1) return;
-    if (lane < rows) M.y[r0 + lane] = sum_partials(M.partial + r0 + lane, M.n, M.splits);
-    if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    swiglu_pair(B, blockIdx.y, a, r0 + lane, lane < rows, M.n, lane, sum);
 }
 
 // Decoded codes of every group, written at its natural position; the same
@@ -723,6 +760,11 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
 __global__ void fill_zero(float *__restrict__ y, uint64_t count) {
     const uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < count) y[i] = 0.f;
+}
+
+__global__ void fill_zero_u16(uint16_t *__restrict__ h, uint64_t count) {
+    const uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < count) h[i] = 0;
 }
 
 // ---------------------------------------------------------------- small batch on the matrix cores
@@ -1275,9 +1317,11 @@ void gemv_dispatch(bool aligned, uint32_t blocks, uint32_t used, const Batch &B,
         hipLaunchKernelGGL((gemv_tiles<false, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0, stream, B);
 }
 
-// One launch for up to VBQ_MAX_MULTI independent GEMVs.
+// One launch for up to VBQ_MAX_MULTI independent GEMVs; with h set, the two
+// matrices are gate and up (same shape, k > 0) and the launch writes
+// h = fp16(silu(gate x) * (up x)) instead of y.
 vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
-                       uint32_t count, hipStream_t stream) {
+                       uint32_t count, hipStream_t stream, uint16_t *h = nullptr) {
     Batch B{};
     uint32_t blocks = 0, total_row_tiles = 0, max_col_tiles = 0;
     bool aligned = true;
@@ -1323,6 +1367,10 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         }
     }
     if (used == 0) return any_launch ? launched(who) : VBQ_OK;
+    if (h) {   // the pair region follows the split regions
+        counter_slots += ceil_div(B.m[0].n, kTileRows);
+        partial_total += partial_bytes(2, B.m[0].n);
+    }
     if (counter_slots) {
         uint32_t *ctr = nullptr;
         char *part = nullptr;
@@ -1335,6 +1383,11 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
             ctr += ceil_div(M.n, kTileRows);
             M.partial = reinterpret_cast<float *>(part);
             part += partial_bytes(M.splits, M.n);
+        }
+        if (h) {
+            B.h = h;
+            B.pair_counters = ctr;
+            B.pair = reinterpret_cast<float *>(part);
         }
     }
     if (plan.waves == 16)
@@ -1410,6 +1463,32 @@ extern "C" vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t
     }
     (void)hipGetLastError();
     return gemv_launch(who, ws, xs, ys, count, static_cast<hipStream_t>(stream));
+}
+
+extern "C" vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *up, const uint16_t *x, uint16_t *h,
+                                      void *stream) {
+    vbq::clear_error();
+    const char *who = "vbq_gemv_swiglu";
+    vbq_status st = check_matrix(who, gate);
+    if (st != VBQ_OK) return st;
+    st = check_matrix(who, up);
+    if (st != VBQ_OK) return st;
+    if (gate->n != up->n || gate->k != up->k)
+        return fail(VBQ_ERR_SHAPE, "%s: gate is %ux%u, up is %ux%u", who, gate->n, gate->k, up->n, up->k);
+    if (gate->n == 0) return VBQ_OK;
+    if (!h || (gate->k && !x)) return fail(VBQ_ERR_NULL, "%s: x or h is NULL", who);
+    if (!aligned16(h) || (gate->k && !aligned16(x)))
+        return fail(VBQ_ERR_ALIGN, "%s: x or h is not 16-byte aligned", who);
+    (void)hipGetLastError();
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gate->k == 0) {   // g = u = 0, so h = silu(0) * 0 = 0
+        hipLaunchKernelGGL(fill_zero_u16, dim3((gate->n + 255) / 256), dim3(256), 0, s, h, uint64_t(gate->n));
+        return launched(who);
+    }
+    const vbq_matrix *ws[2] = {gate, up};
+    const uint16_t *xs[2] = {x, x};
+    float *ys[2] = {nullptr, nullptr};
+    return gemv_launch(who, ws, xs, ys, 2, s, h);
 }
 
 extern "C" vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream) {

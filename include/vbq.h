@@ -175,6 +175,21 @@ VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, vo
 VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                                   uint32_t count, void *stream);
 
+/* Gated-MLP front half in one launch (VBQ §6, "Granularity is
+ * deployment-friendly", states the gated form silu(g) * u of the MLP
+ * intermediates): g = gate x and u = up x exactly as vbq_gemv computes them
+ * (fp32, same order of sums), then h[r] = fp16(g[r] * u[r] / (1 + e^-g[r])),
+ * rounded to nearest even (beyond the fp16 range: +-inf). The launch writes
+ * h itself; g and u stay in the library's scratch. h is the fp16 input of
+ * the down projection's vbq_gemv.
+ * gate, up: device views of one shape n x k. x: device binary16 [k]; h:
+ * device binary16 [n]; both 16-byte aligned; the caller owns them. k == 0
+ * writes h = 0. Scratch as for vbq_gemv_multi. Asynchronous on `stream`.
+ * Errors: NULL, ABI, SHAPE (the shapes differ, k > VBQ_MAX_K), ALIGN,
+ * OFFSETS, HIP. */
+VBQ_API vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *up, const uint16_t *x, uint16_t *h,
+                                   void *stream);
+
 /* Y = X W^T for m <= VBQ_MAX_BATCH fp16 vectors (small-batch decode).
  * x: device binary16 [m][k] row-major; y: device fp32 [m][n] row-major
  * (overwritten). Runs on the matrix cores (each group's codes decoded once,

@@ -175,3 +175,11 @@ def gemv_threaded(p: Packed, x: np.ndarray, row_begin: int, row_end: int, thread
     with ThreadPoolExecutor(max_workers=threads) as ex:
         list(ex.map(run, range(threads)))
     return y[row_begin:row_end]
+
+
+def swiglu(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    """Gated-MLP intermediate silu(g) * u = g * u / (1 + e^-g), fp64 (VBQ §6, "Granularity is
+    deployment-friendly", where the padded channels are inert because silu(0) * u = 0)."""
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g)) * np.asarray(u, np.float64)

@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
         "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize", "vbq_recipe_head_bits",
-        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open",
+        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu",
         "vbq_status_string", "vbq_last_error"])
 
 
@@ -225,3 +225,23 @@ def test_recipe_head_bits_matches_the_reference(V, rows):
     freq = np.minimum(rng.zipf(1.3, rows), 10 ** 6).astype(np.uint64)
     assert np.array_equal(V.vbq_recipe_head_bits(freq), Q.head_bits(freq))
     assert V.lib.vbq_recipe_head_bits(3, None, None) == V.ERR_NULL
+
+
+def test_gemv_swiglu_rejects_bad_arguments_without_launching(V):
+    h = V.vbq_pack(*(lambda b, c, s: (2, 128, b, c, s))(*W.draw_random_matrix(8, 2, 128)))
+    buf = np.zeros(4096, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    g = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
+    u = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
+    other = V.VbqMatrix(1, 3, 128, h.payload_bytes, base, base, base, base)
+    f = V.lib.vbq_gemv_swiglu
+    assert f(None, ctypes.byref(u), base, base, None) == V.ERR_NULL
+    assert f(ctypes.byref(g), ctypes.byref(other), base, base, None) == V.ERR_SHAPE
+    assert f(ctypes.byref(g), ctypes.byref(u), None, base, None) == V.ERR_NULL
+    assert f(ctypes.byref(g), ctypes.byref(u), base, None, None) == V.ERR_NULL
+    assert f(ctypes.byref(g), ctypes.byref(u), base + 8, base, None) == V.ERR_ALIGN
+    assert f(ctypes.byref(g), ctypes.byref(u), base, base + 2, None) == V.ERR_ALIGN
+    v2 = V.VbqMatrix(2, 2, 128, h.payload_bytes, base, base, base, base)
+    assert f(ctypes.byref(g), ctypes.byref(v2), base, base, None) == V.ERR_ABI
+    empty = V.VbqMatrix(1, 0, 128, 0, None, None, None, None)
+    assert f(ctypes.byref(empty), ctypes.byref(empty), None, None, None) == V.OK   # n == 0: nothing to do

@@ -296,3 +296,20 @@ def test_reserved_pattern_decodes_as_most_negative(b):
     p = oracle.Packed(1, 64, np.array([c], np.uint8), np.array([0x3C00], np.uint16),
                       np.array([0, 8 * b], np.uint32), payload)
     assert np.all(oracle.unpack(p) == -(1 << (b - 1)))
+
+
+def test_swiglu_pins():
+    from scipy.special import expit
+    rng = np.random.default_rng(3)
+    u = rng.standard_normal(1000) * 5
+    # the pages' inertness statement: silu(0) * u = 0 for every u
+    assert np.all(oracle.swiglu(np.zeros(1000), u) == 0)
+    g = rng.standard_normal(1000) * 8
+    # g * sigmoid(g) * u through the library logistic
+    assert np.allclose(oracle.swiglu(g, u), g * expit(g) * u, rtol=1e-14, atol=0)
+    # closed form: silu(g) - silu(-g) = g
+    one = np.ones_like(g)
+    assert np.allclose(oracle.swiglu(g, one) - oracle.swiglu(-g, one), g, rtol=1e-13, atol=1e-13)
+    # limits: silu(g) -> g for large g, -> 0 (not NaN) for very negative g
+    assert oracle.swiglu(np.array([60.0]), np.array([2.0]))[0] == 120.0
+    assert oracle.swiglu(np.array([-1000.0]), np.array([3.0]))[0] == 0.0
