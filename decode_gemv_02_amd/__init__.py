@@ -21,7 +21,7 @@ import torch  # import before the library so it binds to the HIP runtime torch h
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libvbq.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 GROUP = 64
 MAX_K = 65536
 MAX_BATCH = 64
@@ -43,7 +43,7 @@ class VbqSizes(ctypes.Structure):
 class VbqMatrix(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
                 ("payload_bytes", ctypes.c_uint32), ("widths", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("tile_offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p)]
+                ("tile_offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p), ("uniform_bits", ctypes.c_uint32)]
 
 
 class VbqError(RuntimeError):
@@ -73,6 +73,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
                                    U32, P]
     lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
     lib.vbq_gemv_swiglu.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(VbqMatrix), P, P, P]
+    lib.vbq_uniform_width.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(U32)]
     lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
     lib.vbq_quantize.argtypes = [U32, U32, P, P, P, P, P]
@@ -84,7 +85,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
-              lib.vbq_gemv_swiglu):
+              lib.vbq_gemv_swiglu, lib.vbq_uniform_width):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -155,6 +156,14 @@ def vbq_pack(n: int, k: int, bits: np.ndarray, codes: np.ndarray, scales: np.nda
     return HostMatrix(n, k, widths, sc, offs, payload)
 
 
+def vbq_uniform_width(m: HostMatrix) -> int:
+    """b when every group of m has width b, else 0."""
+    v = m.view()
+    out = ctypes.c_uint32()
+    _check(lib.vbq_uniform_width(ctypes.byref(v), ctypes.byref(out)))
+    return int(out.value)
+
+
 def vbq_validate_host(m: HostMatrix) -> None:
     v = m.view()
     _check(lib.vbq_validate_host(ctypes.byref(v)))
@@ -165,8 +174,11 @@ def vbq_validate_host(m: HostMatrix) -> None:
 class DeviceMatrix:
     """Packed matrix resident in device memory (torch tensors own the bytes)."""
 
-    def __init__(self, host: HostMatrix, device="cuda"):
+    def __init__(self, host: HostMatrix, device="cuda", uniform: bool = True):
+        """uniform: declare the matrix's single width (when it has one) so launches take the
+        uniform-width kernels; False keeps it on the mixed-width kernel."""
         self.n, self.k = host.n, host.k
+        self.uniform_bits = vbq_uniform_width(host) if uniform else 0
         self.payload_bytes = host.payload_bytes
         self.total_bytes = host.total_bytes
         dev = torch.device(device)
@@ -180,7 +192,8 @@ class DeviceMatrix:
         self._offsets = up(host.tile_offsets.view(np.int32))
         self._payload = up(host.payload)
         self.struct = VbqMatrix(ABI_VERSION, self.n, self.k, self.payload_bytes, self._widths.data_ptr(),
-                                self._scales.data_ptr(), self._offsets.data_ptr(), self._payload.data_ptr())
+                                self._scales.data_ptr(), self._offsets.data_ptr(), self._payload.data_ptr(),
+                                self.uniform_bits)
 
 
 def vbq_gemv(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:

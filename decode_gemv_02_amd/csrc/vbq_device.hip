@@ -104,6 +104,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, static_cast<int>(off), 0, 0));
 }
+__device__ __forceinline__ uint4 buf_load16x(rsrc_t r, uint32_t off) {   // one 128-bit load
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
 __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
     return static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
 }
@@ -286,6 +289,7 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
 // Stage the tile's activations: fp16 pairs, the 4-bit lookup table (sums of
 // the activations selected by the set bits of a 4-bit index) and the
 // per-column bias terms of the unpack paths.
+template <bool kLut = true>
 __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane, float wa, float wb) {
     const uint32_t jl = lane >> 4, k = lane & 15;
     L.xs[jl * kXStride + 2 * k] = xv.x;
@@ -293,11 +297,13 @@ __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane, flo
     const float x0 = half_to_float(xv.x & 0xFFFFu), x1 = half_to_float(xv.x >> 16);
     const float x2 = half_to_float(xv.y & 0xFFFFu), x3 = half_to_float(xv.y >> 16);
     const float a01 = x0 + x1, t5 = x2 + x0, t6 = x2 + x1, t7 = x2 + a01;
-    float4 *t = reinterpret_cast<float4 *>(L.lut + lane * 16);
-    t[0] = make_float4(0.f, x0, x1, a01);
-    t[1] = make_float4(x2, t5, t6, t7);
-    t[2] = make_float4(x3, x3 + x0, x3 + x1, x3 + a01);
-    t[3] = make_float4(x3 + x2, x3 + t5, x3 + t6, x3 + t7);
+    if (kLut) {
+        float4 *t = reinterpret_cast<float4 *>(L.lut + lane * 16);
+        t[0] = make_float4(0.f, x0, x1, a01);
+        t[1] = make_float4(x2, t5, t6, t7);
+        t[2] = make_float4(x3, x3 + x0, x3 + x1, x3 + a01);
+        t[3] = make_float4(x3 + x2, x3 + t5, x3 + t6, x3 + t7);
+    }
     // bias terms. 4-bit: element pairs alternate factor 1 / 16 -> weights 1032 / 72.
     // 2-bit: pair factors 1,4,16,64,256,1,4,16 -> weights 1024/f + 2.
     const float a23 = x2 + x3;
@@ -434,8 +440,8 @@ __device__ __forceinline__ float group1(WaveLds &L, uint32_t info, uint2 v) {
     return L.corr[jl][0] - 2.f * sum;
 }
 
-__device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
-    const uint32_t jl = info >> 6;
+// unscaled product of one 2-bit group of column jl
+__device__ __forceinline__ float dot2bit(WaveLds &L, uint32_t jl, uint2 va, uint2 vb) {
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride);
     const uint32_t magic = opaque(kMagic);
@@ -454,13 +460,16 @@ __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint
         a4 = dot2(p[6], xb.z, a4);
         a16 = dot2(p[7], xb.w, a16);
     }
-    const float d = a1 + 0.25f * a4 + 0.0625f * a16 + 0.015625f * a64 + 0.00390625f * a256 - L.corr[jl][1];
-    store_part(L, info, d);
+    return a1 + 0.25f * a4 + 0.0625f * a16 + 0.015625f * a64 + 0.00390625f * a256 - L.corr[jl][1];
+}
+
+__device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
+    store_part(L, info, dot2bit(L, info >> 6, va, vb));
 }
 
 // 4-bit: a 16-byte half group (h = task & 1); lane pairs add their halves
-__device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uint2 va, uint2 vb) {
-    const uint32_t jl = info >> 6;
+// 4-bit: a 16-byte half group (h = 0, 1) of column jl, without the bias term
+__device__ __forceinline__ float half4bit(WaveLds &L, uint32_t jl, uint32_t h, uint2 va, uint2 vb) {
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 16u * h);
     const uint32_t magic = opaque(kMagic);
@@ -475,14 +484,19 @@ __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uin
         a1 = dot2(p[2], xa.z, a1);
         a16 = dot2(p[3], xa.w, a16);
     }
-    float part = a1 + 0.0625f * a16;
+    return a1 + 0.0625f * a16;
+}
+
+__device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uint2 va, uint2 vb) {
+    const uint32_t jl = info >> 6;
+    float part = half4bit(L, jl, h, va, vb);
     part += dpp<kQuadXor1>(part);
     if (h == 0) store_part(L, info, part - L.corr[jl][2]);
 }
 
 // 8-bit: a 16-byte quarter group (qd = task & 3); lane quads add their quarters
-__device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, uint2 va, uint2 vb) {
-    const uint32_t jl = info >> 6;
+// 8-bit: a 16-byte quarter group (qd = 0..3) of column jl, without the bias term
+__device__ __forceinline__ float quarter8bit(WaveLds &L, uint32_t jl, uint32_t qd, uint2 va, uint2 vb) {
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 8u * qd);
     float a = 0.f;
@@ -497,6 +511,12 @@ __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, ui
         a = dot2(p2, xa.z, a);
         a = dot2(p3, xa.w, a);
     }
+    return a;
+}
+
+__device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, uint2 va, uint2 vb) {
+    const uint32_t jl = info >> 6;
+    float a = quarter8bit(L, jl, qd, va, vb);
     a += dpp<kQuadXor1>(a);
     a += dpp<kQuadXor2>(a);
     if (qd == 0) store_part(L, info, a - 1152.f * L.corr[jl][0]);
@@ -588,6 +608,41 @@ __device__ __forceinline__ void swiglu_pair(const Batch &B, uint32_t which, uint
     if (lane == 0) __hip_atomic_store(&B.pair_counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The workgroup's row sums (waves added in wave order), the split-K
+// reduction when the row tile is split, then y or the gated-MLP epilogue.
+template <uint32_t kWaves>
+__device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M, WaveLds *lds, uint32_t wave,
+                                                bool spare, uint32_t a, uint32_t split, uint32_t r0, uint32_t rows,
+                                                uint32_t lane, float acc) {
+    lds[wave].part[lane] = acc;   // the wave's row sums, in its own (now idle) LDS
+    __syncthreads();
+    if (wave != 0 || spare) return;
+    float sum = lds[0].part[lane];
+#pragma unroll
+    for (uint32_t w = 1; w < kWaves; ++w) sum += lds[w].part[lane];   // in wave order
+    if (M.splits > 1) {
+        // Split row tile: publish the partial sums with coherent (agent-scope) stores,
+        // wait until they have landed, then count arrivals; the last workgroup adds
+        // the partials in split order and resets the counter for the next call.
+        if (lane < rows)
+            __hip_atomic_store(&M.partial[static_cast<uint64_t>(split) * M.n + r0 + lane], sum, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t arrived = 0;
+        if (lane == 0)
+            arrived = __hip_atomic_fetch_add(&M.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __shfl(arrived, 0, kWave);
+        if (arrived != M.splits - 1) return;
+        if (lane < rows) sum = sum_partials(M.partial + r0 + lane, M.n, M.splits);
+        if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (!B.h) {
+        if (lane < rows) M.y[r0 + lane] = sum;
+        return;
+    }
+    swiglu_pair(B, blockIdx.y, a, r0 + lane, lane < rows, M.n, lane, sum);
+}
+
 // kWaves waves per workgroup (4, 8 or 16) share one row tile; the LDS
 // (4992 B per wave) allows 8, 4 or 2 such workgroups per CU, eight waves
 // per SIMD, and the registers are held to the 64 that allow the same.
@@ -643,34 +698,105 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         wave_lds_sync();
         cur = nxt;
     }
-    const uint32_t lane = relane(lane0);
-    L.part[lane] = acc;   // the wave's row sums, in its own (now idle) LDS
-    __syncthreads();
-    if (wave != 0 || spare) return;
-    float sum = lds[0].part[lane];
+    finish_row_tile<kWaves>(B, M, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
+}
+
+// ---------------------------------------------------------------- uniform width
+// Every group of the matrix has width kBits (the deployed recipe stores whole
+// projections at one width). A tile is then a single bucket: group (jl, r)
+// sits (jl * rows + r) * 8 * kBits bytes into its tile, and the tile sits at
+// 8 * kBits * (r0 * G + rows * 4 * ct). No width codes, offset table, scan or
+// lists are needed. A lane owns its row: it loads the row's groups of the
+// tile, forms each product with the mixed kernel's decoders and adds it,
+// scaled, into its own row sum.
+template <uint32_t kBits>
+struct RowGroups {
+    uint4 v[kBits == 1 ? 1 : kBits / 2];   // 8 * kBits bytes (1 bit: the low 8 bytes)
+};
+
+template <uint32_t kBits>
+__device__ __forceinline__ RowGroups<kBits> load_row_group(rsrc_t tile, uint32_t off) {
+    RowGroups<kBits> g;
+    if (kBits == 1) {
+        const uint2 v = buf_load8(tile, off);
+        g.v[0] = make_uint4(v.x, v.y, 0u, 0u);
+    } else {
 #pragma unroll
-    for (uint32_t w = 1; w < kWaves; ++w) sum += lds[w].part[lane];   // in wave order
-    if (M.splits > 1) {
-        // Split row tile: publish the partial sums with coherent (agent-scope) stores,
-        // wait until they have landed, then count arrivals; the last workgroup adds
-        // the partials in split order and resets the counter for the next call.
-        if (lane < rows)
-            __hip_atomic_store(&M.partial[static_cast<uint64_t>(split) * M.n + r0 + lane], sum, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        uint32_t arrived = 0;
-        if (lane == 0)
-            arrived = __hip_atomic_fetch_add(&M.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        arrived = __shfl(arrived, 0, kWave);
-        if (arrived != M.splits - 1) return;
-        if (lane < rows) sum = sum_partials(M.partial + r0 + lane, M.n, M.splits);
-        if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (uint32_t i = 0; i < kBits / 2; ++i) g.v[i] = buf_load16x(tile, off + 16u * i);
     }
-    if (!B.h) {
-        if (lane < rows) M.y[r0 + lane] = sum;
-        return;
+    return g;
+}
+
+template <uint32_t kBits>
+__device__ __forceinline__ float row_group_dot(WaveLds &L, uint32_t jl, const RowGroups<kBits> &g) {
+    if (kBits == 1) return group1(L, jl << 6, make_uint2(g.v[0].x, g.v[0].y));
+    if (kBits == 2) return dot2bit(L, jl, make_uint2(g.v[0].x, g.v[0].y), make_uint2(g.v[0].z, g.v[0].w));
+    if (kBits == 4)
+        return (half4bit(L, jl, 0, make_uint2(g.v[0].x, g.v[0].y), make_uint2(g.v[0].z, g.v[0].w)) +
+                half4bit(L, jl, 1, make_uint2(g.v[1].x, g.v[1].y), make_uint2(g.v[1].z, g.v[1].w))) -
+               L.corr[jl][2];
+    // quarters added as the mixed kernel's lane quads add them, so both kernels give the same bits
+    float q[4];
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i)
+        q[i] = quarter8bit(L, jl, i, make_uint2(g.v[i & (kBits / 2 - 1)].x, g.v[i & (kBits / 2 - 1)].y),
+                           make_uint2(g.v[i & (kBits / 2 - 1)].z, g.v[i & (kBits / 2 - 1)].w));
+    return ((q[0] + q[1]) + (q[2] + q[3])) - 1152.f * L.corr[jl][0];
+}
+
+template <uint32_t kBits, bool kAligned, uint32_t kWaves>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void gemv_uniform(Batch B) {
+    __shared__ WaveLds lds[kWaves];
+    const MatArgs M = B.m[blockIdx.y];
+    const bool spare = blockIdx.x >= M.blocks;
+    const uint32_t bx = spare ? M.blocks - 1 : blockIdx.x;
+    const uint32_t a = bx / M.splits, split = bx % M.splits;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
+    const uint32_t r0 = a * kTileRows;
+    const uint32_t rows = min(kTileRows, M.n - r0);
+    const uint32_t c_lo = (split * M.col_tiles) / M.splits, c_hi = ((split + 1) * M.col_tiles) / M.splits;
+    WaveLds &L = lds[wave];
+    float acc = 0.f;
+    const uint32_t lane0 = lane_id();
+    const uint32_t km = lane0 & 3u;
+    const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
+    const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
+    constexpr uint32_t kChunk = kBits == 8 ? 1 : kTileGroups;   // groups of a row held at once
+    uint32_t ct = c_lo + wave;
+    TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, relane(lane0), true);
+    for (; ct < c_hi; ct += kWaves) {
+        const uint32_t cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - ct * kTileGroups);
+        const uint32_t lr = min(relane(lane0), rows - 1);
+        const uint32_t tile_off = 8u * kBits * (r0 * M.groups + rows * kTileGroups * ct);
+        const rsrc_t tp = tile_rsrc(M.payload, M.payload_bytes, tile_off);
+        RowGroups<kBits> g[kChunk];
+#pragma unroll
+        for (uint32_t jl = 0; jl < kChunk; ++jl)
+            g[jl] = load_row_group<kBits>(tp, (min(jl, cn - 1) * rows + lr) * 8u * kBits);
+        const TileMeta nxt =
+            load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, relane(lane0), true);
+        stage_x<kBits == 1>(L, cur.xv, relane(lane0), wa, wb);
+        wave_lds_sync();
+        const uint32_t lane = relane(lane0);
+#pragma unroll
+        for (uint32_t c0 = 0; c0 < kTileGroups; c0 += kChunk) {
+            if (c0 > 0) {
+#pragma unroll
+                for (uint32_t jl = 0; jl < kChunk; ++jl)
+                    g[jl] = load_row_group<kBits>(tp, (min(c0 + jl, cn - 1) * rows + lr) * 8u * kBits);
+            }
+#pragma unroll
+            for (uint32_t jl = 0; jl < kChunk; ++jl) {
+                const uint32_t j = c0 + jl;
+                const uint32_t sb = (j < 2 ? cur.s01 >> (16 * j) : cur.s23 >> (16 * (j - 2))) & 0xFFFFu;
+                const float d = row_group_dot<kBits>(L, j, g[jl]);
+                if (lane < rows && j < cn) acc += half_to_float(sb) * d;
+            }
+        }
+        wave_lds_sync();
+        cur = nxt;
     }
-    swiglu_pair(B, blockIdx.y, a, r0 + lane, lane < rows, M.n, lane, sum);
+    finish_row_tile<kWaves>(B, M, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
 }
 
 // Decoded codes of every group, written at its natural position; the same
@@ -1213,6 +1339,11 @@ vbq_status check_matrix(const char *who, const vbq_matrix *w) {
         return fail(VBQ_ERR_NULL, "%s: widths, scales, tile_offsets or payload is NULL", who);
     if (!aligned16(w->tile_offsets) || !aligned16(w->widths) || !aligned16(w->scales) || !aligned16(w->payload))
         return fail(VBQ_ERR_ALIGN, "%s: a matrix array is not 16-byte aligned", who);
+    const uint32_t b = w->uniform_bits;
+    if (b != 0 && b != 1 && b != 2 && b != 4 && b != 8)
+        return fail(VBQ_ERR_WIDTH, "%s: uniform_bits=%u is not 0, 1, 2, 4 or 8", who, b);
+    if (b && static_cast<uint64_t>(w->n) * (w->k / VBQ_GROUP) * 8u * b != w->payload_bytes)
+        return fail(VBQ_ERR_OFFSETS, "%s: payload_bytes=%u is not 8*%u bytes per group", who, w->payload_bytes, b);
     return VBQ_OK;
 }
 
@@ -1309,8 +1440,26 @@ GemvPlan gemv_plan(uint32_t row_tiles, uint32_t col_tiles) {
     return best;
 }
 
+template <uint32_t kBits, uint32_t kWaves>
+void gemv_dispatch_uniform(bool aligned, uint32_t blocks, uint32_t used, const Batch &B, hipStream_t stream) {
+    if (aligned)
+        hipLaunchKernelGGL((gemv_uniform<kBits, true, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0, stream,
+                           B);
+    else
+        hipLaunchKernelGGL((gemv_uniform<kBits, false, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0, stream,
+                           B);
+}
+
+// ubits: the width every matrix of the launch has, or 0 (the mixed-width kernel)
 template <uint32_t kWaves>
-void gemv_dispatch(bool aligned, uint32_t blocks, uint32_t used, const Batch &B, hipStream_t stream) {
+void gemv_dispatch(bool aligned, uint32_t ubits, uint32_t blocks, uint32_t used, const Batch &B, hipStream_t stream) {
+    switch (ubits) {
+        case 1: gemv_dispatch_uniform<1, kWaves>(aligned, blocks, used, B, stream); return;
+        case 2: gemv_dispatch_uniform<2, kWaves>(aligned, blocks, used, B, stream); return;
+        case 4: gemv_dispatch_uniform<4, kWaves>(aligned, blocks, used, B, stream); return;
+        case 8: gemv_dispatch_uniform<8, kWaves>(aligned, blocks, used, B, stream); return;
+        default: break;
+    }
     if (aligned)
         hipLaunchKernelGGL((gemv_tiles<true, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0, stream, B);
     else
@@ -1335,6 +1484,14 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     size_t counter_slots = 0, partial_total = 0;
     uint32_t used = 0;
     bool any_launch = false;
+    // the uniform-width kernels run when every matrix launched declares the same width
+    uint32_t ubits = 0;
+    bool first = true;
+    for (uint32_t i = 0; i < count; ++i) {
+        if (ws[i]->n == 0 || ws[i]->k == 0) continue;
+        ubits = first ? ws[i]->uniform_bits : (ubits == ws[i]->uniform_bits ? ubits : 0u);
+        first = false;
+    }
     for (uint32_t i = 0; i < count; ++i) {
         const vbq_matrix *w = ws[i];
         if (w->n == 0) continue;
@@ -1391,11 +1548,11 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         }
     }
     if (plan.waves == 16)
-        gemv_dispatch<16>(aligned, blocks, used, B, stream);
+        gemv_dispatch<16>(aligned, ubits, blocks, used, B, stream);
     else if (plan.waves == 8)
-        gemv_dispatch<8>(aligned, blocks, used, B, stream);
+        gemv_dispatch<8>(aligned, ubits, blocks, used, B, stream);
     else
-        gemv_dispatch<4>(aligned, blocks, used, B, stream);
+        gemv_dispatch<4>(aligned, ubits, blocks, used, B, stream);
     return launched(who);
 }
 

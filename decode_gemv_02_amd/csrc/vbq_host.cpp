@@ -241,6 +241,16 @@ extern "C" vbq_status vbq_validate_host(const vbq_matrix *w) {
     if (total != w->payload_bytes)
         return fail(VBQ_ERR_OFFSETS, "vbq_validate_host: payload_bytes=%u, widths give %llu", w->payload_bytes,
                     (unsigned long long)total);
+    if (w->uniform_bits) {
+        const uint32_t ub = w->uniform_bits;
+        if (ub != 1 && ub != 2 && ub != 4 && ub != 8)
+            return fail(VBQ_ERR_WIDTH, "vbq_validate_host: uniform_bits=%u is not 0, 1, 2, 4 or 8", ub);
+        for (uint32_t r = 0; r < w->n; ++r)
+            for (uint32_t j = 0; j < G; ++j)
+                if (width(r, j) != ub)
+                    return fail(VBQ_ERR_WIDTH, "vbq_validate_host: group (%u, %u) has width %u, uniform_bits=%u", r,
+                                j, width(r, j), ub);
+    }
     for (uint64_t t = 0; t < groups; ++t) {
         if (!half_is_finite(w->scales[t]))
             return fail(VBQ_ERR_SCALE, "vbq_validate_host: scale slot %llu not finite", (unsigned long long)t);
@@ -448,8 +458,31 @@ extern "C" vbq_status vbq_container_open(const uint8_t *buf, uint64_t len, vbq_m
     v.scales = L.scales_bytes ? reinterpret_cast<const uint16_t *>(buf + L.scales) : nullptr;
     v.tile_offsets = reinterpret_cast<const uint32_t *>(buf + L.offsets);
     v.payload = L.payload_bytes ? buf + L.payload : nullptr;
-    const vbq_status st = vbq_validate_host(&v);
+    vbq_status st = vbq_validate_host(&v);
+    if (st != VBQ_OK) return st;
+    st = vbq_uniform_width(&v, &v.uniform_bits);
     if (st != VBQ_OK) return st;
     *view = v;
+    return VBQ_OK;
+}
+
+extern "C" vbq_status vbq_uniform_width(const vbq_matrix *w, uint32_t *bits_out) {
+    vbq::clear_error();
+    if (!w || !bits_out) return fail(VBQ_ERR_NULL, "vbq_uniform_width: a pointer is NULL");
+    if (w->abi_version != VBQ_ABI_VERSION)
+        return fail(VBQ_ERR_ABI, "vbq_uniform_width: abi_version %u, library %u", w->abi_version, VBQ_ABI_VERSION);
+    if (w->k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_uniform_width: k=%u is not a multiple of 64", w->k);
+    const uint64_t groups = uint64_t(w->n) * (w->k / VBQ_GROUP);
+    *bits_out = 0;
+    if (groups == 0) return VBQ_OK;
+    if (!w->widths) return fail(VBQ_ERR_NULL, "vbq_uniform_width: widths is NULL");
+    // four codes a byte: a uniform matrix has every full byte equal to c * 0x55
+    const uint32_t c = w->widths[0] & 3u;
+    const uint8_t full = uint8_t(c * 0x55u);
+    for (uint64_t i = 0; i < groups / 4; ++i)
+        if (w->widths[i] != full) return VBQ_OK;
+    for (uint64_t t = groups / 4 * 4; t < groups; ++t)
+        if (((w->widths[t >> 2] >> (2 * (t & 3))) & 3u) != c) return VBQ_OK;
+    *bits_out = 1u << c;
     return VBQ_OK;
 }

@@ -78,7 +78,7 @@ extern "C" {
 /* Only the entry points below are exported from the shared library. */
 #define VBQ_API __attribute__((visibility("default")))
 
-#define VBQ_ABI_VERSION 1u
+#define VBQ_ABI_VERSION 2u
 #define VBQ_GROUP 64u
 #define VBQ_TILE_ROWS 64u
 #define VBQ_TILE_GROUPS 4u
@@ -126,6 +126,15 @@ typedef struct vbq_matrix {
     const uint16_t *scales;
     const uint32_t *tile_offsets;
     const uint8_t *payload;
+    /* 0, or b in {1, 2, 4, 8} when every group has width b (the deployed
+     * recipe of VBQ §3.4 stores whole projections at one width; §6 notes a
+     * kernel then handles one width per projection). Device entry points
+     * given a launch whose matrices all carry the same b run the
+     * uniform-width kernels, which read neither the width codes nor
+     * tile_offsets. vbq_uniform_width computes it from a host view;
+     * vbq_validate_host checks it; device entry points check only that
+     * payload_bytes == 8 * b * n * k / 64 (OFFSETS otherwise). */
+    uint32_t uniform_bits;
 } vbq_matrix;
 
 /* Library ABI version (compare with VBQ_ABI_VERSION). */
@@ -279,10 +288,15 @@ VBQ_API vbq_status vbq_container_write(const vbq_matrix *host_view, uint8_t *out
 /* Check a container image buf[0, len) and fill *view_out with pointers into
  * buf (no copy; buf must outlive the view). Checks the magic, version,
  * layout constants, that every array lies inside buf at its aligned offset
- * with the sizes n and k give, both checksums, and then runs
- * vbq_validate_host on the view. Errors: NULL; FORMAT (header, sizes or
+ * with the sizes n and k give, both checksums, then runs vbq_validate_host
+ * on the view and sets its uniform_bits (vbq_uniform_width). Errors: NULL; FORMAT (header, sizes or
  * checksum); those of vbq_validate_host. */
 VBQ_API vbq_status vbq_container_open(const uint8_t *buf, uint64_t len, vbq_matrix *view_out);
+
+/* *bits_out = b when every group of the host view has width b, else 0
+ * (also for n == 0 or k == 0). Reads the width codes only. Errors: NULL,
+ * ABI, SHAPE (k % 64). */
+VBQ_API vbq_status vbq_uniform_width(const vbq_matrix *host_view, uint32_t *bits_out);
 
 /* Static English name of a status. */
 VBQ_API const char *vbq_status_string(vbq_status s);

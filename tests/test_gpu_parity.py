@@ -325,3 +325,78 @@ def test_split_path_repeats_exactly(V, torch_mod):
         outs.append(y.cpu().numpy())
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[1], outs[2])
     assert_within_tolerance(outs[0], oracle.gemv(p, x), x, scales, "split")
+
+
+# ------------------------------------------------------------------ uniform-width kernels
+
+@pytest.mark.parametrize("b", [1, 2, 4, 8])
+@pytest.mark.parametrize("n, k", [(64, 256), (300, 4096 + 64), (1000, 1984), (64, 14336), (4096, 4096)])
+def test_uniform_width_kernels(V, torch_mod, b, n, k):
+    # a matrix at one width: the uniform-width kernel (declared width) against the oracle, and bit for
+    # bit against the mixed-width kernel on the same matrix (same launch shape, same order of sums)
+    torch = torch_mod
+    print_case(test="uniform", b=b, n=n, k=k)
+    bits, codes, scales = W.draw_random_matrix((b, n, k), n, k, {b: 1.0})
+    h = V.vbq_pack(n, k, bits, codes, scales)
+    assert V.vbq_uniform_width(h) == b
+    fast, mixed = V.DeviceMatrix(h), V.DeviceMatrix(h, uniform=False)
+    assert fast.uniform_bits == b and mixed.uniform_bits == 0
+    x = W.draw_x((b, n, k, 1), k)
+    xt = torch.from_numpy(x.view(np.float16)).cuda()
+    ys = []
+    for dm in (fast, mixed):
+        y = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
+        V.vbq_gemv(dm, xt[0], y)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    p = oracle.pack(n, k, bits, codes, scales)
+    assert_within_tolerance(ys[0][None], oracle.gemv(p, x[0])[None], x, scales, f"uniform b={b}")
+    assert np.array_equal(ys[0], ys[1])
+
+
+def test_uniform_width_multi_and_mixed_batches(V, torch_mod):
+    # q/k/v-like launch of three 2-bit matrices (uniform kernel), then a batch that mixes a uniform and
+    # a mixed-width matrix (falls back to the mixed kernel for both); also gate+up epilogue at 4 bits
+    torch = torch_mod
+    print_case(test="uniform_multi")
+    n, k = 2048, 2048
+    hs, packs, dms = [], [], []
+    for i, mix in enumerate([{2: 1.0}, {2: 1.0}, {2: 1.0}, W.STD_MIX]):
+        bits, codes, scales = W.draw_random_matrix((70, i), n, k, mix)
+        hs.append(V.vbq_pack(n, k, bits, codes, scales))
+        packs.append((oracle.pack(n, k, bits, codes, scales), scales))
+        dms.append(V.DeviceMatrix(hs[-1]))
+    x = W.draw_x((71,), k)
+    xt = torch.from_numpy(x.view(np.float16)).cuda()
+    for sel in ([0, 1, 2], [0, 3], [3, 1]):
+        ys = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for _ in sel]
+        V.vbq_gemv_multi([dms[i] for i in sel], [xt[0]] * len(sel), ys)
+        torch.cuda.synchronize()
+        for i, y in zip(sel, ys):
+            assert_within_tolerance(y.cpu().numpy()[None], oracle.gemv(packs[i][0], x[0])[None], x, packs[i][1],
+                                    f"batch {sel} matrix {i}")
+    gates = []
+    for i in range(2):
+        bits, codes, scales = W.draw_random_matrix((72, i), 3000, k, {4: 1.0})
+        gates.append(V.vbq_pack(3000, k, bits, codes, scales))
+    hf = torch.empty(3000, dtype=torch.float16, device="cuda")
+    hm = torch.empty(3000, dtype=torch.float16, device="cuda")
+    V.vbq_gemv_swiglu(V.DeviceMatrix(gates[0]), V.DeviceMatrix(gates[1]), xt[0], hf)
+    V.vbq_gemv_swiglu(V.DeviceMatrix(gates[0], uniform=False), V.DeviceMatrix(gates[1], uniform=False), xt[0], hm)
+    torch.cuda.synchronize()
+    assert torch.equal(hf, hm)
+
+
+def test_uniform_width_declaration_is_checked(V):
+    n, k = 64, 512
+    h = V.vbq_pack(n, k, *W.draw_random_matrix((73,), n, k, {2: 1.0}))
+    dm = V.DeviceMatrix(h)
+    import ctypes
+    import torch
+    x = torch.zeros(k, dtype=torch.float16, device="cuda")
+    y = torch.zeros(n, dtype=torch.float32, device="cuda")
+    bad = V.VbqMatrix.from_buffer_copy(dm.struct)
+    bad.uniform_bits = 4                                   # payload_bytes says 2 bits
+    assert V.lib.vbq_gemv(ctypes.byref(bad), x.data_ptr(), y.data_ptr(), None) == V.ERR_OFFSETS
+    bad.uniform_bits = 3
+    assert V.lib.vbq_gemv(ctypes.byref(bad), x.data_ptr(), y.data_ptr(), None) == V.ERR_WIDTH

@@ -23,7 +23,7 @@ def _assembly(tmp_path_factory, name):
     return out.read_text()
 
 
-@pytest.mark.parametrize("source, kernel_names", [("vbq_device.hip", ("gemv_tiles", "unpack_tiles")),
+@pytest.mark.parametrize("source, kernel_names", [("vbq_device.hip", ("gemv_tiles", "gemv_uniform", "unpack_tiles")),
                                                   ("vbq_quantize.hip", ("quantize_groups",))])
 def test_kernels_do_not_spill(tmp_path_factory, source, kernel_names):
     assembly = _assembly(tmp_path_factory, source)

@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
         "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize", "vbq_recipe_head_bits",
-        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu",
+        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width",
         "vbq_status_string", "vbq_last_error"])
 
 
@@ -152,7 +152,7 @@ def test_device_entry_points_reject_bad_arguments_without_launching(V):
     base = (buf.ctypes.data + 255) // 256 * 256
     assert V.lib.vbq_gemv(None, base, base, None) == V.ERR_NULL
     v2 = h.view()
-    v2.abi_version = 2
+    v2.abi_version = 99
     assert V.lib.vbq_gemv(ctypes.byref(v2), base, base, None) == V.ERR_ABI
     v3 = h.view()
     v3.k = 100
@@ -162,18 +162,18 @@ def test_device_entry_points_reject_bad_arguments_without_launching(V):
     assert V.lib.vbq_gemv(ctypes.byref(v4), base, base, None) == V.ERR_SHAPE
     assert V.lib.vbq_gemm_smallbatch(ctypes.byref(v), base, 0, base, None) == V.ERR_SHAPE
     assert V.lib.vbq_gemm_smallbatch(ctypes.byref(v), base, 65, base, None) == V.ERR_SHAPE
-    aligned = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
+    aligned = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base)
     assert V.lib.vbq_gemv(ctypes.byref(aligned), base + 8, base, None) == V.ERR_ALIGN
     assert V.lib.vbq_gemv(ctypes.byref(aligned), base, base + 4, None) == V.ERR_ALIGN
     assert V.lib.vbq_gemv(ctypes.byref(aligned), None, base, None) == V.ERR_NULL
-    mis = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base + 8)
+    mis = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base + 8)
     assert V.lib.vbq_gemv(ctypes.byref(mis), base, base, None) == V.ERR_ALIGN
     assert V.lib.vbq_unpack_codes(ctypes.byref(aligned), None, None) == V.ERR_NULL
     assert V.lib.vbq_unpack_codes(ctypes.byref(aligned), base + 1, None) == V.ERR_ALIGN
-    empty = V.VbqMatrix(1, 0, 128, 0, None, None, None, None)
+    empty = V.VbqMatrix(V.ABI_VERSION, 0, 128, 0, None, None, None, None)
     assert V.lib.vbq_gemv(ctypes.byref(empty), None, None, None) == V.OK    # n == 0: nothing to do
     # every group has at least 8 payload bytes (2 x 2 groups here: 32 bytes at least)
-    short = V.VbqMatrix(1, 2, 128, 31, base, base, base, base)
+    short = V.VbqMatrix(V.ABI_VERSION, 2, 128, 31, base, base, base, base)
     assert V.lib.vbq_gemv(ctypes.byref(short), base, base, None) == V.ERR_OFFSETS
     assert V.lib.vbq_gemm_smallbatch(ctypes.byref(short), base, 16, base, None) == V.ERR_OFFSETS
     assert V.lib.vbq_unpack_codes(ctypes.byref(short), base, None) == V.ERR_OFFSETS
@@ -189,7 +189,7 @@ def test_gemv_multi_rejects_bad_arguments_without_launching(V):
     assert V.lib.vbq_gemv_multi(W17, P17, P17, 17, None) == V.ERR_SHAPE
     assert V.lib.vbq_gemv_multi(None, P17, P17, 2, None) == V.ERR_NULL
     assert V.lib.vbq_gemv_multi(W17, P17, P17, 0, None) == V.OK
-    bad = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
+    bad = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base)
     Wb = (ctypes.POINTER(V.VbqMatrix) * 2)(ctypes.pointer(bad), ctypes.pointer(bad))
     Pm = (ctypes.c_void_p * 2)(base, base + 8)
     assert V.lib.vbq_gemv_multi(Wb, Pm, (ctypes.c_void_p * 2)(base, base), 2, None) == V.ERR_ALIGN
@@ -231,9 +231,9 @@ def test_gemv_swiglu_rejects_bad_arguments_without_launching(V):
     h = V.vbq_pack(*(lambda b, c, s: (2, 128, b, c, s))(*W.draw_random_matrix(8, 2, 128)))
     buf = np.zeros(4096, np.uint8)
     base = (buf.ctypes.data + 255) // 256 * 256
-    g = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
-    u = V.VbqMatrix(1, 2, 128, h.payload_bytes, base, base, base, base)
-    other = V.VbqMatrix(1, 3, 128, h.payload_bytes, base, base, base, base)
+    g = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base)
+    u = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base)
+    other = V.VbqMatrix(V.ABI_VERSION, 3, 128, h.payload_bytes, base, base, base, base)
     f = V.lib.vbq_gemv_swiglu
     assert f(None, ctypes.byref(u), base, base, None) == V.ERR_NULL
     assert f(ctypes.byref(g), ctypes.byref(other), base, base, None) == V.ERR_SHAPE
@@ -241,7 +241,33 @@ def test_gemv_swiglu_rejects_bad_arguments_without_launching(V):
     assert f(ctypes.byref(g), ctypes.byref(u), base, None, None) == V.ERR_NULL
     assert f(ctypes.byref(g), ctypes.byref(u), base + 8, base, None) == V.ERR_ALIGN
     assert f(ctypes.byref(g), ctypes.byref(u), base, base + 2, None) == V.ERR_ALIGN
-    v2 = V.VbqMatrix(2, 2, 128, h.payload_bytes, base, base, base, base)
+    v2 = V.VbqMatrix(99, 2, 128, h.payload_bytes, base, base, base, base)
     assert f(ctypes.byref(g), ctypes.byref(v2), base, base, None) == V.ERR_ABI
-    empty = V.VbqMatrix(1, 0, 128, 0, None, None, None, None)
+    empty = V.VbqMatrix(V.ABI_VERSION, 0, 128, 0, None, None, None, None)
     assert f(ctypes.byref(empty), ctypes.byref(empty), None, None, None) == V.OK   # n == 0: nothing to do
+
+
+@pytest.mark.parametrize("n, k", [(1, 64), (3, 192), (65, 320), (300, 4096)])
+def test_uniform_width_query_and_check(V, n, k):
+    for b in (1, 2, 4, 8):
+        h = V.vbq_pack(n, k, *W.draw_random_matrix((b, n, k), n, k, {b: 1.0}))
+        assert V.vbq_uniform_width(h) == b
+        v = h.view()
+        v.uniform_bits = b
+        assert V.lib.vbq_validate_host(ctypes.byref(v)) == V.OK
+        v.uniform_bits = 8 if b != 8 else 4
+        assert V.lib.vbq_validate_host(ctypes.byref(v)) == V.ERR_WIDTH
+        assert V.vbq_container_open(V.vbq_container_bytes(h)).view().uniform_bits == 0   # HostMatrix drops it
+        img = V.vbq_container_bytes(h)
+        view = V.VbqMatrix()
+        assert V.lib.vbq_container_open(img.ctypes.data, img.size, ctypes.byref(view)) == V.OK
+        assert view.uniform_bits == b
+    # one group of another width anywhere (including the last, ragged byte) makes it mixed
+    bits, codes, scales = W.draw_random_matrix((9, n, k), n, k, {2: 1.0})
+    for r, j in [(0, 0), (n - 1, k // 64 - 1), (n // 2, 0)]:
+        b2 = bits.copy()
+        b2[r, j] = 4
+        c2 = codes.copy()
+        assert V.vbq_uniform_width(V.vbq_pack(n, k, b2, c2, scales)) == (4 if n * (k // 64) == 1 else 0)
+    empty = V.vbq_pack(0, 128, np.zeros((0, 2), np.uint8), np.zeros((0, 128), np.int8), np.zeros((0, 2), np.uint16))
+    assert V.vbq_uniform_width(empty) == 0
