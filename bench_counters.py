@@ -149,7 +149,7 @@ def kernels_summary(a) -> str:
     with open(a.csv) as f:
         for row in csv.DictReader(f):
             name = row["Kernel_Name"]
-            if not any(k in name for k in ("gemv_tiles", "gemm_tiles", "unpack_tiles", "quantize_groups")):
+            if not any(k in name for k in ("gemv_tiles", "gemv_uniform", "gemm_tiles", "unpack_tiles", "quantize_groups")):
                 continue
             key = (name, row["Grid_Size_X"], row["Grid_Size_Y"])
             per.setdefault(key, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0)
