@@ -162,6 +162,13 @@ def test_head_recipe_ties_go_to_the_lower_row():
     assert bits[119] == 2 and bits[120] == 1
 
 
+def test_head_recipe_rounds_tier_edges_half_up():
+    # 300 rows: 0.5% is 1.5 rows -> 2, 2% is 6, 12% is 36; 100 rows: 0.5 -> 1, 2, 12
+    for rows, counts in ((300, {8: 2, 4: 4, 2: 30, 1: 264}), (100, {8: 1, 4: 1, 2: 10, 1: 88})):
+        bits = Q.head_bits(np.arange(rows)[::-1])
+        assert {b: int((bits == b).sum()) for b in (8, 4, 2, 1)} == counts
+
+
 def test_projection_recipe():
     assert Q.projection_bits(True) == 4 and Q.projection_bits(False) == 2
 
