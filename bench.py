@@ -250,6 +250,42 @@ def main():
                         "GBps": round(rbytes / (rms * 1e-3) / 1e9, 2),
                         "pct_hbm_peak": round(100 * rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
         del rlayers
+    # the recipe head (32000x4096, rows tiered 8/4/2/1 bits by a Zipf frequency rank): as four one-width
+    # row blocks in one launch, against the same rows in vocabulary order on the mixed-width kernel
+    hrows, hk = 32000, 4096
+    freq = np.minimum(np.random.default_rng(95).zipf(1.3, hrows), 10 ** 6).astype(np.uint64)
+    order = V.vbq_recipe_head_order(freq)
+    tier = V.vbq_recipe_head_bits(freq)[order]
+    full_bits = np.zeros((hrows, hk // 64), np.uint8)
+    full_codes = np.zeros((hrows, hk), np.int8)
+    full_scales = np.zeros((hrows, hk // 64), np.uint16)
+    blocks, start = [], 0
+    for t, b in enumerate((8, 4, 2, 1)):
+        cnt = int((tier == b).sum())
+        bb, bc, bs = W.draw_random_matrix((95, t), cnt, hk, {b: 1.0})
+        rows_t = order[start:start + cnt]
+        full_bits[rows_t], full_codes[rows_t], full_scales[rows_t] = bb, bc, bs
+        blocks.append(V.vbq_pack(cnt, hk, bb, bc, bs))
+        start += cnt
+    full = V.vbq_pack(hrows, hk, full_bits, full_codes, full_scales)
+    hbytes = full.total_bytes
+    hcopies = max(2, math.ceil(args.rotate_mb * 1e6 / hbytes))
+    grouped = [[V.DeviceMatrix(b, dev) for b in blocks] for _ in range(hcopies)]
+    vocab = [V.DeviceMatrix(full, dev) for _ in range(hcopies)]
+    hx = torch.from_numpy(W.draw_x((96,), hk)[0].view(np.float16)).to(dev)
+    hy = [torch.empty(b.n, dtype=torch.float32, device=dev) for b in blocks]
+    hyf = torch.empty(hrows, dtype=torch.float32, device=dev)
+    g_ms = timed(lambda i: V.vbq_gemv_multi(grouped[i % hcopies], [hx] * len(blocks), hy, stream))
+    # the same blocks with the largest (1-bit) first: its workgroups are dispatched first
+    gr_ms = timed(lambda i: V.vbq_gemv_multi(grouped[i % hcopies][::-1], [hx] * len(blocks), hy[::-1], stream))
+    v_ms = timed(lambda i: V.vbq_gemv(vocab[i % hcopies], hx, hyf, stream))
+    recipe["recipe_head_32000x4096"] = {
+        "mean_bits": round(float(V.vbq_recipe_head_bits(freq).astype(np.float64).mean()), 4),
+        "packed_bytes": hbytes, "grouped_one_launch_us": round(g_ms * 1e3, 3),
+        "grouped_GBps": round(hbytes / (g_ms * 1e-3) / 1e9, 2),
+        "grouped_largest_first_us": round(gr_ms * 1e3, 3), "vocabulary_order_us": round(v_ms * 1e3, 3),
+        "vocabulary_order_GBps": round(hbytes / (v_ms * 1e-3) / 1e9, 2)}
+    del grouped, vocab
     result["deployed_recipe"] = recipe
 
     # ---- dense fp16 GEMV of the same shapes (torch matmul on the same stream, rotated copies)

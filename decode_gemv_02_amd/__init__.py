@@ -78,6 +78,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
     lib.vbq_quantize.argtypes = [U32, U32, P, P, P, P, P]
     lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
+    lib.vbq_recipe_head_order.argtypes = [U32, P, P]
     lib.vbq_check_padding.argtypes = [ctypes.POINTER(VbqMatrix), U32, U32, U32]
     lib.vbq_container_size.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(ctypes.c_uint64)]
     lib.vbq_container_write.argtypes = [ctypes.POINTER(VbqMatrix), P, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
@@ -85,7 +86,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
-              lib.vbq_gemv_swiglu, lib.vbq_uniform_width):
+              lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -313,3 +314,32 @@ def vbq_save(path: str, m: HostMatrix) -> None:
 
 def vbq_load(path: str) -> HostMatrix:
     return vbq_container_open(np.fromfile(path, dtype=np.uint8))
+
+
+def vbq_recipe_head_order(freq: np.ndarray) -> np.ndarray:
+    """Vocabulary rows in rank order (descending frequency, ties to the lower row), uint32."""
+    freq = np.ascontiguousarray(freq, dtype=np.uint64).reshape(-1)
+    out = np.zeros(freq.size, np.uint32)
+    _check(lib.vbq_recipe_head_order(freq.size, _np_ptr(freq), _np_ptr(out)))
+    return out
+
+
+def vbq_pack_grouped_head(freq: np.ndarray, codes: np.ndarray, scales: np.ndarray):
+    """The recipe head as one-width row blocks: returns (order, [HostMatrix per tier present]).
+
+    codes int8 [rows][k] and scales uint16 [rows][k/64] are in vocabulary order and must follow the
+    widths vbq_recipe_head_bits(freq) gives each row. The blocks hold the rows of ranks order[0:...],
+    tier by tier (8, 4, 2, 1 bits); their outputs, concatenated, are the logits of rows `order`."""
+    order = vbq_recipe_head_order(freq)
+    bits = vbq_recipe_head_bits(freq)[order]
+    rows, k = codes.shape
+    blocks = []
+    start = 0
+    while start < rows:
+        b = int(bits[start])
+        end = start + int(np.argmax(bits[start:] != b)) if np.any(bits[start:] != b) else rows
+        sel = order[start:end]
+        blocks.append(vbq_pack(end - start, k, np.full((end - start, k // GROUP), b, np.uint8),
+                               np.ascontiguousarray(codes[sel]), np.ascontiguousarray(scales[sel])))
+        start = end
+    return order, blocks

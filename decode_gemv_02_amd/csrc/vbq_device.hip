@@ -176,6 +176,7 @@ struct MatArgs {
     uint32_t *counters;   // [row tiles] arrival counters when splits > 1 (self-resetting)
     uint32_t n, groups, col_tiles, splits, blocks;   // blocks = row tiles x splits
     uint32_t payload_bytes;
+    uint32_t ubits;   // the matrix's declared single width, or 0
 };
 
 
@@ -308,8 +309,10 @@ __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane, flo
     // 2-bit: pair factors 1,4,16,64,256,1,4,16 -> weights 1024/f + 2.
     const float a23 = x2 + x3;
     float xsum = a01 + a23;
-    float c4 = 1032.f * a01 + 72.f * a23;
-    float c2 = wa * a01 + wb * a23;
+    // explicit fma: every kernel that stages x rounds these the same way, whatever the compiler
+    // would contract in its own context
+    float c4 = fmaf(1032.f, a01, 72.f * a23);
+    float c2 = fmaf(wa, a01, wb * a23);
     xsum = row16_sum(xsum);
     c2 = row16_sum(c2);
     c4 = row16_sum(c4);
@@ -519,7 +522,7 @@ __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, ui
     float a = quarter8bit(L, jl, qd, va, vb);
     a += dpp<kQuadXor1>(a);
     a += dpp<kQuadXor2>(a);
-    if (qd == 0) store_part(L, info, a - 1152.f * L.corr[jl][0]);
+    if (qd == 0) store_part(L, info, fmaf(-1152.f, L.corr[jl][0], a));
 }
 
 // Payload of the first 256 one-bit groups and of the first 64 slices of
@@ -611,9 +614,9 @@ __device__ __forceinline__ void swiglu_pair(const Batch &B, uint32_t which, uint
 // The workgroup's row sums (waves added in wave order), the split-K
 // reduction when the row tile is split, then y or the gated-MLP epilogue.
 template <uint32_t kWaves>
-__device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M, WaveLds *lds, uint32_t wave,
-                                                bool spare, uint32_t a, uint32_t split, uint32_t r0, uint32_t rows,
-                                                uint32_t lane, float acc) {
+__device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M, uint32_t which, WaveLds *lds,
+                                                uint32_t wave, bool spare, uint32_t a, uint32_t split, uint32_t r0,
+                                                uint32_t rows, uint32_t lane, float acc) {
     lds[wave].part[lane] = acc;   // the wave's row sums, in its own (now idle) LDS
     __syncthreads();
     if (wave != 0 || spare) return;
@@ -621,9 +624,14 @@ __device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M
 #pragma unroll
     for (uint32_t w = 1; w < kWaves; ++w) sum += lds[w].part[lane];   // in wave order
     if (M.splits > 1) {
-        // Split row tile: publish the partial sums with coherent (agent-scope) stores,
-        // wait until they have landed, then count arrivals; the last workgroup adds
-        // the partials in split order and resets the counter for the next call.
+        // Split row tile: publish the partial sums with device-scope stores, wait
+        // until they have completed, then count arrivals; the last workgroup reads
+        // them with device-scope loads, adds them in split order and resets the
+        // counter for the next call. No cache holds an older copy of another
+        // split's partials: each line is written only by its split in this launch
+        // and read only by the last arriver, and caches are invalidated between
+        // launches. (Agent-scope release/acquire fences would write back and
+        // invalidate a whole L2 per workgroup: about 4 us per split launch.)
         if (lane < rows)
             __hip_atomic_store(&M.partial[static_cast<uint64_t>(split) * M.n + r0 + lane], sum, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
@@ -640,7 +648,7 @@ __device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M
         if (lane < rows) M.y[r0 + lane] = sum;
         return;
     }
-    swiglu_pair(B, blockIdx.y, a, r0 + lane, lane < rows, M.n, lane, sum);
+    swiglu_pair(B, which, a, r0 + lane, lane < rows, M.n, lane, sum);
 }
 
 // kWaves waves per workgroup (4, 8 or 16) share one row tile; the LDS
@@ -693,12 +701,12 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         if (lane < rows)
             for (uint32_t jl = 0; jl < cn; ++jl) {
                 const uint32_t sb = (jl < 2 ? cur.s01 >> (16 * jl) : cur.s23 >> (16 * (jl - 2))) & 0xFFFFu;
-                acc += half_to_float(sb) * L.part[jl * kTileRows + lane];
+                acc = fmaf(half_to_float(sb), L.part[jl * kTileRows + lane], acc);
             }
         wave_lds_sync();
         cur = nxt;
     }
-    finish_row_tile<kWaves>(B, M, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
+    finish_row_tile<kWaves>(B, M, blockIdx.y, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
 }
 
 // ---------------------------------------------------------------- uniform width
@@ -741,15 +749,18 @@ __device__ __forceinline__ float row_group_dot(WaveLds &L, uint32_t jl, const Ro
     for (uint32_t i = 0; i < 4; ++i)
         q[i] = quarter8bit(L, jl, i, make_uint2(g.v[i & (kBits / 2 - 1)].x, g.v[i & (kBits / 2 - 1)].y),
                            make_uint2(g.v[i & (kBits / 2 - 1)].z, g.v[i & (kBits / 2 - 1)].w));
-    return ((q[0] + q[1]) + (q[2] + q[3])) - 1152.f * L.corr[jl][0];
+    return fmaf(-1152.f, L.corr[jl][0], (q[0] + q[1]) + (q[2] + q[3]));
 }
 
-template <uint32_t kBits, bool kAligned, uint32_t kWaves>
-__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void gemv_uniform(Batch B) {
-    __shared__ WaveLds lds[kWaves];
-    const MatArgs M = B.m[blockIdx.y];
-    const bool spare = blockIdx.x >= M.blocks;
-    const uint32_t bx = spare ? M.blocks - 1 : blockIdx.x;
+// kLean: hold two 4-bit groups of a row at once instead of four (the per-matrix-width kernel, whose
+// register budget is the largest of its four paths plus the dispatch)
+template <uint32_t kBits, bool kAligned, uint32_t kWaves, bool kLean = false>
+__device__ __forceinline__ void uniform_tiles(const Batch &B, const MatArgs &M, uint32_t which, uint32_t bx,
+                                              WaveLds *lds) {
+    // A workgroup past its matrix's end leaves at once: with matrices of very different sizes in one
+    // launch (a head grouped by width) repeating the last row tile would multiply the work.
+    if (bx >= M.blocks) return;
+    const bool spare = false;
     const uint32_t a = bx / M.splits, split = bx % M.splits;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
     const uint32_t r0 = a * kTileRows;
@@ -761,7 +772,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     const uint32_t km = lane0 & 3u;
     const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
     const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
-    constexpr uint32_t kChunk = kBits == 8 ? 1 : kTileGroups;   // groups of a row held at once
+    constexpr uint32_t kChunk = kBits == 8 ? 1 : (kBits == 4 && kLean) ? 2 : kTileGroups;   // groups held at once
     uint32_t ct = c_lo + wave;
     TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, relane(lane0), true);
     for (; ct < c_hi; ct += kWaves) {
@@ -790,13 +801,37 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
                 const uint32_t j = c0 + jl;
                 const uint32_t sb = (j < 2 ? cur.s01 >> (16 * j) : cur.s23 >> (16 * (j - 2))) & 0xFFFFu;
                 const float d = row_group_dot<kBits>(L, j, g[jl]);
-                if (lane < rows && j < cn) acc += half_to_float(sb) * d;
+                if (lane < rows && j < cn) acc = fmaf(half_to_float(sb), d, acc);
             }
         }
         wave_lds_sync();
         cur = nxt;
     }
-    finish_row_tile<kWaves>(B, M, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
+    finish_row_tile<kWaves>(B, M, which, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
+}
+
+template <uint32_t kBits, bool kAligned, uint32_t kWaves>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void gemv_uniform(Batch B) {
+    __shared__ WaveLds lds[kWaves];
+    const MatArgs M = B.m[blockIdx.y];   // by value: loaded into scalar registers once
+    uniform_tiles<kBits, kAligned, kWaves>(B, M, blockIdx.y, blockIdx.x, lds);
+}
+
+// One-width matrices of different widths in one launch (e.g. a head whose rows
+// are grouped by width): each workgroup takes its matrix's width, uniform over
+// the workgroup, so there is no divergence.
+template <bool kAligned, uint32_t kWaves>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void gemv_uniform_mixed(
+    Batch B) {
+    __shared__ WaveLds lds[kWaves];
+    const uint32_t which = blockIdx.y, bx = blockIdx.x;
+    const MatArgs M = B.m[which];
+    switch (M.ubits) {
+        case 1: uniform_tiles<1, kAligned, kWaves>(B, M, which, bx, lds); break;
+        case 2: uniform_tiles<2, kAligned, kWaves>(B, M, which, bx, lds); break;
+        case 4: uniform_tiles<4, kAligned, kWaves, true>(B, M, which, bx, lds); break;
+        default: uniform_tiles<8, kAligned, kWaves>(B, M, which, bx, lds); break;
+    }
 }
 
 // Decoded codes of every group, written at its natural position; the same
@@ -1450,9 +1485,21 @@ void gemv_dispatch_uniform(bool aligned, uint32_t blocks, uint32_t used, const B
                            B);
 }
 
-// ubits: the width every matrix of the launch has, or 0 (the mixed-width kernel)
+// ubits: the width every matrix of the launch has; kPerMatrix when each matrix declares a width but
+// they differ; 0 when some matrix declares none (the mixed-width kernel)
+constexpr uint32_t kPerMatrix = 0xFFu;
+
 template <uint32_t kWaves>
 void gemv_dispatch(bool aligned, uint32_t ubits, uint32_t blocks, uint32_t used, const Batch &B, hipStream_t stream) {
+    if (ubits == kPerMatrix) {
+        if (aligned)
+            hipLaunchKernelGGL((gemv_uniform_mixed<true, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0,
+                               stream, B);
+        else
+            hipLaunchKernelGGL((gemv_uniform_mixed<false, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0,
+                               stream, B);
+        return;
+    }
     switch (ubits) {
         case 1: gemv_dispatch_uniform<1, kWaves>(aligned, blocks, used, B, stream); return;
         case 2: gemv_dispatch_uniform<2, kWaves>(aligned, blocks, used, B, stream); return;
@@ -1484,12 +1531,17 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     size_t counter_slots = 0, partial_total = 0;
     uint32_t used = 0;
     bool any_launch = false;
-    // the uniform-width kernels run when every matrix launched declares the same width
+    // the uniform-width kernels run when every matrix launched declares a width: one kernel per width
+    // when they agree, the per-matrix dispatch when they differ
     uint32_t ubits = 0;
     bool first = true;
     for (uint32_t i = 0; i < count; ++i) {
         if (ws[i]->n == 0 || ws[i]->k == 0) continue;
-        ubits = first ? ws[i]->uniform_bits : (ubits == ws[i]->uniform_bits ? ubits : 0u);
+        const uint32_t b = ws[i]->uniform_bits;
+        if (first || b == 0 || ubits == 0)
+            ubits = first || ubits != 0 ? b : 0u;
+        else if (b != ubits)
+            ubits = kPerMatrix;
         first = false;
     }
     for (uint32_t i = 0; i < count; ++i) {
@@ -1508,6 +1560,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.tile_offsets = w->tile_offsets;
         M.payload = w->payload;
         M.payload_bytes = w->payload_bytes;
+        M.ubits = w->uniform_bits;
         M.x = xs[i];
         M.y = ys[i];
         M.n = w->n;

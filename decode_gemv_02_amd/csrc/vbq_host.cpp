@@ -271,13 +271,21 @@ extern "C" vbq_status vbq_validate_host(const vbq_matrix *w) {
 // VBQ §3.4, the frequency-tiered head: rank rows by descending frequency (ties
 // to the lower row), then cut the ranking at half-up roundings of 0.5%, 2% and
 // 12% of the rows into the 8-, 4- and 2-bit tiers; the rest get 1 bit.
+extern "C" vbq_status vbq_recipe_head_order(uint32_t rows, const uint64_t *freq, uint32_t *order) {
+    vbq::clear_error();
+    if (rows == 0) return VBQ_OK;
+    if (!freq || !order) return fail(VBQ_ERR_NULL, "vbq_recipe_head_order: a pointer is NULL");
+    for (uint32_t r = 0; r < rows; ++r) order[r] = r;
+    std::stable_sort(order, order + rows, [&](uint32_t a, uint32_t b) { return freq[a] > freq[b]; });
+    return VBQ_OK;
+}
+
 extern "C" vbq_status vbq_recipe_head_bits(uint32_t rows, const uint64_t *freq, uint8_t *bits_out) {
     vbq::clear_error();
     if (rows == 0) return VBQ_OK;
     if (!freq || !bits_out) return fail(VBQ_ERR_NULL, "vbq_recipe_head_bits: a pointer is NULL");
     std::vector<uint32_t> order(rows);
-    for (uint32_t r = 0; r < rows; ++r) order[r] = r;
-    std::stable_sort(order.begin(), order.end(), [&](uint32_t a, uint32_t b) { return freq[a] > freq[b]; });
+    vbq_recipe_head_order(rows, freq, order.data());
     const uint64_t cut8 = (5ull * rows + 500) / 1000, cut4 = (20ull * rows + 500) / 1000,
                    cut2 = (120ull * rows + 500) / 1000;
     for (uint64_t rank = 0; rank < rows; ++rank)

@@ -177,7 +177,8 @@ VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, vo
  * i < count <= VBQ_MAX_MULTI. ws, xs and ys are host arrays of count entries
  * (the matrix views and x / y pointers as for vbq_gemv). Matrices that read
  * the same activation (q/k/v, gate/up) or a whole layer's projections run as
- * one dispatch. Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (count),
+ * one dispatch. When every matrix declares a width (uniform_bits), the
+ * uniform-width kernels run, also when the declared widths differ. Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (count),
  * ALIGN, OFFSETS, HIP. Scratch: calls with large-k, small-n matrices use a
  * library-owned device buffer per (device, stream), allocated on first need;
  * calls that overlap on the same stream handle are not allowed. */
@@ -243,6 +244,15 @@ VBQ_API vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const ui
  * (gate, up, down) at 4 bits, all other attention and MLP projections at 2.
  * Errors: NULL (rows > 0 and a NULL pointer). */
 VBQ_API vbq_status vbq_recipe_head_bits(uint32_t rows, const uint64_t *freq, uint8_t *bits_out);
+
+/* The same ranking as vocabulary rows (host): order_out[i] = the row of
+ * rank i (descending frequency, ties to the lower row). The recipe's tiers
+ * are then the rank ranges [0, round(0.005 N)), [.., round(0.02 N)),
+ * [.., round(0.12 N)), [.., N): a head stored as four one-width matrices
+ * over those ranges runs as one launch of vbq_gemv_multi (each matrix
+ * declaring its width), and its outputs, concatenated, are the logits in
+ * rank order. Errors: NULL (rows > 0 and a NULL pointer). */
+VBQ_API vbq_status vbq_recipe_head_order(uint32_t rows, const uint64_t *freq, uint32_t *order_out);
 
 /* Export-time check of the padding contract (VBQ §6, "Granularity is
  * deployment-friendly": MLP intermediates are zero-padded so the contracted

@@ -400,3 +400,65 @@ def test_uniform_width_declaration_is_checked(V):
     assert V.lib.vbq_gemv(ctypes.byref(bad), x.data_ptr(), y.data_ptr(), None) == V.ERR_OFFSETS
     bad.uniform_bits = 3
     assert V.lib.vbq_gemv(ctypes.byref(bad), x.data_ptr(), y.data_ptr(), None) == V.ERR_WIDTH
+
+
+def test_grouped_recipe_head(V, torch_mod):
+    # the frequency-tiered head as four one-width row blocks in one launch (per-matrix widths): logits
+    # in rank order, mapped back through the row order, against the oracle on the vocabulary-order matrix
+    from oracle import quantize as Q
+    torch = torch_mod
+    rows, k = 4000, 1024
+    print_case(test="grouped_head", rows=rows, k=k)
+    freq = np.minimum(np.random.default_rng(80).zipf(1.3, rows), 10 ** 6).astype(np.uint64)
+    bits = np.repeat(Q.head_bits(freq)[:, None], k // 64, axis=1)
+    w = W.draw_weights((81,), rows, k)
+    codes, scales = Q.quantize(w, bits)
+    order, blocks = V.vbq_pack_grouped_head(freq, codes, scales)
+    dms = [V.DeviceMatrix(b) for b in blocks]
+    assert [d.uniform_bits for d in dms] == [8, 4, 2, 1]
+    x = W.draw_x((82,), k)
+    xt = torch.from_numpy(x.view(np.float16)).cuda()
+    ys = [torch.full((d.n,), float("nan"), dtype=torch.float32, device="cuda") for d in dms]
+    V.vbq_gemv_multi(dms, [xt[0]] * len(dms), ys)
+    torch.cuda.synchronize()
+    logits = np.empty(rows)
+    logits[order] = np.concatenate([y.cpu().numpy() for y in ys])
+    ref = oracle.gemv(oracle.pack(rows, k, bits, codes, scales), x[0])
+    assert_within_tolerance(logits[None], ref[None], x, scales, "grouped head")
+    # the vocabulary-order matrix on the mixed kernel agrees too, and so does a single block alone
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    V.vbq_gemv(V.DeviceMatrix(V.vbq_pack(rows, k, bits, codes, scales)), xt[0], y)
+    y1 = torch.empty(dms[2].n, dtype=torch.float32, device="cuda")
+    V.vbq_gemv(dms[2], xt[0], y1)
+    torch.cuda.synchronize()
+    assert_within_tolerance(y.cpu().numpy()[None], ref[None], x, scales, "vocabulary order")
+    assert np.array_equal(y1.cpu().numpy(), ys[2].cpu().numpy())
+
+
+def test_split_partials_are_never_read_stale(V, torch_mod):
+    # Two different matrices of one shape use the same split-K scratch slots. Alternating them many
+    # times, every call must give exactly its matrix's own result: a partial sum left in a cache by
+    # the other matrix's call would show as a large error. Covers the GEMV split tail, the gated-MLP
+    # pair buffer and the GEMM split tail.
+    torch = torch_mod
+    print_case(test="split_stale")
+    n, k = 128, 16384                       # few row tiles, long rows: split row tiles
+    mats = [V.DeviceMatrix(V.vbq_pack(n, k, *W.draw_random_matrix((85, i), n, k, W.STD_MIX))) for i in range(2)]
+    x = torch.from_numpy(W.draw_x((86,), k, 16).view(np.float16)).cuda()
+    first = {}
+    for it in range(24):
+        i = it % 2
+        y = torch.empty(n, dtype=torch.float32, device="cuda")
+        V.vbq_gemv(mats[i], x[0], y)
+        h = torch.empty(n, dtype=torch.float16, device="cuda")
+        V.vbq_gemv_swiglu(mats[i], mats[1 - i], x[0], h)
+        yg = torch.empty((16, n), dtype=torch.float32, device="cuda")
+        V.vbq_gemm_smallbatch(mats[i], x, yg)
+        torch.cuda.synchronize()
+        got = (y.cpu().numpy(), h.cpu().numpy(), yg.cpu().numpy())
+        if i not in first:
+            first[i] = got
+        else:
+            for a, b in zip(got, first[i]):
+                assert np.array_equal(a, b), f"iteration {it}: result changed between calls"
+    assert not np.array_equal(first[0][0], first[1][0])

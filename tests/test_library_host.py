@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
         "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize", "vbq_recipe_head_bits",
-        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width",
+        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width", "vbq_recipe_head_order",
         "vbq_status_string", "vbq_last_error"])
 
 
@@ -271,3 +271,27 @@ def test_uniform_width_query_and_check(V, n, k):
         assert V.vbq_uniform_width(V.vbq_pack(n, k, b2, c2, scales)) == (4 if n * (k // 64) == 1 else 0)
     empty = V.vbq_pack(0, 128, np.zeros((0, 2), np.uint8), np.zeros((0, 128), np.int8), np.zeros((0, 2), np.uint16))
     assert V.vbq_uniform_width(empty) == 0
+
+
+@pytest.mark.parametrize("rows", [1, 100, 300, 32000])
+def test_grouped_head_blocks(V, rows):
+    from oracle import quantize as Q
+    rng = np.random.default_rng(rows)
+    freq = np.minimum(rng.zipf(1.3, rows), 10 ** 6).astype(np.uint64)
+    order = V.vbq_recipe_head_order(freq)
+    # the reference ranking: descending frequency, ties to the lower row
+    assert np.array_equal(order, np.lexsort((np.arange(rows), -freq.astype(np.float64))))
+    k = 128
+    bits = Q.head_bits(freq)
+    w = W.draw_weights((rows, 5), rows, k)
+    codes, scales = Q.quantize(w, np.repeat(bits[:, None], k // 64, axis=1))
+    order2, blocks = V.vbq_pack_grouped_head(freq, codes, scales)
+    assert np.array_equal(order, order2)
+    assert sum(b.n for b in blocks) == rows
+    start = 0
+    for blk in blocks:
+        rws = order[start:start + blk.n]
+        width = V.vbq_uniform_width(blk)
+        assert width in (1, 2, 4, 8) and np.all(bits[rws] == width)
+        start += blk.n
+    assert [V.vbq_uniform_width(b) for b in blocks] == sorted({int(b) for b in bits}, reverse=True)
