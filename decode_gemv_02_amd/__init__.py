@@ -72,6 +72,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_gemv_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P), ctypes.POINTER(P),
                                    U32, P]
     lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
+    lib.vbq_gemv_multi_f16.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P),
+                                       ctypes.POINTER(P), U32, P]
     lib.vbq_gemv_swiglu.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(VbqMatrix), P, P, P]
     lib.vbq_uniform_width.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(U32)]
     lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
@@ -86,7 +88,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
-              lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order):
+              lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -231,6 +233,21 @@ def vbq_gemv_multi(ws, xs, ys, stream=None):
     ya = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
     dev = ws[0].device if count else torch.device("cuda")
     _check(lib.vbq_gemv_multi(wa, xa, ya, count, _stream_handle(stream, dev)))
+    return ys
+
+
+def vbq_gemv_multi_f16(ws, xs, ys, stream=None):
+    """vbq_gemv_multi with fp16 outputs (ys: float16 tensors)."""
+    count = len(ws)
+    assert len(xs) == count and len(ys) == count
+    for w, x, y in zip(ws, xs, ys):
+        assert x.dtype == torch.float16 and y.dtype == torch.float16 and x.is_contiguous() and y.is_contiguous()
+        assert x.numel() == w.k and y.numel() >= w.n
+    wa = (ctypes.POINTER(VbqMatrix) * max(count, 1))(*[ctypes.pointer(w.struct) for w in ws])
+    xa = (ctypes.c_void_p * max(count, 1))(*[x.data_ptr() for x in xs])
+    ya = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
+    dev = ws[0].device if count else torch.device("cuda")
+    _check(lib.vbq_gemv_multi_f16(wa, xa, ya, count, _stream_handle(stream, dev)))
     return ys
 
 

@@ -177,6 +177,7 @@ struct MatArgs {
     uint32_t n, groups, col_tiles, splits, blocks;   // blocks = row tiles x splits
     uint32_t payload_bytes;
     uint32_t ubits;   // the matrix's declared single width, or 0
+    uint16_t *y16;    // when set, y is stored here as fp16 (nearest even) instead of fp32 to y
 };
 
 
@@ -645,7 +646,12 @@ __device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M
         if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (!B.h) {
-        if (lane < rows) M.y[r0 + lane] = sum;
+        if (lane < rows) {
+            if (M.y16)
+                M.y16[r0 + lane] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sum));
+            else
+                M.y[r0 + lane] = sum;
+        }
         return;
     }
     swiglu_pair(B, which, a, r0 + lane, lane < rows, M.n, lane, sum);
@@ -1517,7 +1523,7 @@ void gemv_dispatch(bool aligned, uint32_t ubits, uint32_t blocks, uint32_t used,
 // matrices are gate and up (same shape, k > 0) and the launch writes
 // h = fp16(silu(gate x) * (up x)) instead of y.
 vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
-                       uint32_t count, hipStream_t stream, uint16_t *h = nullptr) {
+                       uint32_t count, hipStream_t stream, uint16_t *h = nullptr, uint16_t *const *ys16 = nullptr) {
     Batch B{};
     uint32_t blocks = 0, total_row_tiles = 0, max_col_tiles = 0;
     bool aligned = true;
@@ -1549,8 +1555,12 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         if (w->n == 0) continue;
         if (w->k == 0) {
             const uint64_t cnt = w->n;
-            hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream, ys[i],
-                               cnt);
+            if (ys16)
+                hipLaunchKernelGGL(fill_zero_u16, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream,
+                                   ys16[i], cnt);
+            else
+                hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream,
+                                   ys[i], cnt);
             any_launch = true;
             continue;
         }
@@ -1562,7 +1572,8 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.payload_bytes = w->payload_bytes;
         M.ubits = w->uniform_bits;
         M.x = xs[i];
-        M.y = ys[i];
+        M.y = ys ? ys[i] : nullptr;
+        M.y16 = ys16 ? ys16[i] : nullptr;
         M.n = w->n;
         M.groups = w->k / VBQ_GROUP;
         M.col_tiles = ceil_div(M.groups, kTileGroups);
@@ -1699,6 +1710,23 @@ extern "C" vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *
     const uint16_t *xs[2] = {x, x};
     float *ys[2] = {nullptr, nullptr};
     return gemv_launch(who, ws, xs, ys, 2, s, h);
+}
+
+extern "C" vbq_status vbq_gemv_multi_f16(const vbq_matrix *const *ws, const uint16_t *const *xs, uint16_t *const *ys,
+                                         uint32_t count, void *stream) {
+    vbq::clear_error();
+    const char *who = "vbq_gemv_multi_f16";
+    if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
+    if (count == 0) return VBQ_OK;
+    if (!ws || !xs || !ys) return fail(VBQ_ERR_NULL, "%s: ws, xs or ys is NULL", who);
+    for (uint32_t i = 0; i < count; ++i) {
+        vbq_status st = check_matrix(who, ws[i]);
+        if (st != VBQ_OK) return st;
+        st = check_vectors(who, ws[i], xs[i], ys[i]);
+        if (st != VBQ_OK) return st;
+    }
+    (void)hipGetLastError();
+    return gemv_launch(who, ws, xs, nullptr, count, static_cast<hipStream_t>(stream), nullptr, ys);
 }
 
 extern "C" vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream) {

@@ -185,6 +185,14 @@ VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, vo
 VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                                   uint32_t count, void *stream);
 
+/* vbq_gemv_multi with fp16 outputs: ys[i] is device binary16 [n_i], each
+ * value the fp32 result vbq_gemv_multi computes, rounded to nearest even
+ * (beyond the fp16 range: +-inf), so a projection feeds the next layer's
+ * fp16 input without a conversion launch. Same arguments, errors and
+ * scratch as vbq_gemv_multi otherwise. */
+VBQ_API vbq_status vbq_gemv_multi_f16(const vbq_matrix *const *ws, const uint16_t *const *xs, uint16_t *const *ys,
+                                      uint32_t count, void *stream);
+
 /* Gated-MLP front half in one launch (VBQ §6, "Granularity is
  * deployment-friendly", states the gated form silu(g) * u of the MLP
  * intermediates): g = gate x and u = up x exactly as vbq_gemv computes them

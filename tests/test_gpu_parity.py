@@ -462,3 +462,24 @@ def test_split_partials_are_never_read_stale(V, torch_mod):
             for a, b in zip(got, first[i]):
                 assert np.array_equal(a, b), f"iteration {it}: result changed between calls"
     assert not np.array_equal(first[0][0], first[1][0])
+
+
+@pytest.mark.parametrize("mix", ["std", "two_bit"])
+def test_fp16_outputs_are_the_rounded_fp32_outputs(V, torch_mod, mix):
+    # q/k/v-like launch (mixed or uniform kernel) and a split launch (long rows): every fp16 output is
+    # exactly the fp32 output of the same launch shape rounded to nearest even
+    torch = torch_mod
+    print_case(test="fp16_out", mix=mix)
+    m = {"std": W.STD_MIX, "two_bit": {2: 1.0}}[mix]
+    shapes = [(2048, 2048), (2048, 2048), (2048, 2048), (64, 14336)]
+    mats = [V.DeviceMatrix(V.vbq_pack(n, k, *W.draw_random_matrix((88, i), n, k, m))) for i, (n, k) in
+            enumerate(shapes)]
+    xs = [torch.from_numpy(W.draw_x((89, i), k)[0].view(np.float16)).cuda() for i, (n, k) in enumerate(shapes)]
+    for sel in ([0, 1, 2], [3]):
+        y32 = [torch.empty(shapes[i][0], dtype=torch.float32, device="cuda") for i in sel]
+        y16 = [torch.full((shapes[i][0],), float("nan"), dtype=torch.float16, device="cuda") for i in sel]
+        V.vbq_gemv_multi([mats[i] for i in sel], [xs[i] for i in sel], y32)
+        V.vbq_gemv_multi_f16([mats[i] for i in sel], [xs[i] for i in sel], y16)
+        torch.cuda.synchronize()
+        for a, b in zip(y32, y16):
+            assert torch.equal(a.half(), b)

@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
         "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize", "vbq_recipe_head_bits",
-        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width", "vbq_recipe_head_order",
+        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width", "vbq_recipe_head_order", "vbq_gemv_multi_f16",
         "vbq_status_string", "vbq_last_error"])
 
 
