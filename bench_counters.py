@@ -144,12 +144,15 @@ def kernels_summary(a) -> str:
 
     For the quantizer every grid is one matrix shape: a workgroup of 256 lanes covers 64 groups of
     64 weights, and each weight costs 5 + 3/64 algorithmic bytes (fp32 read, int8 code written, one
-    width byte read and one binary16 scale written per group), which gives alg_GBps."""
+    width byte read and one binary16 scale written per group), which gives alg_GBps. The soft
+    quantizer runs 16 lanes a group and moves 8 + 52/64 bytes a weight (fp32 read and written; per
+    group 32 bytes of logits and noise read, 16 of pi and 4 of expected bits written)."""
     per, meta = {}, {}
     with open(a.csv) as f:
         for row in csv.DictReader(f):
             name = row["Kernel_Name"]
-            if not any(k in name for k in ("gemv_tiles", "gemv_uniform", "gemm_tiles", "unpack_tiles", "quantize_groups")):
+            if not any(k in name for k in ("gemv_tiles", "gemv_uniform", "gemm_tiles", "unpack_tiles",
+                                           "quantize_groups", "chunk_sums", "mean_of_parts")):
                 continue
             key = (name, row["Grid_Size_X"], row["Grid_Size_Y"])
             per.setdefault(key, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0)
@@ -163,7 +166,10 @@ def kernels_summary(a) -> str:
         lines.append(f"kernel: {name} vgpr={r['VGPR_Count']} sgpr={r['SGPR_Count']} lds={r['LDS_Block_Size']} "
                      f"scratch={r['Scratch_Size']} grid={r['Grid_Size_X']}x{r['Grid_Size_Y']}")
         extra = ""
-        if "quantize_groups" in name:
+        if "soft_quantize_groups" in name:   # 16 lanes a group: weights = lanes * 4; 8 + 52/64 bytes a weight
+            weights = int(r["Grid_Size_X"]) * 4
+            extra = f" weights={weights} alg_GBps={weights * (8 + 52 / 64) / (statistics.fmean(d) * 1e3):.1f}"
+        elif "quantize_groups" in name:
             weights = int(r["Grid_Size_X"]) // 256 * 64 * 64
             extra = f" weights={weights} alg_GBps={weights * (5 + 3 / 64) / (statistics.fmean(d) * 1e3):.1f}"
         lines.append(f"  dispatches={len(d)} avg_us={statistics.fmean(d):.3f} median_us={statistics.median(d):.3f} "

@@ -12,7 +12,9 @@ Algorithmic bytes per weight: 4 (fp32 read) + 1 (int8 code written) + per
 5 + 3/64. The kernel streams each byte once, so HBM bandwidth bounds it.
 Timing: hipEvents on one stream around --passes passes over all matrices
 (1.4 GB of fp32 weights, far beyond the caches). The CPU baseline times the
-reference quantizer (numpy) on one 4096x4096 projection.
+reference quantizer (numpy) on one 4096x4096 projection. A second leg times
+the training-side soft quantizer (§3.2, vbq_soft_quantize) over the seven
+layer matrices: 8 + 52/64 algorithmic bytes per weight.
 
   python bench_quantize.py [--passes 20] [--warmup 3] [--no-cpu-baseline]
 """
@@ -110,6 +112,40 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4)},
         "per_matrix": per,
     }
+    # training-side soft quantizer (§3.2) over the seven layer matrices: per weight 4 bytes read and 4
+    # written, per 64-weight group 16 + 16 bytes of logits and noise read, 16 of pi and 4 of expected
+    # bits written: 8 + 52/64 bytes per weight
+    soft_bpw = 8 + 52 / 64
+    soft = [m for m in mats if m[0] != "head"]
+    sbufs = []
+    for name, n, k, w, *_ in soft:
+        g = n * (k // 64)
+        gen = torch.Generator(device=dev).manual_seed(n + k)
+        lg = torch.randn(g, 4, device=dev, generator=gen)
+        u = torch.rand(g, 4, device=dev, generator=gen).clamp_(1e-7, 1 - 1e-7)
+        sbufs.append((w, lg, -torch.log(-torch.log(u)), torch.empty_like(w), torch.empty(g, 4, device=dev),
+                      torch.empty(g, device=dev), torch.empty(1, dtype=torch.float64, device=dev)))
+    sweights = sum(n * k for _, n, k, *_ in soft)
+
+    def soft_pass():
+        for w, lg, gu, ws, pi, gb, mb in sbufs:
+            V.vbq_soft_quantize(w, lg, gu, 1.0, ws, pi, gb, mb, stream)
+
+    for _ in range(args.warmup):
+        soft_pass()
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.passes):
+        soft_pass()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    sms = t0.elapsed_time(t1) / args.passes
+    result["soft_quantize"] = {"weights_per_pass": sweights, "alg_bytes_per_weight": round(soft_bpw, 5),
+                               "ms_per_pass": round(sms, 4),
+                               "GBps": round(sweights * soft_bpw / (sms * 1e-3) / 1e9, 1),
+                               "pct_hbm_peak": round(100 * sweights * soft_bpw / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                               "workload": "the seven 9B-layer matrices, tau 1.0, N(0,1) logits, Gumbel noise"}
+    del sbufs
     if not args.no_cpu_baseline:
         from oracle import quantize as Q
         n, k = 4096, 4096

@@ -79,6 +79,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
     lib.vbq_quantize.argtypes = [U32, U32, P, P, P, P, P]
+    lib.vbq_soft_quantize.argtypes = [U32, U32, P, P, P, ctypes.c_float, P, P, P, P, P]
     lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
     lib.vbq_recipe_head_order.argtypes = [U32, P, P]
     lib.vbq_check_padding.argtypes = [ctypes.POINTER(VbqMatrix), U32, U32, U32]
@@ -88,7 +89,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     for f in (lib.vbq_pack_sizes, lib.vbq_pack, lib.vbq_validate_host, lib.vbq_gemv, lib.vbq_gemv_multi,
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
-              lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16):
+              lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16,
+              lib.vbq_soft_quantize):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -360,3 +362,20 @@ def vbq_pack_grouped_head(freq: np.ndarray, codes: np.ndarray, scales: np.ndarra
                                np.ascontiguousarray(codes[sel]), np.ascontiguousarray(scales[sel])))
         start = end
     return order, blocks
+
+
+def vbq_soft_quantize(w: torch.Tensor, logits: torch.Tensor, gumbel: torch.Tensor, tau: float, w_soft: torch.Tensor,
+                      pi: torch.Tensor, group_bits: torch.Tensor, mean_bits: torch.Tensor, stream=None):
+    """§3.2 soft quantizer on the device: w fp32 [n][k]; logits, gumbel, pi fp32 [n*k/64][4];
+    w_soft fp32 [n][k]; group_bits fp32 [n*k/64]; mean_bits float64 [1]."""
+    assert w.dtype == torch.float32 and w.dim() == 2 and w.is_contiguous()
+    n, k = w.shape
+    groups = n * (k // GROUP)
+    for t, dt, cnt in ((logits, torch.float32, 4 * groups), (gumbel, torch.float32, 4 * groups),
+                       (pi, torch.float32, 4 * groups), (w_soft, torch.float32, n * k),
+                       (group_bits, torch.float32, groups), (mean_bits, torch.float64, 1)):
+        assert t.dtype == dt and t.is_contiguous() and t.numel() >= cnt
+    _check(lib.vbq_soft_quantize(n, k, w.data_ptr(), logits.data_ptr(), gumbel.data_ptr(), float(tau),
+                                 w_soft.data_ptr(), pi.data_ptr(), group_bits.data_ptr(), mean_bits.data_ptr(),
+                                 _stream_handle(stream, w.device)))
+    return w_soft, pi, group_bits, mean_bits

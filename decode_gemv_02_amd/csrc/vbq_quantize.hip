@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
+#include <unordered_map>
 
 #include "vbq_internal.h"
 
@@ -119,6 +121,100 @@ __global__ __launch_bounds__(kBlock) void quantize_groups(const float4 *__restri
     }
 }
 
+// ---------------------------------------------------------------- soft quantizer (training side)
+// VBQ §3.2 "Differentiable bit selection": per group, pi = softmax((logits + e) / tau) over the widths
+// (1, 2, 4, 8) mixes the group's Eq. (1) reconstructions at the four widths, and the group's expected
+// width is sum_k pi_k * B_k. At training time the scales stay fp32 (no binary16 rounding); scales, ratios
+// and code decisions are fp32 as in the hard quantizer, the 1-bit mean is summed in fp64.
+__device__ __forceinline__ float recon_code(float w, float s, float qmax) {
+    if (s == 0.f) return 0.f;
+    return fminf(fmaxf(roundf(__fdiv_rn(w, s)), -qmax), qmax);
+}
+
+__global__ __launch_bounds__(kBlock) void soft_quantize_groups(const float4 *__restrict__ w,
+                                                              const float4 *__restrict__ logits,
+                                                              const float4 *__restrict__ gumbel, float tau,
+                                                              float4 *__restrict__ w_soft, float4 *__restrict__ pi,
+                                                              float *__restrict__ group_bits, uint64_t groups) {
+    const uint64_t t = static_cast<uint64_t>(blockIdx.x) * kBlock + threadIdx.x;
+    const uint64_t g = t / kLanesPerGroup;   // whole 16-lane teams share a group: they leave together
+    if (g >= groups) return;
+    const float4 v = w[t];
+    const float4 l = logits[g], e = gumbel[g];
+    const float z0 = __fdiv_rn(l.x + e.x, tau), z1 = __fdiv_rn(l.y + e.y, tau);
+    const float z2 = __fdiv_rn(l.z + e.z, tau), z3 = __fdiv_rn(l.w + e.w, tau);
+    const float zm = fmaxf(fmaxf(z0, z1), fmaxf(z2, z3));
+    const float p0 = expf(z0 - zm), p1 = expf(z1 - zm), p2 = expf(z2 - zm), p3 = expf(z3 - zm);
+    const float ps = (p0 + p1) + (p2 + p3);
+    const float4 pk = make_float4(__fdiv_rn(p0, ps), __fdiv_rn(p1, ps), __fdiv_rn(p2, ps), __fdiv_rn(p3, ps));
+    const float m0 = fabsf(v.x), m1 = fabsf(v.y), m2 = fabsf(v.z), m3 = fabsf(v.w);
+    const float s1 = static_cast<float>(group_sum(((static_cast<double>(m0) + m1) + m2) + m3) * (1.0 / 64.0));
+    const float amax = group_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+    const float s2 = amax, s4 = __fdiv_rn(amax, 7.f), s8 = __fdiv_rn(amax, 127.f);
+    const float c1 = pk.x * s1, c2 = pk.y * s2, c4 = pk.z * s4, c8 = pk.w * s8;
+    auto mix = [&](float x) {
+        const float q1 = x < 0.f ? -1.f : 1.f;
+        return fmaf(c8, recon_code(x, s8, 127.f),
+                    fmaf(c4, recon_code(x, s4, 7.f), fmaf(c2, recon_code(x, s2, 1.f), c1 * q1)));
+    };
+    w_soft[t] = make_float4(mix(v.x), mix(v.y), mix(v.z), mix(v.w));
+    if ((t & (kLanesPerGroup - 1)) == 0) {
+        pi[g] = pk;
+        group_bits[g] = fmaf(8.f, pk.w, fmaf(4.f, pk.z, fmaf(2.f, pk.y, pk.x)));
+    }
+}
+
+// Mean of group_bits[0, groups) in fp64, in a fixed order: workgroup b of the first kernel adds the
+// contiguous chunk [b * chunk, (b + 1) * chunk) (strided per lane, then a tree), the second adds the
+// partial sums (a tree over at most kParts values).
+constexpr uint32_t kParts = 1024;
+
+__global__ __launch_bounds__(256) void chunk_sums(const float *__restrict__ group_bits, uint64_t groups,
+                                                  uint64_t chunk, double *__restrict__ part) {
+    __shared__ double s[256];
+    const uint64_t lo = static_cast<uint64_t>(blockIdx.x) * chunk;
+    const uint64_t hi = lo + chunk < groups ? lo + chunk : groups;
+    double acc = 0.0;
+    for (uint64_t i = lo + threadIdx.x; i < hi; i += 256) acc += group_bits[i];
+    s[threadIdx.x] = acc;
+    __syncthreads();
+    for (uint32_t half = 128; half > 0; half >>= 1) {
+        if (threadIdx.x < half) s[threadIdx.x] += s[threadIdx.x + half];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[blockIdx.x] = s[0];
+}
+
+__global__ __launch_bounds__(kParts) void mean_of_parts(const double *__restrict__ part, uint32_t parts,
+                                                        uint64_t groups, double *__restrict__ out) {
+    __shared__ double s[kParts];
+    s[threadIdx.x] = threadIdx.x < parts ? part[threadIdx.x] : 0.0;
+    __syncthreads();
+    for (uint32_t half = kParts / 2; half > 0; half >>= 1) {
+        if (threadIdx.x < half) s[threadIdx.x] += s[threadIdx.x + half];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = groups ? s[0] / static_cast<double>(groups) : 0.0;
+}
+
+// kParts doubles of device scratch per (device, stream), allocated on first use and kept
+std::mutex g_parts_mu;
+std::unordered_map<uint64_t, double *> g_parts;
+
+vbq_status parts_for(hipStream_t stream, double **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_soft_quantize: hipGetDevice failed");
+    const uint64_t key = (static_cast<uint64_t>(dev) << 56) ^ reinterpret_cast<uintptr_t>(stream);
+    std::lock_guard<std::mutex> lock(g_parts_mu);
+    double *&p = g_parts[key];
+    if (!p && hipMalloc(reinterpret_cast<void **>(&p), kParts * sizeof(double)) != hipSuccess) {
+        p = nullptr;
+        return fail(VBQ_ERR_HIP, "vbq_soft_quantize: scratch hipMalloc failed");
+    }
+    *out = p;
+    return VBQ_OK;
+}
+
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 }  // namespace
@@ -141,5 +237,50 @@ extern "C" vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const
                        reinterpret_cast<uint32_t *>(codes_out), scales_out, groups);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_quantize: launch failed: %s", hipGetErrorString(e));
+    return VBQ_OK;
+}
+
+extern "C" vbq_status vbq_soft_quantize(uint32_t n, uint32_t k, const float *w, const float *logits,
+                                        const float *gumbel, float tau, float *w_soft, float *pi, float *group_bits,
+                                        double *mean_bits, void *stream) {
+    vbq::clear_error();
+    if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: k=%u is not a multiple of 64", k);
+    if (!(tau > 0.f) || tau > 3.0e38f) return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: tau must be positive and finite");
+    if (!mean_bits) return fail(VBQ_ERR_NULL, "vbq_soft_quantize: mean_bits is NULL");
+    if (!aligned(mean_bits, 8)) return fail(VBQ_ERR_ALIGN, "vbq_soft_quantize: mean_bits must be 8-byte aligned");
+    const uint64_t groups = static_cast<uint64_t>(n) * (k / VBQ_GROUP);
+    const uint64_t blocks = (groups * kLanesPerGroup + kBlock - 1) / kBlock;
+    if (groups) {
+        if (!w || !logits || !gumbel || !w_soft || !pi || !group_bits)
+            return fail(VBQ_ERR_NULL, "vbq_soft_quantize: a pointer is NULL");
+        if (!aligned(w, 16) || !aligned(w_soft, 16) || !aligned(logits, 16) || !aligned(gumbel, 16) ||
+            !aligned(pi, 16) || !aligned(group_bits, 4))
+            return fail(VBQ_ERR_ALIGN, "vbq_soft_quantize: w, w_soft, logits, gumbel and pi must be 16-byte aligned");
+        if (blocks > 0x7FFFFFFFull)
+            return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: %llu groups exceed one launch",
+                        static_cast<unsigned long long>(groups));
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    double *parts = nullptr;
+    const vbq_status ps = parts_for(s, &parts);
+    if (ps != VBQ_OK) return ps;
+    (void)hipGetLastError();
+    if (groups == 0) {   // no group: the mean is taken as 0
+        hipLaunchKernelGGL(mean_of_parts, dim3(1), dim3(kParts), 0, s, static_cast<const double *>(parts), 0u,
+                           uint64_t(0), mean_bits);
+    } else {
+        hipLaunchKernelGGL(soft_quantize_groups, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
+                           reinterpret_cast<const float4 *>(w), reinterpret_cast<const float4 *>(logits),
+                           reinterpret_cast<const float4 *>(gumbel), tau, reinterpret_cast<float4 *>(w_soft),
+                           reinterpret_cast<float4 *>(pi), group_bits, groups);
+        const uint64_t chunk = (groups + kParts - 1) / kParts;
+        const uint32_t nparts = static_cast<uint32_t>((groups + chunk - 1) / chunk);
+        hipLaunchKernelGGL(chunk_sums, dim3(nparts), dim3(256), 0, s, static_cast<const float *>(group_bits), groups,
+                           chunk, parts);
+        hipLaunchKernelGGL(mean_of_parts, dim3(1), dim3(kParts), 0, s, static_cast<const double *>(parts), nparts,
+                           groups, mean_bits);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_soft_quantize: launch failed: %s", hipGetErrorString(e));
     return VBQ_OK;
 }

@@ -242,6 +242,25 @@ VBQ_API vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, void
 VBQ_API vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const uint8_t *bits, int8_t *codes_out,
                                 uint16_t *scales_out, void *stream);
 
+/* Training-side soft quantizer (VBQ §3.2, "Differentiable bit selection";
+ * device, asynchronous on `stream`). Per group g of w (fp32 [n][k], 16-byte
+ * aligned): pi_g = softmax((logits_g + gumbel_g) / tau) over the widths
+ * (1, 2, 4, 8), w_soft = sum_k pi_g,k * w_hat^(B_k) with w_hat^(b) Eq. (1)
+ * at width b with an fp32 scale (no binary16 rounding; fp32 division and
+ * ties away from zero as in vbq_quantize, the 1-bit mean summed in fp64),
+ * group_bits[g] = sum_k pi_g,k * B_k, and *mean_bits = the mean of
+ * group_bits over the groups, summed in fp64 in a fixed order (0 when there
+ * is no group). logits, gumbel, pi: fp32 [n*k/64][4] (the Gumbel noise is
+ * the caller's draw); w_soft fp32 [n][k]; group_bits fp32 [n*k/64];
+ * mean_bits one double. w, w_soft, logits, gumbel and pi 16-byte aligned,
+ * group_bits 4, mean_bits 8; the caller owns every buffer. The mean uses an
+ * 8 KiB library-owned device buffer per (device, stream), allocated on first
+ * need; calls that overlap on one stream handle are not allowed. Errors: SHAPE
+ * (k % 64, tau not positive and finite, too many groups), NULL, ALIGN, HIP. */
+VBQ_API vbq_status vbq_soft_quantize(uint32_t n, uint32_t k, const float *w, const float *logits,
+                                     const float *gumbel, float tau, float *w_soft, float *pi, float *group_bits,
+                                     double *mean_bits, void *stream);
+
 /* The fixed recipe's head widths (VBQ §3.4, host): one width per vocabulary
  * row from its token frequency freq[rows]. Rows are ranked by descending
  * frequency (ties: lower row first); with N rows, the first round(0.005 N)

@@ -114,3 +114,50 @@ def head_bits(freq: np.ndarray) -> np.ndarray:
     out[rank < cut[1]] = 4
     out[rank < cut[0]] = 8
     return out
+
+
+# ---------------------------------------------------------------- soft quantizer (training side)
+# VBQ §3.2 "Differentiable bit selection": each group has logits over the widths (1, 2, 4, 8); a
+# Gumbel-Softmax sample pi = softmax((logits + e) / tau) mixes the group's reconstructions at the four
+# widths, w_soft = sum_k pi_k * w_hat^(B_k), and the expected bit cost is the mean over groups of
+# sum_k pi_k * B_k. Readings (the pages leave these open):
+#   S1 the Gumbel noise e is an input (drawn by the caller), one value per group and width;
+#   S2 w_hat^(b) is Eq. (1) at training time: the scale stays fp32 (no binary16 rounding), computed as in
+#      Q1 (fp32 max and division; the 1-bit mean summed in fp64 and rounded once to fp32), codes as in
+#      Q3/Q4 with that scale; the code decisions are taken in fp32, as the device takes them;
+#   S3 the softmax, the mixture and the bit cost are fp64 here;
+#   S4 the mean in the bit cost runs over groups (every group has 64 weights, so it is also the mean
+#      over weights).
+WIDTHS = (1, 2, 4, 8)
+
+
+def training_reconstruction(w: np.ndarray, b: int) -> np.ndarray:
+    """w_hat^(b) per group of w (fp32 [n][k]) with fp32 scales (S2); returns float64 [n][k]."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    g = w.reshape(-1, 64)
+    mag = np.abs(g)
+    if b == 1:
+        s = (mag.astype(np.float64).sum(axis=1) / 64.0).astype(np.float32)
+        q = np.where(g < 0, -1.0, 1.0)
+    else:
+        qmax = np.float32(2 ** (b - 1) - 1)
+        s = mag.max(axis=1) / qmax
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = g / s[:, None]
+        q = np.clip(_round_half_away(r), -qmax, qmax)
+        q = np.where(s[:, None] == 0, 0.0, q)
+    return (q.astype(np.float64) * s.astype(np.float64)[:, None]).reshape(n, k)
+
+
+def soft_quantize(w: np.ndarray, logits: np.ndarray, gumbel: np.ndarray, tau: float):
+    """Returns (w_soft float64 [n][k], pi float64 [groups][4], mean expected bits)."""
+    n, k = w.shape
+    z = (np.asarray(logits, np.float64).reshape(-1, 4) + np.asarray(gumbel, np.float64).reshape(-1, 4)) / tau
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    pi = e / e.sum(axis=1, keepdims=True)
+    recon = [training_reconstruction(w, b).reshape(-1, 64) for b in WIDTHS]
+    w_soft = sum(pi[:, i:i + 1] * recon[i] for i in range(4)).reshape(n, k)
+    bits = float((pi * np.array(WIDTHS, np.float64)).sum(axis=1).mean()) if pi.size else 0.0
+    return w_soft, pi, bits

@@ -173,3 +173,55 @@ def test_padded_and_container_matrices_on_device(V):
     assert_within_tolerance(ys[0][None], y_ref[None], x, rs, "padded")
     assert_within_tolerance(ys[1][None], y_ref[None], x, rs, "unpadded")
     assert np.array_equal(ys[0], ys[2])      # a matrix read back from its container runs identically
+
+
+# ---------------------------------------------------------------- soft quantizer (§3.2)
+
+def gpu_soft(V, w, logits, gumbel, tau):
+    import torch
+    n, k = w.shape
+    g = n * (k // 64)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()   # noqa: E731
+    ws = torch.full((n, k), float("nan"), device="cuda")
+    pi = torch.full((g, 4), float("nan"), device="cuda")
+    gb = torch.full((g,), float("nan"), device="cuda")
+    mb = torch.full((1,), float("nan"), dtype=torch.float64, device="cuda")
+    V.vbq_soft_quantize(t(w), t(logits), t(gumbel), tau, ws, pi, gb, mb)
+    torch.cuda.synchronize()
+    return ws.cpu().numpy(), pi.cpu().numpy(), gb.cpu().numpy(), float(mb.cpu().numpy()[0])
+
+
+@pytest.mark.parametrize("n, k", [(3, 128), (65, 320), (300, 4160), (4096, 4096)])
+@pytest.mark.parametrize("tau", [5.0, 0.5])
+def test_soft_quantizer_parity(V, n, k, tau):
+    print_case(test="soft_quantize", n=n, k=k, tau=tau)
+    g = n * (k // 64)
+    rng = np.random.default_rng((n, k, int(tau * 10)))
+    w = W.draw_weights((n, k, 7), n, k)
+    logits = (rng.standard_normal((g, 4)) * 2).astype(np.float32)
+    gumbel = (-np.log(-np.log(rng.random((g, 4)) * (1 - 2e-7) + 1e-7))).astype(np.float32)
+    ws, pi, gb, mb = gpu_soft(V, w, logits, gumbel, tau)
+    rws, rpi, rbits = Q.soft_quantize(w, logits, gumbel, tau)
+    assert np.abs(pi - rpi).max() <= 2e-6
+    assert np.abs(gb - (rpi * np.array(Q.WIDTHS)).sum(axis=1)).max() <= 2e-5
+    assert abs(mb - rbits) <= 1e-6 * rbits
+    rec = np.stack([np.abs(Q.training_reconstruction(w, b)).reshape(-1, 64).max(axis=1) for b in Q.WIDTHS])
+    bound = np.repeat(1e-5 * rec.max(axis=0), 64).reshape(n, k) + 1e-12
+    err = np.abs(ws - rws)
+    assert np.all(err <= bound), f"max error {err.max():.3e}"
+
+
+def test_soft_quantizer_one_hot_is_the_exact_reconstruction(V):
+    # a dominant logit makes pi exactly one-hot in fp32, so w_soft is that width's reconstruction: the
+    # code decisions match the reference exactly, up to the fp32 rounding of s * q
+    n, k = 200, 1024
+    print_case(test="soft_one_hot")
+    w = W.draw_weights((90,), n, k)
+    g = n * (k // 64)
+    for i, b in enumerate(Q.WIDTHS):
+        logits = np.full((g, 4), -60.0, np.float32)
+        logits[:, i] = 60.0
+        ws, pi, gb, mb = gpu_soft(V, w, logits, np.zeros((g, 4), np.float32), 1.0)
+        ref = Q.training_reconstruction(w, b)
+        assert np.all(pi[:, i] == 1.0) and np.all(gb == b) and mb == b
+        assert np.all(np.abs(ws - ref) <= np.abs(ref) * 2.0 ** -24), f"b={b}"

@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
         "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize", "vbq_recipe_head_bits",
-        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width", "vbq_recipe_head_order", "vbq_gemv_multi_f16",
+        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width", "vbq_recipe_head_order", "vbq_gemv_multi_f16", "vbq_soft_quantize",
         "vbq_status_string", "vbq_last_error"])
 
 
@@ -295,3 +295,17 @@ def test_grouped_head_blocks(V, rows):
         assert width in (1, 2, 4, 8) and np.all(bits[rws] == width)
         start += blk.n
     assert [V.vbq_uniform_width(b) for b in blocks] == sorted({int(b) for b in bits}, reverse=True)
+
+
+def test_soft_quantize_rejects_bad_arguments_without_launching(V):
+    buf = np.zeros(8192, np.uint8)
+    b = (buf.ctypes.data + 255) // 256 * 256
+    f = V.lib.vbq_soft_quantize
+    assert f(2, 100, b, b, b, 1.0, b, b, b, b, None) == V.ERR_SHAPE
+    for tau in (0.0, -1.0, float("inf"), float("nan")):
+        assert f(2, 128, b, b, b, tau, b, b, b, b, None) == V.ERR_SHAPE
+    assert f(2, 128, b, b, b, 1.0, b, b, b, None, None) == V.ERR_NULL
+    assert f(2, 128, None, b, b, 1.0, b, b, b, b, None) == V.ERR_NULL
+    assert f(2, 128, b, b, b, 1.0, b, b, b, b + 4, None) == V.ERR_ALIGN
+    assert f(2, 128, b + 8, b, b, 1.0, b, b, b, b, None) == V.ERR_ALIGN
+    assert f(2, 128, b, b + 8, b, 1.0, b, b, b, b, None) == V.ERR_ALIGN

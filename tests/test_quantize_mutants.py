@@ -24,7 +24,7 @@ MUTANTS = {
                                    "r = g[sel] / (mag[sel].max(axis=1) / qmax)[:, None]"),
     "one_bit_mean_through_fp32": ("mean = mag[one].astype(np.float64).sum(axis=1) / 64.0",
                                   "mean = (mag[one].astype(np.float64).sum(axis=1) / 64.0).astype(np.float32)"),
-    "one_bit_mean_count": ("sum(axis=1) / 64.0", "sum(axis=1) / 63.0"),
+    "one_bit_mean_count": ("mean = mag[one].astype(np.float64).sum(axis=1) / 64.0", "mean = mag[one].astype(np.float64).sum(axis=1) / 63.0"),
     "absmean_for_wide_groups": ("s16 = _stored_scale(mag[sel].max(axis=1) / qmax)",
                                 "s16 = _stored_scale(mag[sel].mean(axis=1) / qmax)"),
     "no_saturation": ("return np.where(np.isinf(s16), FP16_MAX, s16)", "return s16"),
@@ -36,6 +36,15 @@ MUTANTS = {
     "ascending_frequency": ("np.lexsort((np.arange(rows), -freq.astype(np.float64)))",
                             "np.lexsort((np.arange(rows), freq.astype(np.float64)))"),
     "first_block_flipped": ("return 4 if first_block_mlp else 2", "return 2 if first_block_mlp else 4"),
+    "soft_tau_ignored": ("np.asarray(gumbel, np.float64).reshape(-1, 4)) / tau", "np.asarray(gumbel, np.float64).reshape(-1, 4))"),
+    "soft_noise_dropped": ("(np.asarray(logits, np.float64).reshape(-1, 4) + np.asarray(gumbel, np.float64).reshape(-1, 4))",
+                           "(np.asarray(logits, np.float64).reshape(-1, 4) + 0 * np.asarray(gumbel, np.float64).reshape(-1, 4))"),
+    "soft_widths_reversed": ("recon = [training_reconstruction(w, b).reshape(-1, 64) for b in WIDTHS]",
+                             "recon = [training_reconstruction(w, b).reshape(-1, 64) for b in WIDTHS[::-1]]"),
+    "soft_cost_uses_index": ("bits = float((pi * np.array(WIDTHS, np.float64)).sum(axis=1).mean())",
+                             "bits = float((pi * np.arange(1, 5, dtype=np.float64)).sum(axis=1).mean())"),
+    "training_scale_rounded_to_half": ("        s = mag.max(axis=1) / qmax\n",
+                                       "        s = (mag.max(axis=1) / qmax).astype(np.float16).astype(np.float32)\n"),
 }
 
 PINS = [(P.test_codes_are_the_nearest_grid_point_of_the_stored_scale, (b,)) for b in (2, 4, 8)] + \
@@ -46,7 +55,9 @@ PINS = [(P.test_codes_are_the_nearest_grid_point_of_the_stored_scale, (b,)) for 
                           P.test_mixed_widths_pick_each_groups_rule, P.test_head_recipe_mean_is_the_pages_1_18_bits,
                           P.test_head_recipe_ties_go_to_the_lower_row,
                           P.test_head_recipe_rounds_tier_edges_half_up, P.test_projection_recipe,
-                          P.test_dequantize_error_bound)]
+                          P.test_dequantize_error_bound,
+                          P.test_training_reconstruction_is_the_nearest_grid_point_with_fp32_scale,
+                          P.test_soft_quantizer_limits_and_bit_cost)]
 
 
 def load_variant(text, path):

@@ -184,3 +184,58 @@ def test_dequantize_error_bound():
     qmax = np.repeat((2 ** (bits.astype(int) - 1) - 1), 64, axis=1)
     inside = np.abs(codes) < qmax
     assert np.all(np.abs(w - wh)[inside] <= s[inside] / 2 * (1 + 1e-6))
+
+
+# ---------------------------------------------------------------- soft quantizer (§3.2)
+
+def test_training_reconstruction_is_the_nearest_grid_point_with_fp32_scale():
+    rng = np.random.default_rng(21)
+    w = (rng.standard_normal((6, 256)) * 0.03).astype(np.float32)
+    for b in (2, 4, 8):
+        wh = Q.training_reconstruction(w, b)
+        qmax = 2 ** (b - 1) - 1
+        for r in range(6):
+            for j in range(4):
+                g = w[r, 64 * j:64 * j + 64]
+                s = float(np.float32(np.abs(g).max()) / np.float32(qmax))
+                grid = s * np.arange(-qmax, qmax + 1)
+                err = np.abs(g.astype(np.float64)[:, None] - grid[None, :])
+                best = grid[err.argmin(axis=1)]
+                tie = np.sort(err, axis=1)[:, 1] - err.min(axis=1) < 1e-12
+                assert np.allclose(wh[r, 64 * j:64 * j + 64][~tie], best[~tie], rtol=0, atol=1e-12)
+    one = Q.training_reconstruction(w, 1)
+    assert np.allclose(np.abs(one[:, :64]), np.abs(w[:, :64]).astype(np.float64).mean(axis=1, keepdims=True),
+                       rtol=1e-7)
+    assert np.array_equal(np.sign(one), np.where(w < 0, -1.0, 1.0))
+
+
+def test_soft_quantizer_limits_and_bit_cost():
+    rng = np.random.default_rng(22)
+    n, k = 5, 192
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    groups = n * k // 64
+    zero = np.zeros((groups, 4))
+    # a dominant logit: the mixture is that width's reconstruction and the cost is that width
+    for i, b in enumerate(Q.WIDTHS):
+        logits = np.full((groups, 4), -60.0)
+        logits[:, i] = 60.0
+        ws, pi, bits = Q.soft_quantize(w, logits, zero, 1.0)
+        assert np.allclose(ws, Q.training_reconstruction(w, b), rtol=0, atol=1e-12)
+        assert bits == pytest.approx(b, abs=1e-12)
+    # equal logits: each width weighs 1/4, the cost is the mean width 3.75
+    ws, pi, bits = Q.soft_quantize(w, zero, zero, 5.0)
+    assert np.allclose(pi, 0.25) and bits == pytest.approx(3.75, abs=1e-12)
+    assert np.allclose(ws, sum(Q.training_reconstruction(w, b) for b in Q.WIDTHS) / 4, rtol=0, atol=1e-15)
+    # softmax of (l + e) / tau: shifting all four by a constant changes nothing; a lower tau sharpens
+    l = rng.standard_normal((groups, 4))
+    e = -np.log(-np.log(rng.random((groups, 4))))
+    a = Q.soft_quantize(w, l, e, 0.7)
+    b2 = Q.soft_quantize(w, l + 3.0, e - 1.0, 0.7)
+    assert np.allclose(a[1], b2[1], rtol=1e-13) and np.allclose(a[0], b2[0], rtol=1e-12)
+    z = (l + e) / 0.7
+    assert np.allclose(a[1], np.exp(z) / np.exp(z).sum(axis=1, keepdims=True), rtol=1e-12)
+    sharp = Q.soft_quantize(w, l, e, 0.05)[1]
+    assert np.all(sharp.max(axis=1) >= a[1].max(axis=1) - 1e-12)
+    # the mixture is a convex combination: it lies between the smallest and largest reconstruction
+    rec = np.stack([Q.training_reconstruction(w, b) for b in Q.WIDTHS])
+    assert np.all(a[0] >= rec.min(axis=0) - 1e-15) and np.all(a[0] <= rec.max(axis=0) + 1e-15)
