@@ -245,10 +245,19 @@ def main():
             for g in groups:
                 V.vbq_gemv_multi([layer[j] for j in g], [xin[j] for j in g], [ys[j] for j in g], stream)
 
+        def rfused(i, rl=rlayers, rc_=rcopies):
+            layer = rl[i % rc_]
+            V.vbq_gemv_multi(layer[0:3], xin[0:3], ys[0:3], stream)
+            V.vbq_gemv(layer[3], xin[3], ys[3], stream)
+            V.vbq_gemv_swiglu(layer[gi_gate], layer[gi_up], xin[gi_gate], hbuf, stream)
+            V.vbq_gemv(layer[gi_down], hbuf, ys[gi_down], stream)
+
         rms = timed(rstep)
+        rfms = timed(rfused)
         recipe[name] = {"packed_bytes_per_step": rbytes, "ms_per_step": round(rms, 5),
                         "GBps": round(rbytes / (rms * 1e-3) / 1e9, 2),
-                        "pct_hbm_peak": round(100 * rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+                        "pct_hbm_peak": round(100 * rbytes / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                        "with_fused_mlp_epilogue_ms_per_step": round(rfms, 5)}
         del rlayers
     # the recipe head (32000x4096, rows tiered 8/4/2/1 bits by a Zipf frequency rank): as four one-width
     # row blocks in one launch, against the same rows in vocabulary order on the mixed-width kernel
