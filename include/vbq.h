@@ -49,11 +49,16 @@
  *   it (kernels read it as -2^(b-1)).
  *   Result: y[m][r] = sum_j s_{r,j} * sum_i q_{r,j,i} * x[m][64j+i]; codes are
  *   exact in fp16, products and sums are fp32, the scale is applied in fp32
- *   once per group, y is fp32.
+ *   once per group, y is fp32 (fp16 from vbq_gemv_multi_f16, and
+ *   fp16(silu(g) * u) from vbq_gemv_swiglu).
+ *   The export side fills this layout: vbq_quantize (§3.1 Eq. (1) on the
+ *   device), the §3.4 recipe's widths, vbq_pack, vbq_check_padding and the
+ *   container; vbq_soft_quantize is the §3.2 training-time mixture.
  *
  * Conventions for every entry point:
  *   - All buffers belong to the caller. Host entry points (vbq_pack*,
- *     vbq_validate_host) take host pointers and run synchronously. Device
+ *     vbq_validate_host, vbq_check_padding, vbq_uniform_width, vbq_container_*,
+ *     vbq_recipe_head_*) take host pointers and run synchronously. Device
  *     entry points take device pointers inside vbq_matrix and as arguments,
  *     enqueue work on `stream` (a hipStream_t passed as void*, NULL = the
  *     null stream) and return without waiting; results are visible after the
