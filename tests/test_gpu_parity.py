@@ -483,3 +483,24 @@ def test_fp16_outputs_are_the_rounded_fp32_outputs(V, torch_mod, mix):
         torch.cuda.synchronize()
         for a, b in zip(y32, y16):
             assert torch.equal(a.half(), b)
+
+
+def test_multi_launch_of_unequal_matrices(V, torch_mod):
+    # one launch over matrices of different row and column counts (the instance whose idle workgroups
+    # leave at once), including a split matrix, a ragged one and a one-row one: each against the oracle
+    torch = torch_mod
+    print_case(test="ragged_multi")
+    shapes = [(4096, 1024), (64, 16384), (1000, 1984), (1, 64), (300, 4160)]
+    cases = []
+    for i, (n, k) in enumerate(shapes):
+        bits, codes, scales = W.draw_random_matrix((95, i), n, k, W.STD_MIX)
+        cases.append((V.DeviceMatrix(V.vbq_pack(n, k, bits, codes, scales)), oracle.pack(n, k, bits, codes, scales),
+                      scales, W.draw_x((96, i), k)))
+    for _ in range(2):   # twice: the split matrix's counters must have reset
+        ys = [torch.full((n,), float("nan"), dtype=torch.float32, device="cuda") for n, _ in shapes]
+        xs = [torch.from_numpy(c[3].view(np.float16)).cuda()[0] for c in cases]
+        V.vbq_gemv_multi([c[0] for c in cases], xs, ys)
+        torch.cuda.synchronize()
+        for (dm, p, scales, x), y in zip(cases, ys):
+            assert_within_tolerance(y.cpu().numpy()[None], oracle.gemv(p, x[0])[None], x, scales,
+                                    f"{dm.n}x{dm.k} in a launch of unequal matrices")
