@@ -143,7 +143,7 @@ def kernels_summary(a) -> str:
     """Dispatch count and duration statistics per kernel name and grid (VBQ kernels only).
 
     For the quantizer every grid is one matrix shape: a workgroup of 256 lanes covers 64 groups of
-    64 weights, and each weight costs 5 + 3/64 algorithmic bytes (fp32 read, int8 code written, one
+    64 weights (16 in the one-group-a-team instance), and each weight costs 5 + 3/64 algorithmic bytes (fp32 read, int8 code written, one
     width byte read and one binary16 scale written per group), which gives alg_GBps. The soft
     quantizer runs 16 lanes a group and moves 8 + 52/64 bytes a weight (fp32 read and written; per
     group 32 bytes of logits and noise read, 16 of pi and 4 of expected bits written)."""
@@ -169,8 +169,8 @@ def kernels_summary(a) -> str:
         if "soft_quantize_groups" in name:   # 16 lanes a group: weights = lanes * 4; 8 + 52/64 bytes a weight
             weights = int(r["Grid_Size_X"]) * 4
             extra = f" weights={weights} alg_GBps={weights * (8 + 52 / 64) / (statistics.fmean(d) * 1e3):.1f}"
-        elif "quantize_groups" in name:
-            weights = int(r["Grid_Size_X"]) // 256 * 64 * 64
+        elif "quantize_groups" in name:   # 16 groups a workgroup with one group a team, else 64
+            weights = int(r["Grid_Size_X"]) // 256 * (16 if "quantize_groups<1u>" in name else 64) * 64
             extra = f" weights={weights} alg_GBps={weights * (5 + 3 / 64) / (statistics.fmean(d) * 1e3):.1f}"
         lines.append(f"  dispatches={len(d)} avg_us={statistics.fmean(d):.3f} median_us={statistics.median(d):.3f} "
                      f"min_us={min(d):.3f} max_us={max(d):.3f}{extra}")

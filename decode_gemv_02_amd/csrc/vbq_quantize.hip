@@ -16,8 +16,9 @@
 //     gives codes 0 at b >= 2.
 //
 // Work decomposition: a team of 16 lanes holds one group, four weights a
-// lane, so one wave reads four groups (1 KiB) per load; each team has four
-// groups' loads in flight before it reduces the first. The group's largest
+// lane, so one wave reads four groups (1 KiB) per load; each team has one
+// (small matrices) or four groups' loads in flight before it reduces the
+// first. The group's largest
 // magnitude or magnitude sum is reduced across its 16 lanes with
 // butterflies, so every lane ends with the same value and the same scale.
 #include <hip/hip_runtime.h>
@@ -35,8 +36,9 @@ namespace {
 constexpr uint32_t kLanesPerGroup = 16;
 constexpr uint32_t kBlock = 256;
 constexpr uint32_t kTeams = kBlock / kLanesPerGroup;          // 16-lane teams per workgroup
-constexpr uint32_t kGroupsPerTeam = 4;                          // loads a team keeps in flight
-constexpr uint32_t kGroupsPerBlock = kTeams * kGroupsPerTeam;
+// Groups a team keeps in flight: four for large matrices; one below kFewGroups groups, where the
+// launch is short and a wider grid fills the chip sooner (4096x4096: 19.1 against 22.0 us).
+constexpr uint64_t kFewGroups = 1u << 19;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -93,9 +95,11 @@ __device__ __forceinline__ uint32_t quantize_quad(float4 v, uint32_t b, uint16_t
 // Workgroup x covers groups [x * kGroupsPerBlock, (x + 1) * kGroupsPerBlock): pass j hands group
 // x * kGroupsPerBlock + j * kTeams + team to a team, so each pass reads 4 KiB contiguous. All of a
 // team's loads are issued before the first reduction.
+template <uint32_t kGroupsPerTeam>
 __global__ __launch_bounds__(kBlock) void quantize_groups(const float4 *__restrict__ w, const uint8_t *__restrict__ bits,
                                                          uint32_t *__restrict__ codes, uint16_t *__restrict__ scales,
                                                          uint64_t groups) {
+    constexpr uint32_t kGroupsPerBlock = kTeams * kGroupsPerTeam;
     const uint32_t team = threadIdx.x / kLanesPerGroup, lane = threadIdx.x % kLanesPerGroup;
     const uint64_t first = static_cast<uint64_t>(blockIdx.x) * kGroupsPerBlock + team;
     float4 v[kGroupsPerTeam];
@@ -228,13 +232,21 @@ extern "C" vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const
     if (!aligned(w, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 2))
         return fail(VBQ_ERR_ALIGN, "vbq_quantize: w must be 16-byte, codes 4-byte and scales 2-byte aligned");
     const uint64_t groups = static_cast<uint64_t>(n) * (k / VBQ_GROUP);
-    const uint64_t blocks = (groups + kGroupsPerBlock - 1) / kGroupsPerBlock;
+    const bool few = groups < kFewGroups;
+    const uint64_t per_block = static_cast<uint64_t>(kTeams) * (few ? 1u : 4u);
+    const uint64_t blocks = (groups + per_block - 1) / per_block;
     if (blocks > 0x7FFFFFFFull) return fail(VBQ_ERR_SHAPE, "vbq_quantize: %llu groups exceed one launch",
                                             static_cast<unsigned long long>(groups));
     (void)hipGetLastError();
-    hipLaunchKernelGGL(quantize_groups, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0,
-                       static_cast<hipStream_t>(stream), reinterpret_cast<const float4 *>(w), bits,
-                       reinterpret_cast<uint32_t *>(codes_out), scales_out, groups);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (few)
+        hipLaunchKernelGGL(quantize_groups<1>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
+                           reinterpret_cast<const float4 *>(w), bits, reinterpret_cast<uint32_t *>(codes_out),
+                           scales_out, groups);
+    else
+        hipLaunchKernelGGL(quantize_groups<4>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
+                           reinterpret_cast<const float4 *>(w), bits, reinterpret_cast<uint32_t *>(codes_out),
+                           scales_out, groups);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_quantize: launch failed: %s", hipGetErrorString(e));
     return VBQ_OK;
