@@ -30,7 +30,7 @@ TILE_ROWS = 64
 TILE_GROUPS = 4
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WIDTH, ERR_CODE, ERR_SCALE, ERR_CAPACITY, ERR_OFFSETS, ERR_ALIGN, \
-    ERR_TOO_LARGE, ERR_HIP, ERR_ABI, ERR_PADDING, ERR_FORMAT = range(14)
+    ERR_TOO_LARGE, ERR_HIP, ERR_ABI, ERR_PADDING, ERR_FORMAT, ERR_NOMEM, ERR_INTERNAL = range(16)
 CONTAINER_HEADER = 128
 
 
@@ -82,6 +82,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_soft_quantize.argtypes = [U32, U32, P, P, P, ctypes.c_float, P, P, P, P, P]
     lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
     lib.vbq_recipe_head_order.argtypes = [U32, P, P]
+    lib.vbq_recipe_head_tiers.argtypes = [U32, P, P, P]
     lib.vbq_check_padding.argtypes = [ctypes.POINTER(VbqMatrix), U32, U32, U32]
     lib.vbq_container_size.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(ctypes.c_uint64)]
     lib.vbq_container_write.argtypes = [ctypes.POINTER(VbqMatrix), P, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
@@ -90,7 +91,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
               lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16,
-              lib.vbq_soft_quantize):
+              lib.vbq_soft_quantize, lib.vbq_recipe_head_tiers):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -223,32 +224,29 @@ def vbq_tile_count(n: int, k: int) -> int:
     return int(lib.vbq_tile_count(n, k))
 
 
-def vbq_gemv_multi(ws, xs, ys, stream=None):
-    """Several independent GEMVs (ys[i] = W_i xs[i]) in one launch; up to 16."""
+def _multi_args(ws, xs, ys, ydtype):
     count = len(ws)
     assert len(xs) == count and len(ys) == count
     for w, x, y in zip(ws, xs, ys):
-        assert x.dtype == torch.float16 and y.dtype == torch.float32 and x.is_contiguous() and y.is_contiguous()
+        assert x.dtype == torch.float16 and y.dtype == ydtype and x.is_contiguous() and y.is_contiguous()
         assert x.numel() == w.k and y.numel() >= w.n
     wa = (ctypes.POINTER(VbqMatrix) * max(count, 1))(*[ctypes.pointer(w.struct) for w in ws])
     xa = (ctypes.c_void_p * max(count, 1))(*[x.data_ptr() for x in xs])
     ya = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
     dev = ws[0].device if count else torch.device("cuda")
+    return wa, xa, ya, count, dev
+
+
+def vbq_gemv_multi(ws, xs, ys, stream=None):
+    """Several independent GEMVs (ys[i] = W_i xs[i]) in one launch; up to 16."""
+    wa, xa, ya, count, dev = _multi_args(ws, xs, ys, torch.float32)
     _check(lib.vbq_gemv_multi(wa, xa, ya, count, _stream_handle(stream, dev)))
     return ys
 
 
 def vbq_gemv_multi_f16(ws, xs, ys, stream=None):
     """vbq_gemv_multi with fp16 outputs (ys: float16 tensors)."""
-    count = len(ws)
-    assert len(xs) == count and len(ys) == count
-    for w, x, y in zip(ws, xs, ys):
-        assert x.dtype == torch.float16 and y.dtype == torch.float16 and x.is_contiguous() and y.is_contiguous()
-        assert x.numel() == w.k and y.numel() >= w.n
-    wa = (ctypes.POINTER(VbqMatrix) * max(count, 1))(*[ctypes.pointer(w.struct) for w in ws])
-    xa = (ctypes.c_void_p * max(count, 1))(*[x.data_ptr() for x in xs])
-    ya = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
-    dev = ws[0].device if count else torch.device("cuda")
+    wa, xa, ya, count, dev = _multi_args(ws, xs, ys, torch.float16)
     _check(lib.vbq_gemv_multi_f16(wa, xa, ya, count, _stream_handle(stream, dev)))
     return ys
 
@@ -343,24 +341,33 @@ def vbq_recipe_head_order(freq: np.ndarray) -> np.ndarray:
     return out
 
 
+def vbq_recipe_head_tiers(freq: np.ndarray):
+    """(order, tier_rows): rows in rank order and the rank counts of the 8-, 4-, 2- and 1-bit tiers."""
+    freq = np.ascontiguousarray(freq, dtype=np.uint64).reshape(-1)
+    order = np.zeros(freq.size, np.uint32)
+    tiers = np.zeros(4, np.uint32)
+    _check(lib.vbq_recipe_head_tiers(freq.size, _np_ptr(freq), _np_ptr(order), tiers.ctypes.data))
+    return order, tiers
+
+
 def vbq_pack_grouped_head(freq: np.ndarray, codes: np.ndarray, scales: np.ndarray):
     """The recipe head as one-width row blocks: returns (order, [HostMatrix per tier present]).
 
     codes int8 [rows][k] and scales uint16 [rows][k/64] are in vocabulary order and must follow the
-    widths vbq_recipe_head_bits(freq) gives each row. The blocks hold the rows of ranks order[0:...],
-    tier by tier (8, 4, 2, 1 bits); their outputs, concatenated, are the logits of rows `order`."""
-    order = vbq_recipe_head_order(freq)
-    bits = vbq_recipe_head_bits(freq)[order]
+    widths vbq_recipe_head_bits(freq) gives each row. The library ranks the rows and cuts the tiers
+    (vbq_recipe_head_tiers); each block holds one tier's rows in rank order (8, 4, 2, 1 bits), and the
+    blocks' outputs, concatenated, are the logits of rows `order`."""
+    order, tiers = vbq_recipe_head_tiers(freq)
     rows, k = codes.shape
     blocks = []
     start = 0
-    while start < rows:
-        b = int(bits[start])
-        end = start + int(np.argmax(bits[start:] != b)) if np.any(bits[start:] != b) else rows
-        sel = order[start:end]
-        blocks.append(vbq_pack(end - start, k, np.full((end - start, k // GROUP), b, np.uint8),
+    for b, cnt in zip((8, 4, 2, 1), tiers):
+        if cnt == 0:
+            continue
+        sel = order[start:start + cnt]
+        blocks.append(vbq_pack(int(cnt), k, np.full((int(cnt), k // GROUP), b, np.uint8),
                                np.ascontiguousarray(codes[sel]), np.ascontiguousarray(scales[sel])))
-        start = end
+        start += int(cnt)
     return order, blocks
 
 

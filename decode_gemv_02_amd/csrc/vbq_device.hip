@@ -34,6 +34,7 @@
 #include <cstdint>
 #include <mutex>
 #include <unordered_map>
+#include <vector>
 
 #include "vbq_internal.h"
 
@@ -1398,11 +1399,14 @@ vbq_status launched(const char *who) {
     return VBQ_OK;
 }
 
-// Scratch for split row tiles: one buffer per (device, stream), grown on demand.
-// The buffer starts with a region that only ever holds arrival counters: it is
-// zeroed when allocated and every counter is reset to zero by the last
-// workgroup of its row tile, so the region is all zeros between calls however
-// the next call lays out its matrices. Partial sums follow it.
+// Scratch for split row tiles and the gated epilogue: one buffer per
+// (device, stream), enlarged on demand. The buffer starts with a region that
+// only ever holds arrival counters: it is zeroed when allocated and every
+// counter is reset to zero by the last workgroup of its row tile, so the
+// region is all zeros between calls however the next call lays out its
+// matrices. Partial sums follow it. A superseded buffer is never freed (a
+// graph captured earlier may still hold its address), and nothing is
+// allocated while the caller's stream is being captured.
 struct Scratch {
     void *ptr = nullptr;
     size_t counter_bytes = 0;
@@ -1411,6 +1415,7 @@ struct Scratch {
 
 std::mutex g_scratch_mu;
 std::unordered_map<uint64_t, Scratch> g_scratch;
+std::vector<void *> g_retired;   // superseded scratch buffers, held until the process ends
 
 vbq_status scratch_for(const char *who, hipStream_t stream, size_t counters, size_t partials, uint32_t **ctr_out,
                        char **part_out) {
@@ -1420,20 +1425,30 @@ vbq_status scratch_for(const char *who, hipStream_t stream, size_t counters, siz
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     Scratch &s = g_scratch[key];
     if (s.counter_bytes < counters || s.partial_bytes < partials) {
-        if (s.ptr) {
-            if (hipStreamSynchronize(stream) != hipSuccess || hipFree(s.ptr) != hipSuccess)
-                return fail(VBQ_ERR_HIP, "%s: could not release the old scratch buffer", who);
-            s.ptr = nullptr;
-        }
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+            return fail(VBQ_ERR_HIP, "%s: could not query the stream's capture state", who);
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(VBQ_ERR_HIP,
+                        "%s: needs %zu B of scratch on a stream that is being captured (the library does not "
+                        "allocate during capture; make one call of the same shapes on this stream first)",
+                        who, counters + partials);
+        g_retired.reserve(g_retired.size() + 1);   // may throw before anything changes
         const size_t cb = std::max<size_t>(counters, std::max<size_t>(s.counter_bytes, 64u << 10));
         const size_t pb = std::max<size_t>(partials, std::max<size_t>(s.partial_bytes, 1u << 20));
-        if (hipMalloc(&s.ptr, cb + pb) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch hipMalloc failed", who);
+        void *fresh = nullptr;
+        if (hipMalloc(&fresh, cb + pb) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch hipMalloc failed", who);
         // zero the counter region on the caller's stream, ahead of the launches that use it (a memset on
         // the null stream is not ordered with non-blocking streams)
         const uint64_t words = cb / 4;
         hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0, stream,
-                           static_cast<float *>(s.ptr), words);
-        if (hipGetLastError() != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch clear failed", who);
+                           static_cast<float *>(fresh), words);
+        if (hipGetLastError() != hipSuccess) {
+            g_retired.push_back(fresh);
+            return fail(VBQ_ERR_HIP, "%s: scratch clear failed", who);
+        }
+        if (s.ptr) g_retired.push_back(s.ptr);
+        s.ptr = fresh;
         s.counter_bytes = cb;
         s.partial_bytes = pb;
     }
@@ -1562,18 +1577,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     }
     for (uint32_t i = 0; i < count; ++i) {
         const vbq_matrix *w = ws[i];
-        if (w->n == 0) continue;
-        if (w->k == 0) {
-            const uint64_t cnt = w->n;
-            if (ys16)
-                hipLaunchKernelGGL(fill_zero_u16, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream,
-                                   ys16[i], cnt);
-            else
-                hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream,
-                                   ys[i], cnt);
-            any_launch = true;
-            continue;
-        }
+        if (w->n == 0 || w->k == 0) continue;
         MatArgs &M = B.m[used++];
         M.widths = w->widths;
         M.scales = w->scales;
@@ -1597,8 +1601,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
             partial_total += partial_bytes(M.splits, M.n);
         }
     }
-    if (used == 0) return any_launch ? launched(who) : VBQ_OK;
-    if (h) {   // the pair region follows the split regions
+    if (h && used) {   // the pair region follows the split regions
         counter_slots += ceil_div(B.m[0].n, kTileRows);
         partial_total += partial_bytes(2, B.m[0].n);
     }
@@ -1621,6 +1624,20 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
             B.pair = reinterpret_cast<float *>(part);
         }
     }
+    // only now that nothing can fail: k == 0 matrices get y = 0
+    for (uint32_t i = 0; i < count; ++i) {
+        const vbq_matrix *w = ws[i];
+        if (w->n == 0 || w->k != 0) continue;
+        const uint64_t cnt = w->n;
+        if (ys16)
+            hipLaunchKernelGGL(fill_zero_u16, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream,
+                               ys16[i], cnt);
+        else
+            hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream,
+                               ys[i], cnt);
+        any_launch = true;
+    }
+    if (used == 0) return any_launch ? launched(who) : VBQ_OK;
     bool ragged = false;   // some matrix has fewer workgroups than the grid is wide
     for (uint32_t i = 0; i < used; ++i) ragged = ragged || B.m[i].blocks != blocks;
     if (plan.waves == 16)
@@ -1683,136 +1700,148 @@ vbq_status check_vectors(const char *who, const vbq_matrix *w, const void *x, co
 
 extern "C" vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                                      uint32_t count, void *stream) {
-    vbq::clear_error();
-    const char *who = "vbq_gemv_multi";
-    if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
-    if (count == 0) return VBQ_OK;
-    if (!ws || !xs || !ys) return fail(VBQ_ERR_NULL, "%s: ws, xs or ys is NULL", who);
-    for (uint32_t i = 0; i < count; ++i) {
-        vbq_status st = check_matrix(who, ws[i]);
-        if (st != VBQ_OK) return st;
-        st = check_vectors(who, ws[i], xs[i], ys[i]);
-        if (st != VBQ_OK) return st;
-    }
-    (void)hipGetLastError();
-    return gemv_launch(who, ws, xs, ys, count, static_cast<hipStream_t>(stream));
+    return vbq::guarded("vbq_gemv_multi", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemv_multi";
+        if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
+        if (count == 0) return VBQ_OK;
+        if (!ws || !xs || !ys) return fail(VBQ_ERR_NULL, "%s: ws, xs or ys is NULL", who);
+        for (uint32_t i = 0; i < count; ++i) {
+            vbq_status st = check_matrix(who, ws[i]);
+            if (st != VBQ_OK) return st;
+            st = check_vectors(who, ws[i], xs[i], ys[i]);
+            if (st != VBQ_OK) return st;
+        }
+        (void)hipGetLastError();
+        return gemv_launch(who, ws, xs, ys, count, static_cast<hipStream_t>(stream));
+    });
 }
 
 extern "C" vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *up, const uint16_t *x, uint16_t *h,
                                       void *stream) {
-    vbq::clear_error();
-    const char *who = "vbq_gemv_swiglu";
-    vbq_status st = check_matrix(who, gate);
-    if (st != VBQ_OK) return st;
-    st = check_matrix(who, up);
-    if (st != VBQ_OK) return st;
-    if (gate->n != up->n || gate->k != up->k)
-        return fail(VBQ_ERR_SHAPE, "%s: gate is %ux%u, up is %ux%u", who, gate->n, gate->k, up->n, up->k);
-    if (gate->n == 0) return VBQ_OK;
-    if (!h || (gate->k && !x)) return fail(VBQ_ERR_NULL, "%s: x or h is NULL", who);
-    if (!aligned16(h) || (gate->k && !aligned16(x)))
-        return fail(VBQ_ERR_ALIGN, "%s: x or h is not 16-byte aligned", who);
-    (void)hipGetLastError();
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (gate->k == 0) {   // g = u = 0, so h = silu(0) * 0 = 0
-        hipLaunchKernelGGL(fill_zero_u16, dim3((gate->n + 255) / 256), dim3(256), 0, s, h, uint64_t(gate->n));
-        return launched(who);
-    }
-    const vbq_matrix *ws[2] = {gate, up};
-    const uint16_t *xs[2] = {x, x};
-    float *ys[2] = {nullptr, nullptr};
-    return gemv_launch(who, ws, xs, ys, 2, s, h);
+    return vbq::guarded("vbq_gemv_swiglu", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemv_swiglu";
+        vbq_status st = check_matrix(who, gate);
+        if (st != VBQ_OK) return st;
+        st = check_matrix(who, up);
+        if (st != VBQ_OK) return st;
+        if (gate->n != up->n || gate->k != up->k)
+            return fail(VBQ_ERR_SHAPE, "%s: gate is %ux%u, up is %ux%u", who, gate->n, gate->k, up->n, up->k);
+        if (gate->n == 0) return VBQ_OK;
+        if (!h || (gate->k && !x)) return fail(VBQ_ERR_NULL, "%s: x or h is NULL", who);
+        if (!aligned16(h) || (gate->k && !aligned16(x)))
+            return fail(VBQ_ERR_ALIGN, "%s: x or h is not 16-byte aligned", who);
+        (void)hipGetLastError();
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if (gate->k == 0) {   // g = u = 0, so h = silu(0) * 0 = 0
+            hipLaunchKernelGGL(fill_zero_u16, dim3((gate->n + 255) / 256), dim3(256), 0, s, h, uint64_t(gate->n));
+            return launched(who);
+        }
+        const vbq_matrix *ws[2] = {gate, up};
+        const uint16_t *xs[2] = {x, x};
+        float *ys[2] = {nullptr, nullptr};
+        return gemv_launch(who, ws, xs, ys, 2, s, h);
+    });
 }
 
 extern "C" vbq_status vbq_gemv_multi_f16(const vbq_matrix *const *ws, const uint16_t *const *xs, uint16_t *const *ys,
                                          uint32_t count, void *stream) {
-    vbq::clear_error();
-    const char *who = "vbq_gemv_multi_f16";
-    if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
-    if (count == 0) return VBQ_OK;
-    if (!ws || !xs || !ys) return fail(VBQ_ERR_NULL, "%s: ws, xs or ys is NULL", who);
-    for (uint32_t i = 0; i < count; ++i) {
-        vbq_status st = check_matrix(who, ws[i]);
-        if (st != VBQ_OK) return st;
-        st = check_vectors(who, ws[i], xs[i], ys[i]);
-        if (st != VBQ_OK) return st;
-    }
-    (void)hipGetLastError();
-    return gemv_launch(who, ws, xs, nullptr, count, static_cast<hipStream_t>(stream), nullptr, ys);
+    return vbq::guarded("vbq_gemv_multi_f16", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemv_multi_f16";
+        if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
+        if (count == 0) return VBQ_OK;
+        if (!ws || !xs || !ys) return fail(VBQ_ERR_NULL, "%s: ws, xs or ys is NULL", who);
+        for (uint32_t i = 0; i < count; ++i) {
+            vbq_status st = check_matrix(who, ws[i]);
+            if (st != VBQ_OK) return st;
+            st = check_vectors(who, ws[i], xs[i], ys[i]);
+            if (st != VBQ_OK) return st;
+        }
+        (void)hipGetLastError();
+        return gemv_launch(who, ws, xs, nullptr, count, static_cast<hipStream_t>(stream), nullptr, ys);
+    });
 }
 
 extern "C" vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream) {
-    vbq::clear_error();
-    const char *who = "vbq_gemv";
-    vbq_status st = check_matrix(who, w);
-    if (st != VBQ_OK) return st;
-    st = check_vectors(who, w, x, y);
-    if (st != VBQ_OK) return st;
-    (void)hipGetLastError();
-    return gemv_launch(who, &w, &x, &y, 1, static_cast<hipStream_t>(stream));
+    return vbq::guarded("vbq_gemv", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemv";
+        vbq_status st = check_matrix(who, w);
+        if (st != VBQ_OK) return st;
+        st = check_vectors(who, w, x, y);
+        if (st != VBQ_OK) return st;
+        (void)hipGetLastError();
+        return gemv_launch(who, &w, &x, &y, 1, static_cast<hipStream_t>(stream));
+    });
 }
 
 extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                                           void *stream) {
-    vbq::clear_error();
-    const char *who = "vbq_gemm_smallbatch";
-    if (m == 0 || m > VBQ_MAX_BATCH) return fail(VBQ_ERR_SHAPE, "%s: m=%u outside [1, %u]", who, m, VBQ_MAX_BATCH);
-    vbq_status st = check_matrix(who, w);
-    if (st != VBQ_OK) return st;
-    st = check_vectors(who, w, x, y);
-    if (st != VBQ_OK) return st;
-    if (w->n == 0) return VBQ_OK;
-    (void)hipGetLastError();
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint64_t tiles = static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
-    if (m > VBQ_MAX_MULTI || (m >= kGemmMinBatch && static_cast<uint64_t>(m) * m * tiles >= kGemmMinWork)) {
-        if (w->k == 0) {
-            const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
-            hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s, y, cnt);
-            return launched(who);
-        }
-        return gemm_launch(who, w, x, m, y, s);
-    }
-    // each input row as its own GEMV of one batched launch
-    const vbq_matrix *ws[VBQ_MAX_MULTI];
-    const uint16_t *xs[VBQ_MAX_MULTI];
-    float *ys[VBQ_MAX_MULTI];
-    for (uint32_t m0 = 0; m0 < m; m0 += VBQ_MAX_MULTI) {
-        const uint32_t cnt = std::min(VBQ_MAX_MULTI, m - m0);
-        for (uint32_t i = 0; i < cnt; ++i) {
-            ws[i] = w;
-            xs[i] = x + static_cast<uint64_t>(m0 + i) * w->k;
-            ys[i] = y + static_cast<uint64_t>(m0 + i) * w->n;
-        }
-        st = gemv_launch(who, ws, xs, ys, cnt, s);
+    return vbq::guarded("vbq_gemm_smallbatch", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemm_smallbatch";
+        if (m == 0 || m > VBQ_MAX_BATCH) return fail(VBQ_ERR_SHAPE, "%s: m=%u outside [1, %u]", who, m, VBQ_MAX_BATCH);
+        vbq_status st = check_matrix(who, w);
         if (st != VBQ_OK) return st;
-    }
-    return VBQ_OK;
+        st = check_vectors(who, w, x, y);
+        if (st != VBQ_OK) return st;
+        if (w->n == 0) return VBQ_OK;
+        (void)hipGetLastError();
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const uint64_t tiles = static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
+        if (m > VBQ_MAX_MULTI || (m >= kGemmMinBatch && static_cast<uint64_t>(m) * m * tiles >= kGemmMinWork)) {
+            if (w->k == 0) {
+                const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
+                hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s, y, cnt);
+                return launched(who);
+            }
+            return gemm_launch(who, w, x, m, y, s);
+        }
+        // each input row as its own GEMV of one batched launch
+        const vbq_matrix *ws[VBQ_MAX_MULTI];
+        const uint16_t *xs[VBQ_MAX_MULTI];
+        float *ys[VBQ_MAX_MULTI];
+        for (uint32_t m0 = 0; m0 < m; m0 += VBQ_MAX_MULTI) {
+            const uint32_t cnt = std::min(VBQ_MAX_MULTI, m - m0);
+            for (uint32_t i = 0; i < cnt; ++i) {
+                ws[i] = w;
+                xs[i] = x + static_cast<uint64_t>(m0 + i) * w->k;
+                ys[i] = y + static_cast<uint64_t>(m0 + i) * w->n;
+            }
+            st = gemv_launch(who, ws, xs, ys, cnt, s);
+            if (st != VBQ_OK) return st;
+        }
+        return VBQ_OK;
+    });
 }
 
 extern "C" vbq_status vbq_unpack_codes(const vbq_matrix *w, int8_t *codes_out, void *stream) {
-    vbq::clear_error();
-    vbq_status st = check_matrix("vbq_unpack_codes", w);
-    if (st != VBQ_OK) return st;
-    if (w->n == 0 || w->k == 0) return VBQ_OK;
-    if (!codes_out) return fail(VBQ_ERR_NULL, "vbq_unpack_codes: codes_out is NULL");
-    if (!aligned16(codes_out)) return fail(VBQ_ERR_ALIGN, "vbq_unpack_codes: codes_out is not 16-byte aligned");
-    (void)hipGetLastError();
-    MatArgs M{};
-    M.payload_bytes = w->payload_bytes;
-    M.widths = w->widths;
-    M.scales = w->scales;
-    M.tile_offsets = w->tile_offsets;
-    M.payload = w->payload;
-    M.n = w->n;
-    M.groups = w->k / VBQ_GROUP;
-    M.col_tiles = ceil_div(M.groups, kTileGroups);
-    M.splits = 1;
-    const uint32_t tiles = ceil_div(M.n, kTileRows) * M.col_tiles;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (M.groups % 4 == 0)
-        hipLaunchKernelGGL(unpack_tiles<true>, dim3(tiles), dim3(64), 0, s, M, codes_out);
-    else
-        hipLaunchKernelGGL(unpack_tiles<false>, dim3(tiles), dim3(64), 0, s, M, codes_out);
-    return launched("vbq_unpack_codes");
+    return vbq::guarded("vbq_unpack_codes", [&]() -> vbq_status {
+        vbq::clear_error();
+        vbq_status st = check_matrix("vbq_unpack_codes", w);
+        if (st != VBQ_OK) return st;
+        if (w->n == 0 || w->k == 0) return VBQ_OK;
+        if (!codes_out) return fail(VBQ_ERR_NULL, "vbq_unpack_codes: codes_out is NULL");
+        if (!aligned16(codes_out)) return fail(VBQ_ERR_ALIGN, "vbq_unpack_codes: codes_out is not 16-byte aligned");
+        (void)hipGetLastError();
+        MatArgs M{};
+        M.payload_bytes = w->payload_bytes;
+        M.widths = w->widths;
+        M.scales = w->scales;
+        M.tile_offsets = w->tile_offsets;
+        M.payload = w->payload;
+        M.n = w->n;
+        M.groups = w->k / VBQ_GROUP;
+        M.col_tiles = ceil_div(M.groups, kTileGroups);
+        M.splits = 1;
+        const uint32_t tiles = ceil_div(M.n, kTileRows) * M.col_tiles;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (M.groups % 4 == 0)
+            hipLaunchKernelGGL(unpack_tiles<true>, dim3(tiles), dim3(64), 0, s, M, codes_out);
+        else
+            hipLaunchKernelGGL(unpack_tiles<false>, dim3(tiles), dim3(64), 0, s, M, codes_out);
+        return launched("vbq_unpack_codes");
+    });
 }

@@ -201,7 +201,8 @@ __global__ __launch_bounds__(kParts) void mean_of_parts(const double *__restrict
     if (threadIdx.x == 0) out[0] = groups ? s[0] / static_cast<double>(groups) : 0.0;
 }
 
-// kParts doubles of device scratch per (device, stream), allocated on first use and kept
+// kParts doubles of device scratch per (device, stream), allocated on first use (never while the
+// stream is being captured) and held until the process ends
 std::mutex g_parts_mu;
 std::unordered_map<uint64_t, double *> g_parts;
 
@@ -211,9 +212,17 @@ vbq_status parts_for(hipStream_t stream, double **out) {
     const uint64_t key = (static_cast<uint64_t>(dev) << 56) ^ reinterpret_cast<uintptr_t>(stream);
     std::lock_guard<std::mutex> lock(g_parts_mu);
     double *&p = g_parts[key];
-    if (!p && hipMalloc(reinterpret_cast<void **>(&p), kParts * sizeof(double)) != hipSuccess) {
-        p = nullptr;
-        return fail(VBQ_ERR_HIP, "vbq_soft_quantize: scratch hipMalloc failed");
+    if (!p) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess)
+            return fail(VBQ_ERR_HIP, "vbq_soft_quantize: could not query the stream's capture state");
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(VBQ_ERR_HIP, "vbq_soft_quantize: first call on a stream that is being captured (the library "
+                                     "does not allocate during capture; call once on this stream first)");
+        if (hipMalloc(reinterpret_cast<void **>(&p), kParts * sizeof(double)) != hipSuccess) {
+            p = nullptr;
+            return fail(VBQ_ERR_HIP, "vbq_soft_quantize: scratch hipMalloc failed");
+        }
     }
     *out = p;
     return VBQ_OK;
@@ -225,74 +234,78 @@ inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintp
 
 extern "C" vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const uint8_t *bits, int8_t *codes_out,
                                    uint16_t *scales_out, void *stream) {
-    vbq::clear_error();
-    if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_quantize: k=%u is not a multiple of 64", k);
-    if (n == 0 || k == 0) return VBQ_OK;
-    if (!w || !bits || !codes_out || !scales_out) return fail(VBQ_ERR_NULL, "vbq_quantize: a pointer is NULL");
-    if (!aligned(w, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 2))
-        return fail(VBQ_ERR_ALIGN, "vbq_quantize: w must be 16-byte, codes 4-byte and scales 2-byte aligned");
-    const uint64_t groups = static_cast<uint64_t>(n) * (k / VBQ_GROUP);
-    const bool few = groups < kFewGroups;
-    const uint64_t per_block = static_cast<uint64_t>(kTeams) * (few ? 1u : 4u);
-    const uint64_t blocks = (groups + per_block - 1) / per_block;
-    if (blocks > 0x7FFFFFFFull) return fail(VBQ_ERR_SHAPE, "vbq_quantize: %llu groups exceed one launch",
-                                            static_cast<unsigned long long>(groups));
-    (void)hipGetLastError();
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (few)
-        hipLaunchKernelGGL(quantize_groups<1>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
-                           reinterpret_cast<const float4 *>(w), bits, reinterpret_cast<uint32_t *>(codes_out),
-                           scales_out, groups);
-    else
-        hipLaunchKernelGGL(quantize_groups<4>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
-                           reinterpret_cast<const float4 *>(w), bits, reinterpret_cast<uint32_t *>(codes_out),
-                           scales_out, groups);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_quantize: launch failed: %s", hipGetErrorString(e));
-    return VBQ_OK;
+    return vbq::guarded("vbq_quantize", [&]() -> vbq_status {
+        vbq::clear_error();
+        if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_quantize: k=%u is not a multiple of 64", k);
+        if (n == 0 || k == 0) return VBQ_OK;
+        if (!w || !bits || !codes_out || !scales_out) return fail(VBQ_ERR_NULL, "vbq_quantize: a pointer is NULL");
+        if (!aligned(w, 16) || !aligned(codes_out, 4) || !aligned(scales_out, 2))
+            return fail(VBQ_ERR_ALIGN, "vbq_quantize: w must be 16-byte, codes 4-byte and scales 2-byte aligned");
+        const uint64_t groups = static_cast<uint64_t>(n) * (k / VBQ_GROUP);
+        const bool few = groups < kFewGroups;
+        const uint64_t per_block = static_cast<uint64_t>(kTeams) * (few ? 1u : 4u);
+        const uint64_t blocks = (groups + per_block - 1) / per_block;
+        if (blocks > 0x7FFFFFFFull) return fail(VBQ_ERR_SHAPE, "vbq_quantize: %llu groups exceed one launch",
+                                                static_cast<unsigned long long>(groups));
+        (void)hipGetLastError();
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if (few)
+            hipLaunchKernelGGL(quantize_groups<1>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
+                               reinterpret_cast<const float4 *>(w), bits, reinterpret_cast<uint32_t *>(codes_out),
+                               scales_out, groups);
+        else
+            hipLaunchKernelGGL(quantize_groups<4>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
+                               reinterpret_cast<const float4 *>(w), bits, reinterpret_cast<uint32_t *>(codes_out),
+                               scales_out, groups);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_quantize: launch failed: %s", hipGetErrorString(e));
+        return VBQ_OK;
+    });
 }
 
 extern "C" vbq_status vbq_soft_quantize(uint32_t n, uint32_t k, const float *w, const float *logits,
                                         const float *gumbel, float tau, float *w_soft, float *pi, float *group_bits,
                                         double *mean_bits, void *stream) {
-    vbq::clear_error();
-    if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: k=%u is not a multiple of 64", k);
-    if (!(tau > 0.f) || tau > 3.0e38f) return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: tau must be positive and finite");
-    if (!mean_bits) return fail(VBQ_ERR_NULL, "vbq_soft_quantize: mean_bits is NULL");
-    if (!aligned(mean_bits, 8)) return fail(VBQ_ERR_ALIGN, "vbq_soft_quantize: mean_bits must be 8-byte aligned");
-    const uint64_t groups = static_cast<uint64_t>(n) * (k / VBQ_GROUP);
-    const uint64_t blocks = (groups * kLanesPerGroup + kBlock - 1) / kBlock;
-    if (groups) {
-        if (!w || !logits || !gumbel || !w_soft || !pi || !group_bits)
-            return fail(VBQ_ERR_NULL, "vbq_soft_quantize: a pointer is NULL");
-        if (!aligned(w, 16) || !aligned(w_soft, 16) || !aligned(logits, 16) || !aligned(gumbel, 16) ||
-            !aligned(pi, 16) || !aligned(group_bits, 4))
-            return fail(VBQ_ERR_ALIGN, "vbq_soft_quantize: w, w_soft, logits, gumbel and pi must be 16-byte aligned");
-        if (blocks > 0x7FFFFFFFull)
-            return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: %llu groups exceed one launch",
-                        static_cast<unsigned long long>(groups));
-    }
-    const hipStream_t s = static_cast<hipStream_t>(stream);
-    double *parts = nullptr;
-    const vbq_status ps = parts_for(s, &parts);
-    if (ps != VBQ_OK) return ps;
-    (void)hipGetLastError();
-    if (groups == 0) {   // no group: the mean is taken as 0
-        hipLaunchKernelGGL(mean_of_parts, dim3(1), dim3(kParts), 0, s, static_cast<const double *>(parts), 0u,
-                           uint64_t(0), mean_bits);
-    } else {
-        hipLaunchKernelGGL(soft_quantize_groups, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
-                           reinterpret_cast<const float4 *>(w), reinterpret_cast<const float4 *>(logits),
-                           reinterpret_cast<const float4 *>(gumbel), tau, reinterpret_cast<float4 *>(w_soft),
-                           reinterpret_cast<float4 *>(pi), group_bits, groups);
-        const uint64_t chunk = (groups + kParts - 1) / kParts;
-        const uint32_t nparts = static_cast<uint32_t>((groups + chunk - 1) / chunk);
-        hipLaunchKernelGGL(chunk_sums, dim3(nparts), dim3(256), 0, s, static_cast<const float *>(group_bits), groups,
-                           chunk, parts);
-        hipLaunchKernelGGL(mean_of_parts, dim3(1), dim3(kParts), 0, s, static_cast<const double *>(parts), nparts,
-                           groups, mean_bits);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_soft_quantize: launch failed: %s", hipGetErrorString(e));
-    return VBQ_OK;
+    return vbq::guarded("vbq_soft_quantize", [&]() -> vbq_status {
+        vbq::clear_error();
+        if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: k=%u is not a multiple of 64", k);
+        if (!(tau > 0.f) || tau > 3.0e38f) return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: tau must be positive and finite");
+        if (!mean_bits) return fail(VBQ_ERR_NULL, "vbq_soft_quantize: mean_bits is NULL");
+        if (!aligned(mean_bits, 8)) return fail(VBQ_ERR_ALIGN, "vbq_soft_quantize: mean_bits must be 8-byte aligned");
+        const uint64_t groups = static_cast<uint64_t>(n) * (k / VBQ_GROUP);
+        const uint64_t blocks = (groups * kLanesPerGroup + kBlock - 1) / kBlock;
+        if (groups) {
+            if (!w || !logits || !gumbel || !w_soft || !pi || !group_bits)
+                return fail(VBQ_ERR_NULL, "vbq_soft_quantize: a pointer is NULL");
+            if (!aligned(w, 16) || !aligned(w_soft, 16) || !aligned(logits, 16) || !aligned(gumbel, 16) ||
+                !aligned(pi, 16) || !aligned(group_bits, 4))
+                return fail(VBQ_ERR_ALIGN, "vbq_soft_quantize: w, w_soft, logits, gumbel and pi must be 16-byte aligned");
+            if (blocks > 0x7FFFFFFFull)
+                return fail(VBQ_ERR_SHAPE, "vbq_soft_quantize: %llu groups exceed one launch",
+                            static_cast<unsigned long long>(groups));
+        }
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        double *parts = nullptr;
+        const vbq_status ps = parts_for(s, &parts);
+        if (ps != VBQ_OK) return ps;
+        (void)hipGetLastError();
+        if (groups == 0) {   // no group: the mean is taken as 0
+            hipLaunchKernelGGL(mean_of_parts, dim3(1), dim3(kParts), 0, s, static_cast<const double *>(parts), 0u,
+                               uint64_t(0), mean_bits);
+        } else {
+            hipLaunchKernelGGL(soft_quantize_groups, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, s,
+                               reinterpret_cast<const float4 *>(w), reinterpret_cast<const float4 *>(logits),
+                               reinterpret_cast<const float4 *>(gumbel), tau, reinterpret_cast<float4 *>(w_soft),
+                               reinterpret_cast<float4 *>(pi), group_bits, groups);
+            const uint64_t chunk = (groups + kParts - 1) / kParts;
+            const uint32_t nparts = static_cast<uint32_t>((groups + chunk - 1) / chunk);
+            hipLaunchKernelGGL(chunk_sums, dim3(nparts), dim3(256), 0, s, static_cast<const float *>(group_bits), groups,
+                               chunk, parts);
+            hipLaunchKernelGGL(mean_of_parts, dim3(1), dim3(kParts), 0, s, static_cast<const double *>(parts), nparts,
+                               groups, mean_bits);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return fail(VBQ_ERR_HIP, "vbq_soft_quantize: launch failed: %s", hipGetErrorString(e));
+        return VBQ_OK;
+    });
 }

@@ -65,6 +65,8 @@
  *     stream is synchronised.
  *   - A non-VBQ_OK status means nothing was written and nothing was enqueued;
  *     vbq_last_error() then holds a one-line description (thread-local).
+ *     No C++ exception leaves the library: a failed host allocation returns
+ *     VBQ_ERR_NOMEM.
  *   - Device entry points trust the metadata (use vbq_validate_host on the
  *     host copy once after packing); they check shapes, pointers, alignment
  *     and the ABI version.
@@ -105,7 +107,9 @@ typedef enum vbq_status {
     VBQ_ERR_HIP = 10,       /* the HIP runtime refused a launch */
     VBQ_ERR_ABI = 11,       /* vbq_matrix.abi_version != VBQ_ABI_VERSION */
     VBQ_ERR_PADDING = 12,   /* a padded row or column does not dequantize to zero */
-    VBQ_ERR_FORMAT = 13     /* a container's header, sizes or checksum is wrong */
+    VBQ_ERR_FORMAT = 13,    /* a container's header, sizes or checksum is wrong */
+    VBQ_ERR_NOMEM = 14,     /* a host allocation inside the library failed */
+    VBQ_ERR_INTERNAL = 15   /* any other C++ exception inside the library (none is expected) */
 } vbq_status;
 
 /* Byte sizes of the four packed arrays. */
@@ -142,7 +146,8 @@ typedef struct vbq_matrix {
     uint32_t uniform_bits;
 } vbq_matrix;
 
-/* Library ABI version (compare with VBQ_ABI_VERSION). */
+/* Library ABI version (compare with VBQ_ABI_VERSION). Plumbing: the pages
+ * define no such call. */
 VBQ_API uint32_t vbq_abi_version(void);
 
 /* Sizes of the packed arrays for an n x k matrix with per-group widths
@@ -161,13 +166,16 @@ VBQ_API vbq_status vbq_pack(uint32_t n, uint32_t k, const uint8_t *bits, const i
                     const uint16_t *scales, uint8_t *widths_out, uint16_t *scales_out,
                     uint32_t *tile_offsets_out, uint8_t *payload_out, uint64_t payload_capacity);
 
-/* Number of tiles of an n x k matrix: ceil(n/64) * ceil(k/256). */
+/* Number of tiles of an n x k matrix: ceil(n/64) * ceil(k/256). Plumbing of
+ * the layout above (the pages fix no tiling). */
 VBQ_API uint64_t vbq_tile_count(uint32_t n, uint32_t k);
 
 /* Check a packed matrix held in host memory: k % 64, tile_offsets equal to
  * the prefix sum of the tile payload sizes, payload_bytes == tile_offsets[tiles],
- * every field on its grid, every scale finite.
- * Errors: NULL, ABI, SHAPE, OFFSETS, CODE, SCALE. */
+ * every field on its grid, every scale finite. This is the export-time check
+ * of the packed contract that VBQ §6, "Granularity is deployment-friendly",
+ * calls for; the device entry points do not repeat it.
+ * Errors: NULL, ABI, SHAPE, OFFSETS, CODE, SCALE, NOMEM. */
 VBQ_API vbq_status vbq_validate_host(const vbq_matrix *host_view);
 
 /* y = W x for one fp16 vector (§6 fused decode at batch 1).
@@ -178,19 +186,33 @@ VBQ_API vbq_status vbq_validate_host(const vbq_matrix *host_view);
  * nothing; k == 0 writes y = 0. */
 VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, void *stream);
 
-/* Several independent batch-1 GEMVs in one launch: ys[i] = W_i xs[i] for
+/* Several independent batch-1 GEMVs in one launch (VBQ §6, "Fused kernels
+ * over packed weights", for each matrix): ys[i] = W_i xs[i] for
  * i < count <= VBQ_MAX_MULTI. ws, xs and ys are host arrays of count entries
  * (the matrix views and x / y pointers as for vbq_gemv). Matrices that read
  * the same activation (q/k/v, gate/up) or a whole layer's projections run as
  * one dispatch. When every matrix declares a width (uniform_bits), the
  * uniform-width kernels run, also when the declared widths differ. Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (count),
- * ALIGN, OFFSETS, HIP. Scratch: calls with large-k, small-n matrices use a
- * library-owned device buffer per (device, stream), allocated on first need;
- * calls that overlap on the same stream handle are not allowed. */
+ * ALIGN, OFFSETS, HIP.
+ * Scratch: launches that split a row tile across workgroups (large k, small
+ * n) and the gated epilogue use a library-owned device buffer per (device,
+ * stream): partial sums and self-resetting arrival counters. It is
+ * allocated (hipMalloc, then a clearing kernel on `stream`) the first time a
+ * call on that stream needs it, and enlarged when a later call needs more;
+ * a superseded buffer is kept, not freed, because a graph captured earlier
+ * may still use it. Every buffer is held until the process ends. While
+ * `stream` is being captured into a graph the library never allocates: a
+ * call that would need a new or larger buffer returns VBQ_ERR_HIP (make one
+ * call of the same shapes on that stream before capturing). A captured graph
+ * uses the scratch of the stream it was captured on. Calls that overlap on
+ * the same stream handle (including replays of such a graph on another
+ * stream) race on the scratch and are not allowed. */
 VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                                   uint32_t count, void *stream);
 
-/* vbq_gemv_multi with fp16 outputs: ys[i] is device binary16 [n_i], each
+/* vbq_gemv_multi with fp16 outputs (VBQ §6, "Fused kernels over packed
+ * weights", with the decode step's fp16 activations handed to the next
+ * projection): ys[i] is device binary16 [n_i], each
  * value the fp32 result vbq_gemv_multi computes, rounded to nearest even
  * (beyond the fp16 range: +-inf), so a projection feeds the next layer's
  * fp16 input without a conversion launch. Same arguments, errors and
@@ -213,7 +235,12 @@ VBQ_API vbq_status vbq_gemv_multi_f16(const vbq_matrix *const *ws, const uint16_
 VBQ_API vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *up, const uint16_t *x, uint16_t *h,
                                    void *stream);
 
-/* Y = X W^T for m <= VBQ_MAX_BATCH fp16 vectors (small-batch decode).
+/* Y = X W^T for m <= VBQ_MAX_BATCH fp16 vectors (small-batch decode). The
+ * pages run decode at batch 1 only (VBQ §6, "Fused kernels over packed
+ * weights": every generated token streams every weight once) and are
+ * silent on batches; this call is the same per-group arithmetic (§3.1
+ * Eq. (1), w_hat = s * q) applied to m activation rows, with each group
+ * decoded once for all rows on the matrix-core path.
  * x: device binary16 [m][k] row-major; y: device fp32 [m][n] row-major
  * (overwritten). Runs on the matrix cores (each group's codes decoded once,
  * 16x16x32 fp16 products, fp32 accumulation) when m > 16, or when m >= 4 and
@@ -259,8 +286,10 @@ VBQ_API vbq_status vbq_quantize(uint32_t n, uint32_t k, const float *w, const ui
  * the caller's draw); w_soft fp32 [n][k]; group_bits fp32 [n*k/64];
  * mean_bits one double. w, w_soft, logits, gumbel and pi 16-byte aligned,
  * group_bits 4, mean_bits 8; the caller owns every buffer. The mean uses an
- * 8 KiB library-owned device buffer per (device, stream), allocated on first
- * need; calls that overlap on one stream handle are not allowed. Errors: SHAPE
+ * 8 KiB library-owned device buffer per (device, stream), allocated on the
+ * first call on that stream and held until the process ends; that first call
+ * must not be made while the stream is being captured (VBQ_ERR_HIP); calls
+ * that overlap on one stream handle are not allowed. Errors: SHAPE
  * (k % 64, tau not positive and finite, too many groups), NULL, ALIGN, HIP. */
 VBQ_API vbq_status vbq_soft_quantize(uint32_t n, uint32_t k, const float *w, const float *logits,
                                      const float *gumbel, float tau, float *w_soft, float *pi, float *group_bits,
@@ -277,7 +306,8 @@ VBQ_API vbq_status vbq_soft_quantize(uint32_t n, uint32_t k, const float *w, con
  * Errors: NULL (rows > 0 and a NULL pointer). */
 VBQ_API vbq_status vbq_recipe_head_bits(uint32_t rows, const uint64_t *freq, uint8_t *bits_out);
 
-/* The same ranking as vocabulary rows (host): order_out[i] = the row of
+/* The same ranking (VBQ §3.4, frequency-tiered head) as vocabulary rows
+ * (host): order_out[i] = the row of
  * rank i (descending frequency, ties to the lower row). The recipe's tiers
  * are then the rank ranges [0, round(0.005 N)), [.., round(0.02 N)),
  * [.., round(0.12 N)), [.., N): a head stored as four one-width matrices
@@ -285,6 +315,18 @@ VBQ_API vbq_status vbq_recipe_head_bits(uint32_t rows, const uint64_t *freq, uin
  * declaring its width), and its outputs, concatenated, are the logits in
  * rank order. Errors: NULL (rows > 0 and a NULL pointer). */
 VBQ_API vbq_status vbq_recipe_head_order(uint32_t rows, const uint64_t *freq, uint32_t *order_out);
+
+/* The frequency-grouped head as row blocks (VBQ §3.4, "From discovery to a
+ * fixed recipe": the head's widths are tiered by token frequency; §6,
+ * "Fused kernels over packed weights": the head runs as frequency-grouped
+ * row buckets). order_out[rows] = the rows in rank order as
+ * vbq_recipe_head_order gives them; tier_rows_out[4] = how many ranks fall in
+ * the 8-, 4-, 2- and 1-bit tiers, so tier t holds the ranks from the sum of
+ * the earlier counts on. Packing each non-empty tier's rows (in rank order)
+ * as one one-width matrix gives the grouped head. Errors: NULL (a NULL
+ * pointer with rows > 0, or tier_rows_out NULL), NOMEM. */
+VBQ_API vbq_status vbq_recipe_head_tiers(uint32_t rows, const uint64_t *freq, uint32_t *order_out,
+                                         uint32_t *tier_rows_out);
 
 /* Export-time check of the padding contract (VBQ §6, "Granularity is
  * deployment-friendly": MLP intermediates are zero-padded so the contracted
@@ -318,32 +360,39 @@ VBQ_API vbq_status vbq_check_padding(const vbq_matrix *host_view, uint32_t n_rea
 #define VBQ_CONTAINER_HEADER 128u
 
 /* Bytes the container of w takes. Host pointers are not read. Errors: NULL,
- * ABI, SHAPE (k % 64). */
+ * ABI, SHAPE (k % 64). The container is the file form of the export step
+ * (VBQ §6, "Granularity is deployment-friendly": packed groups produced at
+ * export and checked there); its byte format is this library's own. */
 VBQ_API vbq_status vbq_container_size(const vbq_matrix *host_view, uint64_t *bytes_out);
 
-/* Write w (host pointers, validated first) into out[0, capacity); the
+/* Write w (host pointers, validated first, as the export-time check of
+ * VBQ §6, "Granularity is deployment-friendly", asks) into out[0, capacity); the
  * caller owns out. *written = the container size. Errors: those of
  * vbq_validate_host; NULL; CAPACITY (capacity below the container size). */
 VBQ_API vbq_status vbq_container_write(const vbq_matrix *host_view, uint8_t *out, uint64_t capacity,
                                        uint64_t *written);
 
 /* Check a container image buf[0, len) and fill *view_out with pointers into
- * buf (no copy; buf must outlive the view). Checks the magic, version,
+ * buf (no copy; buf must outlive the view); the load side of the export
+ * step of VBQ §6, "Granularity is deployment-friendly". Checks the magic, version,
  * layout constants, that every array lies inside buf at its aligned offset
  * with the sizes n and k give, both checksums, then runs vbq_validate_host
  * on the view and sets its uniform_bits (vbq_uniform_width). Errors: NULL; FORMAT (header, sizes or
  * checksum); those of vbq_validate_host. */
 VBQ_API vbq_status vbq_container_open(const uint8_t *buf, uint64_t len, vbq_matrix *view_out);
 
-/* *bits_out = b when every group of the host view has width b, else 0
+/* One width per projection (VBQ §3.4, "From discovery to a fixed recipe",
+ * and §6, one bucket per projection): *bits_out = b when every group of the
+ * host view has width b, else 0
  * (also for n == 0 or k == 0). Reads the width codes only. Errors: NULL,
  * ABI, SHAPE (k % 64). */
 VBQ_API vbq_status vbq_uniform_width(const vbq_matrix *host_view, uint32_t *bits_out);
 
-/* Static English name of a status. */
+/* Static English name of a status. Plumbing: the pages define no such call. */
 VBQ_API const char *vbq_status_string(vbq_status s);
 
-/* Detail of the last failure on the calling thread ("" if none). */
+/* Detail of the last failure on the calling thread ("" if none). Plumbing:
+ * the pages define no such call. */
 VBQ_API const char *vbq_last_error(void);
 
 #ifdef __cplusplus

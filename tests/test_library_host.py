@@ -33,9 +33,32 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
-        "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize", "vbq_recipe_head_bits",
-        "vbq_check_padding", "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width", "vbq_recipe_head_order", "vbq_gemv_multi_f16", "vbq_soft_quantize",
-        "vbq_status_string", "vbq_last_error"])
+        "vbq_gemv_multi", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize",
+        "vbq_recipe_head_bits", "vbq_recipe_head_order", "vbq_recipe_head_tiers", "vbq_check_padding",
+        "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width",
+        "vbq_gemv_multi_f16", "vbq_soft_quantize", "vbq_status_string", "vbq_last_error"])
+
+
+def declaration_comments():
+    """{function: the comment block right above its VBQ_API declaration}."""
+    text = open(HEADER).read()
+    out = {}
+    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*(?:#define[^\n]*\n\s*)*VBQ_API\s+[\w\s\*]*?\b(vbq_\w+)\s*\(",
+                         text, re.S):
+        out[m.group(2)] = m.group(1)
+    return out
+
+
+def test_every_declaration_cites_its_passage():
+    """Each exported call names the passage of the pages it implements (a section mark), says the
+    pages are silent on it, names the callers it is for, or says it is plumbing the pages do not define."""
+    comments = declaration_comments()
+    assert sorted(comments) == declared_functions()
+    for name, text in comments.items():
+        flat = " ".join(text.split())
+        cited = ("§" in flat or "silent" in flat or "cannot allocate" in flat
+                 or "Plumbing" in flat)
+        assert cited, f"{name}: no citation in its comment"
 
 
 def test_library_exports_every_declared_symbol(V):
@@ -53,9 +76,59 @@ def test_library_exports_nothing_else(V):
 
 
 def test_status_strings(V):
-    for s in range(12):
-        assert V.lib.vbq_status_string(s).decode()
+    for s in range(16):
+        assert V.lib.vbq_status_string(s).decode() != "unknown status"
     assert V.lib.vbq_status_string(0).decode() == "ok"
+    assert V.lib.vbq_status_string(16).decode() == "unknown status"
+
+
+NOMEM_SCRIPT = r"""
+import ctypes, resource, sys
+sys.path.insert(0, sys.argv[1])
+import decode_gemv_02_amd as V
+# a view claiming 2^41 groups: the validator sizes its offset table (16 TiB) before it reads any array,
+# so the pointers only need to be non-NULL; the address-space limit makes the allocation fail for sure
+soft, hard = resource.getrlimit(resource.RLIMIT_AS)
+vm = int(open("/proc/self/statm").read().split()[0]) * resource.getpagesize()
+resource.setrlimit(resource.RLIMIT_AS, (vm + (256 << 20), hard))
+buf = (ctypes.c_uint8 * 64)()
+v = V.VbqMatrix(V.ABI_VERSION, 2**31, 64 * 1024, 0, ctypes.addressof(buf), ctypes.addressof(buf),
+                ctypes.addressof(buf), ctypes.addressof(buf), 0)
+st = V.lib.vbq_validate_host(ctypes.byref(v))
+print(st, V.lib.vbq_last_error().decode())
+"""
+
+
+def test_allocation_failure_is_a_status_not_an_exception(tmp_path):
+    """A host allocation that fails inside the library returns VBQ_ERR_NOMEM with a message; no C++
+    exception reaches the C ABI (ctypes would abort the process)."""
+    import subprocess
+    import sys
+    script = tmp_path / "nomem.py"
+    script.write_text(NOMEM_SCRIPT)
+    r = subprocess.run([sys.executable, str(script), ROOT], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    status, _, msg = r.stdout.strip().partition(" ")
+    import decode_gemv_02_amd as V
+    assert int(status) == V.ERR_NOMEM
+    assert "vbq_validate_host" in msg
+
+
+def test_head_tiers_follow_the_ranking(V):
+    """The grouped head's blocks come from the library: tier sizes match the §3.4 cut points and the
+    widths vbq_recipe_head_bits assigns, in rank order."""
+    rng = np.random.default_rng(7)
+    for rows in (0, 1, 7, 200, 32000):
+        freq = rng.zipf(1.3, rows).astype(np.uint64)
+        freq[rng.random(rows) < 0.2] = 5   # ties
+        order, tiers = V.vbq_recipe_head_tiers(freq)
+        assert int(tiers.sum()) == rows
+        assert np.array_equal(order, V.vbq_recipe_head_order(freq))
+        bits = V.vbq_recipe_head_bits(freq)
+        expect = np.concatenate([np.full(int(c), b, np.uint8) for b, c in zip((8, 4, 2, 1), tiers)])
+        assert np.array_equal(bits[order], expect)
+    order, tiers = V.vbq_recipe_head_tiers(np.arange(32000, dtype=np.uint64))
+    assert tiers.tolist() == [160, 480, 3200, 28160]
 
 
 @settings(max_examples=40, deadline=None)
