@@ -31,6 +31,8 @@ TILE_GROUPS = 4
 
 OK, ERR_NULL, ERR_SHAPE, ERR_WIDTH, ERR_CODE, ERR_SCALE, ERR_CAPACITY, ERR_OFFSETS, ERR_ALIGN, \
     ERR_TOO_LARGE, ERR_HIP, ERR_ABI, ERR_PADDING, ERR_FORMAT, ERR_NOMEM, ERR_INTERNAL = range(16)
+NOALLOC_SCRATCH_BYTES = 4 << 20
+NOALLOC_COUNTER_BYTES = 64 << 10
 CONTAINER_HEADER = 128
 
 
@@ -71,6 +73,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_tile_count.argtypes = [U32, U32]
     lib.vbq_gemv_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P), ctypes.POINTER(P),
                                    U32, P]
+    lib.vbq_gemv_multi_noalloc.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P),
+                                           ctypes.POINTER(P), U32, P]
     lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
     lib.vbq_gemv_multi_f16.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P),
                                        ctypes.POINTER(P), U32, P]
@@ -91,7 +95,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
               lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16,
-              lib.vbq_soft_quantize, lib.vbq_recipe_head_tiers):
+              lib.vbq_soft_quantize, lib.vbq_gemv_multi_noalloc, lib.vbq_recipe_head_tiers):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -241,6 +245,14 @@ def vbq_gemv_multi(ws, xs, ys, stream=None):
     """Several independent GEMVs (ys[i] = W_i xs[i]) in one launch; up to 16."""
     wa, xa, ya, count, dev = _multi_args(ws, xs, ys, torch.float32)
     _check(lib.vbq_gemv_multi(wa, xa, ya, count, _stream_handle(stream, dev)))
+    return ys
+
+
+def vbq_gemv_multi_noalloc(ws, xs, ys, stream=None):
+    """vbq_gemv_multi that never allocates: its scratch is the library's fixed per-GPU array (calls that
+    overlap on one GPU race)."""
+    wa, xa, ya, count, dev = _multi_args(ws, xs, ys, torch.float32)
+    _check(lib.vbq_gemv_multi_noalloc(wa, xa, ya, count, _stream_handle(stream, dev)))
     return ys
 
 

@@ -1457,6 +1457,47 @@ vbq_status scratch_for(const char *who, hipStream_t stream, size_t counters, siz
     return VBQ_OK;
 }
 
+// Scratch of vbq_gemv_multi_noalloc: a fixed array in the library's device
+// memory (one copy per GPU, zero-initialised when the code object loads).
+// Host code never uses the name `scratch` as an address: the device address
+// of each GPU's copy comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address reaches kernels.
+static __device__ __align__(256) uint8_t scratch[VBQ_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void *g_static_ptr[kMaxDevices] = {};
+
+vbq_status static_scratch(const char *who, hipStream_t stream, size_t counters, size_t partials, uint32_t **ctr_out,
+                          char **part_out) {
+    if (counters > VBQ_NOALLOC_COUNTER_BYTES || partials > VBQ_NOALLOC_SCRATCH_BYTES - VBQ_NOALLOC_COUNTER_BYTES)
+        return fail(VBQ_ERR_CAPACITY,
+                    "%s: the launch needs %zu B of counters and %zu B of partial sums; the fixed scratch holds %u "
+                    "and %u",
+                    who, counters, partials, VBQ_NOALLOC_COUNTER_BYTES,
+                    VBQ_NOALLOC_SCRATCH_BYTES - VBQ_NOALLOC_COUNTER_BYTES);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(VBQ_ERR_HIP, "%s: hipGetDevice failed", who);
+    if (dev < 0 || dev >= kMaxDevices) return fail(VBQ_ERR_HIP, "%s: device %d beyond %d", who, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(VBQ_ERR_HIP, "%s: hipGetSymbolAddress of the scratch array failed: %s", who,
+                        hipGetErrorString(e));
+        // the counters are zero at load and every call leaves them zero; clear them once anyway, with a
+        // kernel (not a memset) so a first call under graph capture records nothing a replay mishandles
+        const uint64_t words = VBQ_NOALLOC_COUNTER_BYTES / 4;
+        hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((words + 255) / 256)), dim3(256), 0, stream,
+                           static_cast<float *>(ptr), words);
+        if (hipGetLastError() != hipSuccess) return fail(VBQ_ERR_HIP, "%s: scratch clear failed", who);
+        g_static_ptr[dev] = ptr;
+    }
+    *ctr_out = static_cast<uint32_t *>(g_static_ptr[dev]);
+    *part_out = static_cast<char *>(g_static_ptr[dev]) + VBQ_NOALLOC_COUNTER_BYTES;
+    return VBQ_OK;
+}
+
 inline size_t partial_bytes(uint32_t splits, uint32_t n) {
     return (static_cast<size_t>(splits) * n * 4 + 255) / 256 * 256;
 }
@@ -1547,8 +1588,10 @@ void gemv_dispatch(bool aligned, bool ragged, uint32_t ubits, uint32_t blocks, u
 // One launch for up to VBQ_MAX_MULTI independent GEMVs; with h set, the two
 // matrices are gate and up (same shape, k > 0) and the launch writes
 // h = fp16(silu(gate x) * (up x)) instead of y.
+// no_alloc: the split scratch comes from the fixed array (vbq_gemv_multi_noalloc), never from hipMalloc.
 vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
-                       uint32_t count, hipStream_t stream, uint16_t *h = nullptr, uint16_t *const *ys16 = nullptr) {
+                       uint32_t count, hipStream_t stream, uint16_t *h = nullptr, uint16_t *const *ys16 = nullptr,
+                       bool no_alloc = false) {
     Batch B{};
     uint32_t blocks = 0, total_row_tiles = 0, max_col_tiles = 0;
     bool aligned = true;
@@ -1608,7 +1651,8 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     if (counter_slots) {
         uint32_t *ctr = nullptr;
         char *part = nullptr;
-        vbq_status st = scratch_for(who, stream, counter_slots * 4, partial_total, &ctr, &part);
+        vbq_status st = no_alloc ? static_scratch(who, stream, counter_slots * 4, partial_total, &ctr, &part)
+                                 : scratch_for(who, stream, counter_slots * 4, partial_total, &ctr, &part);
         if (st != VBQ_OK) return st;
         for (uint32_t i = 0; i < used; ++i) {
             MatArgs &M = B.m[i];
@@ -1714,6 +1758,25 @@ extern "C" vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t
         }
         (void)hipGetLastError();
         return gemv_launch(who, ws, xs, ys, count, static_cast<hipStream_t>(stream));
+    });
+}
+
+extern "C" vbq_status vbq_gemv_multi_noalloc(const vbq_matrix *const *ws, const uint16_t *const *xs,
+                                             float *const *ys, uint32_t count, void *stream) {
+    return vbq::guarded("vbq_gemv_multi_noalloc", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemv_multi_noalloc";
+        if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
+        if (count == 0) return VBQ_OK;
+        if (!ws || !xs || !ys) return fail(VBQ_ERR_NULL, "%s: ws, xs or ys is NULL", who);
+        for (uint32_t i = 0; i < count; ++i) {
+            vbq_status st = check_matrix(who, ws[i]);
+            if (st != VBQ_OK) return st;
+            st = check_vectors(who, ws[i], xs[i], ys[i]);
+            if (st != VBQ_OK) return st;
+        }
+        (void)hipGetLastError();
+        return gemv_launch(who, ws, xs, ys, count, static_cast<hipStream_t>(stream), nullptr, nullptr, true);
     });
 }
 

@@ -206,7 +206,8 @@ VBQ_API vbq_status vbq_gemv(const vbq_matrix *w, const uint16_t *x, float *y, vo
  * call of the same shapes on that stream before capturing). A captured graph
  * uses the scratch of the stream it was captured on. Calls that overlap on
  * the same stream handle (including replays of such a graph on another
- * stream) race on the scratch and are not allowed. */
+ * stream) race on the scratch and are not allowed. vbq_gemv_multi_noalloc is
+ * the variant that never allocates. */
 VBQ_API vbq_status vbq_gemv_multi(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                                   uint32_t count, void *stream);
 
@@ -250,6 +251,26 @@ VBQ_API vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *up,
  * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                                void *stream);
+
+/* vbq_gemv_multi for callers that cannot allocate device memory: code under
+ * graph capture, serving loops and harnesses that forbid hipMalloc. Same
+ * arguments, kernels, launch shapes and results (bit for bit) as
+ * vbq_gemv_multi, but the split-K partial sums and arrival counters live in
+ * a fixed array in the library's device memory (VBQ_NOALLOC_SCRATCH_BYTES per
+ * GPU, the first VBQ_NOALLOC_COUNTER_BYTES of it counters that are zero
+ * between calls), so the call never allocates, frees or synchronizes. Each
+ * GPU the library runs on holds its own copy of the array until the process
+ * ends; the first call on a GPU clears its counters with a kernel on
+ * `stream`. Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (on any streams, graph replays included) race and are
+ * not allowed. Errors: those of vbq_gemv_multi, and CAPACITY when the
+ * launch needs more than the array holds (more counter slots than
+ * VBQ_NOALLOC_COUNTER_BYTES / 4, i.e. 64-row tiles, or more partial sums
+ * than the rest of the array). */
+#define VBQ_NOALLOC_SCRATCH_BYTES (4u << 20)
+#define VBQ_NOALLOC_COUNTER_BYTES (64u << 10)
+VBQ_API vbq_status vbq_gemv_multi_noalloc(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
+                                          uint32_t count, void *stream);
 
 /* Decoded integer codes int8 [n][k] of a device matrix, produced with the
  * same in-register field decoding the GEMV and GEMM kernels use (a test and
