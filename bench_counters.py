@@ -53,11 +53,18 @@ def kernel_source_sha(path: str = KERNEL_SOURCE) -> str:
 
 
 def _by_launch(vals: list, warmup: int, steps: int, what: str) -> tuple[dict, list]:
-    """Step dispatches per launch name, and the dominant launch's back-to-back dispatches that follow them."""
-    n_step = len(LAUNCHES) * (warmup + steps)
-    if len(vals) != n_step + steps:
-        raise SystemExit(f"{what}: {len(vals)} GEMV dispatches, expected {n_step} in the steps and {steps} after")
-    return {nm: vals[i:n_step:len(LAUNCHES)] for i, nm in enumerate(LAUNCHES)}, vals[n_step:]
+    """Timed step dispatches per launch name, and the dominant launch's timed back-to-back dispatches.
+
+    bench.py --only-timed dispatches, in order: `warmup` eager steps, the graph of `steps` steps replayed
+    twice (untimed, then timed), then the dominant launch alone: `warmup` eager launches and its graph of
+    `steps` launches replayed twice. The timed replays are the ones kept."""
+    nl = len(LAUNCHES)
+    n_step = nl * (warmup + 2 * steps)
+    if len(vals) != n_step + warmup + 2 * steps:
+        raise SystemExit(f"{what}: {len(vals)} GEMV dispatches, expected {n_step} in the steps and "
+                         f"{warmup + 2 * steps} after")
+    timed = vals[n_step - nl * steps:n_step]
+    return {nm: timed[i::nl] for i, nm in enumerate(LAUNCHES)}, vals[len(vals) - steps:]
 
 
 def _counter_rows(db: str, counter: str):

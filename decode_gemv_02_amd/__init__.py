@@ -87,6 +87,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
     lib.vbq_recipe_head_order.argtypes = [U32, P, P]
     lib.vbq_recipe_head_tiers.argtypes = [U32, P, P, P]
+    lib.vbq_probe_stream_read.argtypes = [P, ctypes.c_uint64, P, U32, P]
+    lib.vbq_probe_dense_gemv.argtypes = [P, P, P, U32, U32, P]
     lib.vbq_check_padding.argtypes = [ctypes.POINTER(VbqMatrix), U32, U32, U32]
     lib.vbq_container_size.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(ctypes.c_uint64)]
     lib.vbq_container_write.argtypes = [ctypes.POINTER(VbqMatrix), P, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64)]
@@ -95,7 +97,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
               lib.vbq_gemm_smallbatch, lib.vbq_unpack_codes, lib.vbq_quantize, lib.vbq_recipe_head_bits,
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
               lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16,
-              lib.vbq_soft_quantize, lib.vbq_gemv_multi_noalloc, lib.vbq_recipe_head_tiers):
+              lib.vbq_soft_quantize, lib.vbq_gemv_multi_noalloc, lib.vbq_recipe_head_tiers,
+              lib.vbq_probe_stream_read, lib.vbq_probe_dense_gemv):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -351,6 +354,24 @@ def vbq_recipe_head_order(freq: np.ndarray) -> np.ndarray:
     out = np.zeros(freq.size, np.uint32)
     _check(lib.vbq_recipe_head_order(freq.size, _np_ptr(freq), _np_ptr(out)))
     return out
+
+
+def vbq_probe_stream_read(buf: torch.Tensor, nbytes: int, sink: torch.Tensor, blocks: int, stream=None):
+    """Read nbytes of buf (device) once: the HBM read ceiling of a launch that size (measurement only)."""
+    assert buf.is_contiguous() and nbytes <= buf.numel() * buf.element_size()
+    assert sink.dtype == torch.int32 and sink.numel() >= blocks * 256
+    _check(lib.vbq_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), blocks,
+                                     _stream_handle(stream, buf.device)))
+
+
+def vbq_probe_dense_gemv(w: torch.Tensor, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """y[n] (fp32) = W x for dense fp16 W [n][k]: the dense baseline (measurement only)."""
+    assert w.dtype == torch.float16 and x.dtype == torch.float16 and y.dtype == torch.float32
+    assert w.dim() == 2 and w.is_contiguous() and x.is_contiguous() and y.is_contiguous()
+    n, k = w.shape
+    assert x.numel() == k and y.numel() >= n
+    _check(lib.vbq_probe_dense_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k, _stream_handle(stream, w.device)))
+    return y
 
 
 def vbq_recipe_head_tiers(freq: np.ndarray):

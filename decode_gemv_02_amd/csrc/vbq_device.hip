@@ -122,40 +122,50 @@ __device__ __forceinline__ rsrc_t tile_rsrc(const uint8_t *payload, uint32_t pay
 
 // ---------------------------------------------------------------- per-width unpack
 // Each helper turns one little-endian 32-bit word of a group into fp16 pairs
-// (1024 + 2^s * u) where u = q + 2^(b-1) is the offset-binary code; the pairs
-// come out in natural element order (2i, 2i+1) thanks to the in-group field
-// layout, and multiply fp16 activation pairs with v_dot2.
+// whose bit patterns are f * u, u = q + 2^(b-1) the offset-binary code and f
+// the field's power-of-two position factor: fp16 subnormals of value
+// f * u * 2^-24, exact. The pairs come out in natural element order (2i,
+// 2i+1) thanks to the in-group field layout and multiply fp16 activation
+// pairs with v_dot2, which keeps fp16 subnormal inputs, so each product is
+// exact in fp32; the group's sum is scaled by 2^24 / f and the offset
+// 2^(b-1) * (sum of the group's activations) is taken off once per group.
 
 // 8-bit: elements 4w..4w+3 -> pairs (0,1), (2,3); factor 1
 __device__ __forceinline__ void unpack8(uint32_t v, uint32_t &p0, uint32_t &p1) {
     v ^= 0x80808080u;
-    p0 = __builtin_amdgcn_perm(0x64646464u, v, 0x04010400u);   // bytes {v0, 64, v1, 64}
-    p1 = __builtin_amdgcn_perm(0x64646464u, v, 0x04030402u);   // bytes {v2, 64, v3, 64}
+    p0 = __builtin_amdgcn_perm(0u, v, 0x0C010C00u);   // bytes {v0, 0, v1, 0}
+    p1 = __builtin_amdgcn_perm(0u, v, 0x0C030C02u);   // bytes {v2, 0, v3, 0}
 }
 
-// 4-bit: elements 8w..8w+7 -> pairs (0,1) x1, (2,3) x16, (4,5) x1, (6,7) x16.
-// magic holds kMagic in a register so each pair is one mask-and-or.
-__device__ __forceinline__ void unpack4(uint32_t v, uint32_t magic, uint32_t p[4]) {
+// 4-bit: elements 8w..8w+7 -> pairs (0,1) x1, (2,3) x16, (4,5) x1, (6,7) x16: one mask each
+__device__ __forceinline__ void unpack4(uint32_t v, uint32_t p[4]) {
     v = xor_opaque(v, 0x88888888u);
     const uint32_t h = v >> 8;
-    p[0] = (v & 0x000F000Fu) | magic;
-    p[1] = (v & 0x00F000F0u) | magic;
-    p[2] = (h & 0x000F000Fu) | magic;
-    p[3] = (h & 0x00F000F0u) | magic;
+    p[0] = v & 0x000F000Fu;
+    p[1] = v & 0x00F000F0u;
+    p[2] = h & 0x000F000Fu;
+    p[3] = h & 0x00F000F0u;
 }
 
 // 2-bit: elements 16w..16w+15 -> pairs m = 0..7 with factors 1,4,16,64,256,1,4,16
-__device__ __forceinline__ void unpack2(uint32_t v, uint32_t magic, uint32_t p[8]) {
+__device__ __forceinline__ void unpack2(uint32_t v, uint32_t p[8]) {
     v = xor_opaque(v, 0xAAAAAAAAu);
     const uint32_t h = v >> 10;
-    p[0] = (v & 0x00030003u) | magic;
-    p[1] = (v & 0x000C000Cu) | magic;
-    p[2] = (v & 0x00300030u) | magic;
-    p[3] = (v & 0x00C000C0u) | magic;
-    p[4] = (v & 0x03000300u) | magic;
-    p[5] = (h & 0x00030003u) | magic;
-    p[6] = (h & 0x000C000Cu) | magic;
-    p[7] = (h & 0x00300030u) | magic;
+    p[0] = v & 0x00030003u;
+    p[1] = v & 0x000C000Cu;
+    p[2] = v & 0x00300030u;
+    p[3] = v & 0x00C000C0u;
+    p[4] = v & 0x03000300u;
+    p[5] = h & 0x00030003u;
+    p[6] = h & 0x000C000Cu;
+    p[7] = h & 0x00300030u;
+}
+
+// 8-bit for the matrix-core decode: pairs (1024 + u) for an exact fp16 integer after one fma
+__device__ __forceinline__ void unpack8_1024(uint32_t v, uint32_t &p0, uint32_t &p1) {
+    v ^= 0x80808080u;
+    p0 = __builtin_amdgcn_perm(0x64646464u, v, 0x04010400u);   // bytes {v0, 64, v1, 64}
+    p1 = __builtin_amdgcn_perm(0x64646464u, v, 0x04030402u);   // bytes {v2, 64, v3, 64}
 }
 
 // 1-bit: bit i is the sign of element i; pair k = (2k, 2k+1) as fp16 +-1
@@ -194,15 +204,24 @@ struct Batch {
 };
 
 // 4992 bytes per wave: eight 4-wave, four 8-wave or two 16-wave workgroups
-// fit one CU's 160 KiB.
-struct alignas(16) WaveLds {
+// fit one CU's 160 KiB. 64-byte aligned: the lookup table's addresses are
+// formed with XORs below 64.
+//
+// Lookup table layout: table k (activations 4k..4k+3 of a column, k < 16) of
+// column jl is the 64 bytes at 256 k + 64 jl, and its entry u (the sum of the
+// activations picked by the set bits of u) sits at word u ^ 4 sw(k) with
+// sw(k) = (k >> 1) & 3. One k's tables of the four columns then lie in four
+// different groups of 16 banks (reads by lanes of different columns do not
+// collide), and the 16 lanes that build one column's tables write their four
+// 16-byte pieces to different banks.
+struct alignas(64) WaveLds {
     union {
-        float lut[kTileGroups * 16 * 16];     // [column][nibble position][4-bit index]
+        float lut[16 * kTileGroups * 16];     // [nibble position][column][4-bit index, swizzled]
         float part[kTileGroups * kTileRows];  // group dot products (unscaled) at column * 64 + row, once
                                               // the 1-bit groups are done
     };
     uint32_t xs[kTileGroups * kXStride];     // fp16 activation pairs per column
-    float corr[kTileGroups][4];              // per column: sum x, 2-bit and 4-bit bias terms
+    float corr[kTileGroups];                 // per column: the sum of its 64 activations
     uint8_t list[kTileRows * kTileGroups];   // the tile's groups in stream order, 1-bit bucket first:
                                              // column * 64 + row
 };
@@ -289,11 +308,24 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
     return t;
 }
 
+typedef __attribute__((address_space(3))) char lds_char;
+
+// LDS byte address of a workgroup-shared object
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_char *)p));
+}
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void lds_store16(uint32_t byte_addr, f32x4_t v) {
+    *reinterpret_cast<__attribute__((address_space(3))) f32x4_t *>(byte_addr) = v;
+}
+
 // Stage the tile's activations: fp16 pairs, the 4-bit lookup table (sums of
-// the activations selected by the set bits of a 4-bit index) and the
-// per-column bias terms of the unpack paths.
+// the activations selected by the set bits of a 4-bit index) and each
+// column's activation sum (the offset of the unpack paths).
 template <bool kLut = true>
-__device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane, float wa, float wb) {
+__device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
     const uint32_t jl = lane >> 4, k = lane & 15;
     L.xs[jl * kXStride + 2 * k] = xv.x;
     L.xs[jl * kXStride + 2 * k + 1] = xv.y;
@@ -301,28 +333,16 @@ __device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane, flo
     const float x2 = half_to_float(xv.y & 0xFFFFu), x3 = half_to_float(xv.y >> 16);
     const float a01 = x0 + x1, t5 = x2 + x0, t6 = x2 + x1, t7 = x2 + a01;
     if (kLut) {
-        float4 *t = reinterpret_cast<float4 *>(L.lut + lane * 16);
-        t[0] = make_float4(0.f, x0, x1, a01);
-        t[1] = make_float4(x2, t5, t6, t7);
-        t[2] = make_float4(x3, x3 + x0, x3 + x1, x3 + a01);
-        t[3] = make_float4(x3 + x2, x3 + t5, x3 + t6, x3 + t7);
+        // piece c of table (k, jl) at byte 256 k + 64 jl + 16 (c ^ sw(k)): the table is 64-byte
+        // aligned, so the four addresses are one base and three XORs
+        const uint32_t base = lds_addr(L.lut) + 256u * k + 64u * jl + 16u * ((k >> 1) & 3u);
+        lds_store16(base, f32x4_t{0.f, x0, x1, a01});
+        lds_store16(base ^ 16u, f32x4_t{x2, t5, t6, t7});
+        lds_store16(base ^ 32u, f32x4_t{x3, x3 + x0, x3 + x1, x3 + a01});
+        lds_store16(base ^ 48u, f32x4_t{x3 + x2, x3 + t5, x3 + t6, x3 + t7});
     }
-    // bias terms. 4-bit: element pairs alternate factor 1 / 16 -> weights 1032 / 72.
-    // 2-bit: pair factors 1,4,16,64,256,1,4,16 -> weights 1024/f + 2.
-    const float a23 = x2 + x3;
-    float xsum = a01 + a23;
-    // explicit fma: every kernel that stages x rounds these the same way, whatever the compiler
-    // would contract in its own context
-    float c4 = fmaf(1032.f, a01, 72.f * a23);
-    float c2 = fmaf(wa, a01, wb * a23);
-    xsum = row16_sum(xsum);
-    c2 = row16_sum(c2);
-    c4 = row16_sum(c4);
-    if (k == 0) {
-        L.corr[jl][0] = xsum;
-        L.corr[jl][1] = c2;
-        L.corr[jl][2] = c4;
-    }
+    const float xsum = row16_sum(a01 + (x2 + x3));
+    if (k == 0) L.corr[jl] = xsum;
 }
 
 // Inclusive prefix sum over the 64 lanes (DPP: row shifts, then row broadcasts).
@@ -419,42 +439,52 @@ __device__ __forceinline__ float sum_partials(const float *p, uint64_t stride, u
 
 __device__ __forceinline__ void store_part(WaveLds &L, uint32_t info, float v) { L.part[info] = v; }
 
+// The two constants of the 1-bit lookup addresses, held in registers for a whole kernel
+struct LutKeys {
+    uint32_t mask, swz;
+};
+__device__ __forceinline__ LutKeys lut_keys() { return LutKeys{opaque(0x3c3c3c3cu), opaque(0x30201000u)}; }
+
 // returns the product: L.part shares its bytes with the lookup table, so it
 // is stored once every 1-bit group of the tile is done
-__device__ __forceinline__ float group1(WaveLds &L, uint32_t info, uint2 v) {
+__device__ __forceinline__ float group1(WaveLds &L, uint32_t info, uint2 v, LutKeys keys) {
     const uint32_t jl = info >> 6;
-    // table k (one per 4 activations) starts at byte 64k; the entry for nibble u is at +4u.
-    // Bytes of lo/hi hold 4 * (nibble 2t / 2t+1) of each word.
-    const char *lut = reinterpret_cast<const char *>(L.lut + jl * 256u);
+    // table k of column jl at byte 256 k + 64 jl, entry u at byte 4 u ^ 16 sw(k). Bytes t of lo / hi hold
+    // 4 * (nibble 2t / 2t+1) of each word; nibble positions k = 8q + 2t and 8q + 2t + 1 both have
+    // sw(k) = t, so one mask-then-XOR (v_bitop3, truth table 0x6a = (a & b) ^ c) serves both
+    const char *lut = reinterpret_cast<const char *>(L.lut + jl * 16u);
+    const uint32_t mask = keys.mask, swz = keys.swz;
     const uint32_t w[2] = {v.x, v.y};
     float acc[4];
 #pragma unroll
     for (uint32_t q = 0; q < 2; ++q) {
         uint32_t lo, hi;
-        asm("v_lshlrev_b32 %0, 2, %1\n\tv_and_b32 %0, 0x3c3c3c3c, %0" : "=&v"(lo) : "v"(w[q]));
-        asm("v_lshrrev_b32 %0, 2, %1\n\tv_and_b32 %0, 0x3c3c3c3c, %0" : "=&v"(hi) : "v"(w[q]));
+        asm("v_lshlrev_b32 %0, 2, %1\n\tv_bitop3_b32 %0, %0, %2, %3 bitop3:0x6a"
+            : "=&v"(lo) : "v"(w[q]), "v"(mask), "v"(swz));
+        asm("v_lshrrev_b32 %0, 2, %1\n\tv_bitop3_b32 %0, %0, %2, %3 bitop3:0x6a"
+            : "=&v"(hi) : "v"(w[q]), "v"(mask), "v"(swz));
 #pragma unroll
         for (uint32_t t = 0; t < 4; ++t) {
             const uint32_t k = 8 * q + 2 * t;
-            const float a = *reinterpret_cast<const float *>(lut + 64u * k + ((lo >> (8 * t)) & 0xFFu));
-            const float b = *reinterpret_cast<const float *>(lut + 64u * (k + 1) + ((hi >> (8 * t)) & 0xFFu));
+            const float a = *reinterpret_cast<const float *>(lut + 256u * k + ((lo >> (8 * t)) & 0xFFu));
+            const float b = *reinterpret_cast<const float *>(lut + 256u * (k + 1) + ((hi >> (8 * t)) & 0xFFu));
             acc[t] = q == 0 ? a + b : acc[t] + (a + b);
         }
     }
     const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    return L.corr[jl][0] - 2.f * sum;
+    return L.corr[jl] - 2.f * sum;
 }
 
-// unscaled product of one 2-bit group of column jl
+// unscaled product of one 2-bit group of column jl: pair m holds 4^m u (4^(m-5) u for m >= 5) as
+// subnormals, so sum u x = 2^24 (a1 + a4 / 4 + ...), and q = u - 2
 __device__ __forceinline__ float dot2bit(WaveLds &L, uint32_t jl, uint2 va, uint2 vb) {
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride);
-    const uint32_t magic = opaque(kMagic);
     float a1 = 0.f, a4 = 0.f, a16 = 0.f, a64 = 0.f, a256 = 0.f;
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         uint32_t p[8];
-        unpack2(w[q], magic, p);
+        unpack2(w[q], p);
         const uint4 xa = xp[2 * q], xb = xp[2 * q + 1];
         a1 = dot2(p[0], xa.x, a1);
         a4 = dot2(p[1], xa.y, a4);
@@ -465,42 +495,47 @@ __device__ __forceinline__ float dot2bit(WaveLds &L, uint32_t jl, uint2 va, uint
         a4 = dot2(p[6], xb.z, a4);
         a16 = dot2(p[7], xb.w, a16);
     }
-    return a1 + 0.25f * a4 + 0.0625f * a16 + 0.015625f * a64 + 0.00390625f * a256 - L.corr[jl][1];
+    // explicit fma: the mixed and the one-width kernels inline this and must round it alike
+    const float ux = fmaf(0x1p16f, a256, fmaf(0x1p18f, a64, fmaf(0x1p20f, a16, fmaf(0x1p22f, a4, 0x1p24f * a1))));
+    return fmaf(-2.f, L.corr[jl], ux);
 }
 
 __device__ __forceinline__ void group2(WaveLds &L, uint32_t info, uint2 va, uint2 vb) {
     store_part(L, info, dot2bit(L, info >> 6, va, vb));
 }
 
-// 4-bit: a 16-byte half group (h = task & 1); lane pairs add their halves
-// 4-bit: a 16-byte half group (h = 0, 1) of column jl, without the bias term
+// 4-bit: a 16-byte half group (h = 0, 1) of column jl: sum u x / 2^24 over its 32 elements
 __device__ __forceinline__ float half4bit(WaveLds &L, uint32_t jl, uint32_t h, uint2 va, uint2 vb) {
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 16u * h);
-    const uint32_t magic = opaque(kMagic);
     float a1 = 0.f, a16 = 0.f;
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         uint32_t p[4];
-        unpack4(w[q], magic, p);
+        unpack4(w[q], p);
         const uint4 xa = xp[q];
         a1 = dot2(p[0], xa.x, a1);
         a16 = dot2(p[1], xa.y, a16);
         a1 = dot2(p[2], xa.z, a1);
         a16 = dot2(p[3], xa.w, a16);
     }
-    return a1 + 0.0625f * a16;
+    return fmaf(0.0625f, a16, a1);
 }
 
+// the group's product from its two halves' sums (q = u - 8)
+__device__ __forceinline__ float finish4bit(WaveLds &L, uint32_t jl, float halves) {
+    return fmaf(-8.f, L.corr[jl], 0x1p24f * halves);
+}
+
+// 4-bit: lane pairs add their halves (h = lane & 1)
 __device__ __forceinline__ void task4(WaveLds &L, uint32_t info, uint32_t h, uint2 va, uint2 vb) {
     const uint32_t jl = info >> 6;
     float part = half4bit(L, jl, h, va, vb);
     part += dpp<kQuadXor1>(part);
-    if (h == 0) store_part(L, info, part - L.corr[jl][2]);
+    if (h == 0) store_part(L, info, finish4bit(L, jl, part));
 }
 
-// 8-bit: a 16-byte quarter group (qd = task & 3); lane quads add their quarters
-// 8-bit: a 16-byte quarter group (qd = 0..3) of column jl, without the bias term
+// 8-bit: a 16-byte quarter group (qd = 0..3) of column jl: sum u x / 2^24 over its 16 elements
 __device__ __forceinline__ float quarter8bit(WaveLds &L, uint32_t jl, uint32_t qd, uint2 va, uint2 vb) {
     const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
     const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 8u * qd);
@@ -519,12 +554,18 @@ __device__ __forceinline__ float quarter8bit(WaveLds &L, uint32_t jl, uint32_t q
     return a;
 }
 
+// the group's product from its quarters' sum (q = u - 128)
+__device__ __forceinline__ float finish8bit(WaveLds &L, uint32_t jl, float quarters) {
+    return fmaf(-128.f, L.corr[jl], 0x1p24f * quarters);
+}
+
+// 8-bit: lane quads add their quarters (qd = lane & 3)
 __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, uint2 va, uint2 vb) {
     const uint32_t jl = info >> 6;
     float a = quarter8bit(L, jl, qd, va, vb);
     a += dpp<kQuadXor1>(a);
     a += dpp<kQuadXor2>(a);
-    if (qd == 0) store_part(L, info, fmaf(-1152.f, L.corr[jl][0], a));
+    if (qd == 0) store_part(L, info, finish8bit(L, jl, a));
 }
 
 // Payload of the first 256 one-bit groups and of the first 64 slices of
@@ -556,7 +597,7 @@ __device__ __forceinline__ void stage_payload(rsrc_t tile, const uint32_t cnt[4]
 // Staged work first, then the rounds that load their own bytes (rare: more
 // than 64 two-bit groups or 64 slices of a wider width in one tile).
 __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, rsrc_t tile, const uint32_t cnt[4],
-                                              uint32_t lane) {
+                                              uint32_t lane, LutKeys keys) {
     // A lane without a group in a round parks its (unused) result in a spare
     // slot past L.part, so the deferred stores need no branches.
     uint32_t info1[4];
@@ -567,7 +608,7 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, rsrc_
         const uint32_t e = L.list[lane + kWave * i];
         info1[i] = on ? e : kTileGroups * kTileRows + lane;
         v1[i] = 0.f;
-        if (on) v1[i] = group1(L, e, S.p1[i]);
+        if (on) v1[i] = group1(L, e, S.p1[i], keys);
     }
     // the lookup table is dead from here: its bytes take the products
 #pragma unroll
@@ -683,10 +724,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     WaveLds &L = lds[wave];
     float acc = 0.f;
     const uint32_t lane0 = lane_id();
-    // 2-bit bias weights of this lane's activation pairs (pair factors 1,4,16,64,256,1,4,16: 1024/f + 2)
-    const uint32_t km = lane0 & 3u;
-    const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
-    const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
+    const LutKeys keys = lut_keys();
     uint32_t ct = c_lo + wave;
     // metadata loads are unconditional (a wave without a next tile reloads its
     // own): a conditional load would make its result a branch merge, and the
@@ -703,10 +741,10 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         // the next tile's metadata travels while this tile computes
         const TileMeta nxt =
             load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, relane(lane0), true);
-        stage_x(L, cur.xv, relane(lane0), wa, wb);
+        stage_x(L, cur.xv, relane(lane0));
         build_lists(L, cur, P, cnt, rows, cn, relane(lane0));
         wave_lds_sync();
-        tile_products(L, S, tp, cnt, relane(lane0));
+        tile_products(L, S, tp, cnt, relane(lane0), keys);
         wave_lds_sync();
         const uint32_t lane = relane(lane0);
         if (lane < rows)
@@ -747,20 +785,20 @@ __device__ __forceinline__ RowGroups<kBits> load_row_group(rsrc_t tile, uint32_t
 }
 
 template <uint32_t kBits>
-__device__ __forceinline__ float row_group_dot(WaveLds &L, uint32_t jl, const RowGroups<kBits> &g) {
-    if (kBits == 1) return group1(L, jl << 6, make_uint2(g.v[0].x, g.v[0].y));
-    if (kBits == 2) return dot2bit(L, jl, make_uint2(g.v[0].x, g.v[0].y), make_uint2(g.v[0].z, g.v[0].w));
-    if (kBits == 4)
-        return (half4bit(L, jl, 0, make_uint2(g.v[0].x, g.v[0].y), make_uint2(g.v[0].z, g.v[0].w)) +
-                half4bit(L, jl, 1, make_uint2(g.v[1].x, g.v[1].y), make_uint2(g.v[1].z, g.v[1].w))) -
-               L.corr[jl][2];
-    // quarters added as the mixed kernel's lane quads add them, so both kernels give the same bits
-    float q[4];
+__device__ __forceinline__ float row_group_dot(WaveLds &L, uint32_t jl, const RowGroups<kBits> &g, LutKeys keys) {
+    if constexpr (kBits == 1) return group1(L, jl << 6, make_uint2(g.v[0].x, g.v[0].y), keys);
+    else if constexpr (kBits == 2) return dot2bit(L, jl, make_uint2(g.v[0].x, g.v[0].y), make_uint2(g.v[0].z, g.v[0].w));
+    else if constexpr (kBits == 4)
+        return finish4bit(L, jl, half4bit(L, jl, 0, make_uint2(g.v[0].x, g.v[0].y), make_uint2(g.v[0].z, g.v[0].w)) +
+                                     half4bit(L, jl, 1, make_uint2(g.v[1].x, g.v[1].y), make_uint2(g.v[1].z, g.v[1].w)));
+    else {
+        // quarters added as the mixed kernel's lane quads add them, so both kernels give the same bits
+        float q[4];
 #pragma unroll
-    for (uint32_t i = 0; i < 4; ++i)
-        q[i] = quarter8bit(L, jl, i, make_uint2(g.v[i & (kBits / 2 - 1)].x, g.v[i & (kBits / 2 - 1)].y),
-                           make_uint2(g.v[i & (kBits / 2 - 1)].z, g.v[i & (kBits / 2 - 1)].w));
-    return fmaf(-1152.f, L.corr[jl][0], (q[0] + q[1]) + (q[2] + q[3]));
+        for (uint32_t i = 0; i < 4; ++i)
+            q[i] = quarter8bit(L, jl, i, make_uint2(g.v[i].x, g.v[i].y), make_uint2(g.v[i].z, g.v[i].w));
+        return finish8bit(L, jl, (q[0] + q[1]) + (q[2] + q[3]));
+    }
 }
 
 // kLean: hold two 4-bit groups of a row at once instead of four (the per-matrix-width kernel, whose
@@ -780,9 +818,7 @@ __device__ __forceinline__ void uniform_tiles(const Batch &B, const MatArgs &M, 
     WaveLds &L = lds[wave];
     float acc = 0.f;
     const uint32_t lane0 = lane_id();
-    const uint32_t km = lane0 & 3u;
-    const float wa = km == 0 ? 1026.f : km == 1 ? 66.f : km == 2 ? 6.f : 258.f;
-    const float wb = km == 0 ? 258.f : km == 1 ? 18.f : km == 2 ? 1026.f : 66.f;
+    const LutKeys keys = lut_keys();
     constexpr uint32_t kChunk = kBits == 8 ? 1 : (kBits == 4 && kLean) ? 2 : kTileGroups;   // groups held at once
     uint32_t ct = c_lo + wave;
     TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, relane(lane0), true);
@@ -797,7 +833,7 @@ __device__ __forceinline__ void uniform_tiles(const Batch &B, const MatArgs &M, 
             g[jl] = load_row_group<kBits>(tp, (min(jl, cn - 1) * rows + lr) * 8u * kBits);
         const TileMeta nxt =
             load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, relane(lane0), true);
-        stage_x<kBits == 1>(L, cur.xv, relane(lane0), wa, wb);
+        stage_x<kBits == 1>(L, cur.xv, relane(lane0));
         wave_lds_sync();
         const uint32_t lane = relane(lane0);
 #pragma unroll
@@ -811,7 +847,7 @@ __device__ __forceinline__ void uniform_tiles(const Batch &B, const MatArgs &M, 
             for (uint32_t jl = 0; jl < kChunk; ++jl) {
                 const uint32_t j = c0 + jl;
                 const uint32_t sb = (j < 2 ? cur.s01 >> (16 * j) : cur.s23 >> (16 * (j - 2))) & 0xFFFFu;
-                const float d = row_group_dot<kBits>(L, j, g[jl]);
+                const float d = row_group_dot<kBits>(L, j, g[jl], keys);
                 if (lane < rows && j < cn) acc = fmaf(half_to_float(sb), d, acc);
             }
         }
@@ -887,12 +923,13 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
                     }
                 } else if (b == 2) {
                     uint32_t p[8];
-                    unpack2(v, opaque(kMagic), p);
+                    unpack2(v, p);
                     const float f[8] = {1.f, 4.f, 16.f, 64.f, 256.f, 1.f, 4.f, 16.f};
                     uint32_t outw[4] = {0, 0, 0, 0};
                     for (uint32_t m = 0; m < 8; ++m) {
-                        const int qa = static_cast<int>((half_to_float(p[m] & 0xFFFFu) - 1024.f) / f[m]) - 2;
-                        const int qb = static_cast<int>((half_to_float(p[m] >> 16) - 1024.f) / f[m]) - 2;
+                        // a pair half is the subnormal f u 2^-24: exact after scaling back
+                        const int qa = static_cast<int>(half_to_float(p[m] & 0xFFFFu) * 0x1p24f / f[m]) - 2;
+                        const int qb = static_cast<int>(half_to_float(p[m] >> 16) * 0x1p24f / f[m]) - 2;
                         const uint32_t e0 = 2 * m, e1 = 2 * m + 1;
                         outw[e0 >> 2] |= (static_cast<uint32_t>(qa) & 0xFFu) << (8 * (e0 & 3));
                         outw[e1 >> 2] |= (static_cast<uint32_t>(qb) & 0xFFu) << (8 * (e1 & 3));
@@ -900,12 +937,12 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
                     for (uint32_t o = 0; o < 4; ++o) dst[wd * 4 + o] = outw[o];
                 } else if (b == 4) {
                     uint32_t p[4];
-                    unpack4(v, opaque(kMagic), p);
+                    unpack4(v, p);
                     uint32_t outw[2] = {0, 0};
                     for (uint32_t m = 0; m < 4; ++m) {
                         const float f = (m & 1) ? 16.f : 1.f;
-                        const int qa = static_cast<int>((half_to_float(p[m] & 0xFFFFu) - 1024.f) / f) - 8;
-                        const int qb = static_cast<int>((half_to_float(p[m] >> 16) - 1024.f) / f) - 8;
+                        const int qa = static_cast<int>(half_to_float(p[m] & 0xFFFFu) * 0x1p24f / f) - 8;
+                        const int qb = static_cast<int>(half_to_float(p[m] >> 16) * 0x1p24f / f) - 8;
                         const uint32_t e0 = 2 * m, e1 = 2 * m + 1;
                         outw[e0 >> 2] |= (static_cast<uint32_t>(qa) & 0xFFu) << (8 * (e0 & 3));
                         outw[e1 >> 2] |= (static_cast<uint32_t>(qb) & 0xFFu) << (8 * (e1 & 3));
@@ -915,10 +952,10 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
                 } else {
                     uint32_t p0, p1;
                     unpack8(v, p0, p1);
-                    const int q0 = static_cast<int>(half_to_float(p0 & 0xFFFFu)) - 1152;
-                    const int q1 = static_cast<int>(half_to_float(p0 >> 16)) - 1152;
-                    const int q2 = static_cast<int>(half_to_float(p1 & 0xFFFFu)) - 1152;
-                    const int q3 = static_cast<int>(half_to_float(p1 >> 16)) - 1152;
+                    const int q0 = static_cast<int>(half_to_float(p0 & 0xFFFFu) * 0x1p24f) - 128;
+                    const int q1 = static_cast<int>(half_to_float(p0 >> 16) * 0x1p24f) - 128;
+                    const int q2 = static_cast<int>(half_to_float(p1 & 0xFFFFu) * 0x1p24f) - 128;
+                    const int q3 = static_cast<int>(half_to_float(p1 >> 16) * 0x1p24f) - 128;
                     dst[wd] = (static_cast<uint32_t>(q0) & 0xFFu) | ((static_cast<uint32_t>(q1) & 0xFFu) << 8) |
                               ((static_cast<uint32_t>(q2) & 0xFFu) << 16) | ((static_cast<uint32_t>(q3) & 0xFFu) << 24);
                 }
@@ -1067,7 +1104,7 @@ __device__ __forceinline__ void decode8(uint4 v, uint16_t *dst) {
 #pragma unroll
     for (uint32_t q = 0; q < 4; ++q) {
         uint32_t p0, p1;
-        unpack8(w[q], p0, p1);
+        unpack8_1024(w[q], p0, p1);
         o[2 * q] = half2_fma(p0, one, a8);
         o[2 * q + 1] = half2_fma(p1, one, a8);
     }

@@ -409,6 +409,27 @@ VBQ_API vbq_status vbq_container_open(const uint8_t *buf, uint64_t len, vbq_matr
  * ABI, SHAPE (k % 64). */
 VBQ_API vbq_status vbq_uniform_width(const vbq_matrix *host_view, uint32_t *bits_out);
 
+/* ---- measurement: what the packed GEMV is compared with (not its path) ---- */
+
+/* Read bytes of device memory at buf once with 16-byte loads and keep nothing
+ * (device, asynchronous on `stream`): the HBM read rate a streaming launch of
+ * that size reaches on this GPU, ramp and drain included, i.e. the practical
+ * ceiling of the packed GEMV's launches. Plumbing of the measurement: the
+ * pages define no such call. buf and bytes are multiples of 16; blocks
+ * (1..2^20) workgroups of 256 threads; sink: device uint32 [blocks * 256],
+ * written only for a value the buffer's XOR practically never takes.
+ * Errors: NULL, ALIGN, SHAPE, HIP. */
+VBQ_API vbq_status vbq_probe_stream_read(const void *buf, uint64_t bytes, uint32_t *sink, uint32_t blocks,
+                                         void *stream);
+
+/* y = W x for a dense fp16 W [n][k] row-major, fp16 x [k], fp32 y [n] (device,
+ * asynchronous on `stream`): the dense baseline VBQ §6 compares packed decode
+ * with (Figure 5 and the Table 2 caption: the same weights dequantized to
+ * dense FP16). fp16 products, fp32 sums. w and x 16-byte aligned; k a
+ * multiple of 64 up to 16384. Errors: NULL, ALIGN, SHAPE, HIP. */
+VBQ_API vbq_status vbq_probe_dense_gemv(const uint16_t *w, const uint16_t *x, float *y, uint32_t n, uint32_t k,
+                                        void *stream);
+
 /* Static English name of a status. Plumbing: the pages define no such call. */
 VBQ_API const char *vbq_status_string(vbq_status s);
 

@@ -31,12 +31,13 @@ def test_traffic_summary_is_read_only_for_the_current_kernel(tmp_path):
 
 
 def test_launches_are_split_by_dispatch_order():
-    # one warmup step and one timed step (8 dispatches), then the roofline leg (one dispatch per timed step)
-    per, tail = bench_counters._by_launch(list(range(9)), 1, 1, "test")
-    assert per == {"q+k+v": [0, 4], "o": [1, 5], "gate+up": [2, 6], "down": [3, 7]}
-    assert tail == [8]
+    # one eager warmup step, the graph of two steps replayed twice (16 dispatches), then the roofline leg:
+    # one eager warmup launch and its graph of two launches replayed twice
+    per, tail = bench_counters._by_launch(list(range(20 + 5)), 1, 2, "test")
+    assert per == {"q+k+v": [12, 16], "o": [13, 17], "gate+up": [14, 18], "down": [15, 19]}
+    assert tail == [23, 24]
     try:
-        bench_counters._by_launch(list(range(8)), 1, 1, "test")
+        bench_counters._by_launch(list(range(20 + 4)), 1, 2, "test")
     except SystemExit:
         pass
     else:
