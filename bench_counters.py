@@ -184,6 +184,129 @@ def kernels_summary(a) -> str:
     return "\n".join(lines) + "\n"
 
 
+# instruction and occupancy counters per launch (one rocprofv3 --pmc pass per line of PMC_PASSES)
+PMC_PASSES = [
+    "SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_SMEM SQ_INSTS_VMEM_RD SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES",
+    "SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM SQ_LDS_BANK_CONFLICT "
+    "SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_ANY SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",   # GRBM_GUI_ACTIVE tells the dispatches apart
+]
+CU_NUM = 256
+
+
+def _launch_signatures(con) -> list:
+    """GEMV dispatches as (dispatch_id, launch name): a launch is told apart by its kernel, workgroup
+    and grid (its first appearance follows LAUNCHES' order; the roofline leg repeats gate+up's)."""
+    rows = con.execute("select distinct dispatch_id, kernel_name, workgroup_size, grid_size_x, grid_size_y "
+                       "from counters_collection order by dispatch_id").fetchall()
+    names, out = {}, []
+    for did, kn, wg, gx, gy in rows:
+        if GEMV_KERNEL not in kn:
+            continue
+        sig = (kn, wg, gx, gy)
+        if sig not in names:
+            if len(names) >= len(LAUNCHES):
+                raise SystemExit(f"more than {len(LAUNCHES)} distinct GEMV launches")
+            names[sig] = LAUNCHES[len(names)]
+        out.append((did, names[sig]))
+    return out
+
+
+def counters_summary(a) -> str:
+    """Per launch and per wave (one wave = one 64x256 tile in these launches): instructions by kind,
+    LDS bank-conflict share, VALU busy share of the CUs' cycles, mean wave lifetime."""
+    totals = {nm: {} for nm in LAUNCHES}
+    gui = {nm: [] for nm in LAUNCHES}
+    dispatches = {}
+    for db in a.db:
+        con = sqlite3.connect(db)
+        try:
+            which = dict(_launch_signatures(con))
+            for nm in LAUNCHES:
+                dispatches.setdefault(nm, sum(1 for v in which.values() if v == nm))
+            for did, cn, val in con.execute("select dispatch_id, counter_name, value from counters_collection "
+                                            "order by dispatch_id"):
+                nm = which.get(did)
+                if nm is None:
+                    continue
+                if cn == "GRBM_GUI_ACTIVE":
+                    gui[nm].append((did, val))
+                    continue
+                totals[nm][cn] = totals[nm].get(cn, 0.0) + val
+        finally:
+            con.close()
+    lines = ["# Instruction and occupancy counters per launch of gemv_tiles, layer_9b decode step "
+             "(q+k+v | o | gate+up | down), batch 1",
+             "# commands (repository root; one rocprofv3 run per counter set):"]
+    for i, pas in enumerate(PMC_PASSES):
+        lines.append(f"#   rocprofv3 --pmc {pas} -d <dir> -o pmc{i} -- python bench.py --steps 5 --warmup 2 "
+                     f"--only-timed --no-cpu-baseline")
+    lines.append("#   python bench_counters.py counters --db <dir>/pmc0_results.db <dir>/pmc1_results.db --out <this file>")
+    lines.append("# per wave: instructions issued by one wave (one tile); valu_us_per_simd: SQ_ACTIVE_INST_VALU "
+                 f"(quad-cycles) x 4 / {4 * CU_NUM} SIMDs at 2.4 GHz, the mean time a SIMD issues this launch's "
+                 "VALU work (compare with its kernel-trace duration); lds_conflict: SQ_LDS_BANK_CONFLICT / "
+                 "(SQ_LDS_IDX_ACTIVE - SQ_LDS_BANK_CONFLICT); cycles are per wave")
+    if a.title:
+        lines.append(f"# {a.title}")
+    lines.append(f"kernel_source_sha256: {a.kernel_sha or kernel_source_sha()}")
+    for nm in LAUNCHES:
+        t = totals[nm]
+        waves = t.get("SQ_WAVES", 0.0)
+        if not waves:
+            continue
+        per = {k.replace("SQ_", "").lower(): v / waves for k, v in sorted(t.items()) if k != "SQ_WAVES"}
+        parts = [f"waves_per_dispatch={waves / dispatches[nm]:.0f}"]   # SQ_WAVES is in one counter set
+        parts += [f"{k}={v:.1f}" for k, v in per.items() if k.startswith("insts_")]
+        if "SQ_LDS_IDX_ACTIVE" in t and "SQ_LDS_BANK_CONFLICT" in t:
+            c = t["SQ_LDS_BANK_CONFLICT"]
+            parts.append(f"lds_conflict={c / max(1.0, t['SQ_LDS_IDX_ACTIVE'] - c):.3f}")
+        if "SQ_ACTIVE_INST_VALU" in t and gui[nm]:
+            cycles = 4 * t["SQ_ACTIVE_INST_VALU"] / (4 * CU_NUM) / len(set(d for d, _ in gui[nm]))
+            parts.append(f"valu_us_per_simd={cycles / 2400.0:.2f}")
+        if "SQ_WAVE_CYCLES" in t:
+            parts.append(f"wave_lifetime_cycles={4 * t['SQ_WAVE_CYCLES'] / waves:.0f}")
+        if "SQ_WAIT_INST_ANY" in t:
+            parts.append(f"wait_inst_any_cycles={4 * t['SQ_WAIT_INST_ANY'] / waves:.0f}")
+        lines.append(f"launch {nm}: " + " ".join(parts))
+    return "\n".join(lines) + "\n"
+
+
+PROBE_KERNEL = "stream_read"
+
+
+def probe_summary(a) -> str:
+    """The read-only stream probe of a full bench.py run, by dispatch order: the step-shaped probe (four
+    launches of the step's launch sizes per step: `warmup` eager steps, then its graph of `steps` steps
+    replayed twice), the large read (`warmup` eager launches, a graph of 8 replayed twice) and the probe
+    of the dominant launch's size (`warmup` eager, a graph of `steps` replayed twice). Timed replays only."""
+    with open(a.csv, newline="") as f:
+        rows = [r for r in csv.DictReader(f) if PROBE_KERNEL in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    dur = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    w, k, nl = a.warmup, a.steps, len(LAUNCHES)
+    n_step = nl * (w + 2 * k)
+    n_big = w + 2 * 8
+    n_dom = w + 2 * k
+    if len(dur) != n_step + n_big + n_dom:
+        raise SystemExit(f"{a.csv}: {len(dur)} probe dispatches, expected {n_step + n_big + n_dom}")
+    step = dur[n_step - nl * k:n_step]
+    big = dur[n_step + n_big - 8:n_step + n_big]
+    dom = dur[len(dur) - k:]
+    lines = ["# Read-only HBM stream probe (vbq_probe_stream_read, 2048 x 256 threads, 16-byte loads), the "
+             "ceiling of the layer_9b decode step's launches",
+             "# command (repository root):",
+             f"#   rocprofv3 --kernel-trace --stats -f csv -d <dir> -o kp -- python bench.py --steps {k} "
+             f"--warmup {w} --no-cpu-baseline",
+             "#   python bench_counters.py probe --csv <dir>/kp_kernel_trace.csv --out <this file>"]
+    for i, nm in enumerate(LAUNCHES):
+        v = step[i::nl]
+        lines.append(f"probe of the {nm} launch's bytes: dispatches={len(v)} avg_us={statistics.fmean(v):.3f} "
+                     f"min_us={min(v):.3f} max_us={max(v):.3f}")
+    lines.append(f"probe step (four launches): sum_of_avg_us={sum(statistics.fmean(step[i::nl]) for i in range(nl)):.3f}")
+    lines.append(f"large read: dispatches={len(big)} avg_us={statistics.fmean(big):.3f}")
+    lines.append(f"dominant launch's bytes alone, back to back: dispatches={len(dom)} avg_us={statistics.fmean(dom):.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path: str) -> dict | None:
     """{launch: traffic bytes} from a traffic summary, or None if absent or taken on another kernel source."""
     if not os.path.exists(path):
@@ -224,8 +347,20 @@ def main():
     n.add_argument("--title", required=True)
     n.add_argument("--command", required=True)
     n.add_argument("--out", required=True)
+    pr = sub.add_parser("probe")
+    pr.add_argument("--csv", required=True)
+    pr.add_argument("--steps", type=int, default=20)
+    pr.add_argument("--warmup", type=int, default=5)
+    pr.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--db", nargs="+", required=True)
+    c.add_argument("--out", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--kernel-sha", default="", help="sha256 of the kernel source the counters were taken on "
+                                                     "(default: the current source)")
     a = ap.parse_args()
-    text = {"traffic": traffic_summary, "trace": trace_summary, "kernels": kernels_summary}[a.cmd](a)
+    text = {"traffic": traffic_summary, "trace": trace_summary, "kernels": kernels_summary,
+            "counters": counters_summary, "probe": probe_summary}[a.cmd](a)
     with open(a.out, "w") as f:
         f.write(text)
     print(text, end="")

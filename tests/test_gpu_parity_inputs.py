@@ -1,0 +1,134 @@
+"""GPU parity on inputs the seeded workloads do not draw: activations with a
+common mode, payloads that hold the reserved two's-complement pattern, and
+negative scales. Every case runs through the mixed-width kernel (matrices
+that do not declare their width), the one-width kernels (matrices that do)
+and the small-batch paths, against the CPU oracle at the parity bar
+(relative L2 <= 1e-3 and max abs <= 2e-3 * ||x||_2 * max|s| per output
+vector); decoded codes are compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.conftest import gpu_available
+from tests.helpers import assert_within_tolerance, tolerance_report
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def V():
+    import torch  # noqa: F401
+    import decode_gemv_02_amd as V
+    return V
+
+
+def print_case(**kw):
+    print("CASE", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def run(V, dm, x_bits):
+    """Y [m, n] in float64: the GEMV for m = 1, the small-batch entry point otherwise."""
+    import torch
+    x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.float16)).cuda()
+    m = x.shape[0]
+    y = torch.full((m, dm.n), float("nan"), dtype=torch.float32, device="cuda")
+    if m == 1:
+        V.vbq_gemv(dm, x[0], y[0])
+    else:
+        V.vbq_gemm_smallbatch(dm, x, y)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def both_kernels(V, host):
+    """The same packed bytes as a one-width matrix (declared) and as a mixed-width one (not declared)."""
+    return {"declared": V.DeviceMatrix(host), "mixed": V.DeviceMatrix(host, uniform=False)}
+
+
+@pytest.mark.parametrize("mean", [1.0, 4.0, -16.0])
+@pytest.mark.parametrize("mix", [{2: 1.0}, {4: 1.0}, {8: 1.0}, {1: 1.0}, W.STD_MIX])
+def test_offset_activations(V, mean, mix):
+    """x = mean + 0.5 N(0,1): the 2-, 4- and 8-bit paths take 2^(b-1) times the group's activation
+    sum off once per group, so a large common mode must not cost precision."""
+    n, k = 200, 4096 + 256
+    b = max(mix) if len(mix) == 1 else 0
+    bits, codes, scales = W.draw_random_matrix((110, b, int(mean) + 100), n, k, mix)
+    host = V.vbq_pack(n, k, bits, codes, scales)
+    p = oracle.pack(n, k, bits, codes, scales)
+    for m in (1, 16, 64):
+        x = W.draw_x_offset((111, b, m, int(mean) + 100), k, m, mean=mean, sigma=0.5)
+        ref = oracle.gemm(p, x)
+        for name, dm in both_kernels(V, host).items():
+            if name == "declared" and not b:
+                continue
+            print_case(test="offset_x", mean=mean, b=b, m=m, kernel=name)
+            got = run(V, dm, x)
+            assert_within_tolerance(got, ref, x, scales, f"mean={mean} b={b} m={m} {name}")
+            if m == 1:
+                rel = tolerance_report(got, ref, x, scales)[0][0]
+                assert rel <= 2e-5, f"mean={mean} b={b} {name}: rel L2 {rel:.2e} (cancellation?)"
+
+
+def plant_reserved(payload: np.ndarray, b: int, rng, frac: float = 0.05) -> int:
+    """Set about frac of the b-bit fields of a one-width payload to the reserved pattern 2^(b-1)
+    (two's complement -2^(b-1)); fields never straddle a byte. Returns how many were set."""
+    per_byte = 8 // b
+    fields = payload.size * per_byte
+    pick = np.unique(rng.integers(0, fields, size=max(1, int(frac * fields))))
+    byte, slot = pick // per_byte, pick % per_byte
+    shift = (slot * b).astype(np.uint8)
+    mask = np.left_shift(np.uint8((1 << b) - 1), shift)
+    val = np.left_shift(np.uint8(1 << (b - 1)), shift)
+    np.bitwise_and.at(payload, byte, ~mask)
+    np.bitwise_or.at(payload, byte, val)
+    return int(pick.size)
+
+
+@pytest.mark.parametrize("b", [2, 4, 8])
+def test_reserved_pattern_decodes_as_the_oracle(V, b):
+    """The packer never writes -2^(b-1), but a payload may hold it: the kernels read it as
+    -2^(b-1), exactly as the oracle does (codes bit for bit, products at the parity bar)."""
+    import torch
+    n, k = 130, 1280
+    bits, codes, scales = W.draw_random_matrix((112, b), n, k, {b: 1.0})
+    host = V.vbq_pack(n, k, bits, codes, scales)
+    p = oracle.pack(n, k, bits, codes, scales)
+    assert np.array_equal(host.payload, p.payload)
+    planted = plant_reserved(host.payload, b, np.random.default_rng(113 + b))
+    p.payload[:] = host.payload
+    assert planted > 0
+    with pytest.raises(V.VbqError) as err:
+        V.vbq_validate_host(host)
+    assert err.value.status == V.ERR_CODE
+    want = oracle.unpack(p)
+    assert int((want == -(1 << (b - 1))).sum()) == planted
+    for name, dm in both_kernels(V, host).items():
+        print_case(test="reserved", b=b, kernel=name)
+        out = torch.empty((n, k), dtype=torch.int8, device="cuda")
+        V.vbq_unpack_codes(dm, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want)
+        for m in (1, 17, 64):
+            x = W.draw_x((114, b, m), k, m)
+            assert_within_tolerance(run(V, dm, x), oracle.gemm(p, x), x, scales, f"reserved b={b} m={m} {name}")
+
+
+@pytest.mark.parametrize("mix", [W.STD_MIX, W.HEAD_MIX, {1: 1.0}, {8: 1.0}])
+def test_negative_scales(V, mix):
+    """Scales of either sign (binary16 with the sign bit set): every path multiplies by s as it is."""
+    n, k = 300, 2048 + 192
+    bits, codes, _ = W.draw_random_matrix((115, len(mix)), n, k, mix)
+    scales = W.draw_signed_scales((116, len(mix)), n, k // 64)
+    assert (scales >> 15).any() and not (scales >> 15).all()
+    host = V.vbq_pack(n, k, bits, codes, scales)
+    p = oracle.pack(n, k, bits, codes, scales)
+    for m in (1, 5, 16, 64):
+        x = W.draw_x((117, len(mix), m), k, m)
+        ref = oracle.gemm(p, x)
+        for name, dm in both_kernels(V, host).items():
+            if name == "declared" and len(mix) > 1:
+                continue
+            print_case(test="negative_scales", mix=len(mix), m=m, kernel=name)
+            assert_within_tolerance(run(V, dm, x), ref, x, scales, f"signed scales m={m} {name}")

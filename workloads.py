@@ -157,6 +157,19 @@ def draw_x(seed, k: int, m: int = 1) -> np.ndarray:
     return rng.standard_normal((m, k)).astype(np.float16).view(np.uint16)
 
 
+def draw_x_offset(seed, k: int, m: int = 1, mean: float = 1.0, sigma: float = 0.1) -> np.ndarray:
+    """fp16 activations mean + sigma * N(0,1) (a common mode, as post-activation or un-centred
+    inputs have) as uint16 bit patterns, shape [m, k]."""
+    rng = np.random.default_rng(np.random.SeedSequence(tuple(np.atleast_1d(seed).tolist()) + (6007,)))
+    return (mean + sigma * rng.standard_normal((m, k))).astype(np.float16).view(np.uint16)
+
+
+def draw_signed_scales(seed, n: int, groups: int, sigma: float = 0.02) -> np.ndarray:
+    """fp16 scales N(0, sigma) with either sign (the format allows negative scales)."""
+    rng = np.random.default_rng(np.random.SeedSequence(tuple(np.atleast_1d(seed).tolist()) + (4421,)))
+    return rng.normal(0.0, sigma, size=(n, groups)).astype(np.float16).view(np.uint16)
+
+
 def x_seed(spec: MatrixSpec) -> tuple:
     """Matrices of one layer that read the same input share this key."""
     return (spec.seed[0], 10_000 + spec.layer, spec.role)
