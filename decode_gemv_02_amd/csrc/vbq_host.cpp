@@ -201,7 +201,7 @@ extern "C" vbq_status vbq_pack(uint32_t n, uint32_t k, const uint8_t *bits, cons
         std::vector<uint64_t> off(groups);
         place_groups(n, G, [&](uint32_t r, uint32_t j) { return uint32_t(bits[uint64_t(r) * G + j]); }, off.data(),
                      tile_offsets_out);
-        std::memset(widths_out, 0, sz.widths_bytes);
+        if (sz.widths_bytes) std::memset(widths_out, 0, sz.widths_bytes);
         if (sz.payload_bytes) std::memset(payload_out, 0, sz.payload_bytes);
         for (uint64_t t = 0; t < groups; ++t) {
             const uint32_t b = bits[t];
