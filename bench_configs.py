@@ -5,7 +5,9 @@ microseconds per pass and GB/s of packed bytes (for batch > 1 also TFLOP/s
 of useful multiply-adds, 2*m flop per weight). A pass runs every matrix of
 the workload once in decode order: per layer the q/k/v GEMVs share one
 launch, then o, then gate/up in one launch, then down (vbq_gemv_multi); at
-batch > 1 every matrix is one vbq_gemm_smallbatch call. Weights are uploaded
+batch > 1 each such group is one vbq_gemm_smallbatch_multi call (matrices on
+the matrix cores launch alone, the rest share GEMV launches of up to 32
+(matrix, row) products). Weights are uploaded
 as enough distinct copies that one round of passes reads at least
 --rotate-mb of HBM, so caches do not hold them. Timing: hipEvents on one
 stream around passes replayed from a HIP graph (one graph holds one pass per
@@ -109,8 +111,8 @@ def main():
                     for g in groups:
                         V.vbq_gemv_multi([layer[j] for j in g], [xin[j][0] for j in g], [ys[j][0] for j in g], stream)
                 else:
-                    for j in range(len(specs)):
-                        V.vbq_gemm_smallbatch(layer[j], xin[j], ys[j], stream)
+                    for g in groups:
+                        V.vbq_gemm_smallbatch_multi([layer[j] for j in g], xin[g[0]], [ys[j] for j in g], stream)
 
             t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(stream):
@@ -124,7 +126,8 @@ def main():
                 torch.cuda.synchronize()
                 eager_us = t0.elapsed_time(t1) * 1e3 / args.passes
                 # one graph: one pass per copy (the scratch buffers exist already, so nothing allocates)
-                launches = len(groups) if m == 1 else len(specs)
+                # at most one launch per matrix and row
+                launches = len(groups) if m == 1 else len(specs) * m
                 per_graph = max(1, min(copies, args.graph_launches // launches))
                 us = graph_time(torch, stream, one_pass, per_graph, args.passes)
             gbps = packed / (us * 1e-6) / 1e9
@@ -132,8 +135,8 @@ def main():
                     "weights": cfg.weights, "us_per_pass": round(us, 3), "GBps": round(gbps, 2),
                     "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "eager_us_per_pass": round(eager_us, 3),
                     "rotated_copies": copies, "passes_per_graph": per_graph,
-                    "launches_per_pass": len(groups) if m == 1 else len(specs),
-                    "entry": "vbq_gemv_multi" if m == 1 else "vbq_gemm_smallbatch"}
+                    "calls_per_pass": len(groups),
+                    "entry": "vbq_gemv_multi" if m == 1 else "vbq_gemm_smallbatch_multi"}
             if m > 1:
                 line["TFLOPs"] = round(2.0 * m * cfg.weights / (us * 1e-6) / 1e12, 2)
             if not args.no_fp16:

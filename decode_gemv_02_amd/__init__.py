@@ -25,7 +25,7 @@ ABI_VERSION = 2
 GROUP = 64
 MAX_K = 65536
 MAX_BATCH = 64
-MAX_MULTI = 16
+MAX_MULTI = 32
 TILE_ROWS = 64
 TILE_GROUPS = 4
 
@@ -75,6 +75,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
                                    U32, P]
     lib.vbq_gemv_multi_noalloc.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P),
                                            ctypes.POINTER(P), U32, P]
+    lib.vbq_gemm_smallbatch_multi.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), P, U32, ctypes.POINTER(P),
+                                              U32, P]
     lib.vbq_gemv.argtypes = [ctypes.POINTER(VbqMatrix), P, P, P]
     lib.vbq_gemv_multi_f16.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), ctypes.POINTER(P),
                                        ctypes.POINTER(P), U32, P]
@@ -98,7 +100,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
               lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16,
               lib.vbq_soft_quantize, lib.vbq_gemv_multi_noalloc, lib.vbq_recipe_head_tiers,
-              lib.vbq_probe_stream_read, lib.vbq_probe_dense_gemv):
+              lib.vbq_probe_stream_read, lib.vbq_probe_dense_gemv, lib.vbq_gemm_smallbatch_multi):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -245,7 +247,7 @@ def _multi_args(ws, xs, ys, ydtype):
 
 
 def vbq_gemv_multi(ws, xs, ys, stream=None):
-    """Several independent GEMVs (ys[i] = W_i xs[i]) in one launch; up to 16."""
+    """Several independent GEMVs (ys[i] = W_i xs[i]) in one launch; up to MAX_MULTI."""
     wa, xa, ya, count, dev = _multi_args(ws, xs, ys, torch.float32)
     _check(lib.vbq_gemv_multi(wa, xa, ya, count, _stream_handle(stream, dev)))
     return ys
@@ -273,6 +275,18 @@ def vbq_gemm_smallbatch(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, strea
     _check(lib.vbq_gemm_smallbatch(ctypes.byref(w.struct), x.data_ptr(), x.shape[0], y.data_ptr(),
                                    _stream_handle(stream, w.device)))
     return y
+
+
+def vbq_gemm_smallbatch_multi(ws, x: torch.Tensor, ys, stream=None):
+    """ys[i][m][n_i] (fp32) = x[m][k] (fp16) W_i^T for matrices sharing x (q/k/v, gate/up), few launches."""
+    count = len(ws)
+    assert count == len(ys) and x.dtype == torch.float16 and x.dim() == 2 and x.is_contiguous()
+    for w, y in zip(ws, ys):
+        assert w.k == x.shape[1] and y.dtype == torch.float32 and y.is_contiguous() and y.numel() >= x.shape[0] * w.n
+    wa = (ctypes.POINTER(VbqMatrix) * max(count, 1))(*[ctypes.pointer(w.struct) for w in ws])
+    ya = (ctypes.c_void_p * max(count, 1))(*[y.data_ptr() for y in ys])
+    _check(lib.vbq_gemm_smallbatch_multi(wa, x.data_ptr(), x.shape[0], ya, count, _stream_handle(stream, x.device)))
+    return ys
 
 
 def vbq_unpack_codes(w: DeviceMatrix, out: torch.Tensor, stream=None) -> torch.Tensor:

@@ -196,6 +196,9 @@ struct MatArgs {
 // matrix's arguments with one scalar load and no search.
 struct Batch {
     MatArgs m[VBQ_MAX_MULTI];
+    // 1D launches (matrices of different declared widths): matrix i owns workgroups
+    // [first_block[i], first_block[i + 1]); entries past the last matrix hold the total
+    uint32_t first_block[VBQ_MAX_MULTI + 1];
     // Gated-MLP epilogue, when h is set: matrix 0 is gate and matrix 1 is up
     // (same n), and instead of y the launch writes h = fp16(silu(g) * u).
     uint16_t *h;
@@ -866,12 +869,19 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 
 // One-width matrices of different widths in one launch (e.g. a head whose rows
 // are grouped by width): each workgroup takes its matrix's width, uniform over
-// the workgroup, so there is no divergence.
+// the workgroup, so there is no divergence. The grid is 1D, the matrices'
+// workgroups one after the other, so no workgroup is launched only to leave:
+// such workgroups hold a CU slot (and 78 KiB of LDS) for the latency of their
+// argument load, and with a few large matrices among small ones they delayed
+// the large matrix's workgroups by microseconds.
 template <bool kAligned, uint32_t kWaves>
 __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void gemv_uniform_mixed(
     Batch B) {
     __shared__ WaveLds lds[kWaves];
-    const uint32_t which = blockIdx.y, bx = blockIdx.x;
+    uint32_t which = 0;
+#pragma unroll
+    for (uint32_t i = 1; i < VBQ_MAX_MULTI; ++i) which += blockIdx.x >= B.first_block[i] ? 1u : 0u;
+    const uint32_t bx = blockIdx.x - B.first_block[which];
     const MatArgs M = B.m[which];
     switch (M.ubits) {
         case 1: uniform_tiles<1, kAligned, kWaves>(B, M, which, bx, lds); break;
@@ -1000,9 +1010,10 @@ typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
 // when m^2 x tiles reaches 85000 (LM head 32000x4096, 8000 tiles: m = 3 24.9
 // vs 27.6 us as GEMVs, m = 4 27.4 vs 31.3 on the matrix cores; 14336x4096:
 // m = 4 19.2 vs 20.0 as GEMVs, m = 6 20.4 vs 25.7; 4096x4096: m = 8 11.1 vs
-// 12.2 as GEMVs, m = 12 12.7 vs 15.6), and always beyond the 16 rows one GEMV
-// launch takes.
+// 12.2 as GEMVs, m = 12 12.7 vs 15.6), and always beyond 16 rows (the row
+// count those measurements reached; one GEMV launch takes up to 32).
 constexpr uint32_t kGemmMinBatch = 4;
+constexpr uint32_t kGemmAlwaysBatch = 16;   // beyond this many rows of X, always the matrix cores
 constexpr uint64_t kGemmMinWork = 85000;   // rows of X squared times tiles of W
 constexpr uint32_t kAStride = 136;   // fp16 per staged row: two columns of 64 codes + 8 pad (272 B)
 
@@ -1595,13 +1606,12 @@ constexpr uint32_t kPerMatrix = 0xFFu;
 template <uint32_t kWaves>
 void gemv_dispatch(bool aligned, bool ragged, uint32_t ubits, uint32_t blocks, uint32_t used, const Batch &B,
                    hipStream_t stream) {
-    if (ubits == kPerMatrix) {
+    if (ubits == kPerMatrix) {   // 1D grid: every matrix's workgroups, back to back
+        const uint32_t total = B.first_block[VBQ_MAX_MULTI];
         if (aligned)
-            hipLaunchKernelGGL((gemv_uniform_mixed<true, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0,
-                               stream, B);
+            hipLaunchKernelGGL((gemv_uniform_mixed<true, kWaves>), dim3(total), dim3(kWaves * kWave), 0, stream, B);
         else
-            hipLaunchKernelGGL((gemv_uniform_mixed<false, kWaves>), dim3(blocks, used), dim3(kWaves * kWave), 0,
-                               stream, B);
+            hipLaunchKernelGGL((gemv_uniform_mixed<false, kWaves>), dim3(total), dim3(kWaves * kWave), 0, stream, B);
         return;
     }
     switch (ubits) {
@@ -1721,6 +1731,11 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     if (used == 0) return any_launch ? launched(who) : VBQ_OK;
     bool ragged = false;   // some matrix has fewer workgroups than the grid is wide
     for (uint32_t i = 0; i < used; ++i) ragged = ragged || B.m[i].blocks != blocks;
+    uint32_t acc = 0;
+    for (uint32_t i = 0; i <= VBQ_MAX_MULTI; ++i) {
+        B.first_block[i] = acc;
+        if (i < used) acc += B.m[i].blocks;
+    }
     if (plan.waves == 16)
         gemv_dispatch<16>(aligned, ragged, ubits, blocks, used, B, stream);
     else if (plan.waves == 8)
@@ -1768,6 +1783,13 @@ vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, 
         default: hipLaunchKernelGGL(gemm_tiles<4>, grid, block, 0, stream, G); break;
     }
     return launched(who);
+}
+
+// The small-batch rule: matrix cores for m > 16 rows of X, or from 4 rows when m^2 x tiles reaches
+// kGemmMinWork; one GEMV per row otherwise (measured, see kGemmMinWork)
+bool uses_matrix_cores(const vbq_matrix *w, uint32_t m) {
+    const uint64_t tiles = static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
+    return m > kGemmAlwaysBatch || (m >= kGemmMinBatch && static_cast<uint64_t>(m) * m * tiles >= kGemmMinWork);
 }
 
 vbq_status check_vectors(const char *who, const vbq_matrix *w, const void *x, const void *y) {
@@ -1890,8 +1912,7 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
         if (w->n == 0) return VBQ_OK;
         (void)hipGetLastError();
         hipStream_t s = static_cast<hipStream_t>(stream);
-        const uint64_t tiles = static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
-        if (m > VBQ_MAX_MULTI || (m >= kGemmMinBatch && static_cast<uint64_t>(m) * m * tiles >= kGemmMinWork)) {
+        if (uses_matrix_cores(w, m)) {
             if (w->k == 0) {
                 const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
                 hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s, y, cnt);
@@ -1914,6 +1935,69 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
             if (st != VBQ_OK) return st;
         }
         return VBQ_OK;
+    });
+}
+
+// Small-batch products of several matrices that read the same rows of X
+// (q, k, v; gate, up): matrices the rule gives the matrix cores get their own
+// launch; the others become one GEMV per (matrix, row) and share launches of
+// up to VBQ_MAX_MULTI GEMVs, matrix by matrix and row by row.
+extern "C" vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, const uint16_t *x, uint32_t m,
+                                                float *const *ys, uint32_t count, void *stream) {
+    return vbq::guarded("vbq_gemm_smallbatch_multi", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemm_smallbatch_multi";
+        if (m == 0 || m > VBQ_MAX_BATCH) return fail(VBQ_ERR_SHAPE, "%s: m=%u outside [1, %u]", who, m, VBQ_MAX_BATCH);
+        if (count == 0) return VBQ_OK;
+        if (!ws || !ys) return fail(VBQ_ERR_NULL, "%s: ws or ys is NULL", who);
+        for (uint32_t i = 0; i < count; ++i) {
+            vbq_status st = check_matrix(who, ws[i]);
+            if (st != VBQ_OK) return st;
+            if (ws[i]->k != ws[0]->k)
+                return fail(VBQ_ERR_SHAPE, "%s: matrix %u has k=%u, matrix 0 k=%u (they share X)", who, i, ws[i]->k,
+                            ws[0]->k);
+            st = check_vectors(who, ws[i], x, ys[i]);
+            if (st != VBQ_OK) return st;
+        }
+        (void)hipGetLastError();
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const uint32_t k = ws[0]->k;
+        const vbq_matrix *gw[VBQ_MAX_MULTI];
+        const uint16_t *gx[VBQ_MAX_MULTI];
+        float *gy[VBQ_MAX_MULTI];
+        uint32_t pending = 0;
+        auto flush = [&]() -> vbq_status {
+            const vbq_status st = pending ? gemv_launch(who, gw, gx, gy, pending, s) : VBQ_OK;
+            pending = 0;
+            return st;
+        };
+        for (uint32_t i = 0; i < count; ++i) {
+            const vbq_matrix *w = ws[i];
+            if (w->n == 0) continue;
+            if (uses_matrix_cores(w, m)) {
+                vbq_status st;
+                if (k == 0) {
+                    const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
+                    hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s,
+                                       ys[i], cnt);
+                    st = launched(who);
+                } else {
+                    st = gemm_launch(who, w, x, m, ys[i], s);
+                }
+                if (st != VBQ_OK) return st;
+                continue;
+            }
+            for (uint32_t r = 0; r < m; ++r) {
+                gw[pending] = w;
+                gx[pending] = x + static_cast<uint64_t>(r) * k;
+                gy[pending] = ys[i] + static_cast<uint64_t>(r) * w->n;
+                if (++pending == VBQ_MAX_MULTI) {
+                    const vbq_status st = flush();
+                    if (st != VBQ_OK) return st;
+                }
+            }
+        }
+        return flush();
     });
 }
 

@@ -91,7 +91,7 @@ extern "C" {
 #define VBQ_TILE_GROUPS 4u
 #define VBQ_MAX_K 65536u      /* k limit of the device entry points */
 #define VBQ_MAX_BATCH 64u     /* m limit of vbq_gemm_smallbatch */
-#define VBQ_MAX_MULTI 16u     /* matrices per vbq_gemv_multi call */
+#define VBQ_MAX_MULTI 32u     /* matrices per vbq_gemv_multi call */
 
 typedef enum vbq_status {
     VBQ_OK = 0,
@@ -251,6 +251,20 @@ VBQ_API vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *up,
  * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                                void *stream);
+
+/* Small-batch products of several matrices that read the same m rows of X
+ * (VBQ §6, "Fused kernels over packed weights", batched: q, k and v, or gate
+ * and up, at one decode step of m sequences; the pages are silent on
+ * batches): ys[i] = X W_i^T, each exactly as vbq_gemm_smallbatch computes
+ * it. x: device binary16 [m][k] shared by all matrices (every ws[i] has the
+ * same k); ys[i]: device fp32 [m][n_i]. Matrices the small-batch rule gives
+ * the matrix cores get their own launch; the others run as one GEMV per
+ * (matrix, row) and share launches of up to VBQ_MAX_MULTI GEMVs, so a layer's
+ * projections at batch 8 take as many launches as at batch 1. Asynchronous on
+ * `stream`; scratch as for vbq_gemv_multi. Errors: NULL, ABI, SHAPE (m, or the
+ * k's differ), ALIGN, OFFSETS, HIP. */
+VBQ_API vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, const uint16_t *x, uint32_t m,
+                                             float *const *ys, uint32_t count, void *stream);
 
 /* vbq_gemv_multi for callers that cannot allocate device memory: code under
  * graph capture, serving loops and harnesses that forbid hipMalloc. Same

@@ -435,6 +435,31 @@ def test_grouped_recipe_head(V, torch_mod):
     assert np.array_equal(y1.cpu().numpy(), ys[2].cpu().numpy())
 
 
+@pytest.mark.parametrize("m", [1, 8, 12, 20])
+def test_gemm_smallbatch_multi_matches_oracle(V, torch_mod, m):
+    # matrices sharing the m rows of X, as q/k/v do: ragged row counts; at m = 12 the 8192-row matrix
+    # takes the matrix cores (m * m * tiles >= 85000) while the others share GEMV launches, whose
+    # (matrix, row) count passes 32 so they are split; at m = 20 all take the matrix cores
+    torch = torch_mod
+    k = 2048
+    shapes = [97, 8192, 300, 64, 1000]
+    print_case(test="gemm_multi", m=m, k=k, shapes=shapes)
+    x = W.draw_x((90, m), k, m)
+    xt = torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).cuda()
+    packs, dms, hs = [], [], []
+    for i, n in enumerate(shapes):
+        bits, codes, scales, p = make_case((91, m, i), n, k, W.STD_MIX)
+        h, dm = upload(V, bits, codes, scales)
+        hs.append(h)
+        dms.append(dm)
+        packs.append((p, scales))
+    ys = [torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda") for n in shapes]
+    V.vbq_gemm_smallbatch_multi(dms, xt, ys)
+    torch.cuda.synchronize()
+    for i, (y, (p, scales)) in enumerate(zip(ys, packs)):
+        assert_within_tolerance(y.cpu().numpy(), oracle.gemm(p, x), x, scales, f"multi m={m} matrix {i}")
+
+
 def test_split_partials_are_never_read_stale(V, torch_mod):
     # Two different matrices of one shape use the same split-K scratch slots. Alternating them many
     # times, every call must give exactly its matrix's own result: a partial sum left in a cache by

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     assert declared_functions() == sorted([
         "vbq_abi_version", "vbq_pack_sizes", "vbq_pack", "vbq_tile_count", "vbq_validate_host", "vbq_gemv",
-        "vbq_gemv_multi", "vbq_gemv_multi_noalloc", "vbq_gemm_smallbatch", "vbq_unpack_codes", "vbq_quantize",
+        "vbq_gemv_multi", "vbq_gemv_multi_noalloc", "vbq_gemm_smallbatch", "vbq_gemm_smallbatch_multi",
+        "vbq_unpack_codes", "vbq_quantize",
         "vbq_recipe_head_bits", "vbq_recipe_head_order", "vbq_recipe_head_tiers", "vbq_check_padding",
         "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width",
         "vbq_gemv_multi_f16", "vbq_soft_quantize", "vbq_status_string", "vbq_last_error",
@@ -258,15 +259,37 @@ def test_gemv_multi_rejects_bad_arguments_without_launching(V):
     v = h.view()
     buf = np.zeros(4096, np.uint8)
     base = (buf.ctypes.data + 255) // 256 * 256
-    W17 = (ctypes.POINTER(V.VbqMatrix) * 17)(*([ctypes.pointer(v)] * 17))
-    P17 = (ctypes.c_void_p * 17)(*([base] * 17))
-    assert V.lib.vbq_gemv_multi(W17, P17, P17, 17, None) == V.ERR_SHAPE
-    assert V.lib.vbq_gemv_multi(None, P17, P17, 2, None) == V.ERR_NULL
-    assert V.lib.vbq_gemv_multi(W17, P17, P17, 0, None) == V.OK
+    over = V.MAX_MULTI + 1
+    Wo = (ctypes.POINTER(V.VbqMatrix) * over)(*([ctypes.pointer(v)] * over))
+    Po = (ctypes.c_void_p * over)(*([base] * over))
+    assert V.lib.vbq_gemv_multi(Wo, Po, Po, over, None) == V.ERR_SHAPE
+    assert V.lib.vbq_gemv_multi(None, Po, Po, 2, None) == V.ERR_NULL
+    assert V.lib.vbq_gemv_multi(Wo, Po, Po, 0, None) == V.OK
     bad = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base)
     Wb = (ctypes.POINTER(V.VbqMatrix) * 2)(ctypes.pointer(bad), ctypes.pointer(bad))
     Pm = (ctypes.c_void_p * 2)(base, base + 8)
     assert V.lib.vbq_gemv_multi(Wb, Pm, (ctypes.c_void_p * 2)(base, base), 2, None) == V.ERR_ALIGN
+
+
+def test_gemm_smallbatch_multi_rejects_bad_arguments_without_launching(V):
+    h = V.vbq_pack(*(lambda b, c, s: (2, 128, b, c, s))(*W.draw_random_matrix(7, 2, 128)))
+    v = h.view()
+    buf = np.zeros(4096, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    ok = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base)
+    other_k = V.VbqMatrix(V.ABI_VERSION, 2, 192, h.payload_bytes, base, base, base, base)
+    Wk = (ctypes.POINTER(V.VbqMatrix) * 2)(ctypes.pointer(ok), ctypes.pointer(other_k))
+    Y = (ctypes.c_void_p * 2)(base, base)
+    f = V.lib.vbq_gemm_smallbatch_multi
+    assert f(Wk, base, 0, Y, 2, None) == V.ERR_SHAPE                       # m = 0
+    assert f(Wk, base, V.MAX_BATCH + 1, Y, 2, None) == V.ERR_SHAPE         # m too large
+    assert f(Wk, base, 4, Y, 0, None) == V.OK                              # nothing to do
+    assert f(None, base, 4, Y, 2, None) == V.ERR_NULL
+    assert f(Wk, base, 4, None, 2, None) == V.ERR_NULL
+    assert f(Wk, base, 4, Y, 2, None) == V.ERR_SHAPE                       # the k's differ
+    W1 = (ctypes.POINTER(V.VbqMatrix) * 1)(ctypes.pointer(ok))
+    assert f(W1, base + 2, 4, Y, 1, None) == V.ERR_ALIGN
+    del v
 
 
 def test_tile_count(V):
