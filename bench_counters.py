@@ -158,7 +158,7 @@ def kernels_summary(a) -> str:
     with open(a.csv) as f:
         for row in csv.DictReader(f):
             name = row["Kernel_Name"]
-            if not any(k in name for k in ("gemv_tiles", "gemv_uniform", "gemm_tiles", "unpack_tiles",
+            if not any(k in name for k in ("gemv_tiles", "gemv_uniform", "gemm_frag", "unpack_tiles",
                                            "quantize_groups", "chunk_sums", "mean_of_parts")):
                 continue
             key = (name, row["Grid_Size_X"], row["Grid_Size_Y"])

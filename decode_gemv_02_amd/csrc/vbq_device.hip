@@ -45,9 +45,7 @@ namespace {
 constexpr uint32_t kWave = 64;
 constexpr uint32_t kTileRows = VBQ_TILE_ROWS;     // 64
 constexpr uint32_t kTileGroups = VBQ_TILE_GROUPS; // 4
-constexpr uint32_t kWavesPerBlock = 4;
 constexpr uint32_t kXStride = 36;                 // dwords per staged column (32 used, padded)
-constexpr uint32_t kMagic = 0x64006400u;          // two fp16 1024.0
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -159,13 +157,6 @@ __device__ __forceinline__ void unpack2(uint32_t v, uint32_t p[8]) {
     p[5] = h & 0x00030003u;
     p[6] = h & 0x000C000Cu;
     p[7] = h & 0x00300030u;
-}
-
-// 8-bit for the matrix-core decode: pairs (1024 + u) for an exact fp16 integer after one fma
-__device__ __forceinline__ void unpack8_1024(uint32_t v, uint32_t &p0, uint32_t &p1) {
-    v ^= 0x80808080u;
-    p0 = __builtin_amdgcn_perm(0x64646464u, v, 0x04010400u);   // bytes {v0, 64, v1, 64}
-    p1 = __builtin_amdgcn_perm(0x64646464u, v, 0x04030402u);   // bytes {v2, 64, v3, 64}
 }
 
 // 1-bit: bit i is the sign of element i; pair k = (2k, 2k+1) as fp16 +-1
@@ -1002,20 +993,19 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t ushort2_t __attribute__((ext_vector_type(2)));
 
-// When the matrix cores run a small batch (measured on MI355X, graph-replayed):
-// the matrix-core kernel costs about the same for any m up to 16, while m
-// GEMVs in one launch cost more with every row, less so on small matrices
-// whose launches leave the chip idle. The crossover row count falls with the
-// tile count roughly as 1/sqrt(tiles): the matrix cores win from m = 4 rows
-// when m^2 x tiles reaches 85000 (LM head 32000x4096, 8000 tiles: m = 3 24.9
-// vs 27.6 us as GEMVs, m = 4 27.4 vs 31.3 on the matrix cores; 14336x4096:
-// m = 4 19.2 vs 20.0 as GEMVs, m = 6 20.4 vs 25.7; 4096x4096: m = 8 11.1 vs
-// 12.2 as GEMVs, m = 12 12.7 vs 15.6), and always beyond 16 rows (the row
-// count those measurements reached; one GEMV launch takes up to 32).
+// When the matrix cores run a small batch (measured on MI355X, graph-replayed,
+// standard width mix): the matrix-core kernel costs about the same for any m up
+// to 16, with a floor of 7-12 us on small matrices (one tile per wave, a long
+// dependent chain per tile), while m GEMVs in one launch cost more with every
+// row. The crossover row count falls with the tile count roughly as
+// 1/sqrt(tiles): the matrix cores win from m = 4 rows when m^2 x tiles reaches
+// 85000 (32000x4096, 8000 tiles: m = 3 25.0 us as GEMVs vs 26.6, m = 4 25.6 vs
+// 31.6 as GEMVs; 4096x4096: m = 8 10.7 as GEMVs vs 11.5, m = 12 12.0 vs 14.9 as
+// GEMVs; 5632x2048: m = 8 9.1 as GEMVs vs 9.8, m = 12 10.0 vs 13.0 as GEMVs;
+// 2048x2048 and smaller: GEMVs up to 16 rows), and always beyond 16 rows.
 constexpr uint32_t kGemmMinBatch = 4;
 constexpr uint32_t kGemmAlwaysBatch = 16;   // beyond this many rows of X, always the matrix cores
 constexpr uint64_t kGemmMinWork = 85000;   // rows of X squared times tiles of W
-constexpr uint32_t kAStride = 136;   // fp16 per staged row: two columns of 64 codes + 8 pad (272 B)
 
 struct GemmArgs {
     const uint8_t *widths;
@@ -1030,97 +1020,10 @@ struct GemmArgs {
     uint32_t payload_bytes;
 };
 
-struct alignas(16) GemmWaveLds {
-    uint16_t a[kTileRows * kAStride];            // decoded codes of two columns, exact fp16, row-major
-    float scale[kTileGroups][kTileRows];         // group scales as fp32 [column][row]
-    uint8_t list[4][kTileRows * kTileGroups];    // per width: row | column << 6, in bucket order
-};
-
 __device__ __forceinline__ uint32_t half2_fma(uint32_t v, uint32_t mul, uint32_t add) {
     const half2_t r = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, v), __builtin_bit_cast(half2_t, mul),
                                                 __builtin_bit_cast(half2_t, add));
     return __builtin_bit_cast(uint32_t, r);
-}
-
-// fp16 pair constants: (mul, add) turn 1024 + f*u into u - bias exactly
-constexpr uint32_t h2(uint32_t h) { return h | (h << 16); }
-
-// 1-bit group (8 payload bytes) -> 64 codes +-1 at dst
-__device__ __forceinline__ void decode1(uint2 v, uint16_t *dst) {
-    const uint32_t ones = opaque(0x3C003C00u);
-#pragma unroll
-    for (uint32_t t = 0; t < 8; ++t) {
-        const uint32_t w = t < 4 ? v.x : v.y;
-        const uint32_t sel = (t & 3u) | 0x0C000000u | 0x00000C00u | ((t & 3u) << 16);
-        const uint32_t d = __builtin_amdgcn_perm(0u, w, sel);          // {byte t, 0, byte t, 0}
-        uint32_t o[4];
-#pragma unroll
-        for (uint32_t p = 0; p < 4; ++p) {
-            const ushort2_t sh = {static_cast<uint16_t>(15 - 2 * p), static_cast<uint16_t>(14 - 2 * p)};
-            const uint32_t s = __builtin_bit_cast(uint32_t, __builtin_bit_cast(ushort2_t, d) << sh);
-            o[p] = (s & 0x80008000u) | ones;                           // sign bits 2p, 2p+1 -> fp16 +-1
-        }
-        *reinterpret_cast<uint4 *>(dst + 8 * t) = make_uint4(o[0], o[1], o[2], o[3]);
-    }
-}
-
-// 2-bit group (16 payload bytes) -> 64 codes at dst
-__device__ __forceinline__ void decode2(uint4 v, uint16_t *dst) {
-    // offset binary: u = q + 2 in every field
-    const uint32_t w[4] = {xor_opaque(v.x, 0xAAAAAAAAu), xor_opaque(v.y, 0xAAAAAAAAu), xor_opaque(v.z, 0xAAAAAAAAu),
-                           xor_opaque(v.w, 0xAAAAAAAAu)};
-    const uint32_t magic = opaque(kMagic);
-    // pair p = fields p, p+8 -> 1024 + 4^p u (p < 5) or, from word >> 10, 1024 + 4^(p-5) u
-    constexpr uint32_t mul[5] = {h2(0x3C00), h2(0x3400), h2(0x2C00), h2(0x2400), h2(0x1C00)};   // 4^-p
-    constexpr uint32_t add[5] = {h2(0xE402), h2(0xDC08), h2(0xD420), h2(0xCC80), h2(0xC600)};   // -(1024/4^p + 2)
-#pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
-        const uint32_t lo = w[q], hi = w[q] >> 10;
-        uint32_t o[8];
-#pragma unroll
-        for (uint32_t p = 0; p < 8; ++p) {
-            const uint32_t src = p < 5 ? lo : hi, c = p < 5 ? p : p - 5;
-            const uint32_t f = (src & (0x00030003u << (2 * c))) | magic;
-            o[p] = half2_fma(f, mul[c], add[c]);
-        }
-        *reinterpret_cast<uint4 *>(dst + 16 * q) = make_uint4(o[0], o[1], o[2], o[3]);
-        *reinterpret_cast<uint4 *>(dst + 16 * q + 8) = make_uint4(o[4], o[5], o[6], o[7]);
-    }
-}
-
-// 16 payload bytes of a 4-bit group (32 elements) -> 32 codes at dst
-__device__ __forceinline__ void decode4(uint4 v, uint16_t *dst) {
-    // offset binary: u = q + 8 in every field
-    const uint32_t w[4] = {xor_opaque(v.x, 0x88888888u), xor_opaque(v.y, 0x88888888u), xor_opaque(v.z, 0x88888888u),
-                           xor_opaque(v.w, 0x88888888u)};
-    const uint32_t magic = opaque(kMagic);
-    constexpr uint32_t m1 = h2(0x3C00), a1 = h2(0xE408);    // 1, -(1024 + 8)
-    constexpr uint32_t m16 = h2(0x2C00), a16 = h2(0xD480);  // 1/16, -(64 + 8)
-#pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
-        const uint32_t lo = w[q], hi = w[q] >> 8;
-        const uint32_t o0 = half2_fma((lo & 0x000F000Fu) | magic, m1, a1);
-        const uint32_t o1 = half2_fma((lo & 0x00F000F0u) | magic, m16, a16);
-        const uint32_t o2 = half2_fma((hi & 0x000F000Fu) | magic, m1, a1);
-        const uint32_t o3 = half2_fma((hi & 0x00F000F0u) | magic, m16, a16);
-        *reinterpret_cast<uint4 *>(dst + 8 * q) = make_uint4(o0, o1, o2, o3);
-    }
-}
-
-// 16 payload bytes of an 8-bit group (16 elements) -> 16 codes at dst
-__device__ __forceinline__ void decode8(uint4 v, uint16_t *dst) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    constexpr uint32_t one = h2(0x3C00), a8 = h2(0xE480);   // 1, -(1024 + 128)
-    uint32_t o[8];
-#pragma unroll
-    for (uint32_t q = 0; q < 4; ++q) {
-        uint32_t p0, p1;
-        unpack8_1024(w[q], p0, p1);
-        o[2 * q] = half2_fma(p0, one, a8);
-        o[2 * q + 1] = half2_fma(p1, one, a8);
-    }
-    *reinterpret_cast<uint4 *>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-    *reinterpret_cast<uint4 *>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
 // How many groups of each width come before each column (16 bits per width),
@@ -1141,166 +1044,182 @@ __device__ __forceinline__ uint32_t field16(uint64_t v, uint32_t w) {
     return static_cast<uint32_t>((v >> (16 * w)) & 0xFFFFu);
 }
 
-// Per-width lists of one tile (bucket order) from the tile scan, and the
-// scales of the tile as fp32.
-__device__ __forceinline__ void gemm_lists(GemmWaveLds &L, const TileMeta &t, const TileScan &T,
-                                           const uint64_t colstart[kTileGroups + 1], uint32_t rows, uint32_t cn,
-                                           uint32_t lane) {
-    const bool valid = lane < rows;
-#pragma unroll
-    for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
-        if (jl >= cn) break;
-        const uint32_t c = (t.codes >> (2 * jl)) & 3u;
-        const uint32_t excl = T.incl[jl] - (1u << (8 * c));
-        const uint32_t slot = field16(colstart[jl], c) + ((excl >> (8 * c)) & 0xFFu);
-        if (valid) {
-            L.list[c][slot] = static_cast<uint8_t>(lane | (jl << 6));
-            const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
-            L.scale[jl][lane] = half_to_float(sb);
-        }
-    }
-}
+// ---------------------------------------------------------------- small-batch GEMM, A fragments decoded in registers
+//
+// One wave owns one 64x256 tile at a time and multiplies it with the m rows
+// of X on v_mfma_f32_16x16x32_f16, one group (64 codes) per two instructions,
+// then scales the group's products by its fp32 scale. The A operand of a
+// 16-row block is decoded by the lanes straight from the payload into the
+// fragment registers, with no round trip through LDS: lane (i, q) holds codes
+// 8q..8q+7 (first instruction) and 32+8q..32+8q+7 (second) of row 16rb+i's
+// group, which are whole bytes of that group at places fixed by its width
+// (1 bit: byte 4h+q; 2 bits: the word 2h+q/2; 4 bits: the word 4h+q; 8 bits:
+// bytes 32h+8q..32h+8q+7, h the instruction). The rows of one block may have
+// different widths. A block whose 16 rows are all 1-bit in the column (most
+// blocks of a head dominated by 1-bit rows) runs the 1-bit decoder; any other
+// runs one width-generic decoder whose per-lane constants come from a table: for pair p (codes 2p, 2p+1), t = perm(hi, lo, sel0 + p dsel) brings
+// the pair's bytes into the 16-bit halves, a packed shift by sh0 + p dsh moves
+// each field to its place, (t & A) ^ B keeps the field, flips its top bit
+// (two's complement to offset binary) and sets the fp16 exponent of 1024, and
+// an fp16 fma (mul, add) maps 1024 + 2^s u to the code, exactly.
 
-// 16 payload bytes at an 8-byte aligned offset (buckets start at multiples of 8)
-__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
-    const uint2 lo = buf_load8(r, off), hi = buf_load8(r, off + 8u);
-    return make_uint4(lo.x, lo.y, hi.x, hi.y);
-}
-
-
-// Payload of one pass (two columns of a tile): the first 128 one-bit groups
-// and the first 64 tasks of each wider width, loaded before any is decoded.
-struct PassStage {
-    uint2 p1[2];
-    uint4 p2, p4, p8;
+struct FragParams {
+    uint32_t sel0, dsel, sh0, dsh, A, B, mul, add;
 };
 
-// List range [e0, e1) of width wi for the columns of `pass`, and the byte
-// offset of that width's bucket in the tile.
-__device__ __forceinline__ void pass_range(const uint64_t colstart[kTileGroups + 1], uint32_t pass, uint32_t cn,
-                                           uint32_t wi, uint32_t &e0, uint32_t &e1, uint32_t &base) {
-    const uint32_t c_end = min(2 * pass + 2, cn);
-    e0 = field16(colstart[2 * pass], wi);
-    e1 = field16(colstart[c_end], wi);
-    const uint64_t total = colstart[kTileGroups];
-    base = 0;
-    for (uint32_t w = 0; w < wi; ++w) base += (8u << w) * field16(total, w);
-}
-
-__device__ __forceinline__ PassStage gemm_stage_pass(rsrc_t tile, const uint64_t colstart[kTileGroups + 1],
-                                                     uint32_t pass, uint32_t cn) {
-    const uint32_t lane = lane_id();
-    // unconditional loads through the tile's descriptor (a lane without a task
-    // reads later bytes, or zeros past the payload, and ignores them), so the
-    // compiler counts them
-    PassStage S;
-    uint32_t e0, e1, base;
-    pass_range(colstart, pass, cn, 0, e0, e1, base);
-    S.p1[0] = buf_load8(tile, base + 8u * (e0 + lane));
-    S.p1[1] = buf_load8(tile, base + 8u * (e0 + lane + kWave));
-    pass_range(colstart, pass, cn, 1, e0, e1, base);
-    S.p2 = buf_load16(tile, base + 16u * (e0 + lane));
-    pass_range(colstart, pass, cn, 2, e0, e1, base);
-    S.p4 = buf_load16(tile, base + 32u * e0 + 16u * lane);
-    pass_range(colstart, pass, cn, 3, e0, e1, base);
-    S.p8 = buf_load16(tile, base + 64u * e0 + 16u * lane);
-    return S;
-}
-
-// Decode columns 2*pass and 2*pass+1 of the tile into L.a; tasks past the
-// staged ones load their bytes here.
-__device__ __forceinline__ void gemm_decode_pass(GemmWaveLds &L, const PassStage &S, rsrc_t tile,
-                                                 const uint64_t colstart[kTileGroups + 1], uint32_t pass, uint32_t cn) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (uint32_t wi = 0; wi < 4; ++wi) {
-        const uint32_t b = 1u << wi;
-        uint32_t e0, e1, base;
-        pass_range(colstart, pass, cn, wi, e0, e1, base);
-        const uint32_t tpg = wi < 2 ? 1u : (b >> 1);           // tasks per group: 1, 1, 2, 4
-        const uint32_t tasks = (e1 - e0) * tpg;
-        uint32_t round = 0;
-        for (uint32_t t = lane; t < tasks; t += kWave, ++round) {
-            const uint32_t e = e0 + t / tpg, sl = t % tpg;
-            const uint32_t info = L.list[wi][e];
-            const uint32_t r = info & 63u, jj = (info >> 6) - 2 * pass;
-            uint16_t *dst = L.a + r * kAStride + 64u * jj;
-            const uint32_t src = base + 8u * b * e;   // the group's byte offset in the tile
-            if (wi == 0) {
-                decode1(round == 0 ? S.p1[0] : round == 1 ? S.p1[1] : buf_load8(tile, src), dst);
-            } else if (wi == 1) {
-                decode2(round == 0 ? S.p2 : buf_load16(tile, src), dst);
-            } else if (wi == 2) {
-                decode4(round == 0 ? S.p4 : buf_load16(tile, src + 16u * sl), dst + 32u * sl);
-            } else {
-                decode8(round == 0 ? S.p8 : buf_load16(tile, src + 16u * sl), dst + 16u * sl);
-            }
-        }
+// constants of width code c (1, 2, 4, 8 bits) for lanes of quarter q
+__device__ __forceinline__ FragParams frag_params(uint32_t c, uint32_t q) {
+    switch (c) {
+        case 0:   // byte q into the high byte of both halves; bit 8+2p (8+2p+1) down to bit 1; 1 - 2f = 1025 - v
+            return FragParams{0x000C000Cu | (q << 8) | (q << 24), 0u, 7u | (8u << 16), 0x00020002u, 0x00020002u,
+                              0x64006400u, 0xBC00BC00u, 0x64016401u};
+        case 1:   // fields 4(q&1)+p and 12+4(q&1)+p of the word: bits 8(q&1)+2p of each half; q = v - 1026
+            return FragParams{0x03020100u, 0u, (8u * (q & 1u)) * 0x00010001u, 0x00020002u, 0x00030003u,
+                              0x64026402u, 0x3C003C00u, 0xE402E402u};
+        case 2:   // nibbles p and 4+p of the word: bits 4p of each half; q = v - 1032
+            return FragParams{0x03020100u, 0u, 0u, 0x00040004u, 0x000F000Fu, 0x64086408u, 0x3C003C00u, 0xE408E408u};
+        default:  // bytes 2p, 2p+1 of the eight into the low byte of each half; q = v - 1152
+            return FragParams{0x0C010C00u, 0x00020002u, 0u, 0u, 0x00FF00FFu, 0x64806480u, 0x3C003C00u, 0xE480E480u};
     }
 }
 
-// Activations of one pass: lane holds X[16mb + lane%16][k .. k+7] for each
-// column jj and half h of the pass. Rows past m and columns past the tile
-// load a valid neighbour instead: the products they feed are never stored
-// (a matrix-core output column depends on its own input column only) or
-// never computed, and branch-free loads are waited for exactly.
-template <uint32_t MB>
-__device__ __forceinline__ void load_bx(const GemmArgs &G, uint32_t j0, uint32_t pass, uint32_t cn,
-                                        half8_t bx[2][2][MB]) {
-    const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
-#pragma unroll
-    for (uint32_t jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (uint32_t h = 0; h < 2; ++h)
-#pragma unroll
-            for (uint32_t mb = 0; mb < MB; ++mb) {
-                const uint32_t m = min(16 * mb + mr, G.m - 1), jl = min(2 * pass + jj, cn - 1);
-                const uint4 v = *reinterpret_cast<const uint4 *>(G.x + static_cast<uint64_t>(m) * G.k +
-                                                                 64u * (j0 + jl) + 32u * h + 8u * q);
-                bx[jj][h][mb] = __builtin_bit_cast(half8_t, v);
-            }
+// (t & a) ^ b in one instruction (v_bitop3_b32, truth table 0x6a)
+__device__ __forceinline__ uint32_t and_xor(uint32_t t, uint32_t a, uint32_t b) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x6a" : "=v"(r) : "v"(t), "v"(a), "v"(b));
+    return r;
 }
 
-// Codes of the pass (L.a) times activations, scaled per group, into acc.
+__device__ __forceinline__ uint32_t shr16x2(uint32_t v, uint32_t s) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(ushort2_t, v) >> __builtin_bit_cast(ushort2_t, s));
+}
+
+__device__ __forceinline__ half8_t frag_of(uint32_t o0, uint32_t o1, uint32_t o2, uint32_t o3) {
+    return __builtin_bit_cast(half8_t, make_uint4(o0, o1, o2, o3));
+}
+
+// both fragment halves, pair by pair (one selector and one shift live at a time)
+__device__ __forceinline__ void frag_generic(uint2 w0, uint2 w1, const FragParams &P, half8_t &a0, half8_t &a1) {
+    uint32_t o0[4], o1[4];
+    uint32_t sel = P.sel0, sh = P.sh0;
+#pragma unroll
+    for (uint32_t p = 0; p < 4; ++p) {
+        if (p > 0) {
+            sel += P.dsel;
+            sh += P.dsh;
+        }
+        o0[p] = half2_fma(and_xor(shr16x2(__builtin_amdgcn_perm(w0.y, w0.x, sel), sh), P.A, P.B), P.mul, P.add);
+        o1[p] = half2_fma(and_xor(shr16x2(__builtin_amdgcn_perm(w1.y, w1.x, sel), sh), P.A, P.B), P.mul, P.add);
+    }
+    a0 = frag_of(o0[0], o0[1], o0[2], o0[3]);
+    a1 = frag_of(o1[0], o1[1], o1[2], o1[3]);
+}
+
+// The lane's payload bytes of one column of the tile: for each 16-row block, eight bytes per fragment half
+struct FragCol {
+    uint2 w[4][2];
+};
+
+struct alignas(16) FragTables {
+    uint32_t where[kTileGroups][kTileRows];   // group byte offset in the tile | width code (0 past the rows)
+    float scale[kTileGroups][kTileRows];      // group scale as fp32 (0 past the rows)
+};
+constexpr uint32_t kRedStride = kTileRows + 4;   // floats per parked activation row (spreads the banks)
+
+template <uint32_t MB, uint32_t kWaves>
+union alignas(16) FragLds {
+    struct {
+        FragParams params[16];   // [width code][quarter]
+        uint2 nib1[16];          // 1-bit nibble n -> its four codes +-1 as two fp16 pairs
+        FragTables tab[kWaves];
+    } run;
+    float red[kWaves][16 * MB * kRedStride];   // each wave's sums, [activation row][tile row]
+};
+
+// Lane r = row r: the byte offset and width of each of its groups, and its scales as fp32. Returns
+// (uniform) bit 4 jl + rb set when every row of 16-row block rb is 1-bit in column jl.
+__device__ __forceinline__ uint32_t frag_tables(FragTables &T, const TileMeta &t, const TileScan &S,
+                                                const uint64_t colstart[kTileGroups + 1], const uint32_t cnt[4],
+                                                uint32_t rows, uint32_t cn, uint32_t lane) {
+    const bool valid = lane < rows;
+    const uint32_t b1 = 8u * cnt[0], b2 = b1 + 16u * cnt[1], b3 = b2 + 32u * cnt[2];   // bucket starts
+    uint32_t ones = 0;
+#pragma unroll
+    for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
+        const uint32_t c = (t.codes >> (2 * jl)) & 3u;
+        const uint32_t excl = S.incl[jl] - (1u << (8 * c));
+        const uint32_t slot = field16(colstart[jl], c) + ((excl >> (8 * c)) & 0xFFu);
+        const uint32_t base = c == 0 ? 0u : c == 1 ? b1 : c == 2 ? b2 : b3;
+        const bool ok = valid && jl < cn;
+        T.where[jl][lane] = ok ? ((base + (8u << c) * slot) | c) : 0u;
+        const uint32_t sb = (jl < 2 ? (t.s01 >> (16 * jl)) : (t.s23 >> (16 * (jl - 2)))) & 0xFFFFu;
+        T.scale[jl][lane] = ok ? half_to_float(sb) : 0.f;
+        const uint64_t wide = __builtin_amdgcn_ballot_w64(ok && c != 0);   // rows with a wider group
+#pragma unroll
+        for (uint32_t rb = 0; rb < 4; ++rb)
+            ones |= (((wide >> (16 * rb)) & 0xFFFFu) == 0 ? 1u : 0u) << (4 * jl + rb);
+    }
+    return ones;
+}
+
+// Activations of the tile's column jl: lane holds X[16mb + lane%16][64(j0 + jl) + 32h + 8q .. +7], from
+// xp[mb] = the lane's row at 64 j0 + 8q. Rows past m read row m-1: a matrix-core output column depends
+// only on its own input column, and those outputs are not stored.
 template <uint32_t MB>
-__device__ __forceinline__ void mfma_pass(const GemmWaveLds &L, const half8_t bx[2][2][MB], uint32_t pass,
-                                          uint32_t cn, float4_t acc[4][MB]) {
+__device__ __forceinline__ void frag_x_rows(const GemmArgs &G, uint32_t j0, const uint16_t *xp[MB]) {
     const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
 #pragma unroll
-    for (uint32_t jj = 0; jj < 2; ++jj) {
-        const uint32_t jl = 2 * pass + jj;
-        if (jl >= cn) break;
+    for (uint32_t mb = 0; mb < MB; ++mb)
+        xp[mb] = G.x + static_cast<uint64_t>(min(16 * mb + mr, G.m - 1)) * G.k + 64u * j0 + 8u * q;
+}
+
+template <uint32_t MB>
+__device__ __forceinline__ void frag_load_x(const uint16_t *const xp[MB], uint32_t jl, half8_t bx[2][MB]) {
 #pragma unroll
-        for (uint32_t rb = 0; rb < 4; ++rb) {
-            const uint16_t *arow = L.a + (16 * rb + mr) * kAStride + 64u * jj + 8u * q;
-            const half8_t a0 = *reinterpret_cast<const half8_t *>(arow);
-            const half8_t a1 = *reinterpret_cast<const half8_t *>(arow + 32);
-            float4_t d[MB];
+    for (uint32_t h = 0; h < 2; ++h)
 #pragma unroll
-            for (uint32_t mb = 0; mb < MB; ++mb)
-                d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[jj][0][mb], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                               0);
+        for (uint32_t mb = 0; mb < MB; ++mb)
+            bx[h][mb] = __builtin_bit_cast(half8_t, *reinterpret_cast<const uint4 *>(xp[mb] + 64u * jl + 32u * h));
+}
+
+// A 1-bit block's lanes read their group's eight bytes once (both halves); other blocks read eight bytes
+// per half at the width's places.
+__device__ __forceinline__ FragCol frag_col_load(const FragTables &T, rsrc_t tile, uint32_t jl, uint32_t ones,
+                                                 uint32_t q, uint32_t i) {
+    FragCol B;
 #pragma unroll
-            for (uint32_t mb = 0; mb < MB; ++mb)
-                d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[jj][1][mb], d[mb], 0, 0, 0);
-            // rows 16rb + 4q .. +3 of this column
-            const float4_t sc = *reinterpret_cast<const float4_t *>(&L.scale[jl][16 * rb + 4 * q]);
-#pragma unroll
-            for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] += sc * d[mb];
+    for (uint32_t rb = 0; rb < 4; ++rb) {
+        const uint32_t where = T.where[jl][16 * rb + i];
+        if ((ones >> (4 * jl + rb)) & 1u) {
+            B.w[rb][0] = buf_load8(tile, where);   // width code 0: where is the offset
+        } else {
+            const uint32_t qoff = ((4u * (q >> 1)) << 8) | ((4u * q) << 16) | ((8u * q) << 24);   // byte c: width c
+            const uint32_t c = where & 3u;
+            const uint32_t o0 = (where & ~7u) + ((qoff >> (8 * c)) & 0xFFu);
+            B.w[rb][0] = buf_load8(tile, o0);
+            B.w[rb][1] = buf_load8(tile, o0 + (4u << c));
         }
     }
+    return B;
 }
 
-template <uint32_t MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB <= 2 ? 2 : 1, 8))) void gemm_tiles(GemmArgs G) {
-    __shared__ GemmWaveLds lds[kWavesPerBlock];
+template <uint32_t MB, uint32_t kWaves, bool kAligned>
+__global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmArgs G) {
+    __shared__ FragLds<MB, kWaves> S;
     __shared__ uint32_t arrived_s;
     const uint32_t a = blockIdx.x / G.splits, split = blockIdx.x % G.splits;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
     const uint32_t r0 = a * kTileRows;
     const uint32_t rows = min(kTileRows, G.n - r0);
     const uint32_t c_lo = (split * G.col_tiles) / G.splits, c_hi = ((split + 1) * G.col_tiles) / G.splits;
-    GemmWaveLds &L = lds[wave];
+    if (threadIdx.x < 16) {
+        S.run.params[threadIdx.x] = frag_params(threadIdx.x >> 2, threadIdx.x & 3u);
+        const uint32_t n = threadIdx.x;   // bit t set: code 4..+t is -1
+        auto pm = [](uint32_t bit) { return bit ? 0xBC00u : 0x3C00u; };
+        S.run.nib1[n] = make_uint2(pm(n & 1u) | (pm(n & 2u) << 16), pm(n & 4u) | (pm(n & 8u) << 16));
+    }
+    __syncthreads();
+    FragTables &T = S.run.tab[wave];
 
     float4_t acc[4][MB];
 #pragma unroll
@@ -1308,71 +1227,114 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB <= 2 ? 2
 #pragma unroll
         for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
 
+    // (a wave usually owns one or two tiles, and the other waves of the CU cover its metadata wait: no
+    // prefetch of the next tile's metadata, whose registers would be held across the whole tile)
     uint32_t ct = c_lo + wave;
-    TileMeta cur = load_meta<false>(G, a, ct < c_hi ? ct : c_lo, lane_id(), false);
-    for (; ct < c_hi; ct += kWavesPerBlock) {
-        const uint32_t j0 = ct * kTileGroups, cn = min(kTileGroups, G.groups - j0);
-        // counts first: every payload byte of the tile is requested before the lists are built
+    TileMeta meta = load_meta<kAligned>(G, a, ct < c_hi ? ct : c_lo, lane_id(), false);
+    for (; ct < c_hi; ct += kWaves) {
+        const uint32_t j0 = ct * kTileGroups, cn = kAligned ? kTileGroups : min(kTileGroups, G.groups - j0);
         uint32_t cnt[4];
-        const TileScan T = tile_scan(cur, rows, cn, lane_id(), cnt);
+        const TileScan sc = tile_scan(meta, rows, cn, lane_id(), cnt);
         uint64_t colstart[kTileGroups + 1];
-        column_starts(T, colstart);
-        const rsrc_t tile = tile_rsrc(G.payload, G.payload_bytes, cur.off);
-        const PassStage s0 = gemm_stage_pass(tile, colstart, 0, cn);
-        const PassStage s1 = gemm_stage_pass(tile, colstart, cn > 2 ? 1 : 0, cn);
-        half8_t bx[2][2][MB], bx1[2][2][MB];
-        load_bx<MB>(G, j0, 0, cn, bx);
-        if (MB <= 2) load_bx<MB>(G, j0, cn > 2 ? 1 : 0, cn, bx1);   // both passes' activations up front
+        column_starts(sc, colstart);
+        const uint32_t ones = frag_tables(T, meta, sc, colstart, cnt, rows, cn, lane_id());
+        const rsrc_t tile = tile_rsrc(G.payload, G.payload_bytes, meta.off);
+        const uint16_t *xp[MB];
+        frag_x_rows<MB>(G, j0, xp);
+        const uint32_t lane = lane_id(), q = lane >> 4, i = lane & 15u;
+        wave_lds_sync();
+        // two-stage pipeline over the columns: the next column's payload bytes are requested before this
+        // column is decoded, so a wave waits for memory about once per tile
+        FragCol cur = frag_col_load(T, tile, 0, ones, q, i);
+        half8_t bx[2][MB];
+        frag_load_x<MB>(xp, 0, bx);
         // the next tile's metadata travels while this tile computes
-        const TileMeta nxt = load_meta<false>(G, a, ct + kWavesPerBlock < c_hi ? ct + kWavesPerBlock : ct,
-                                              lane_id(), false);
-        gemm_lists(L, cur, T, colstart, rows, cn, lane_id());
-        wave_lds_sync();
-        gemm_decode_pass(L, s0, tile, colstart, 0, cn);
-        wave_lds_sync();
-        mfma_pass<MB>(L, bx, 0, cn, acc);
-        if (cn > 2) {
-            wave_lds_sync();
-            gemm_decode_pass(L, s1, tile, colstart, 1, cn);
-            // (issued after the decode: its own loads of later rounds would otherwise wait for these)
-            if (MB > 2) load_bx<MB>(G, j0, 1, cn, bx1);
-            wave_lds_sync();
-            mfma_pass<MB>(L, bx1, 1, cn, acc);
+        meta = load_meta<kAligned>(G, a, ct + kWaves < c_hi ? ct + kWaves : ct, lane_id(), false);
+        // (a rolled loop: unrolled, the compiler hoists every column's loads and runs out of registers)
+#pragma unroll 1
+        for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
+            if (jl >= cn) break;
+            // (the next column's activations too when they are few: beyond 16 rows they would cost occupancy)
+            FragCol nxt;
+            half8_t bxn[2][MB];
+            if (jl + 1 < cn) {
+                nxt = frag_col_load(T, tile, jl + 1, ones, q, i);
+                if constexpr (MB == 1) frag_load_x<MB>(xp, jl + 1, bxn);
+            }
+            if constexpr (MB > 1) {
+                if (jl > 0) frag_load_x<MB>(xp, jl, bx);
+            }
+#pragma unroll
+            for (uint32_t rb = 0; rb < 4; ++rb) {
+                half8_t a0, a1;
+                if ((ones >> (4 * jl + rb)) & 1u) {   // every row of the block 1-bit: codes by nibble table
+                    const uint2 *nib = S.run.nib1;
+                    const uint32_t w0 = cur.w[rb][0].x, w1 = cur.w[rb][0].y;
+                    const uint2 p00 = nib[__builtin_amdgcn_ubfe(w0, 8 * q, 4)], p01 = nib[__builtin_amdgcn_ubfe(w0, 8 * q + 4, 4)];
+                    const uint2 p10 = nib[__builtin_amdgcn_ubfe(w1, 8 * q, 4)], p11 = nib[__builtin_amdgcn_ubfe(w1, 8 * q + 4, 4)];
+                    a0 = frag_of(p00.x, p00.y, p01.x, p01.y);
+                    a1 = frag_of(p10.x, p10.y, p11.x, p11.y);
+                } else {
+                    const uint32_t c = T.where[jl][16 * rb + i] & 3u;
+                    frag_generic(cur.w[rb][0], cur.w[rb][1], S.run.params[4 * c + q], a0, a1);
+                }
+                float4_t d[MB];
+#pragma unroll
+                for (uint32_t mb = 0; mb < MB; ++mb)
+                    d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[0][mb], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                   0);
+#pragma unroll
+                for (uint32_t mb = 0; mb < MB; ++mb)
+                    d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[1][mb], d[mb], 0, 0, 0);
+                // rows 16rb + 4q .. +3 of this column
+                const float4_t s = *static_cast<const float4_t *>(
+                    __builtin_assume_aligned(&T.scale[jl][16 * rb + 4 * q], 16));
+#pragma unroll
+                for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] += s * d[mb];
+            }
+            cur = nxt;
+            if constexpr (MB == 1) {
+#pragma unroll
+                for (uint32_t h = 0; h < 2; ++h) bx[h][0] = bxn[h][0];
+            }
         }
         wave_lds_sync();
-        cur = nxt;
     }
 
-    // Workgroup sum in wave order: each wave parks its accumulators as fp32 [m][row]
+    // Workgroup sum in wave order: each wave parks its sums as fp32 [activation row][tile row]
+    __syncthreads();
     {
-        float *red = reinterpret_cast<float *>(L.a);
+        float *red = S.red[wave];
         const uint32_t lane = lane_id(), q = lane >> 4, mr = lane & 15u;
 #pragma unroll
         for (uint32_t rb = 0; rb < 4; ++rb)
 #pragma unroll
             for (uint32_t mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (uint32_t v = 0; v < 4; ++v) red[(16 * mb + mr) * kTileRows + 16 * rb + 4 * q + v] = acc[rb][mb][v];
+                *reinterpret_cast<float4_t *>(&red[(16 * mb + mr) * kRedStride + 16 * rb + 4 * q]) = acc[rb][mb];
     }
     __syncthreads();
-    // output i = m * 64 + row; thread t owns outputs t, t + 256, ... (at most 16)
     const uint32_t outs = G.m * kTileRows;
-    const float *r0p = reinterpret_cast<const float *>(lds[0].a), *r1p = reinterpret_cast<const float *>(lds[1].a);
-    const float *r2p = reinterpret_cast<const float *>(lds[2].a), *r3p = reinterpret_cast<const float *>(lds[3].a);
-    constexpr uint32_t kPerThread = (VBQ_MAX_BATCH * kTileRows) / (kWavesPerBlock * kWave);   // 16
+    constexpr uint32_t kThreads = kWaves * kWave;
+    auto wg_sum = [&](uint32_t i) {
+        const uint32_t at = (i / kTileRows) * kRedStride + i % kTileRows;
+        float t = S.red[0][at];
+#pragma unroll
+        for (uint32_t w = 1; w < kWaves; ++w) t += S.red[w][at];
+        return t;
+    };
     if (G.splits == 1) {
-        for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
+        for (uint32_t i = threadIdx.x; i < outs; i += kThreads) {
             const uint32_t m = i / kTileRows, row = i % kTileRows;
-            if (row < rows) G.y[static_cast<uint64_t>(m) * G.n + r0 + row] = ((r0p[i] + r1p[i]) + r2p[i]) + r3p[i];
+            if (row < rows) G.y[static_cast<uint64_t>(m) * G.n + r0 + row] = wg_sum(i);
         }
         return;
     }
     // split row tile: publish partial sums, count arrivals, the last workgroup adds them in split order
-    for (uint32_t i = threadIdx.x; i < outs; i += blockDim.x) {
+    for (uint32_t i = threadIdx.x; i < outs; i += kThreads) {
         const uint32_t m = i / kTileRows, row = i % kTileRows;
         if (row < rows)
-            __hip_atomic_store(&G.partial[(static_cast<uint64_t>(split) * G.m + m) * G.n + r0 + row],
-                               ((r0p[i] + r1p[i]) + r2p[i]) + r3p[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&G.partial[(static_cast<uint64_t>(split) * G.m + m) * G.n + r0 + row], wg_sum(i),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -1382,12 +1344,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB <= 2 ? 2
     if (arrived_s != G.splits - 1) return;
     // every output's partials are requested before any is added (clamped
     // addresses for outputs past m x rows, which are not stored)
+    constexpr uint32_t kPerThread = (VBQ_MAX_BATCH * kTileRows) / kThreads;
     const uint64_t stride = static_cast<uint64_t>(G.m) * G.n;
     for (uint32_t s0 = 0; s0 < G.splits; s0 += 2) {
         float v[kPerThread][2];
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
-            const uint32_t i = min(threadIdx.x + j * blockDim.x, outs - 1);
+            const uint32_t i = min(threadIdx.x + j * kThreads, outs - 1);
             const uint32_t m = i / kTileRows, row = min(i % kTileRows, rows - 1);
             const float *p = G.partial + static_cast<uint64_t>(m) * G.n + r0 + row;
 #pragma unroll
@@ -1397,7 +1360,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB <= 2 ? 2
         }
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
-            const uint32_t i = threadIdx.x + j * blockDim.x;
+            const uint32_t i = threadIdx.x + j * kThreads;
             if (i >= outs) break;
             const uint32_t m = i / kTileRows, row = i % kTileRows;
             float *y = G.y + static_cast<uint64_t>(m) * G.n + r0 + row;
@@ -1745,6 +1708,24 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     return launched(who);
 }
 
+template <bool kAligned>
+void gemm_frag_dispatch(uint32_t mb, uint32_t waves, dim3 grid, const GemmArgs &G, hipStream_t stream) {
+    if (mb == 1 && waves == 16)
+        hipLaunchKernelGGL((gemm_frag<1, 16, kAligned>), grid, dim3(16 * kWave), 0, stream, G);
+    else if (mb == 1 && waves == 8)
+        hipLaunchKernelGGL((gemm_frag<1, 8, kAligned>), grid, dim3(8 * kWave), 0, stream, G);
+    else if (mb == 1)
+        hipLaunchKernelGGL((gemm_frag<1, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+    else if (mb == 2 && waves == 8)
+        hipLaunchKernelGGL((gemm_frag<2, 8, kAligned>), grid, dim3(8 * kWave), 0, stream, G);
+    else if (mb == 2)
+        hipLaunchKernelGGL((gemm_frag<2, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+    else if (mb == 3)
+        hipLaunchKernelGGL((gemm_frag<3, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+    else
+        hipLaunchKernelGGL((gemm_frag<4, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+}
+
 // Small-batch GEMM on the matrix cores: one launch for up to 64 rows of X.
 vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                        hipStream_t stream) {
@@ -1762,10 +1743,15 @@ vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, 
     G.m = m;
     G.k = w->k;
     const uint32_t row_tiles = ceil_div(G.n, kTileRows);
+    // a wave per column tile of the row tile: 16 waves for up to 16 activation rows, 8 for 32, 4 beyond
+    // (the workgroup's sum buffer is 68 KiB in each case); no more waves than column tiles need
+    const uint32_t mb = ceil_div(m, 16);
+    uint32_t waves = mb == 1 ? 8u : mb == 2 ? 8u : 4u;
+    while (waves > 4 && waves / 2 >= G.col_tiles) waves /= 2;
     // two workgroups per CU are resident (LDS): split the column tiles only
     // while the row tiles alone leave CUs idle
     const uint32_t want_blocks = 512;
-    G.splits = std::max(1u, std::min(ceil_div(G.col_tiles, kWavesPerBlock), want_blocks / row_tiles));
+    G.splits = std::max(1u, std::min(ceil_div(G.col_tiles, waves), want_blocks / row_tiles));
     if (G.splits > 1) {
         uint32_t *ctr = nullptr;
         char *part = nullptr;
@@ -1775,13 +1761,11 @@ vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, 
         G.counters = ctr;
         G.partial = reinterpret_cast<float *>(part);
     }
-    const dim3 grid(row_tiles * G.splits), block(kWavesPerBlock * kWave);
-    switch (ceil_div(m, 16)) {
-        case 1: hipLaunchKernelGGL(gemm_tiles<1>, grid, block, 0, stream, G); break;
-        case 2: hipLaunchKernelGGL(gemm_tiles<2>, grid, block, 0, stream, G); break;
-        case 3: hipLaunchKernelGGL(gemm_tiles<3>, grid, block, 0, stream, G); break;
-        default: hipLaunchKernelGGL(gemm_tiles<4>, grid, block, 0, stream, G); break;
-    }
+    const dim3 grid(row_tiles * G.splits);
+    if (G.groups % kTileGroups == 0)
+        gemm_frag_dispatch<true>(mb, waves, grid, G, stream);
+    else
+        gemm_frag_dispatch<false>(mb, waves, grid, G, stream);
     return launched(who);
 }
 

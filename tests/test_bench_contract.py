@@ -64,7 +64,7 @@ def test_kernel_summary_groups_dispatches_by_kernel(tmp_path):
     rows = [["KERNEL_DISPATCH", "gemv_tiles<true>(Batch)", "1000", "3000", "28160", "0", "48", "112", "256", "1"],
             ["KERNEL_DISPATCH", "gemv_tiles<true>(Batch)", "5000", "9000", "28160", "0", "48", "112", "256", "1"],
             ["KERNEL_DISPATCH", "copyBuffer", "0", "100", "0", "0", "8", "32", "1", "1"],
-            ["KERNEL_DISPATCH", "gemm_tiles<1u>(GemmArgs)", "0", "10000", "78336", "0", "88", "112", "128", "1"]]
+            ["KERNEL_DISPATCH", "gemm_frag<1u, 8u, true>(GemmArgs)", "0", "10000", "35328", "0", "56", "80", "256", "1"]]
     p = tmp_path / "kt.csv"
     p.write_text("\n".join(",".join(f'"{v}"' for v in r) for r in [cols] + rows) + "\n")
 

@@ -1,4 +1,4 @@
-"""The GEMV, unpack and quantizer kernels keep every live value in registers.
+"""The GEMV, GEMM, unpack and quantizer kernels keep every live value in registers.
 
 A register spill puts a per-lane private segment in HBM: every wave then
 writes and re-reads it, which shows up as extra memory traffic of a few KiB
@@ -23,7 +23,7 @@ def _assembly(tmp_path_factory, name):
     return out.read_text()
 
 
-@pytest.mark.parametrize("source, kernel_names", [("vbq_device.hip", ("gemv_tiles", "gemv_uniform", "unpack_tiles")),
+@pytest.mark.parametrize("source, kernel_names", [("vbq_device.hip", ("gemv_tiles", "gemv_uniform", "unpack_tiles", "gemm_frag")),
                                                   ("vbq_quantize.hip", ("quantize_groups",))])
 def test_kernels_do_not_spill(tmp_path_factory, source, kernel_names):
     assembly = _assembly(tmp_path_factory, source)
