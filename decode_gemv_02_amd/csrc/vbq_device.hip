@@ -177,6 +177,7 @@ struct MatArgs {
     float *partial;       // [splits][n] when splits > 1
     uint32_t *counters;   // [row tiles] arrival counters when splits > 1 (self-resetting)
     uint32_t n, groups, col_tiles, splits, blocks;   // blocks = row tiles x splits
+    uint32_t units;   // work units along K: column tiles, or groups of one chunk for uniform 8- and lean 4-bit
     uint32_t payload_bytes;
     uint32_t ubits;   // the matrix's declared single width, or 0
     uint16_t *y16;    // when set, y is stored here as fp16 (nearest even) instead of fp32 to y
@@ -796,8 +797,9 @@ __device__ __forceinline__ float row_group_dot(WaveLds &L, uint32_t jl, const Ro
 }
 
 // kLean: hold two 4-bit groups of a row at once instead of four (the per-matrix-width kernel, whose
-// register budget is the largest of its four paths plus the dispatch)
-template <uint32_t kBits, bool kAligned, uint32_t kWaves, bool kLean = false>
+// register budget is the largest of its four paths plus the dispatch). kChunkUnits: a wave's unit of
+// work along K is the groups it holds at once (the per-matrix-width kernel), else a whole tile.
+template <uint32_t kBits, bool kAligned, uint32_t kWaves, bool kLean = false, bool kChunkUnits = false>
 __device__ __forceinline__ void uniform_tiles(const Batch &B, const MatArgs &M, uint32_t which, uint32_t bx,
                                               WaveLds *lds) {
     // A workgroup past its matrix's end leaves at once: with matrices of very different sizes in one
@@ -808,15 +810,19 @@ __device__ __forceinline__ void uniform_tiles(const Batch &B, const MatArgs &M, 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
     const uint32_t r0 = a * kTileRows;
     const uint32_t rows = min(kTileRows, M.n - r0);
-    const uint32_t c_lo = (split * M.col_tiles) / M.splits, c_hi = ((split + 1) * M.col_tiles) / M.splits;
     WaveLds &L = lds[wave];
     float acc = 0.f;
     const uint32_t lane0 = lane_id();
     const LutKeys keys = lut_keys();
     constexpr uint32_t kChunk = kBits == 8 ? 1 : (kBits == 4 && kLean) ? 2 : kTileGroups;   // groups held at once
-    uint32_t ct = c_lo + wave;
-    TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, relane(lane0), true);
-    for (; ct < c_hi; ct += kWaves) {
+    // A wave's unit of work: a whole tile, or with kChunkUnits the groups it holds at once (8 bits: one,
+    // lean 4 bits: two), so that it waits for its payload once per unit; M.units counts them along K.
+    constexpr uint32_t kUnit = kChunkUnits ? kChunk : kTileGroups;
+    const uint32_t u_lo = (split * M.units) / M.splits, u_hi = ((split + 1) * M.units) / M.splits;
+    uint32_t u = u_lo + wave;
+    TileMeta cur = load_meta<kAligned>(M, a, (u < u_hi ? u : u_lo) * kUnit / kTileGroups, relane(lane0), true);
+    for (; u < u_hi; u += kWaves) {
+        const uint32_t ct = u * kUnit / kTileGroups, g0 = u * kUnit % kTileGroups;   // tile, first group
         const uint32_t cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - ct * kTileGroups);
         const uint32_t lr = min(relane(lane0), rows - 1);
         const uint32_t tile_off = 8u * kBits * (r0 * M.groups + rows * kTileGroups * ct);
@@ -824,22 +830,22 @@ __device__ __forceinline__ void uniform_tiles(const Batch &B, const MatArgs &M, 
         RowGroups<kBits> g[kChunk];
 #pragma unroll
         for (uint32_t jl = 0; jl < kChunk; ++jl)
-            g[jl] = load_row_group<kBits>(tp, (min(jl, cn - 1) * rows + lr) * 8u * kBits);
-        const TileMeta nxt =
-            load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, relane(lane0), true);
+            g[jl] = load_row_group<kBits>(tp, (min(g0 + jl, cn - 1) * rows + lr) * 8u * kBits);
+        const TileMeta nxt = load_meta<kAligned>(
+            M, a, (u + kWaves < u_hi ? u + kWaves : u) * kUnit / kTileGroups, relane(lane0), true);
         stage_x<kBits == 1>(L, cur.xv, relane(lane0));
         wave_lds_sync();
         const uint32_t lane = relane(lane0);
 #pragma unroll
-        for (uint32_t c0 = 0; c0 < kTileGroups; c0 += kChunk) {
+        for (uint32_t c0 = 0; c0 < kUnit; c0 += kChunk) {
             if (c0 > 0) {
 #pragma unroll
                 for (uint32_t jl = 0; jl < kChunk; ++jl)
-                    g[jl] = load_row_group<kBits>(tp, (min(c0 + jl, cn - 1) * rows + lr) * 8u * kBits);
+                    g[jl] = load_row_group<kBits>(tp, (min(g0 + c0 + jl, cn - 1) * rows + lr) * 8u * kBits);
             }
 #pragma unroll
             for (uint32_t jl = 0; jl < kChunk; ++jl) {
-                const uint32_t j = c0 + jl;
+                const uint32_t j = g0 + c0 + jl;
                 const uint32_t sb = (j < 2 ? cur.s01 >> (16 * j) : cur.s23 >> (16 * (j - 2))) & 0xFFFFu;
                 const float d = row_group_dot<kBits>(L, j, g[jl], keys);
                 if (lane < rows && j < cn) acc = fmaf(half_to_float(sb), d, acc);
@@ -877,8 +883,8 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     switch (M.ubits) {
         case 1: uniform_tiles<1, kAligned, kWaves>(B, M, which, bx, lds); break;
         case 2: uniform_tiles<2, kAligned, kWaves>(B, M, which, bx, lds); break;
-        case 4: uniform_tiles<4, kAligned, kWaves, true>(B, M, which, bx, lds); break;
-        default: uniform_tiles<8, kAligned, kWaves>(B, M, which, bx, lds); break;
+        case 4: uniform_tiles<4, kAligned, kWaves, true, true>(B, M, which, bx, lds); break;
+        default: uniform_tiles<8, kAligned, kWaves, false, true>(B, M, which, bx, lds); break;
     }
 }
 
@@ -1645,7 +1651,13 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.groups = w->k / VBQ_GROUP;
         M.col_tiles = ceil_div(M.groups, kTileGroups);
         const uint32_t row_tiles = ceil_div(M.n, kTileRows);
-        M.splits = std::max(1u, std::min(ceil_div(M.col_tiles, plan.waves), plan.splits));
+        // a wave's unit along K (see uniform_tiles): a tile, or in the per-matrix-width kernel one group of
+        // an 8-bit matrix and two of a 4-bit one, with up to that many times the plan's splits, so that a
+        // small such matrix (the 8-bit tier of a grouped head) waits for its payload once per wave
+        const uint32_t ub = ubits == kPerMatrix ? w->uniform_bits : 0u;
+        const uint32_t unit = ub == 8 ? 1u : ub == 4 ? 2u : kTileGroups;
+        M.units = unit == kTileGroups ? M.col_tiles : ceil_div(M.groups, unit);
+        M.splits = std::max(1u, std::min(ceil_div(M.units, plan.waves), plan.splits * (kTileGroups / unit)));
         M.blocks = row_tiles * M.splits;
         blocks = std::max(blocks, M.blocks);
         if (M.groups % 4) aligned = false;
