@@ -1026,6 +1026,15 @@ struct GemmArgs {
     uint32_t payload_bytes;
 };
 
+// Up to kGemmMulti matrices that read the same X in one launch (gate and up, at a few rows of X): a 1D
+// grid, matrix i owning workgroups [first_block[i], first_block[i + 1]); entries past the last hold the
+// total.
+constexpr uint32_t kGemmMulti = 8;
+struct GemmBatch {
+    GemmArgs g[kGemmMulti];
+    uint32_t first_block[kGemmMulti + 1];
+};
+
 __device__ __forceinline__ uint32_t half2_fma(uint32_t v, uint32_t mul, uint32_t add) {
     const half2_t r = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, v), __builtin_bit_cast(half2_t, mul),
                                                 __builtin_bit_cast(half2_t, add));
@@ -1209,11 +1218,20 @@ __device__ __forceinline__ FragCol frag_col_load(const FragTables &T, rsrc_t til
     return B;
 }
 
-template <uint32_t MB, uint32_t kWaves, bool kAligned>
-__global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmArgs G) {
+// kMulti: the launch holds several matrices, and a workgroup finds its own from the block prefix (one
+// more dependent scalar load, about half a microsecond, so single-matrix launches skip it).
+template <uint32_t MB, uint32_t kWaves, bool kAligned, bool kMulti>
+__global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
     __shared__ FragLds<MB, kWaves> S;
     __shared__ uint32_t arrived_s;
-    const uint32_t a = blockIdx.x / G.splits, split = blockIdx.x % G.splits;
+    uint32_t which = 0;
+    if constexpr (kMulti) {
+#pragma unroll
+        for (uint32_t i = 1; i < kGemmMulti; ++i) which += blockIdx.x >= B.first_block[i] ? 1u : 0u;
+    }
+    const GemmArgs G = B.g[which];   // by value: scalar registers
+    const uint32_t bx = kMulti ? blockIdx.x - B.first_block[which] : blockIdx.x;
+    const uint32_t a = bx / G.splits, split = bx % G.splits;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
     const uint32_t r0 = a * kTileRows;
     const uint32_t rows = min(kTileRows, G.n - r0);
@@ -1720,71 +1738,99 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     return launched(who);
 }
 
-template <bool kAligned>
-void gemm_frag_dispatch(uint32_t mb, uint32_t waves, dim3 grid, const GemmArgs &G, hipStream_t stream) {
-    if (mb == 1 && waves == 16)
-        hipLaunchKernelGGL((gemm_frag<1, 16, kAligned>), grid, dim3(16 * kWave), 0, stream, G);
-    else if (mb == 1 && waves == 8)
-        hipLaunchKernelGGL((gemm_frag<1, 8, kAligned>), grid, dim3(8 * kWave), 0, stream, G);
+template <bool kAligned, bool kMulti>
+void gemm_frag_dispatch(uint32_t mb, uint32_t waves, dim3 grid, const GemmBatch &G, hipStream_t stream) {
+    if (mb == 1 && waves == 8)
+        hipLaunchKernelGGL((gemm_frag<1, 8, kAligned, kMulti>), grid, dim3(8 * kWave), 0, stream, G);
     else if (mb == 1)
-        hipLaunchKernelGGL((gemm_frag<1, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+        hipLaunchKernelGGL((gemm_frag<1, 4, kAligned, kMulti>), grid, dim3(4 * kWave), 0, stream, G);
     else if (mb == 2 && waves == 8)
-        hipLaunchKernelGGL((gemm_frag<2, 8, kAligned>), grid, dim3(8 * kWave), 0, stream, G);
+        hipLaunchKernelGGL((gemm_frag<2, 8, kAligned, kMulti>), grid, dim3(8 * kWave), 0, stream, G);
     else if (mb == 2)
-        hipLaunchKernelGGL((gemm_frag<2, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+        hipLaunchKernelGGL((gemm_frag<2, 4, kAligned, kMulti>), grid, dim3(4 * kWave), 0, stream, G);
     else if (mb == 3)
-        hipLaunchKernelGGL((gemm_frag<3, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+        hipLaunchKernelGGL((gemm_frag<3, 4, kAligned, kMulti>), grid, dim3(4 * kWave), 0, stream, G);
     else
-        hipLaunchKernelGGL((gemm_frag<4, 4, kAligned>), grid, dim3(4 * kWave), 0, stream, G);
+        hipLaunchKernelGGL((gemm_frag<4, 4, kAligned, kMulti>), grid, dim3(4 * kWave), 0, stream, G);
 }
 
-// Small-batch GEMM on the matrix cores: one launch for up to 64 rows of X.
-vbq_status gemm_launch(const char *who, const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
-                       hipStream_t stream) {
-    GemmArgs G{};
-    G.widths = w->widths;
-    G.scales = w->scales;
-    G.tile_offsets = w->tile_offsets;
-    G.payload = w->payload;
-    G.payload_bytes = w->payload_bytes;
-    G.x = x;
-    G.y = y;
-    G.n = w->n;
-    G.groups = w->k / VBQ_GROUP;
-    G.col_tiles = ceil_div(G.groups, kTileGroups);
-    G.m = m;
-    G.k = w->k;
-    const uint32_t row_tiles = ceil_div(G.n, kTileRows);
-    // a wave per column tile of the row tile: 16 waves for up to 16 activation rows, 8 for 32, 4 beyond
-    // (the workgroup's sum buffer is 68 KiB in each case); no more waves than column tiles need
+// Small-batch GEMM on the matrix cores: one launch for up to 64 rows of X and up to kGemmMulti matrices
+// that read them (same k, n > 0, k > 0).
+vbq_status gemm_launch(const char *who, const vbq_matrix *const *ws, float *const *ys, uint32_t count,
+                       const uint16_t *x, uint32_t m, hipStream_t stream) {
+    GemmBatch B{};
+    const uint32_t k = ws[0]->k, groups = k / VBQ_GROUP, col_tiles = ceil_div(groups, kTileGroups);
+    // a wave per column tile of the row tile: 8 waves for up to 32 activation rows, 4 beyond (the
+    // workgroup's sum buffer is at most 68 KiB); no more waves than column tiles need
     const uint32_t mb = ceil_div(m, 16);
-    uint32_t waves = mb == 1 ? 8u : mb == 2 ? 8u : 4u;
-    while (waves > 4 && waves / 2 >= G.col_tiles) waves /= 2;
+    uint32_t waves = mb <= 2 ? 8u : 4u;
+    while (waves > 4 && waves / 2 >= col_tiles) waves /= 2;
+    uint32_t total_row_tiles = 0;
+    for (uint32_t i = 0; i < count; ++i) total_row_tiles += ceil_div(ws[i]->n, kTileRows);
     // two workgroups per CU are resident (LDS): split the column tiles only
     // while the row tiles alone leave CUs idle
-    const uint32_t want_blocks = 512;
-    G.splits = std::max(1u, std::min(ceil_div(G.col_tiles, waves), want_blocks / row_tiles));
-    if (G.splits > 1) {
-        uint32_t *ctr = nullptr;
-        char *part = nullptr;
-        const size_t partials = (static_cast<size_t>(G.splits) * m * G.n * 4 + 255) / 256 * 256;
-        vbq_status st = scratch_for(who, stream, static_cast<size_t>(row_tiles) * 4, partials, &ctr, &part);
+    const uint32_t splits = std::max(1u, std::min(ceil_div(col_tiles, waves), 512u / total_row_tiles));
+    uint32_t *ctr = nullptr;
+    char *part = nullptr;
+    if (splits > 1) {
+        size_t partials = 0;
+        for (uint32_t i = 0; i < count; ++i)
+            partials += (static_cast<size_t>(splits) * m * ws[i]->n * 4 + 255) / 256 * 256;
+        vbq_status st = scratch_for(who, stream, static_cast<size_t>(total_row_tiles) * 4, partials, &ctr, &part);
         if (st != VBQ_OK) return st;
-        G.counters = ctr;
-        G.partial = reinterpret_cast<float *>(part);
     }
-    const dim3 grid(row_tiles * G.splits);
-    if (G.groups % kTileGroups == 0)
-        gemm_frag_dispatch<true>(mb, waves, grid, G, stream);
-    else
-        gemm_frag_dispatch<false>(mb, waves, grid, G, stream);
+    uint32_t blocks = 0;
+    for (uint32_t i = 0; i <= kGemmMulti; ++i) {
+        B.first_block[i] = blocks;
+        if (i >= count) continue;
+        const vbq_matrix *w = ws[i];
+        GemmArgs &G = B.g[i];
+        G.widths = w->widths;
+        G.scales = w->scales;
+        G.tile_offsets = w->tile_offsets;
+        G.payload = w->payload;
+        G.payload_bytes = w->payload_bytes;
+        G.x = x;
+        G.y = ys[i];
+        G.n = w->n;
+        G.groups = groups;
+        G.col_tiles = col_tiles;
+        G.m = m;
+        G.k = k;
+        G.splits = splits;
+        const uint32_t row_tiles = ceil_div(G.n, kTileRows);
+        if (splits > 1) {
+            G.counters = ctr;
+            ctr += row_tiles;
+            G.partial = reinterpret_cast<float *>(part);
+            part += (static_cast<size_t>(splits) * m * G.n * 4 + 255) / 256 * 256;
+        }
+        blocks += row_tiles * splits;
+    }
+    const dim3 grid(blocks);
+    if (groups % kTileGroups == 0) {
+        if (count > 1)
+            gemm_frag_dispatch<true, true>(mb, waves, grid, B, stream);
+        else
+            gemm_frag_dispatch<true, false>(mb, waves, grid, B, stream);
+    } else {
+        if (count > 1)
+            gemm_frag_dispatch<false, true>(mb, waves, grid, B, stream);
+        else
+            gemm_frag_dispatch<false, false>(mb, waves, grid, B, stream);
+    }
     return launched(who);
 }
 
 // The small-batch rule: matrix cores for m > 16 rows of X, or from 4 rows when m^2 x tiles reaches
 // kGemmMinWork; one GEMV per row otherwise (measured, see kGemmMinWork)
-bool uses_matrix_cores(const vbq_matrix *w, uint32_t m) {
-    const uint64_t tiles = static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
+uint64_t tile_count(const vbq_matrix *w) {
+    return static_cast<uint64_t>(ceil_div(w->n, kTileRows)) * ceil_div(w->k / VBQ_GROUP, kTileGroups);
+}
+
+// tiles: of one matrix, or of all the matrices one launch would hold (their products share the launch's
+// latency, so the matrix cores pay off at fewer rows)
+bool uses_matrix_cores(uint64_t tiles, uint32_t m) {
     return m > kGemmAlwaysBatch || (m >= kGemmMinBatch && static_cast<uint64_t>(m) * m * tiles >= kGemmMinWork);
 }
 
@@ -1908,13 +1954,13 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
         if (w->n == 0) return VBQ_OK;
         (void)hipGetLastError();
         hipStream_t s = static_cast<hipStream_t>(stream);
-        if (uses_matrix_cores(w, m)) {
+        if (uses_matrix_cores(tile_count(w), m)) {
             if (w->k == 0) {
                 const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
                 hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s, y, cnt);
                 return launched(who);
             }
-            return gemm_launch(who, w, x, m, y, s);
+            return gemm_launch(who, &w, &y, 1, x, m, s);
         }
         // each input row as its own GEMV of one batched launch
         const vbq_matrix *ws[VBQ_MAX_MULTI];
@@ -1935,9 +1981,11 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
 }
 
 // Small-batch products of several matrices that read the same rows of X
-// (q, k, v; gate, up): matrices the rule gives the matrix cores get their own
-// launch; the others become one GEMV per (matrix, row) and share launches of
-// up to VBQ_MAX_MULTI GEMVs, matrix by matrix and row by row.
+// (q, k, v; gate, up). The small-batch rule is applied to all of them
+// together: on the matrix cores they share launches of up to kGemmMulti
+// matrices (the launch's latency is paid once), otherwise each becomes one
+// GEMV per row, and those share launches of up to VBQ_MAX_MULTI GEMVs,
+// matrix by matrix and row by row.
 extern "C" vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, const uint16_t *x, uint32_t m,
                                                 float *const *ys, uint32_t count, void *stream) {
     return vbq::guarded("vbq_gemm_smallbatch_multi", [&]() -> vbq_status {
@@ -1967,22 +2015,37 @@ extern "C" vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, con
             pending = 0;
             return st;
         };
-        for (uint32_t i = 0; i < count; ++i) {
-            const vbq_matrix *w = ws[i];
-            if (w->n == 0) continue;
-            if (uses_matrix_cores(w, m)) {
-                vbq_status st;
+        // the rule on all the matrices together: on the matrix cores they share one launch
+        uint64_t tiles = 0;
+        for (uint32_t i = 0; i < count; ++i) tiles += tile_count(ws[i]);
+        if (uses_matrix_cores(tiles, m)) {
+            const vbq_matrix *mw[kGemmMulti];
+            float *my[kGemmMulti];
+            uint32_t held = 0;
+            for (uint32_t i = 0; i < count; ++i) {
+                const vbq_matrix *w = ws[i];
+                if (w->n == 0) continue;
                 if (k == 0) {
                     const uint64_t cnt = static_cast<uint64_t>(m) * w->n;
                     hipLaunchKernelGGL(fill_zero, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, s,
                                        ys[i], cnt);
-                    st = launched(who);
-                } else {
-                    st = gemm_launch(who, w, x, m, ys[i], s);
+                    const vbq_status st = launched(who);
+                    if (st != VBQ_OK) return st;
+                    continue;
                 }
-                if (st != VBQ_OK) return st;
-                continue;
+                mw[held] = w;
+                my[held] = ys[i];
+                if (++held == kGemmMulti || i + 1 == count) {
+                    const vbq_status st = gemm_launch(who, mw, my, held, x, m, s);
+                    if (st != VBQ_OK) return st;
+                    held = 0;
+                }
             }
+            return held ? gemm_launch(who, mw, my, held, x, m, s) : VBQ_OK;
+        }
+        for (uint32_t i = 0; i < count; ++i) {
+            const vbq_matrix *w = ws[i];
+            if (w->n == 0) continue;
             for (uint32_t r = 0; r < m; ++r) {
                 gw[pending] = w;
                 gx[pending] = x + static_cast<uint64_t>(r) * k;

@@ -255,14 +255,17 @@ VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, u
 /* Small-batch products of several matrices that read the same m rows of X
  * (VBQ §6, "Fused kernels over packed weights", batched: q, k and v, or gate
  * and up, at one decode step of m sequences; the pages are silent on
- * batches): ys[i] = X W_i^T, each exactly as vbq_gemm_smallbatch computes
- * it. x: device binary16 [m][k] shared by all matrices (every ws[i] has the
- * same k); ys[i]: device fp32 [m][n_i]. Matrices the small-batch rule gives
- * the matrix cores get their own launch; the others run as one GEMV per
- * (matrix, row) and share launches of up to VBQ_MAX_MULTI GEMVs, so a layer's
- * projections at batch 8 take as many launches as at batch 1. Asynchronous on
- * `stream`; scratch as for vbq_gemv_multi. Errors: NULL, ABI, SHAPE (m, or the
- * k's differ), ALIGN, OFFSETS, HIP. */
+ * batches): ys[i] = X W_i^T. x: device binary16 [m][k] shared by all
+ * matrices (every ws[i] has the same k); ys[i]: device fp32 [m][n_i]. The
+ * small-batch rule is applied to the matrices together (their tile counts
+ * summed): on the matrix cores they share launches of up to 8 matrices,
+ * whose latency they then pay once; otherwise each runs as one GEMV per
+ * (matrix, row), and those share launches of up to VBQ_MAX_MULTI GEMVs, so a
+ * layer's projections at batch 8 take as many launches as at batch 1. The
+ * results agree with vbq_gemm_smallbatch on each matrix within the GEMV
+ * tolerance (the two may take different paths). Asynchronous on `stream`;
+ * scratch as for vbq_gemv_multi. Errors: NULL, ABI, SHAPE (m, or the k's
+ * differ), ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, const uint16_t *x, uint32_t m,
                                              float *const *ys, uint32_t count, void *stream);
 

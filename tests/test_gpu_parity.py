@@ -435,20 +435,24 @@ def test_grouped_recipe_head(V, torch_mod):
     assert np.array_equal(y1.cpu().numpy(), ys[2].cpu().numpy())
 
 
-@pytest.mark.parametrize("m", [1, 8, 12, 20])
-def test_gemm_smallbatch_multi_matches_oracle(V, torch_mod, m):
-    # matrices sharing the m rows of X, as q/k/v do: ragged row counts; at m = 12 the 8192-row matrix
-    # takes the matrix cores (m * m * tiles >= 85000) while the others share GEMV launches, whose
-    # (matrix, row) count passes 32 so they are split; at m = 20 all take the matrix cores
+@pytest.mark.parametrize("m, k, shapes", [
+    (1, 2048, [97, 8192, 300, 64, 1000]),
+    (8, 2048, [97, 8192, 300, 64, 1000]),      # 1216 tiles: 64 x 1216 < 85000, GEMVs (40 per matrix set)
+    (12, 2048, [97, 8192, 300, 64, 1000]),     # 144 x 1216 >= 85000: one matrix-core launch for all five
+    (20, 2048, [97, 8192, 300, 64, 1000]),
+    (20, 1088, [97, 130, 64, 300, 33, 200, 64, 1000, 70, 5]),   # ten matrices: two launches; k % 256 != 0
+])
+def test_gemm_smallbatch_multi_matches_oracle(V, torch_mod, m, k, shapes):
+    # matrices sharing the m rows of X, as q/k/v and gate/up do, with ragged row counts: the small-batch
+    # rule applies to all of them together, so they share matrix-core launches (up to eight matrices
+    # each) or GEMV launches (up to 32 products each)
     torch = torch_mod
-    k = 2048
-    shapes = [97, 8192, 300, 64, 1000]
     print_case(test="gemm_multi", m=m, k=k, shapes=shapes)
     x = W.draw_x((90, m), k, m)
     xt = torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).cuda()
     packs, dms, hs = [], [], []
     for i, n in enumerate(shapes):
-        bits, codes, scales, p = make_case((91, m, i), n, k, W.STD_MIX)
+        bits, codes, scales, p = make_case((91, m, k, i), n, k, W.STD_MIX)
         h, dm = upload(V, bits, codes, scales)
         hs.append(h)
         dms.append(dm)
