@@ -1220,111 +1220,12 @@ __device__ __forceinline__ FragCol frag_col_load(const FragTables &T, rsrc_t til
 
 // kMulti: the launch holds several matrices, and a workgroup finds its own from the block prefix (one
 // more dependent scalar load, about half a microsecond, so single-matrix launches skip it).
-template <uint32_t MB, uint32_t kWaves, bool kAligned, bool kMulti>
-__global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
-    __shared__ FragLds<MB, kWaves> S;
-    __shared__ uint32_t arrived_s;
-    uint32_t which = 0;
-    if constexpr (kMulti) {
-#pragma unroll
-        for (uint32_t i = 1; i < kGemmMulti; ++i) which += blockIdx.x >= B.first_block[i] ? 1u : 0u;
-    }
-    const GemmArgs G = B.g[which];   // by value: scalar registers
-    const uint32_t bx = kMulti ? blockIdx.x - B.first_block[which] : blockIdx.x;
-    const uint32_t a = bx / G.splits, split = bx % G.splits;
-    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
-    const uint32_t r0 = a * kTileRows;
-    const uint32_t rows = min(kTileRows, G.n - r0);
-    const uint32_t c_lo = (split * G.col_tiles) / G.splits, c_hi = ((split + 1) * G.col_tiles) / G.splits;
-    if (threadIdx.x < 16) {
-        S.run.params[threadIdx.x] = frag_params(threadIdx.x >> 2, threadIdx.x & 3u);
-        const uint32_t n = threadIdx.x;   // bit t set: code 4..+t is -1
-        auto pm = [](uint32_t bit) { return bit ? 0xBC00u : 0x3C00u; };
-        S.run.nib1[n] = make_uint2(pm(n & 1u) | (pm(n & 2u) << 16), pm(n & 4u) | (pm(n & 8u) << 16));
-    }
-    __syncthreads();
-    FragTables &T = S.run.tab[wave];
-
-    float4_t acc[4][MB];
-#pragma unroll
-    for (uint32_t rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    // (a wave usually owns one or two tiles, and the other waves of the CU cover its metadata wait: no
-    // prefetch of the next tile's metadata, whose registers would be held across the whole tile)
-    uint32_t ct = c_lo + wave;
-    TileMeta meta = load_meta<kAligned>(G, a, ct < c_hi ? ct : c_lo, lane_id(), false);
-    for (; ct < c_hi; ct += kWaves) {
-        const uint32_t j0 = ct * kTileGroups, cn = kAligned ? kTileGroups : min(kTileGroups, G.groups - j0);
-        uint32_t cnt[4];
-        const TileScan sc = tile_scan(meta, rows, cn, lane_id(), cnt);
-        uint64_t colstart[kTileGroups + 1];
-        column_starts(sc, colstart);
-        const uint32_t ones = frag_tables(T, meta, sc, colstart, cnt, rows, cn, lane_id());
-        const rsrc_t tile = tile_rsrc(G.payload, G.payload_bytes, meta.off);
-        const uint16_t *xp[MB];
-        frag_x_rows<MB>(G, j0, xp);
-        const uint32_t lane = lane_id(), q = lane >> 4, i = lane & 15u;
-        wave_lds_sync();
-        // two-stage pipeline over the columns: the next column's payload bytes are requested before this
-        // column is decoded, so a wave waits for memory about once per tile
-        FragCol cur = frag_col_load(T, tile, 0, ones, q, i);
-        half8_t bx[2][MB];
-        frag_load_x<MB>(xp, 0, bx);
-        // the next tile's metadata travels while this tile computes
-        meta = load_meta<kAligned>(G, a, ct + kWaves < c_hi ? ct + kWaves : ct, lane_id(), false);
-        // (a rolled loop: unrolled, the compiler hoists every column's loads and runs out of registers)
-#pragma unroll 1
-        for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
-            if (jl >= cn) break;
-            // (the next column's activations too when they are few: beyond 16 rows they would cost occupancy)
-            FragCol nxt;
-            half8_t bxn[2][MB];
-            if (jl + 1 < cn) {
-                nxt = frag_col_load(T, tile, jl + 1, ones, q, i);
-                if constexpr (MB == 1) frag_load_x<MB>(xp, jl + 1, bxn);
-            }
-            if constexpr (MB > 1) {
-                if (jl > 0) frag_load_x<MB>(xp, jl, bx);
-            }
-#pragma unroll
-            for (uint32_t rb = 0; rb < 4; ++rb) {
-                half8_t a0, a1;
-                if ((ones >> (4 * jl + rb)) & 1u) {   // every row of the block 1-bit: codes by nibble table
-                    const uint2 *nib = S.run.nib1;
-                    const uint32_t w0 = cur.w[rb][0].x, w1 = cur.w[rb][0].y;
-                    const uint2 p00 = nib[__builtin_amdgcn_ubfe(w0, 8 * q, 4)], p01 = nib[__builtin_amdgcn_ubfe(w0, 8 * q + 4, 4)];
-                    const uint2 p10 = nib[__builtin_amdgcn_ubfe(w1, 8 * q, 4)], p11 = nib[__builtin_amdgcn_ubfe(w1, 8 * q + 4, 4)];
-                    a0 = frag_of(p00.x, p00.y, p01.x, p01.y);
-                    a1 = frag_of(p10.x, p10.y, p11.x, p11.y);
-                } else {
-                    const uint32_t c = T.where[jl][16 * rb + i] & 3u;
-                    frag_generic(cur.w[rb][0], cur.w[rb][1], S.run.params[4 * c + q], a0, a1);
-                }
-                float4_t d[MB];
-#pragma unroll
-                for (uint32_t mb = 0; mb < MB; ++mb)
-                    d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[0][mb], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                   0);
-#pragma unroll
-                for (uint32_t mb = 0; mb < MB; ++mb)
-                    d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[1][mb], d[mb], 0, 0, 0);
-                // rows 16rb + 4q .. +3 of this column
-                const float4_t s = *static_cast<const float4_t *>(
-                    __builtin_assume_aligned(&T.scale[jl][16 * rb + 4 * q], 16));
-#pragma unroll
-                for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] += s * d[mb];
-            }
-            cur = nxt;
-            if constexpr (MB == 1) {
-#pragma unroll
-                for (uint32_t h = 0; h < 2; ++h) bx[h][0] = bxn[h][0];
-            }
-        }
-        wave_lds_sync();
-    }
-
+// The workgroup's sums (each wave's acc over its tiles of row tile a) added in wave order through LDS, then
+// stored, or, for a split row tile, published as partials and added in split order by the last arriver.
+template <uint32_t MB, uint32_t kWaves>
+__device__ __forceinline__ void frag_finish(FragLds<MB, kWaves> &S, const GemmArgs &G, uint32_t wave, uint32_t a,
+                                            uint32_t split, uint32_t r0, uint32_t rows, const float4_t acc[4][MB],
+                                            uint32_t &arrived_s) {
     // Workgroup sum in wave order: each wave parks its sums as fp32 [activation row][tile row]
     __syncthreads();
     {
@@ -1397,6 +1298,120 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
         }
     }
     if (threadIdx.x == 0) __hip_atomic_store(&G.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One 16-row block rb of column jl: decode the lane's A fragments (a block whose rows are all 1-bit by the
+// nibble table, any other by the width-generic decoder), multiply with the activations on the matrix
+// cores, scale each row by its group scale and add into acc (rows 16rb + 4q .. +3, activation row mr).
+template <uint32_t MB>
+__device__ __forceinline__ void frag_block(const FragParams *params, const uint2 *nib, const FragTables &T,
+                                           uint32_t jl, uint32_t rb, bool one_bit, const uint2 w[2],
+                                           const half8_t bx[2][MB], uint32_t q, uint32_t i, float4_t acc[MB]) {
+    half8_t a0, a1;
+    if (one_bit) {
+        const uint32_t w0 = w[0].x, w1 = w[0].y;
+        const uint2 p00 = nib[__builtin_amdgcn_ubfe(w0, 8 * q, 4)], p01 = nib[__builtin_amdgcn_ubfe(w0, 8 * q + 4, 4)];
+        const uint2 p10 = nib[__builtin_amdgcn_ubfe(w1, 8 * q, 4)], p11 = nib[__builtin_amdgcn_ubfe(w1, 8 * q + 4, 4)];
+        a0 = frag_of(p00.x, p00.y, p01.x, p01.y);
+        a1 = frag_of(p10.x, p10.y, p11.x, p11.y);
+    } else {
+        const uint32_t c = T.where[jl][16 * rb + i] & 3u;
+        frag_generic(w[0], w[1], params[4 * c + q], a0, a1);
+    }
+    float4_t d[MB];
+#pragma unroll
+    for (uint32_t mb = 0; mb < MB; ++mb)
+        d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[0][mb], float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (uint32_t mb = 0; mb < MB; ++mb) d[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[1][mb], d[mb], 0, 0, 0);
+    const float4_t s = *static_cast<const float4_t *>(__builtin_assume_aligned(&T.scale[jl][16 * rb + 4 * q], 16));
+#pragma unroll
+    for (uint32_t mb = 0; mb < MB; ++mb) acc[mb] += s * d[mb];
+}
+
+template <uint32_t MB, uint32_t kWaves, bool kAligned, bool kMulti>
+__global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
+    __shared__ FragLds<MB, kWaves> S;
+    __shared__ uint32_t arrived_s;
+    uint32_t which = 0;
+    if constexpr (kMulti) {
+#pragma unroll
+        for (uint32_t i = 1; i < kGemmMulti; ++i) which += blockIdx.x >= B.first_block[i] ? 1u : 0u;
+    }
+    const GemmArgs G = B.g[which];   // by value: scalar registers
+    const uint32_t bx = kMulti ? blockIdx.x - B.first_block[which] : blockIdx.x;
+    const uint32_t a = bx / G.splits, split = bx % G.splits;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
+    const uint32_t r0 = a * kTileRows;
+    const uint32_t rows = min(kTileRows, G.n - r0);
+    const uint32_t c_lo = (split * G.col_tiles) / G.splits, c_hi = ((split + 1) * G.col_tiles) / G.splits;
+    if (threadIdx.x < 16) {
+        S.run.params[threadIdx.x] = frag_params(threadIdx.x >> 2, threadIdx.x & 3u);
+        const uint32_t n = threadIdx.x;   // bit t set: code 4..+t is -1
+        auto pm = [](uint32_t bit) { return bit ? 0xBC00u : 0x3C00u; };
+        S.run.nib1[n] = make_uint2(pm(n & 1u) | (pm(n & 2u) << 16), pm(n & 4u) | (pm(n & 8u) << 16));
+    }
+    __syncthreads();
+    FragTables &T = S.run.tab[wave];
+
+    float4_t acc[4][MB];
+#pragma unroll
+    for (uint32_t rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (uint32_t mb = 0; mb < MB; ++mb) acc[rb][mb] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // (a wave usually owns one or two tiles, and the other waves of the CU cover its metadata wait: no
+    // prefetch of the next tile's metadata, whose registers would be held across the whole tile)
+    uint32_t ct = c_lo + wave;
+    TileMeta meta = load_meta<kAligned>(G, a, ct < c_hi ? ct : c_lo, lane_id(), false);
+    for (; ct < c_hi; ct += kWaves) {
+        const uint32_t j0 = ct * kTileGroups, cn = kAligned ? kTileGroups : min(kTileGroups, G.groups - j0);
+        uint32_t cnt[4];
+        const TileScan sc = tile_scan(meta, rows, cn, lane_id(), cnt);
+        uint64_t colstart[kTileGroups + 1];
+        column_starts(sc, colstart);
+        const uint32_t ones = frag_tables(T, meta, sc, colstart, cnt, rows, cn, lane_id());
+        const rsrc_t tile = tile_rsrc(G.payload, G.payload_bytes, meta.off);
+        const uint16_t *xp[MB];
+        frag_x_rows<MB>(G, j0, xp);
+        const uint32_t lane = lane_id(), q = lane >> 4, i = lane & 15u;
+        wave_lds_sync();
+        // two-stage pipeline over the columns: the next column's payload bytes are requested before this
+        // column is decoded, so a wave waits for memory about once per tile
+        FragCol cur = frag_col_load(T, tile, 0, ones, q, i);
+        half8_t bx[2][MB];
+        frag_load_x<MB>(xp, 0, bx);
+        // the next tile's metadata travels while this tile computes
+        meta = load_meta<kAligned>(G, a, ct + kWaves < c_hi ? ct + kWaves : ct, lane_id(), false);
+        // (a rolled loop: unrolled, the compiler hoists every column's loads and runs out of registers)
+#pragma unroll 1
+        for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
+            if (jl >= cn) break;
+            // (the next column's activations too when they are few: beyond 16 rows they would cost occupancy)
+            FragCol nxt;
+            half8_t bxn[2][MB];
+            if (jl + 1 < cn) {
+                nxt = frag_col_load(T, tile, jl + 1, ones, q, i);
+                if constexpr (MB == 1) frag_load_x<MB>(xp, jl + 1, bxn);
+            }
+            if constexpr (MB > 1) {
+                if (jl > 0) frag_load_x<MB>(xp, jl, bx);
+            }
+#pragma unroll
+            for (uint32_t rb = 0; rb < 4; ++rb) {
+                frag_block<MB>(S.run.params, S.run.nib1, T, jl, rb, (ones >> (4 * jl + rb)) & 1u, cur.w[rb], bx, q, i,
+                               acc[rb]);
+            }
+            cur = nxt;
+            if constexpr (MB == 1) {
+#pragma unroll
+                for (uint32_t h = 0; h < 2; ++h) bx[h][0] = bxn[h][0];
+            }
+        }
+        wave_lds_sync();
+    }
+
+    frag_finish<MB, kWaves>(S, G, wave, a, split, r0, rows, acc, arrived_s);
 }
 
 // ---------------------------------------------------------------- host side
