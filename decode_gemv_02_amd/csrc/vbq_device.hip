@@ -320,24 +320,29 @@ __device__ __forceinline__ void lds_store16(uint32_t byte_addr, f32x4_t v) {
 // the activations selected by the set bits of a 4-bit index) and each
 // column's activation sum (the offset of the unpack paths).
 template <bool kLut = true>
-__device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
+__device__ __forceinline__ void stage_x_at(float *lut, uint32_t *xs, float *corr, uint2 xv, uint32_t lane) {
     const uint32_t jl = lane >> 4, k = lane & 15;
-    L.xs[jl * kXStride + 2 * k] = xv.x;
-    L.xs[jl * kXStride + 2 * k + 1] = xv.y;
+    xs[jl * kXStride + 2 * k] = xv.x;
+    xs[jl * kXStride + 2 * k + 1] = xv.y;
     const float x0 = half_to_float(xv.x & 0xFFFFu), x1 = half_to_float(xv.x >> 16);
     const float x2 = half_to_float(xv.y & 0xFFFFu), x3 = half_to_float(xv.y >> 16);
     const float a01 = x0 + x1, t5 = x2 + x0, t6 = x2 + x1, t7 = x2 + a01;
     if (kLut) {
         // piece c of table (k, jl) at byte 256 k + 64 jl + 16 (c ^ sw(k)): the table is 64-byte
         // aligned, so the four addresses are one base and three XORs
-        const uint32_t base = lds_addr(L.lut) + 256u * k + 64u * jl + 16u * ((k >> 1) & 3u);
+        const uint32_t base = lds_addr(lut) + 256u * k + 64u * jl + 16u * ((k >> 1) & 3u);
         lds_store16(base, f32x4_t{0.f, x0, x1, a01});
         lds_store16(base ^ 16u, f32x4_t{x2, t5, t6, t7});
         lds_store16(base ^ 32u, f32x4_t{x3, x3 + x0, x3 + x1, x3 + a01});
         lds_store16(base ^ 48u, f32x4_t{x3 + x2, x3 + t5, x3 + t6, x3 + t7});
     }
     const float xsum = row16_sum(a01 + (x2 + x3));
-    if (k == 0) L.corr[jl] = xsum;
+    if (k == 0) corr[jl] = xsum;
+}
+
+template <bool kLut = true>
+__device__ __forceinline__ void stage_x(WaveLds &L, uint2 xv, uint32_t lane) {
+    stage_x_at<kLut>(L.lut, L.xs, L.corr, xv, lane);
 }
 
 // Inclusive prefix sum over the 64 lanes (DPP: row shifts, then row broadcasts).
@@ -389,7 +394,8 @@ __device__ __forceinline__ TileScan tile_scan(const TileMeta &t, uint32_t rows, 
 
 // Lane r = row r of the tile: put each of its groups into the list at its
 // place in the stream's order (buckets by width, column-major inside a bucket).
-__device__ __forceinline__ void build_lists(WaveLds &L, const TileMeta &t, const TileScan &T, const uint32_t cnt[4],
+template <class Lds>
+__device__ __forceinline__ void build_lists(Lds &L, const TileMeta &t, const TileScan &T, const uint32_t cnt[4],
                                             uint32_t rows, uint32_t cn, uint32_t lane) {
     const bool valid = lane < rows;
     // bucket starts, then the groups of each width in earlier columns, 16 bits per width (uniform)
@@ -751,6 +757,302 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         cur = nxt;
     }
     finish_row_tile<kWaves>(B, M, blockIdx.y, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
+}
+
+// ---------------------------------------------------------------- several rows of X
+// Small batches: a wave decodes each tile once and multiplies it by kR = 2
+// rows of X, so the per-tile work that does not depend on x (metadata,
+// counts, list, payload loads, field masks, the 1-bit lookup addresses) is
+// shared by the rows. Each row has its own staged activations, lookup table
+// and products in LDS (the single-row layout, kR times), and per row the
+// arithmetic is the single-row kernel's, in the same order. x row r is at
+// x + r k and y row r at y + r n.
+template <uint32_t kR>
+struct alignas(64) RowsLds {
+    union {
+        float lut[kR][16 * kTileGroups * 16];             // per row: the single-row table layout
+        float part[kR][kTileGroups * kTileRows + kWave];  // per row: products, then one spare slot per lane
+    };
+    uint32_t xs[kR][kTileGroups * kXStride];
+    float corr[kR][kTileGroups];
+    uint8_t list[kTileRows * kTileGroups];
+};
+
+// Activations 4k..4k+3 of column lane/16 (k = lane % 16) of each row, as load_meta loads one row's
+template <bool kAligned, uint32_t kR>
+__device__ __forceinline__ void load_x_rows(const MatArgs &M, uint32_t ct, uint32_t lane, uint2 xv[kR]) {
+    const uint32_t j0 = ct * kTileGroups, cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - j0);
+    const uint32_t jl = min(lane >> 4, cn - 1), k = lane & 15;
+    const uint32_t xoff = 128u * (j0 + jl) + 8u * k;
+    const uint64_t row_bytes = 128ull * M.groups;
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r)
+        xv[r] = *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(M.x) + r * row_bytes + xoff);
+}
+
+// 1-bit group of column info >> 6 for every row: the table offsets are formed once (as in group1) and
+// each row reads its own table, 4 KiB further on
+template <uint32_t kR>
+__device__ __forceinline__ void group1_rows(RowsLds<kR> &L, uint32_t info, uint2 v, LutKeys keys, float out[kR]) {
+    const uint32_t jl = info >> 6;
+    const char *lut = reinterpret_cast<const char *>(L.lut[0] + jl * 16u);
+    const uint32_t w[2] = {v.x, v.y};
+    float acc[kR][4];
+#pragma unroll
+    for (uint32_t q = 0; q < 2; ++q) {
+        uint32_t lo, hi;
+        asm("v_lshlrev_b32 %0, 2, %1\n\tv_bitop3_b32 %0, %0, %2, %3 bitop3:0x6a"
+            : "=&v"(lo) : "v"(w[q]), "v"(keys.mask), "v"(keys.swz));
+        asm("v_lshrrev_b32 %0, 2, %1\n\tv_bitop3_b32 %0, %0, %2, %3 bitop3:0x6a"
+            : "=&v"(hi) : "v"(w[q]), "v"(keys.mask), "v"(keys.swz));
+#pragma unroll
+        for (uint32_t t = 0; t < 4; ++t) {
+            const uint32_t k = 8 * q + 2 * t;
+            const char *pa = lut + 256u * k + ((lo >> (8 * t)) & 0xFFu);
+            const char *pb = lut + 256u * (k + 1) + ((hi >> (8 * t)) & 0xFFu);
+#pragma unroll
+            for (uint32_t r = 0; r < kR; ++r) {
+                const float a = *reinterpret_cast<const float *>(pa + sizeof(L.lut[0]) * r);
+                const float b = *reinterpret_cast<const float *>(pb + sizeof(L.lut[0]) * r);
+                acc[r][t] = q == 0 ? a + b : acc[r][t] + (a + b);
+            }
+        }
+    }
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) {
+        const float sum = (acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3]);
+        out[r] = L.corr[r][jl] - 2.f * sum;
+    }
+}
+
+// 2-bit group: each word unpacked once, then dotted with every row (dot2bit's order per row)
+template <uint32_t kR>
+__device__ __forceinline__ void group2_rows(RowsLds<kR> &L, uint32_t info, uint2 va, uint2 vb) {
+    const uint32_t jl = info >> 6;
+    const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
+    float a1[kR], a4[kR], a16[kR], a64[kR], a256[kR];
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) a1[r] = a4[r] = a16[r] = a64[r] = a256[r] = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        uint32_t p[8];
+        unpack2(w[q], p);
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) {
+            const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs[r] + jl * kXStride);
+            const uint4 xa = xp[2 * q], xb = xp[2 * q + 1];
+            a1[r] = dot2(p[0], xa.x, a1[r]);
+            a4[r] = dot2(p[1], xa.y, a4[r]);
+            a16[r] = dot2(p[2], xa.z, a16[r]);
+            a64[r] = dot2(p[3], xa.w, a64[r]);
+            a256[r] = dot2(p[4], xb.x, a256[r]);
+            a1[r] = dot2(p[5], xb.y, a1[r]);
+            a4[r] = dot2(p[6], xb.z, a4[r]);
+            a16[r] = dot2(p[7], xb.w, a16[r]);
+        }
+    }
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) {
+        const float ux = fmaf(0x1p16f, a256[r],
+                              fmaf(0x1p18f, a64[r], fmaf(0x1p20f, a16[r], fmaf(0x1p22f, a4[r], 0x1p24f * a1[r]))));
+        L.part[r][info] = fmaf(-2.f, L.corr[r][jl], ux);
+    }
+}
+
+// 4-bit half group h of every row; lane pairs add their halves (task4's order per row)
+template <uint32_t kR>
+__device__ __forceinline__ void task4_rows(RowsLds<kR> &L, uint32_t info, uint32_t h, uint2 va, uint2 vb) {
+    const uint32_t jl = info >> 6;
+    const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
+    float a1[kR], a16[kR];
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) a1[r] = a16[r] = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < 4; ++q) {
+        uint32_t p[4];
+        unpack4(w[q], p);
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) {
+            const uint4 xa = reinterpret_cast<const uint4 *>(L.xs[r] + jl * kXStride + 16u * h)[q];
+            a1[r] = dot2(p[0], xa.x, a1[r]);
+            a16[r] = dot2(p[1], xa.y, a16[r]);
+            a1[r] = dot2(p[2], xa.z, a1[r]);
+            a16[r] = dot2(p[3], xa.w, a16[r]);
+        }
+    }
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) {
+        float part = fmaf(0.0625f, a16[r], a1[r]);
+        part += dpp<kQuadXor1>(part);
+        if (h == 0) L.part[r][info] = fmaf(-8.f, L.corr[r][jl], 0x1p24f * part);
+    }
+}
+
+// 8-bit quarter group qd of every row; lane quads add their quarters (task8's order per row)
+template <uint32_t kR>
+__device__ __forceinline__ void task8_rows(RowsLds<kR> &L, uint32_t info, uint32_t qd, uint2 va, uint2 vb) {
+    const uint32_t jl = info >> 6;
+    const uint32_t w[4] = {va.x, va.y, vb.x, vb.y};
+    float a[kR];
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) a[r] = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < 2; ++q) {
+        uint32_t p0, p1, p2, p3;
+        unpack8(w[2 * q], p0, p1);
+        unpack8(w[2 * q + 1], p2, p3);
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) {
+            const uint4 xa = reinterpret_cast<const uint4 *>(L.xs[r] + jl * kXStride + 8u * qd)[q];
+            a[r] = dot2(p0, xa.x, a[r]);
+            a[r] = dot2(p1, xa.y, a[r]);
+            a[r] = dot2(p2, xa.z, a[r]);
+            a[r] = dot2(p3, xa.w, a[r]);
+        }
+    }
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) {
+        float v = a[r];
+        v += dpp<kQuadXor1>(v);
+        v += dpp<kQuadXor2>(v);
+        if (qd == 0) L.part[r][info] = fmaf(-128.f, L.corr[r][jl], 0x1p24f * v);
+    }
+}
+
+// tile_products for kR rows: the same rounds and the same staged loads
+template <uint32_t kR>
+__device__ __forceinline__ void tile_products_rows(RowsLds<kR> &L, const Staged &S, rsrc_t tile, const uint32_t cnt[4],
+                                                   uint32_t lane, LutKeys keys) {
+    uint32_t info1[4];
+    float v1[4][kR];
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) {
+        const bool on = lane + kWave * i < cnt[0];
+        const uint32_t e = L.list[lane + kWave * i];
+        info1[i] = on ? e : kTileGroups * kTileRows + lane;
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) v1[i][r] = 0.f;
+        if (on) group1_rows<kR>(L, e, S.p1[i], keys, v1[i]);
+    }
+    // the lookup tables are dead from here: their bytes take the products
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i)
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) L.part[r][info1[i]] = v1[i][r];
+    const uint32_t o2 = 8u * cnt[0], o4 = o2 + 16u * cnt[1], o8 = o4 + 32u * cnt[2];
+    const uint8_t *l2 = L.list + cnt[0], *l4 = l2 + cnt[1], *l8 = l4 + cnt[2];
+    if (lane < cnt[1]) group2_rows<kR>(L, l2[lane], S.p2a, S.p2b);
+    if (lane < 2u * cnt[2]) task4_rows<kR>(L, l4[lane >> 1], lane & 1u, S.p4a, S.p4b);
+    if (lane < 4u * cnt[3]) task8_rows<kR>(L, l8[lane >> 2], lane & 3u, S.p8a, S.p8b);
+    for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
+        group2_rows<kR>(L, l2[e], buf_load8(tile, o2 + 16u * e), buf_load8(tile, o2 + 16u * e + 8u));
+    for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
+        task4_rows<kR>(L, l4[e >> 1], e & 1u, buf_load8(tile, o4 + 16u * e), buf_load8(tile, o4 + 16u * e + 8u));
+    for (uint32_t e = lane + kWave; e < 4u * cnt[3]; e += kWave)
+        task8_rows<kR>(L, l8[e >> 2], e & 3u, buf_load8(tile, o8 + 16u * e), buf_load8(tile, o8 + 16u * e + 8u));
+}
+
+// The workgroup's row sums per row of X (waves in wave order), the split-K
+// reduction (one arrival count per row tile for all the rows; partial sums
+// of row r and split s at partial[(r * splits + s) * n]), then y.
+template <uint32_t kWaves, uint32_t kR>
+__device__ __forceinline__ void finish_rows(const MatArgs &M, RowsLds<kR> *lds, uint32_t wave, uint32_t a,
+                                            uint32_t split, uint32_t r0, uint32_t rows, uint32_t lane,
+                                            const float acc[kR]) {
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) lds[wave].part[r][lane] = acc[r];
+    __syncthreads();
+    if (wave != 0) return;
+    float sum[kR];
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) {
+        sum[r] = lds[0].part[r][lane];
+#pragma unroll
+        for (uint32_t w = 1; w < kWaves; ++w) sum[r] += lds[w].part[r][lane];   // in wave order
+    }
+    if (M.splits > 1) {
+        // the split-K publication protocol of finish_row_tile, for every row of X
+        if (lane < rows) {
+#pragma unroll
+            for (uint32_t r = 0; r < kR; ++r)
+                __hip_atomic_store(&M.partial[(static_cast<uint64_t>(r) * M.splits + split) * M.n + r0 + lane],
+                                   sum[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        uint32_t arrived = 0;
+        if (lane == 0)
+            arrived = __hip_atomic_fetch_add(&M.counters[a], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __shfl(arrived, 0, kWave);
+        if (arrived != M.splits - 1) return;
+        if (lane < rows) {
+#pragma unroll
+            for (uint32_t r = 0; r < kR; ++r)
+                sum[r] = sum_partials(M.partial + static_cast<uint64_t>(r) * M.splits * M.n + r0 + lane, M.n,
+                                      M.splits);
+        }
+        if (lane == 0) __hip_atomic_store(&M.counters[a], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane < rows) {
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) M.y[static_cast<uint64_t>(r) * M.n + r0 + lane] = sum[r];
+    }
+}
+
+// kR rows of X per wave. The LDS (kR times the single-row layout) allows
+// 8 / kR waves per SIMD, so the registers may grow to match. Workgroups past
+// their matrix's end leave at once.
+template <bool kAligned, uint32_t kWaves, uint32_t kR>
+__global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8 / kR, 8 / kR))) void gemv_rows(
+    Batch B) {
+    __shared__ RowsLds<kR> lds[kWaves];
+    const MatArgs M = B.m[blockIdx.y];
+    if (blockIdx.x >= M.blocks) return;
+    const uint32_t a = blockIdx.x / M.splits, split = blockIdx.x % M.splits;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / kWave;
+    const uint32_t r0 = a * kTileRows;
+    const uint32_t rows = min(kTileRows, M.n - r0);
+    const uint32_t c_lo = (split * M.col_tiles) / M.splits, c_hi = ((split + 1) * M.col_tiles) / M.splits;
+    RowsLds<kR> &L = lds[wave];
+    float acc[kR];
+#pragma unroll
+    for (uint32_t r = 0; r < kR; ++r) acc[r] = 0.f;
+    const uint32_t lane0 = lane_id();
+    const LutKeys keys = lut_keys();
+    uint32_t ct = c_lo + wave;
+    TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, relane(lane0), false);
+    uint2 xc[kR];
+    load_x_rows<kAligned, kR>(M, ct < c_hi ? ct : c_lo, relane(lane0), xc);
+    for (; ct < c_hi; ct += kWaves) {
+        const uint32_t cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - ct * kTileGroups);
+        uint32_t cnt[4];
+        const TileScan P = tile_scan(cur, rows, cn, relane(lane0), cnt);
+        const rsrc_t tp = tile_rsrc(M.payload, M.payload_bytes, cur.off);
+        Staged S;
+        stage_payload(tp, cnt, relane(lane0), S);
+        const uint32_t cnx = ct + kWaves < c_hi ? ct + kWaves : ct;
+        const TileMeta nxt = load_meta<kAligned>(M, a, cnx, relane(lane0), false);
+        uint2 xn[kR];
+        load_x_rows<kAligned, kR>(M, cnx, relane(lane0), xn);
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) stage_x_at(L.lut[r], L.xs[r], L.corr[r], xc[r], relane(lane0));
+        build_lists(L, cur, P, cnt, rows, cn, relane(lane0));
+        wave_lds_sync();
+        tile_products_rows<kR>(L, S, tp, cnt, relane(lane0), keys);
+        wave_lds_sync();
+        const uint32_t lane = relane(lane0);
+        if (lane < rows)
+            for (uint32_t jl = 0; jl < cn; ++jl) {
+                const uint32_t sb = (jl < 2 ? cur.s01 >> (16 * jl) : cur.s23 >> (16 * (jl - 2))) & 0xFFFFu;
+#pragma unroll
+                for (uint32_t r = 0; r < kR; ++r)
+                    acc[r] = fmaf(half_to_float(sb), L.part[r][jl * kTileRows + lane], acc[r]);
+            }
+        wave_lds_sync();
+        cur = nxt;
+#pragma unroll
+        for (uint32_t r = 0; r < kR; ++r) xc[r] = xn[r];
+    }
+    finish_rows<kWaves, kR>(M, lds, wave, a, split, r0, rows, relane(lane0), acc);
 }
 
 // ---------------------------------------------------------------- uniform width
@@ -1566,22 +1868,46 @@ struct GemvPlan {
     uint32_t waves, splits;
 };
 
-GemvPlan gemv_plan(uint32_t row_tiles, uint32_t col_tiles) {
+// Cost of a tile in gemv_rows (two rows of X) relative to the single-row
+// kernel, from the kernels' instruction counts per tile.
+constexpr double kRowsCost2 = 1.15;
+
+// Rows of X a GEMV wave takes in the small-batch GEMV route. Two rows per
+// decoded tile pay off only at m = 2 and where the launch is bound by issue
+// rate, from kRowsMinTiles tiles in the call (9B q+k+v 11.2 -> 10.1 us,
+// 14336x4096 gate+up 19.1 -> 16.8, LM head 19.9 -> 17.2). Smaller launches are
+// bound by each wave's latency, and halving their waves costs more than the
+// shared decoding saves (1.0B q+k+v, 768 tiles: 5.8 -> 6.8 us); at m = 3 and 4
+// one row per wave keeps more waves in flight and wins (LM head m = 3: 26.5
+// against 28.7 with pairs). Four rows per wave (211 VGPRs, two waves per
+// SIMD) lost everywhere the matrix cores do not already win.
+constexpr uint64_t kRowsMinTiles = 2048;
+inline uint32_t rows_per_wave(uint32_t m, uint64_t tiles) { return m == 2 && tiles >= kRowsMinTiles ? 2u : 1u; }
+
+// rows: rows of X per wave (gemv_rows); its LDS per wave is that many times
+// larger, so fewer workgroups are resident, and a tile costs more to handle.
+GemvPlan gemv_plan(uint32_t row_tiles, uint32_t col_tiles, uint32_t rows = 1) {
     constexpr uint32_t kCUs = 256;
-    const uint32_t waves[3] = {4, 8, 16}, per_cu[3] = {8, 4, 2};   // resident workgroups per CU (LDS bound)
+    constexpr uint32_t kLdsPerCu = 160u * 1024u;
+    const uint32_t waves[3] = {4, 8, 16};
+    const uint32_t lds_per_wave = rows == 1 ? sizeof(WaveLds) : sizeof(RowsLds<2>);
+    const double tile_cost = rows == 1 ? 1.1 : 1.1 * kRowsCost2;
     GemvPlan best{4, 1};
     double best_cost = 1e300;
     for (uint32_t w = 0; w < 3; ++w) {
         const uint32_t gw = waves[w];
+        const uint32_t per_cu = kLdsPerCu / (gw * lds_per_wave);   // resident workgroups per CU (LDS bound)
+        if (per_cu == 0) continue;
         for (uint32_t s = 1; s <= ceil_div(col_tiles, gw); ++s) {
             const double wgs = static_cast<double>(row_tiles) * s;
             const uint32_t ct_per = ceil_div(col_tiles, s);              // column tiles of a workgroup (at most)
             const uint32_t active = std::min(gw, ct_per);                // waves with a tile
             const uint32_t tpw = ceil_div(ct_per, gw);                   // tiles per wave (at most)
             const double cu_load = std::max(1.0, wgs / kCUs);            // workgroups per occupied CU
-            const double rounds = std::ceil(cu_load / per_cu[w]);
+            const double rounds = std::ceil(cu_load / per_cu);
             const double slots = tpw * (active / 4.0) * cu_load;
-            const double cost = 1.1 * slots + 2.5 * ((tpw - 1) + (rounds - 1)) + (s > 1 ? 1.4 + 0.23 * s : 0.0);
+            const double cost =
+                tile_cost * slots + 2.5 * ((tpw - 1) + (rounds - 1)) + (s > 1 ? 1.4 + 0.23 * s : 0.0);
             if (cost < best_cost) {
                 best_cost = cost;
                 best = GemvPlan{gw, s};
@@ -1634,13 +1960,24 @@ void gemv_dispatch(bool aligned, bool ragged, uint32_t ubits, uint32_t blocks, u
         hipLaunchKernelGGL((gemv_tiles<false, kWaves, false>), grid, block, 0, stream, B);
 }
 
+template <uint32_t kWaves, uint32_t kR>
+void gemv_rows_dispatch(bool aligned, uint32_t blocks, uint32_t used, const Batch &B, hipStream_t stream) {
+    const dim3 grid(blocks, used), block(kWaves * kWave);
+    if (aligned)
+        hipLaunchKernelGGL((gemv_rows<true, kWaves, kR>), grid, block, 0, stream, B);
+    else
+        hipLaunchKernelGGL((gemv_rows<false, kWaves, kR>), grid, block, 0, stream, B);
+}
+
 // One launch for up to VBQ_MAX_MULTI independent GEMVs; with h set, the two
 // matrices are gate and up (same shape, k > 0) and the launch writes
 // h = fp16(silu(gate x) * (up x)) instead of y.
 // no_alloc: the split scratch comes from the fixed array (vbq_gemv_multi_noalloc), never from hipMalloc.
+// rows = 2: every entry is two rows of X (row r at xs[i] + r k) against ws[i], written to ys[i] + r n,
+// by gemv_rows (no h, no fp16 y).
 vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                        uint32_t count, hipStream_t stream, uint16_t *h = nullptr, uint16_t *const *ys16 = nullptr,
-                       bool no_alloc = false) {
+                       bool no_alloc = false, uint32_t rows = 1) {
     Batch B{};
     uint32_t blocks = 0, total_row_tiles = 0, max_col_tiles = 0;
     bool aligned = true;
@@ -1650,7 +1987,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         total_row_tiles += ceil_div(w->n, kTileRows);
         max_col_tiles = std::max(max_col_tiles, ceil_div(w->k / VBQ_GROUP, kTileGroups));
     }
-    const GemvPlan plan = total_row_tiles ? gemv_plan(total_row_tiles, max_col_tiles) : GemvPlan{4, 1};
+    const GemvPlan plan = total_row_tiles ? gemv_plan(total_row_tiles, max_col_tiles, rows) : GemvPlan{4, 1};
     size_t counter_slots = 0, partial_total = 0;
     uint32_t used = 0;
     bool any_launch = false;
@@ -1658,7 +1995,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     // when they agree, the per-matrix dispatch when they differ
     uint32_t ubits = 0;
     bool first = true;
-    for (uint32_t i = 0; i < count; ++i) {
+    for (uint32_t i = 0; i < count && rows == 1; ++i) {
         if (ws[i]->n == 0 || ws[i]->k == 0) continue;
         const uint32_t b = ws[i]->uniform_bits;
         if (first || b == 0 || ubits == 0)
@@ -1696,7 +2033,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         if (M.groups % 4) aligned = false;
         if (M.splits > 1) {
             counter_slots += row_tiles;
-            partial_total += partial_bytes(M.splits, M.n);
+            partial_total += partial_bytes(M.splits * rows, M.n);
         }
     }
     if (h && used) {   // the pair region follows the split regions
@@ -1715,7 +2052,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
             M.counters = ctr;
             ctr += ceil_div(M.n, kTileRows);
             M.partial = reinterpret_cast<float *>(part);
-            part += partial_bytes(M.splits, M.n);
+            part += partial_bytes(M.splits * rows, M.n);
         }
         if (h) {
             B.h = h;
@@ -1727,7 +2064,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     for (uint32_t i = 0; i < count; ++i) {
         const vbq_matrix *w = ws[i];
         if (w->n == 0 || w->k != 0) continue;
-        const uint64_t cnt = w->n;
+        const uint64_t cnt = static_cast<uint64_t>(w->n) * rows;
         if (ys16)
             hipLaunchKernelGGL(fill_zero_u16, dim3(static_cast<uint32_t>((cnt + 255) / 256)), dim3(256), 0, stream,
                                ys16[i], cnt);
@@ -1744,7 +2081,14 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         B.first_block[i] = acc;
         if (i < used) acc += B.m[i].blocks;
     }
-    if (plan.waves == 16)
+    if (rows == 2) {
+        if (plan.waves == 16)
+            gemv_rows_dispatch<16, 2>(aligned, blocks, used, B, stream);
+        else if (plan.waves == 8)
+            gemv_rows_dispatch<8, 2>(aligned, blocks, used, B, stream);
+        else
+            gemv_rows_dispatch<4, 2>(aligned, blocks, used, B, stream);
+    } else if (plan.waves == 16)
         gemv_dispatch<16>(aligned, ragged, ubits, blocks, used, B, stream);
     else if (plan.waves == 8)
         gemv_dispatch<8>(aligned, ragged, ubits, blocks, used, B, stream);
@@ -1977,19 +2321,21 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
             }
             return gemm_launch(who, &w, &y, 1, x, m, s);
         }
-        // each input row as its own GEMV of one batched launch
+        // GEMV launches whose waves take rows_per_wave rows of X each
+        const uint32_t rw = rows_per_wave(m, tile_count(w));
         const vbq_matrix *ws[VBQ_MAX_MULTI];
         const uint16_t *xs[VBQ_MAX_MULTI];
         float *ys[VBQ_MAX_MULTI];
-        for (uint32_t m0 = 0; m0 < m; m0 += VBQ_MAX_MULTI) {
-            const uint32_t cnt = std::min(VBQ_MAX_MULTI, m - m0);
-            for (uint32_t i = 0; i < cnt; ++i) {
-                ws[i] = w;
-                xs[i] = x + static_cast<uint64_t>(m0 + i) * w->k;
-                ys[i] = y + static_cast<uint64_t>(m0 + i) * w->n;
+        uint32_t cnt = 0;
+        for (uint32_t r0 = 0; r0 < m; r0 += rw) {
+            ws[cnt] = w;
+            xs[cnt] = x + static_cast<uint64_t>(r0) * w->k;
+            ys[cnt] = y + static_cast<uint64_t>(r0) * w->n;
+            if (++cnt == VBQ_MAX_MULTI || r0 + rw >= m) {
+                st = gemv_launch(who, ws, xs, ys, cnt, s, nullptr, nullptr, false, rw);
+                if (st != VBQ_OK) return st;
+                cnt = 0;
             }
-            st = gemv_launch(who, ws, xs, ys, cnt, s);
-            if (st != VBQ_OK) return st;
         }
         return VBQ_OK;
     });
@@ -1998,8 +2344,9 @@ extern "C" vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x
 // Small-batch products of several matrices that read the same rows of X
 // (q, k, v; gate, up). The small-batch rule is applied to all of them
 // together: on the matrix cores they share launches of up to kGemmMulti
-// matrices (the launch's latency is paid once), otherwise each becomes one
-// GEMV per row, and those share launches of up to VBQ_MAX_MULTI GEMVs,
+// matrices (the launch's latency is paid once), otherwise each becomes
+// GEMVs of one or two rows of X per wave (rows_per_wave, on the tiles of
+// all of them), and those share launches of up to VBQ_MAX_MULTI entries,
 // matrix by matrix and row by row.
 extern "C" vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, const uint16_t *x, uint32_t m,
                                                 float *const *ys, uint32_t count, void *stream) {
@@ -2021,18 +2368,19 @@ extern "C" vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, con
         (void)hipGetLastError();
         hipStream_t s = static_cast<hipStream_t>(stream);
         const uint32_t k = ws[0]->k;
+        uint64_t tiles = 0;
+        for (uint32_t i = 0; i < count; ++i) tiles += tile_count(ws[i]);
+        const uint32_t rw = rows_per_wave(m, tiles);
         const vbq_matrix *gw[VBQ_MAX_MULTI];
         const uint16_t *gx[VBQ_MAX_MULTI];
         float *gy[VBQ_MAX_MULTI];
         uint32_t pending = 0;
         auto flush = [&]() -> vbq_status {
-            const vbq_status st = pending ? gemv_launch(who, gw, gx, gy, pending, s) : VBQ_OK;
+            const vbq_status st = pending ? gemv_launch(who, gw, gx, gy, pending, s, nullptr, nullptr, false, rw) : VBQ_OK;
             pending = 0;
             return st;
         };
         // the rule on all the matrices together: on the matrix cores they share one launch
-        uint64_t tiles = 0;
-        for (uint32_t i = 0; i < count; ++i) tiles += tile_count(ws[i]);
         if (uses_matrix_cores(tiles, m)) {
             const vbq_matrix *mw[kGemmMulti];
             float *my[kGemmMulti];
@@ -2061,7 +2409,7 @@ extern "C" vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, con
         for (uint32_t i = 0; i < count; ++i) {
             const vbq_matrix *w = ws[i];
             if (w->n == 0) continue;
-            for (uint32_t r = 0; r < m; ++r) {
+            for (uint32_t r = 0; r < m; r += rw) {
                 gw[pending] = w;
                 gx[pending] = x + static_cast<uint64_t>(r) * k;
                 gy[pending] = ys[i] + static_cast<uint64_t>(r) * w->n;

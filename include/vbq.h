@@ -246,8 +246,10 @@ VBQ_API vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *up,
  * (overwritten). Runs on the matrix cores (each group's codes decoded once,
  * 16x16x32 fp16 products, fp32 accumulation) when m > 16, or when m >= 4 and
  * m * m times the matrix's tile count (64x256 weights per tile) is at least
- * 85000; otherwise as one batch-1 GEMV per row of X in one launch on the vector
- * units (the faster choice, measured). Scratch as for vbq_gemv_multi.
+ * 85000; otherwise on the vector units as GEMVs in one launch: one row of X
+ * per wave, or, at m = 2 on a matrix of at least 2048 tiles, both rows per
+ * wave (each tile decoded once for both); the faster choices, measured.
+ * Scratch as for vbq_gemv_multi.
  * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN, OFFSETS, HIP. */
 VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, uint32_t m, float *y,
                                void *stream);
@@ -259,9 +261,11 @@ VBQ_API vbq_status vbq_gemm_smallbatch(const vbq_matrix *w, const uint16_t *x, u
  * matrices (every ws[i] has the same k); ys[i]: device fp32 [m][n_i]. The
  * small-batch rule is applied to the matrices together (their tile counts
  * summed): on the matrix cores they share launches of up to 8 matrices,
- * whose latency they then pay once; otherwise each runs as one GEMV per
- * (matrix, row), and those share launches of up to VBQ_MAX_MULTI GEMVs, so a
- * layer's projections at batch 8 take as many launches as at batch 1. The
+ * whose latency they then pay once; otherwise each runs as GEMVs of one row
+ * of X per wave (both rows at m = 2 when the matrices have at least 2048
+ * tiles together), and those share launches of up to VBQ_MAX_MULTI
+ * (matrix, rows) entries, so a layer's projections at batch 8 take as many
+ * launches as at batch 1. The
  * results agree with vbq_gemm_smallbatch on each matrix within the GEMV
  * tolerance (the two may take different paths). Asynchronous on `stream`;
  * scratch as for vbq_gemv_multi. Errors: NULL, ABI, SHAPE (m, or the k's

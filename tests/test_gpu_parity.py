@@ -121,10 +121,35 @@ def test_gemm_matches_oracle(V, torch_mod, m):
     assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"gemm m={m}")
 
 
+# The GEMV route of the small-batch call: at m = 2 on calls of at least 2048 tiles its waves take both
+# rows of X per decoded tile; otherwise (m = 3, 5, 8; 5632 x 2048 has 704 tiles) one row per wave. Shapes:
+# 256 x 8 tiles, 64 x 32 (split row tiles), a ragged 2200 x 15424 (35 x 61 tiles, k % 256 != 0) and
+# 8 x 256 tiles (many splits). Each result against the oracle; a second call gives the same bits; the
+# y row after the m rows stays untouched.
+@pytest.mark.parametrize("n,k,m", [(16384, 2048, 2), (16384, 2048, 3), (4096, 8192, 2), (4096, 8192, 5),
+                                   (2200, 15424, 2), (512, 65536, 2), (5632, 2048, 2), (5632, 2048, 8)])
+def test_gemv_rows_route(V, torch_mod, n, k, m):
+    torch = torch_mod
+    print_case(test="gemv_rows", n=n, k=k, m=m)
+    bits, codes, scales, p = make_case((n, k, m, 41), n, k, W.STD_MIX)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x((n, k, m, 42), k, m)
+    xt = torch.from_numpy(np.ascontiguousarray(x).view(np.float16)).cuda()
+    y = torch.full((m + 1, n), float("nan"), dtype=torch.float32, device="cuda")
+    V.vbq_gemm_smallbatch(dm, xt, y[:m])
+    torch.cuda.synchronize()
+    first = y.cpu().numpy()
+    assert np.isnan(first[m]).all()
+    assert_within_tolerance(first[:m].astype(np.float64), oracle.gemm(p, x), x, scales, f"rows {n}x{k} m={m}")
+    V.vbq_gemm_smallbatch(dm, xt, y[:m])
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy()[:m], first[:m])
+
+
 @pytest.mark.parametrize("m", [4, 8, 12, 16])
 def test_gemm_both_paths_below_17_rows(V, torch_mod, m):
     # 1280x8192 has 640 tiles: m = 12 and 16 reach the matrix cores (m * m * tiles >= 85000),
-    # m = 4 and 8 run as one GEMV per row; 97x1088 (10 tiles) stays on the GEMVs
+    # m = 4 and 8 run on the GEMV route (four rows of X per wave); 97x1088 (10 tiles) stays on it
     for n, k in ((1280, 8192), (97, 1088)):
         print_case(test="gemm_paths", n=n, k=k, m=m)
         bits, codes, scales, p = make_case((m, n, k, 31), n, k, W.STD_MIX)
@@ -437,15 +462,17 @@ def test_grouped_recipe_head(V, torch_mod):
 
 @pytest.mark.parametrize("m, k, shapes", [
     (1, 2048, [97, 8192, 300, 64, 1000]),
-    (8, 2048, [97, 8192, 300, 64, 1000]),      # 1216 tiles: 64 x 1216 < 85000, GEMVs (40 per matrix set)
+    (8, 2048, [97, 8192, 300, 64, 1000]),      # 1216 tiles: 64 x 1216 < 85000, GEMV route (two 4-row entries each)
     (12, 2048, [97, 8192, 300, 64, 1000]),     # 144 x 1216 >= 85000: one matrix-core launch for all five
     (20, 2048, [97, 8192, 300, 64, 1000]),
     (20, 1088, [97, 130, 64, 300, 33, 200, 64, 1000, 70, 5]),   # ten matrices: two launches; k % 256 != 0
+    (2, 4096, [4096, 4096, 4096]),             # 3072 tiles: both rows of X per GEMV wave
+    (3, 4096, [97, 16384, 300]),               # 4208 tiles: one row per GEMV wave
 ])
 def test_gemm_smallbatch_multi_matches_oracle(V, torch_mod, m, k, shapes):
     # matrices sharing the m rows of X, as q/k/v and gate/up do, with ragged row counts: the small-batch
     # rule applies to all of them together, so they share matrix-core launches (up to eight matrices
-    # each) or GEMV launches (up to 32 products each)
+    # each) or GEMV launches (up to 32 entries of up to four rows each)
     torch = torch_mod
     print_case(test="gemm_multi", m=m, k=k, shapes=shapes)
     x = W.draw_x((90, m), k, m)

@@ -23,8 +23,10 @@ def _assembly(tmp_path_factory, name):
     return out.read_text()
 
 
-@pytest.mark.parametrize("source, kernel_names", [("vbq_device.hip", ("gemv_tiles", "gemv_uniform", "unpack_tiles", "gemm_frag")),
-                                                  ("vbq_quantize.hip", ("quantize_groups",))])
+@pytest.mark.parametrize("source, kernel_names", [
+    ("vbq_device.hip", ("gemv_tiles", "gemv_rows", "gemv_uniform", "unpack_tiles", "gemm_frag")),
+    ("vbq_quantize.hip", ("quantize_groups",)),
+])
 def test_kernels_do_not_spill(tmp_path_factory, source, kernel_names):
     assembly = _assembly(tmp_path_factory, source)
     sizes = dict(re.findall(r"\.set (\S+)\.private_seg_size, (\d+)", assembly))
