@@ -1191,8 +1191,9 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
 }
 
 // Decoded codes of every group, written at its natural position; the same
-// field decoders as the product kernels (fp16 pairs 1024 + 2^s*u, then exact
-// integer recovery) plus the sign bits of 1-bit groups.
+// field decoders as the GEMV kernels (fp16 pairs whose halves are the
+// subnormals f u 2^-24, then exact integer recovery) plus the sign bits of
+// 1-bit groups.
 template <bool kAligned>
 __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict__ codes) {
     __shared__ WaveLds L;
