@@ -560,3 +560,32 @@ def test_multi_launch_of_unequal_matrices(V, torch_mod):
         for (dm, p, scales, x), y in zip(cases, ys):
             assert_within_tolerance(y.cpu().numpy()[None], oracle.gemv(p, x[0])[None], x, scales,
                                     f"{dm.n}x{dm.k} in a launch of unequal matrices")
+
+
+# Seeded random shapes across every route of the GEMV / small-batch call: n from 1 row to a few thousand,
+# k any multiple of 64 (ragged column tiles included), m from 1 to 40 (single-row and two-row GEMVs,
+# matrix cores), widths from a random mix per case. Each against the oracle.
+def _random_cases(count=24):
+    rng = np.random.default_rng(20261204)
+    mixes = [W.STD_MIX, W.FIRST_MLP_MIX, W.HEAD_MIX, {1: 0.25, 2: 0.25, 4: 0.25, 8: 0.25}, {8: 0.5, 1: 0.5}]
+    cases = []
+    while len(cases) < count:
+        n = int(rng.integers(1, 4097))
+        k = 64 * int(rng.integers(1, 161))
+        m = int(rng.choice([1, 1, 2, 2, 3, 5, 8, 16, 17, 40]))
+        if n * k * m > 60_000_000:
+            continue
+        cases.append((len(cases), n, k, m, int(rng.integers(len(mixes)))))
+    return cases, mixes
+
+
+_CASES, _MIXES = _random_cases()
+
+
+@pytest.mark.parametrize("idx,n,k,m,mix", _CASES)
+def test_random_shapes_match_oracle(V, torch_mod, idx, n, k, m, mix):
+    print_case(test="random_shapes", idx=idx, n=n, k=k, m=m, mix=mix)
+    bits, codes, scales, p = make_case((idx, n, k, 51), n, k, _MIXES[mix])
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x((idx, n, k, 52), k, m)
+    assert_within_tolerance(gpu_gemm(V, torch_mod, dm, x), oracle.gemm(p, x), x, scales, f"random {idx}")
