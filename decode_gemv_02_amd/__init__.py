@@ -21,7 +21,7 @@ import torch  # import before the library so it binds to the HIP runtime torch h
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libvbq.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 GROUP = 64
 MAX_K = 65536
 MAX_BATCH = 64
@@ -45,7 +45,8 @@ class VbqSizes(ctypes.Structure):
 class VbqMatrix(ctypes.Structure):
     _fields_ = [("abi_version", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
                 ("payload_bytes", ctypes.c_uint32), ("widths", ctypes.c_void_p), ("scales", ctypes.c_void_p),
-                ("tile_offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p), ("uniform_bits", ctypes.c_uint32)]
+                ("tile_offsets", ctypes.c_void_p), ("payload", ctypes.c_void_p), ("uniform_bits", ctypes.c_uint32),
+                ("stream_index", ctypes.c_void_p)]
 
 
 class VbqError(RuntimeError):
@@ -84,6 +85,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_uniform_width.argtypes = [ctypes.POINTER(VbqMatrix), ctypes.POINTER(U32)]
     lib.vbq_gemm_smallbatch.argtypes = [ctypes.POINTER(VbqMatrix), P, U32, P, P]
     lib.vbq_unpack_codes.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
+    lib.vbq_stream_index_bytes.argtypes = [U32, U32, ctypes.POINTER(ctypes.c_uint64)]
+    lib.vbq_build_stream_index.argtypes = [ctypes.POINTER(VbqMatrix), P, P]
     lib.vbq_quantize.argtypes = [U32, U32, P, P, P, P, P]
     lib.vbq_soft_quantize.argtypes = [U32, U32, P, P, P, ctypes.c_float, P, P, P, P, P]
     lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
@@ -100,7 +103,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
               lib.vbq_check_padding, lib.vbq_container_size, lib.vbq_container_write, lib.vbq_container_open,
               lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16,
               lib.vbq_soft_quantize, lib.vbq_gemv_multi_noalloc, lib.vbq_recipe_head_tiers,
-              lib.vbq_probe_stream_read, lib.vbq_probe_dense_gemv, lib.vbq_gemm_smallbatch_multi):
+              lib.vbq_probe_stream_read, lib.vbq_probe_dense_gemv, lib.vbq_gemm_smallbatch_multi,
+              lib.vbq_stream_index_bytes, lib.vbq_build_stream_index):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -189,9 +193,11 @@ def vbq_validate_host(m: HostMatrix) -> None:
 class DeviceMatrix:
     """Packed matrix resident in device memory (torch tensors own the bytes)."""
 
-    def __init__(self, host: HostMatrix, device="cuda", uniform: bool = True):
+    def __init__(self, host: HostMatrix, device="cuda", uniform: bool = True, stream_index: bool = True):
         """uniform: declare the matrix's single width (when it has one) so launches take the
-        uniform-width kernels; False keeps it on the mixed-width kernel."""
+        uniform-width kernels; False keeps it on the mixed-width kernel. stream_index: build the
+        matrix's stream index on the device (vbq_build_stream_index, 264 bytes per tile), which the
+        mixed-width kernel then reads instead of deriving each tile's counts and list."""
         self.n, self.k = host.n, host.k
         self.uniform_bits = vbq_uniform_width(host) if uniform else 0
         self.payload_bytes = host.payload_bytes
@@ -208,7 +214,15 @@ class DeviceMatrix:
         self._payload = up(host.payload)
         self.struct = VbqMatrix(ABI_VERSION, self.n, self.k, self.payload_bytes, self._widths.data_ptr(),
                                 self._scales.data_ptr(), self._offsets.data_ptr(), self._payload.data_ptr(),
-                                self.uniform_bits)
+                                self.uniform_bits, None)
+        self._index = None
+        if stream_index and self.n and self.k:
+            self._index = torch.empty(vbq_stream_index_bytes(self.n, self.k), dtype=torch.uint8, device=dev)
+            s = torch.cuda.current_stream(dev)
+            _check(lib.vbq_build_stream_index(ctypes.byref(self.struct), self._index.data_ptr(), int(s.cuda_stream)))
+            s.synchronize()   # built once; later calls may run on any stream
+            self.struct.stream_index = self._index.data_ptr()
+        self.index_bytes = 0 if self._index is None else self._index.numel()
 
 
 def vbq_gemv(w: DeviceMatrix, x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
@@ -231,6 +245,19 @@ def vbq_gemv_swiglu(gate: DeviceMatrix, up: DeviceMatrix, x: torch.Tensor, h: to
 
 def vbq_tile_count(n: int, k: int) -> int:
     return int(lib.vbq_tile_count(n, k))
+
+
+def vbq_stream_index_bytes(n: int, k: int) -> int:
+    out = ctypes.c_uint64()
+    _check(lib.vbq_stream_index_bytes(n, k, ctypes.byref(out)))
+    return int(out.value)
+
+
+def vbq_build_stream_index(w: DeviceMatrix, out: torch.Tensor, stream=None) -> torch.Tensor:
+    """Write w's stream index to the uint8 device tensor out (vbq_stream_index_bytes(n, k) bytes)."""
+    assert out.dtype == torch.uint8 and out.is_contiguous() and out.numel() >= vbq_stream_index_bytes(w.n, w.k)
+    _check(lib.vbq_build_stream_index(ctypes.byref(w.struct), out.data_ptr(), _stream_handle(stream, w.device)))
+    return out
 
 
 def _multi_args(ws, xs, ys, ydtype):

@@ -181,6 +181,7 @@ struct MatArgs {
     uint32_t payload_bytes;
     uint32_t ubits;   // the matrix's declared single width, or 0
     uint16_t *y16;    // when set, y is stored here as fp16 (nearest even) instead of fp32 to y
+    const uint8_t *index;   // the matrix's stream index (gemv_tiles<..., kIndexed = true>), else NULL
 };
 
 
@@ -256,7 +257,7 @@ struct TileMeta {
 
 template <bool kAligned, class Args>
 __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_t ct, uint32_t lane,
-                                              bool with_x) {
+                                              bool with_x, bool with_codes = true) {
     TileMeta t;
     const uint32_t r0 = a * kTileRows, rows = min(kTileRows, M.n - r0);
     // kAligned: the group count is a multiple of 4, so every tile has four columns
@@ -283,17 +284,19 @@ __device__ __forceinline__ TileMeta load_meta(const Args &M, uint32_t a, uint32_
         const uint32_t lr = min(lane, rows - 1);
         if (kAligned || cn == kTileGroups) {
             // base is a multiple of 4: one width byte and one 8-byte scale load per row
-            t.codes = M.widths[(base >> 2) + lr];
+            if (with_codes) t.codes = M.widths[(base >> 2) + lr];
             const uint2 sv =
                 *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(M.scales) + 2u * (base + 4u * lr));
             t.s01 = sv.x;
             t.s23 = sv.y;
         } else {
             const uint64_t g = base + static_cast<uint64_t>(lr) * cn;
-            const uint64_t wbytes = (static_cast<uint64_t>(M.n) * M.groups + 3) >> 2;
-            uint32_t two = M.widths[g >> 2];
-            if ((g >> 2) + 1 < wbytes) two |= static_cast<uint32_t>(M.widths[(g >> 2) + 1]) << 8;
-            t.codes = (two >> (2 * (g & 3))) & ((1u << (2 * cn)) - 1u);
+            if (with_codes) {
+                const uint64_t wbytes = (static_cast<uint64_t>(M.n) * M.groups + 3) >> 2;
+                uint32_t two = M.widths[g >> 2];
+                if ((g >> 2) + 1 < wbytes) two |= static_cast<uint32_t>(M.widths[(g >> 2) + 1]) << 8;
+                t.codes = (two >> (2 * (g & 3))) & ((1u << (2 * cn)) - 1u);
+            }
             uint32_t sc[4] = {0u, 0u, 0u, 0u};
             for (uint32_t q = 0; q < cn; ++q) sc[q] = M.scales[g + q];
             t.s01 = sc[0] | (sc[1] << 16);
@@ -700,13 +703,45 @@ __device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M
     swiglu_pair(B, which, a, r0 + lane, lane < rows, M.n, lane, sum);
 }
 
+// A tile's entry in the stream index: the list bytes 4 lane .. 4 lane + 3 and
+// the per-width counts (uniform, a scalar load like the tile offset).
+struct TileIndex {
+    uint32_t list4;
+    uint32_t c01, c23;   // counts of width codes 0 | 1 << 16, 2 | 3 << 16
+};
+
+__device__ __forceinline__ TileIndex load_index(const MatArgs &M, uint32_t tile, uint32_t lane) {
+    TileIndex t;
+    t.list4 = reinterpret_cast<const uint32_t *>(M.index + 256ull * tile)[lane];
+    const uint64_t tiles = static_cast<uint64_t>((M.n + kTileRows - 1) / kTileRows) * M.col_tiles;
+    typedef const __attribute__((address_space(4))) uint32_t *const_u32p;
+    const const_u32p c = (const_u32p)(reinterpret_cast<uintptr_t>(M.index + 256ull * tiles));
+    t.c01 = c[2ull * tile];
+    t.c23 = c[2ull * tile + 1];
+    return t;
+}
+
+// The counts of an index entry, each held to what is left of the tile's 256
+// groups, so that a damaged index cannot move a bucket past the list.
+__device__ __forceinline__ void index_counts(const TileIndex &t, uint32_t cnt[4]) {
+    const uint32_t c0 = min(t.c01 & 0xFFFFu, 256u);
+    const uint32_t c1 = min(t.c01 >> 16, 256u - c0);
+    const uint32_t c2 = min(t.c23 & 0xFFFFu, 256u - c0 - c1);
+    cnt[0] = c0;
+    cnt[1] = c1;
+    cnt[2] = c2;
+    cnt[3] = min(t.c23 >> 16, 256u - c0 - c1 - c2);
+}
+
 // kWaves waves per workgroup (4, 8 or 16) share one row tile; the LDS
 // (4992 B per wave) allows 8, 4 or 2 such workgroups per CU, eight waves
 // per SIMD, and the registers are held to the 64 that allow the same.
 // kExit: the launch's matrices differ in size, so workgroups past a smaller matrix's end leave at once
 // (all seven 9B-layer matrices in one launch: 32.9 -> 23.7 us); launches of equal matrices have none and
 // skip the test, which would put a dependent load ahead of the others (about 0.7 us a step).
-template <bool kAligned, uint32_t kWaves, bool kExit>
+// kIndexed: every matrix of the launch has a stream index; a tile's counts and list are read from it
+// instead of being derived from the width codes (the scan and list build, about 80 VALU per tile).
+template <bool kAligned, uint32_t kWaves, bool kExit, bool kIndexed>
 __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(8, 8))) void gemv_tiles(Batch B) {
     __shared__ WaveLds lds[kWaves];
     // which matrix, row tile and split this block serves (uniform)
@@ -730,20 +765,32 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
     // metadata loads are unconditional (a wave without a next tile reloads its
     // own): a conditional load would make its result a branch merge, and the
     // merge copy would wait for the load
-    TileMeta cur = load_meta<kAligned>(M, a, ct < c_hi ? ct : c_lo, relane(lane0), true);
+    const uint32_t ct0 = ct < c_hi ? ct : c_lo;
+    TileMeta cur = load_meta<kAligned>(M, a, ct0, relane(lane0), true, !kIndexed);
+    TileIndex cix{};
+    if constexpr (kIndexed) cix = load_index(M, a * M.col_tiles + ct0, relane(lane0));
     for (; ct < c_hi; ct += kWaves) {
         const uint32_t cn = kAligned ? kTileGroups : min(kTileGroups, M.groups - ct * kTileGroups);
         // counts first: the payload loads leave before the tables and lists are built
         uint32_t cnt[4];
-        const TileScan P = tile_scan(cur, rows, cn, relane(lane0), cnt);
+        TileScan P;
+        if constexpr (kIndexed)
+            index_counts(cix, cnt);
+        else
+            P = tile_scan(cur, rows, cn, relane(lane0), cnt);
         const rsrc_t tp = tile_rsrc(M.payload, M.payload_bytes, cur.off);
         Staged S;
         stage_payload(tp, cnt, relane(lane0), S);
         // the next tile's metadata travels while this tile computes
-        const TileMeta nxt =
-            load_meta<kAligned>(M, a, ct + kWaves < c_hi ? ct + kWaves : ct, relane(lane0), true);
+        const uint32_t cnx = ct + kWaves < c_hi ? ct + kWaves : ct;
+        const TileMeta nxt = load_meta<kAligned>(M, a, cnx, relane(lane0), true, !kIndexed);
+        TileIndex nix{};
+        if constexpr (kIndexed) nix = load_index(M, a * M.col_tiles + cnx, relane(lane0));
         stage_x(L, cur.xv, relane(lane0));
-        build_lists(L, cur, P, cnt, rows, cn, relane(lane0));
+        if constexpr (kIndexed)
+            reinterpret_cast<uint32_t *>(L.list)[relane(lane0)] = cix.list4;
+        else
+            build_lists(L, cur, P, cnt, rows, cn, relane(lane0));
         wave_lds_sync();
         tile_products(L, S, tp, cnt, relane(lane0), keys);
         wave_lds_sync();
@@ -755,6 +802,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
             }
         wave_lds_sync();
         cur = nxt;
+        if constexpr (kIndexed) cix = nix;
     }
     finish_row_tile<kWaves>(B, M, blockIdx.y, lds, wave, spare, a, split, r0, rows, relane(lane0), acc);
 }
@@ -1276,6 +1324,32 @@ __global__ __launch_bounds__(64) void unpack_tiles(MatArgs M, int8_t *__restrict
     }
 }
 
+// The stream index (layout in vbq.h): one wave per tile derives the tile's
+// per-width counts and its list of groups in payload order with the mixed
+// kernel's own tile_scan and build_lists, and stores them.
+template <bool kAligned>
+__global__ __launch_bounds__(64) void stream_index_tiles(MatArgs M, uint8_t *__restrict__ index, uint64_t tiles) {
+    __shared__ WaveLds L;
+    const uint32_t lane = threadIdx.x;
+    const uint32_t a = blockIdx.x / M.col_tiles, ct = blockIdx.x % M.col_tiles;
+    const uint32_t rows = min(kTileRows, M.n - a * kTileRows);
+    const uint32_t cn = min(kTileGroups, M.groups - ct * kTileGroups);
+    const TileMeta t = load_meta<kAligned>(M, a, ct, lane, false);
+    uint32_t cnt[4];
+    const TileScan P = tile_scan(t, rows, cn, lane, cnt);
+    reinterpret_cast<uint32_t *>(L.list)[lane] = 0u;   // a smaller tile's unused entries stay 0
+    wave_lds_sync();
+    build_lists(L, t, P, cnt, rows, cn, lane);
+    wave_lds_sync();
+    reinterpret_cast<uint32_t *>(index + 256ull * blockIdx.x)[lane] = reinterpret_cast<const uint32_t *>(L.list)[lane];
+    if (lane == 0) {
+        uint2 c;
+        c.x = cnt[0] | (cnt[1] << 16);
+        c.y = cnt[2] | (cnt[3] << 16);
+        reinterpret_cast<uint2 *>(index + 256ull * tiles)[blockIdx.x] = c;
+    }
+}
+
 __global__ void fill_zero(float *__restrict__ y, uint64_t count) {
     const uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < count) y[i] = 0.f;
@@ -1744,7 +1818,8 @@ vbq_status check_matrix(const char *who, const vbq_matrix *w) {
                     w->payload_bytes, w->n, w->k);
     if (!w->tile_offsets || !w->widths || !w->scales || !w->payload)
         return fail(VBQ_ERR_NULL, "%s: widths, scales, tile_offsets or payload is NULL", who);
-    if (!aligned16(w->tile_offsets) || !aligned16(w->widths) || !aligned16(w->scales) || !aligned16(w->payload))
+    if (!aligned16(w->tile_offsets) || !aligned16(w->widths) || !aligned16(w->scales) || !aligned16(w->payload) ||
+        !aligned16(w->stream_index))
         return fail(VBQ_ERR_ALIGN, "%s: a matrix array is not 16-byte aligned", who);
     const uint32_t b = w->uniform_bits;
     if (b != 0 && b != 1 && b != 2 && b != 4 && b != 8)
@@ -1940,9 +2015,23 @@ void gemv_dispatch_uniform(bool aligned, uint32_t blocks, uint32_t used, const B
 // they differ; 0 when some matrix declares none (the mixed-width kernel)
 constexpr uint32_t kPerMatrix = 0xFFu;
 
+template <uint32_t kWaves, bool kIndexed>
+void gemv_dispatch_mixed(bool aligned, bool ragged, dim3 grid, const Batch &B, hipStream_t stream) {
+    const dim3 block(kWaves * kWave);
+    if (aligned && ragged)
+        hipLaunchKernelGGL((gemv_tiles<true, kWaves, true, kIndexed>), grid, block, 0, stream, B);
+    else if (aligned)
+        hipLaunchKernelGGL((gemv_tiles<true, kWaves, false, kIndexed>), grid, block, 0, stream, B);
+    else if (ragged)
+        hipLaunchKernelGGL((gemv_tiles<false, kWaves, true, kIndexed>), grid, block, 0, stream, B);
+    else
+        hipLaunchKernelGGL((gemv_tiles<false, kWaves, false, kIndexed>), grid, block, 0, stream, B);
+}
+
+// indexed: the mixed-width kernel reads every matrix's stream index
 template <uint32_t kWaves>
-void gemv_dispatch(bool aligned, bool ragged, uint32_t ubits, uint32_t blocks, uint32_t used, const Batch &B,
-                   hipStream_t stream) {
+void gemv_dispatch(bool aligned, bool ragged, bool indexed, uint32_t ubits, uint32_t blocks, uint32_t used,
+                   const Batch &B, hipStream_t stream) {
     if (ubits == kPerMatrix) {   // 1D grid: every matrix's workgroups, back to back
         const uint32_t total = B.first_block[VBQ_MAX_MULTI];
         if (aligned)
@@ -1958,15 +2047,10 @@ void gemv_dispatch(bool aligned, bool ragged, uint32_t ubits, uint32_t blocks, u
         case 8: gemv_dispatch_uniform<8, kWaves>(aligned, blocks, used, B, stream); return;
         default: break;
     }
-    const dim3 grid(blocks, used), block(kWaves * kWave);
-    if (aligned && ragged)
-        hipLaunchKernelGGL((gemv_tiles<true, kWaves, true>), grid, block, 0, stream, B);
-    else if (aligned)
-        hipLaunchKernelGGL((gemv_tiles<true, kWaves, false>), grid, block, 0, stream, B);
-    else if (ragged)
-        hipLaunchKernelGGL((gemv_tiles<false, kWaves, true>), grid, block, 0, stream, B);
+    if (indexed)
+        gemv_dispatch_mixed<kWaves, true>(aligned, ragged, dim3(blocks, used), B, stream);
     else
-        hipLaunchKernelGGL((gemv_tiles<false, kWaves, false>), grid, block, 0, stream, B);
+        gemv_dispatch_mixed<kWaves, false>(aligned, ragged, dim3(blocks, used), B, stream);
 }
 
 template <uint32_t kWaves, uint32_t kR>
@@ -2026,6 +2110,7 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.x = xs[i];
         M.y = ys ? ys[i] : nullptr;
         M.y16 = ys16 ? ys16[i] : nullptr;
+        M.index = w->stream_index;
         M.n = w->n;
         M.groups = w->k / VBQ_GROUP;
         M.col_tiles = ceil_div(M.groups, kTileGroups);
@@ -2085,6 +2170,8 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
     if (used == 0) return any_launch ? launched(who) : VBQ_OK;
     bool ragged = false;   // some matrix has fewer workgroups than the grid is wide
     for (uint32_t i = 0; i < used; ++i) ragged = ragged || B.m[i].blocks != blocks;
+    bool indexed = rows == 1;   // the mixed-width kernel reads stream indexes when every matrix has one
+    for (uint32_t i = 0; i < used; ++i) indexed = indexed && B.m[i].index != nullptr;
     uint32_t acc = 0;
     for (uint32_t i = 0; i <= VBQ_MAX_MULTI; ++i) {
         B.first_block[i] = acc;
@@ -2098,11 +2185,11 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         else
             gemv_rows_dispatch<4, 2>(aligned, blocks, used, B, stream);
     } else if (plan.waves == 16)
-        gemv_dispatch<16>(aligned, ragged, ubits, blocks, used, B, stream);
+        gemv_dispatch<16>(aligned, ragged, indexed, ubits, blocks, used, B, stream);
     else if (plan.waves == 8)
-        gemv_dispatch<8>(aligned, ragged, ubits, blocks, used, B, stream);
+        gemv_dispatch<8>(aligned, ragged, indexed, ubits, blocks, used, B, stream);
     else
-        gemv_dispatch<4>(aligned, ragged, ubits, blocks, used, B, stream);
+        gemv_dispatch<4>(aligned, ragged, indexed, ubits, blocks, used, B, stream);
     return launched(who);
 }
 
@@ -2429,6 +2516,38 @@ extern "C" vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, con
             }
         }
         return flush();
+    });
+}
+
+extern "C" vbq_status vbq_build_stream_index(const vbq_matrix *w, uint8_t *index_out, void *stream) {
+    return vbq::guarded("vbq_build_stream_index", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_build_stream_index";
+        vbq_status st = check_matrix(who, w);
+        if (st != VBQ_OK) return st;
+        if (w->n == 0 || w->k == 0) return VBQ_OK;
+        if (!index_out) return fail(VBQ_ERR_NULL, "%s: index_out is NULL", who);
+        if (!aligned16(index_out)) return fail(VBQ_ERR_ALIGN, "%s: index_out is not 16-byte aligned", who);
+        (void)hipGetLastError();
+        MatArgs M{};
+        M.payload_bytes = w->payload_bytes;
+        M.widths = w->widths;
+        M.scales = w->scales;
+        M.tile_offsets = w->tile_offsets;
+        M.payload = w->payload;
+        M.n = w->n;
+        M.groups = w->k / VBQ_GROUP;
+        M.col_tiles = ceil_div(M.groups, kTileGroups);
+        M.splits = 1;
+        // fewer than 2^29 groups (the payload fits 32-bit offsets at 8 bytes or more a group), so the tile
+        // count fits the grid
+        const uint32_t tiles = ceil_div(M.n, kTileRows) * M.col_tiles;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (M.groups % 4 == 0)
+            hipLaunchKernelGGL(stream_index_tiles<true>, dim3(tiles), dim3(64), 0, s, M, index_out, uint64_t(tiles));
+        else
+            hipLaunchKernelGGL(stream_index_tiles<false>, dim3(tiles), dim3(64), 0, s, M, index_out, uint64_t(tiles));
+        return launched(who);
     });
 }
 

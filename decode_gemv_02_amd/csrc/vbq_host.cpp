@@ -146,6 +146,17 @@ uint64_t place_groups(uint32_t n, uint32_t G, WidthFn width, uint64_t *group_off
 
 extern "C" uint64_t vbq_tile_count(uint32_t n, uint32_t k) { return tiles_of(n, k / VBQ_GROUP); }
 
+// 256 list bytes and 8 count bytes per tile
+extern "C" vbq_status vbq_stream_index_bytes(uint32_t n, uint32_t k, uint64_t *bytes_out) {
+    return vbq::guarded("vbq_stream_index_bytes", [&]() -> vbq_status {
+        vbq::clear_error();
+        if (!bytes_out) return fail(VBQ_ERR_NULL, "vbq_stream_index_bytes: bytes_out is NULL");
+        if (k % VBQ_GROUP) return fail(VBQ_ERR_SHAPE, "vbq_stream_index_bytes: k=%u is not a multiple of 64", k);
+        *bytes_out = 264u * tiles_of(n, k / VBQ_GROUP);
+        return VBQ_OK;
+    });
+}
+
 extern "C" vbq_status vbq_pack_sizes(uint32_t n, uint32_t k, const uint8_t *bits, vbq_sizes *out) {
     return vbq::guarded("vbq_pack_sizes", [&]() -> vbq_status {
         vbq::clear_error();

@@ -85,7 +85,7 @@ extern "C" {
 /* Only the entry points below are exported from the shared library. */
 #define VBQ_API __attribute__((visibility("default")))
 
-#define VBQ_ABI_VERSION 2u
+#define VBQ_ABI_VERSION 3u
 #define VBQ_GROUP 64u
 #define VBQ_TILE_ROWS 64u
 #define VBQ_TILE_GROUPS 4u
@@ -144,11 +144,40 @@ typedef struct vbq_matrix {
      * vbq_validate_host checks it; device entry points check only that
      * payload_bytes == 8 * b * n * k / 64 (OFFSETS otherwise). */
     uint32_t uniform_bits;
+    /* NULL, or the matrix's stream index (derived data, device memory,
+     * 16-byte aligned, vbq_stream_index_bytes bytes; vbq_build_stream_index
+     * writes it): for tile t, bytes [256 t, 256 t + 256) list the tile's
+     * groups in payload order (width buckets 1, 2, 4, 8 bits, column-major
+     * inside a bucket, as the layout above stores them), one byte each,
+     * (j - j0) * 64 + (r - r0); unused bytes of smaller tiles are 0. After
+     * all tiles' lists, at 256 * tiles + 8 t: the tile's group counts per
+     * width code 0..3 as four uint16. The mixed-width GEMV kernels then read
+     * the index instead of the width codes and skip deriving the counts and
+     * the list per tile and call. It belongs to the widths it was built
+     * from: rebuild it when they change. */
+    const uint8_t *stream_index;
 } vbq_matrix;
 
 /* Library ABI version (compare with VBQ_ABI_VERSION). Plumbing: the pages
  * define no such call. */
 VBQ_API uint32_t vbq_abi_version(void);
+
+/* Bytes of an n x k matrix's stream index: 264 per tile (host). The pages
+ * are silent: the index is a decode-side acceleration of the layout above
+ * (VBQ §6, "Fused kernels over packed weights": the kernel walks each width
+ * bucket; the index says in advance which group each bucket entry is).
+ * Errors: NULL, SHAPE (k % 64). */
+VBQ_API vbq_status vbq_stream_index_bytes(uint32_t n, uint32_t k, uint64_t *bytes_out);
+
+/* Write w's stream index (layout at vbq_matrix.stream_index) to the device
+ * buffer index_out of vbq_stream_index_bytes(w->n, w->k) bytes, 16-byte
+ * aligned: one wave per tile counts its widths and lists its groups, the
+ * same derivation the mixed-width kernels (VBQ §6, "Fused kernels over
+ * packed weights") otherwise repeat per tile and call; the pages are silent
+ * on such an index. w->stream_index is not read (but must be NULL or
+ * aligned). Asynchronous on `stream`. Errors: NULL, ABI, SHAPE, ALIGN,
+ * OFFSETS, HIP. */
+VBQ_API vbq_status vbq_build_stream_index(const vbq_matrix *w, uint8_t *index_out, void *stream);
 
 /* Sizes of the packed arrays for an n x k matrix with per-group widths
  * bits[n*(k/64)] (host). Errors: NULL, SHAPE (k % 64), WIDTH, TOO_LARGE.

@@ -38,7 +38,7 @@ def test_header_declares_the_abi():
         "vbq_recipe_head_bits", "vbq_recipe_head_order", "vbq_recipe_head_tiers", "vbq_check_padding",
         "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width",
         "vbq_gemv_multi_f16", "vbq_soft_quantize", "vbq_status_string", "vbq_last_error",
-        "vbq_probe_stream_read", "vbq_probe_dense_gemv"])
+        "vbq_probe_stream_read", "vbq_probe_dense_gemv", "vbq_stream_index_bytes", "vbq_build_stream_index"])
 
 
 def declaration_comments():
@@ -252,6 +252,26 @@ def test_device_entry_points_reject_bad_arguments_without_launching(V):
     assert V.lib.vbq_gemv(ctypes.byref(short), base, base, None) == V.ERR_OFFSETS
     assert V.lib.vbq_gemm_smallbatch(ctypes.byref(short), base, 16, base, None) == V.ERR_OFFSETS
     assert V.lib.vbq_unpack_codes(ctypes.byref(short), base, None) == V.ERR_OFFSETS
+    # the stream index: 16-byte aligned when present; the build checks its output buffer
+    mis_index = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base, 0, base + 8)
+    assert V.lib.vbq_gemv(ctypes.byref(mis_index), base, base, None) == V.ERR_ALIGN
+    assert V.lib.vbq_build_stream_index(ctypes.byref(aligned), None, None) == V.ERR_NULL
+    assert V.lib.vbq_build_stream_index(ctypes.byref(aligned), base + 4, None) == V.ERR_ALIGN
+    assert V.lib.vbq_build_stream_index(ctypes.byref(short), base, None) == V.ERR_OFFSETS
+    assert V.lib.vbq_build_stream_index(ctypes.byref(empty), None, None) == V.OK
+
+
+@pytest.mark.parametrize("n,k,tiles", [(0, 128, 0), (1, 64, 1), (64, 256, 1), (65, 256, 2), (64, 320, 2),
+                                       (4096, 14336, 64 * 56)])
+def test_stream_index_bytes(V, n, k, tiles):
+    assert V.vbq_stream_index_bytes(n, k) == 264 * tiles
+    assert V.vbq_tile_count(n, k) == tiles
+
+
+def test_stream_index_bytes_rejects(V):
+    out = ctypes.c_uint64(7)
+    assert V.lib.vbq_stream_index_bytes(2, 100, ctypes.byref(out)) == V.ERR_SHAPE
+    assert V.lib.vbq_stream_index_bytes(2, 128, None) == V.ERR_NULL
 
 
 def test_gemv_multi_rejects_bad_arguments_without_launching(V):
