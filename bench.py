@@ -351,11 +351,16 @@ def main():
     hy = [torch.empty(b.n, dtype=torch.float32, device=dev) for b in blocks]
     hyf = torch.empty(hrows, dtype=torch.float32, device=dev)
     g_ms = T.graph_ms(lambda i: V.vbq_gemv_multi(grouped[i % hcopies], [hx] * len(blocks), hy, stream))
+    hmap = torch.from_numpy(order.astype(np.int32)).to(dev)
+    gm_ms = T.graph_ms(lambda i: V.vbq_gemv_head_grouped(grouped[i % hcopies], hx, hmap, hyf, stream))
     v_ms = T.graph_ms(lambda i: V.vbq_gemv(vocab[i % hcopies], hx, hyf, stream))
     recipe["recipe_head_32000x4096"] = {
         "mean_bits": round(float(V.vbq_recipe_head_bits(freq).astype(np.float64).mean()), 4),
         "packed_bytes": hbytes, "grouped_one_launch_us": round(g_ms * 1e3, 3),
         "grouped_GBps": round(hbytes / (g_ms * 1e-3) / 1e9, 2),
+        "grouped_vocabulary_order_us": round(gm_ms * 1e3, 3),
+        "grouped_vocabulary_order_note": "vbq_gemv_head_grouped: the same launch storing each rank's logit at its "
+                                         "vocabulary row",
         "vocabulary_order_us": round(v_ms * 1e3, 3),
         "vocabulary_order_GBps": round(hbytes / (v_ms * 1e-3) / 1e9, 2)}
     del grouped, vocab

@@ -92,6 +92,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vbq_recipe_head_bits.argtypes = [U32, P, P]
     lib.vbq_recipe_head_order.argtypes = [U32, P, P]
     lib.vbq_recipe_head_tiers.argtypes = [U32, P, P, P]
+    lib.vbq_gemv_head_grouped.argtypes = [ctypes.POINTER(ctypes.POINTER(VbqMatrix)), U32, P, P, P, U32, P]
     lib.vbq_probe_stream_read.argtypes = [P, ctypes.c_uint64, P, U32, P]
     lib.vbq_probe_dense_gemv.argtypes = [P, P, P, U32, U32, P]
     lib.vbq_check_padding.argtypes = [ctypes.POINTER(VbqMatrix), U32, U32, U32]
@@ -104,7 +105,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
               lib.vbq_gemv_swiglu, lib.vbq_uniform_width, lib.vbq_recipe_head_order, lib.vbq_gemv_multi_f16,
               lib.vbq_soft_quantize, lib.vbq_gemv_multi_noalloc, lib.vbq_recipe_head_tiers,
               lib.vbq_probe_stream_read, lib.vbq_probe_dense_gemv, lib.vbq_gemm_smallbatch_multi,
-              lib.vbq_stream_index_bytes, lib.vbq_build_stream_index):
+              lib.vbq_stream_index_bytes, lib.vbq_build_stream_index, lib.vbq_gemv_head_grouped):
         f.restype = ctypes.c_int
     if lib.vbq_abi_version() != ABI_VERSION:
         raise ImportError(f"libvbq.so ABI {lib.vbq_abi_version()} != binding ABI {ABI_VERSION}")
@@ -412,6 +413,20 @@ def vbq_probe_dense_gemv(w: torch.Tensor, x: torch.Tensor, y: torch.Tensor, stre
     n, k = w.shape
     assert x.numel() == k and y.numel() >= n
     _check(lib.vbq_probe_dense_gemv(w.data_ptr(), x.data_ptr(), y.data_ptr(), n, k, _stream_handle(stream, w.device)))
+    return y
+
+
+def vbq_gemv_head_grouped(tiers, x: torch.Tensor, row_map: torch.Tensor, y: torch.Tensor, stream=None):
+    """y[row_map[rank]] = the grouped head's logit of that rank; tiers are DeviceMatrix row blocks in rank
+    order (same k), row_map a device uint32 tensor (torch.int32 storage) with one entry per rank."""
+    count = len(tiers)
+    assert count <= MAX_MULTI and x.dtype == torch.float16 and y.dtype == torch.float32
+    assert row_map.dtype in (torch.int32, torch.uint32) and row_map.is_contiguous() and y.is_contiguous()
+    assert row_map.numel() == sum(t.n for t in tiers) and all(t.k == x.numel() for t in tiers)
+    arr = (ctypes.POINTER(VbqMatrix) * max(count, 1))(*[ctypes.pointer(t.struct) for t in tiers])
+    dev = tiers[0].device if count else y.device
+    _check(lib.vbq_gemv_head_grouped(arr, count, x.data_ptr(), row_map.data_ptr(), y.data_ptr(), y.numel(),
+                                     _stream_handle(stream, dev)))
     return y
 
 

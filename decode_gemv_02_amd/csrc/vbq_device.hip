@@ -197,6 +197,11 @@ struct Batch {
     uint16_t *h;
     float *pair;              // [2][n]: each row tile's finished g and u values
     uint32_t *pair_counters;  // [row tiles] arrival counters (self-resetting)
+    // Grouped head: when row_map is set, the matrices are row blocks of one head, matrix i holding the
+    // ranks after those of matrices 0..i-1, and row r of matrix i is stored at y[row_map[rank]] (every
+    // matrix's y is the head's y); map values at or past y_rows are not stored.
+    const uint32_t *row_map;
+    uint32_t y_rows;
 };
 
 // 4992 bytes per wave: eight 4-wave, four 8-wave or two 16-wave workgroups
@@ -664,6 +669,13 @@ template <uint32_t kWaves>
 __device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M, uint32_t which, WaveLds *lds,
                                                 uint32_t wave, bool spare, uint32_t a, uint32_t split, uint32_t r0,
                                                 uint32_t rows, uint32_t lane, float acc) {
+    // a grouped head's output row, requested before the barrier so that the load's trip overlaps it
+    uint32_t out_row = r0 + lane;
+    if (B.row_map && wave == 0) {
+        uint32_t rank0 = 0;
+        for (uint32_t j = 0; j < which; ++j) rank0 += B.m[j].n;
+        out_row = B.row_map[rank0 + r0 + min(lane, rows - 1)];
+    }
     lds[wave].part[lane] = acc;   // the wave's row sums, in its own (now idle) LDS
     __syncthreads();
     if (wave != 0 || spare) return;
@@ -693,10 +705,13 @@ __device__ __forceinline__ void finish_row_tile(const Batch &B, const MatArgs &M
     }
     if (!B.h) {
         if (lane < rows) {
-            if (M.y16)
+            if (B.row_map) {
+                if (out_row < B.y_rows) M.y[out_row] = sum;
+            } else if (M.y16) {
                 M.y16[r0 + lane] = __builtin_bit_cast(uint16_t, static_cast<_Float16>(sum));
-            else
+            } else {
                 M.y[r0 + lane] = sum;
+            }
         }
         return;
     }
@@ -1353,6 +1368,12 @@ __global__ __launch_bounds__(64) void stream_index_tiles(MatArgs M, uint8_t *__r
 __global__ void fill_zero(float *__restrict__ y, uint64_t count) {
     const uint64_t i = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i < count) y[i] = 0.f;
+}
+
+// y[row_map[r]] = 0 for r < rows, skipping map values at or past y_rows (a grouped head with k = 0)
+__global__ void scatter_zero(float *y, const uint32_t *row_map, uint64_t rows, uint32_t y_rows) {
+    const uint64_t r = static_cast<uint64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (r < rows && row_map[r] < y_rows) y[row_map[r]] = 0.f;
 }
 
 __global__ void fill_zero_u16(uint16_t *__restrict__ h, uint64_t count) {
@@ -2068,10 +2089,14 @@ void gemv_rows_dispatch(bool aligned, uint32_t blocks, uint32_t used, const Batc
 // no_alloc: the split scratch comes from the fixed array (vbq_gemv_multi_noalloc), never from hipMalloc.
 // rows = 2: every entry is two rows of X (row r at xs[i] + r k) against ws[i], written to ys[i] + r n,
 // by gemv_rows (no h, no fp16 y).
+// row_map, y_rows: a grouped head (Batch::row_map); the matrices are its row blocks in rank order.
 vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
                        uint32_t count, hipStream_t stream, uint16_t *h = nullptr, uint16_t *const *ys16 = nullptr,
-                       bool no_alloc = false, uint32_t rows = 1) {
+                       bool no_alloc = false, uint32_t rows = 1, const uint32_t *row_map = nullptr,
+                       uint32_t y_rows = 0) {
     Batch B{};
+    B.row_map = row_map;
+    B.y_rows = y_rows;
     uint32_t blocks = 0, total_row_tiles = 0, max_col_tiles = 0;
     bool aligned = true;
     for (uint32_t i = 0; i < count; ++i) {
@@ -2125,8 +2150,39 @@ vbq_status gemv_launch(const char *who, const vbq_matrix *const *ws, const uint1
         M.blocks = row_tiles * M.splits;
         blocks = std::max(blocks, M.blocks);
         if (M.groups % 4) aligned = false;
+    }
+    if (ubits == kPerMatrix) {
+        // The per-matrix-width kernel multiplies the splits of 8- and 4-bit matrices (above). Where that
+        // pushes the grid past one round of resident workgroups, the last ones would start only when
+        // others leave and add a whole workgroup's time (the grouped 32000-row head: 518 workgroups of 16
+        // waves for 512 places); the multipliers are then halved, matrix by matrix, until the grid fits
+        // or none is left.
+        const uint32_t room =
+            256u * std::max(1u, (160u * 1024u) / (plan.waves * static_cast<uint32_t>(sizeof(WaveLds))));
+        auto total_blocks = [&]() {
+            uint32_t t = 0;
+            for (uint32_t i = 0; i < used; ++i) t += B.m[i].blocks;
+            return t;
+        };
+        for (uint32_t pass = 0; pass < 4 && total_blocks() > room; ++pass) {
+            bool changed = false;
+            for (uint32_t i = 0; i < used && total_blocks() > room; ++i) {
+                MatArgs &M = B.m[i];
+                const uint32_t floor_splits = std::max(1u, std::min(ceil_div(M.units, plan.waves), plan.splits));
+                if (M.ubits < 4 || M.splits <= floor_splits) continue;
+                M.splits = std::max(floor_splits, M.splits / 2);
+                M.blocks = ceil_div(M.n, kTileRows) * M.splits;
+                changed = true;
+            }
+            if (!changed) break;
+        }
+        blocks = 0;
+        for (uint32_t i = 0; i < used; ++i) blocks = std::max(blocks, B.m[i].blocks);
+    }
+    for (uint32_t i = 0; i < used; ++i) {
+        const MatArgs &M = B.m[i];
         if (M.splits > 1) {
-            counter_slots += row_tiles;
+            counter_slots += ceil_div(M.n, kTileRows);
             partial_total += partial_bytes(M.splits * rows, M.n);
         }
     }
@@ -2361,6 +2417,46 @@ extern "C" vbq_status vbq_gemv_swiglu(const vbq_matrix *gate, const vbq_matrix *
         const uint16_t *xs[2] = {x, x};
         float *ys[2] = {nullptr, nullptr};
         return gemv_launch(who, ws, xs, ys, 2, s, h);
+    });
+}
+
+extern "C" vbq_status vbq_gemv_head_grouped(const vbq_matrix *const *tiers, uint32_t count, const uint16_t *x,
+                                            const uint32_t *row_map, float *y, uint32_t y_rows, void *stream) {
+    return vbq::guarded("vbq_gemv_head_grouped", [&]() -> vbq_status {
+        vbq::clear_error();
+        const char *who = "vbq_gemv_head_grouped";
+        if (count > VBQ_MAX_MULTI) return fail(VBQ_ERR_SHAPE, "%s: count=%u exceeds %u", who, count, VBQ_MAX_MULTI);
+        if (count == 0) return VBQ_OK;
+        if (!tiers) return fail(VBQ_ERR_NULL, "%s: tiers is NULL", who);
+        uint64_t ranks = 0;
+        for (uint32_t i = 0; i < count; ++i) {
+            vbq_status st = check_matrix(who, tiers[i]);
+            if (st != VBQ_OK) return st;
+            if (tiers[i]->k != tiers[0]->k)
+                return fail(VBQ_ERR_SHAPE, "%s: tier %u has k=%u, tier 0 k=%u (they share x)", who, i, tiers[i]->k,
+                            tiers[0]->k);
+            ranks += tiers[i]->n;
+        }
+        if (ranks == 0) return VBQ_OK;
+        if (ranks > 0xFFFFFFFFull) return fail(VBQ_ERR_SHAPE, "%s: %llu ranks exceed 32 bits", who,
+                                               static_cast<unsigned long long>(ranks));
+        if (!row_map || !y || (tiers[0]->k && !x)) return fail(VBQ_ERR_NULL, "%s: x, row_map or y is NULL", who);
+        if (!aligned16(row_map) || !aligned16(y) || (tiers[0]->k && !aligned16(x)))
+            return fail(VBQ_ERR_ALIGN, "%s: x, row_map or y is not 16-byte aligned", who);
+        (void)hipGetLastError();
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        if (tiers[0]->k == 0) {   // every logit is 0
+            hipLaunchKernelGGL(scatter_zero, dim3(static_cast<uint32_t>((ranks + 255) / 256)), dim3(256), 0, s, y,
+                               row_map, ranks, y_rows);
+            return launched(who);
+        }
+        const uint16_t *xs[VBQ_MAX_MULTI];
+        float *ys[VBQ_MAX_MULTI];
+        for (uint32_t i = 0; i < count; ++i) {
+            xs[i] = x;
+            ys[i] = y;
+        }
+        return gemv_launch(who, tiers, xs, ys, count, s, nullptr, nullptr, false, 1, row_map, y_rows);
     });
 }
 

@@ -399,6 +399,26 @@ VBQ_API vbq_status vbq_recipe_head_order(uint32_t rows, const uint64_t *freq, ui
 VBQ_API vbq_status vbq_recipe_head_tiers(uint32_t rows, const uint64_t *freq, uint32_t *order_out,
                                          uint32_t *tier_rows_out);
 
+/* The frequency-grouped head in one launch, its logits in vocabulary order
+ * (VBQ §6, "Fused kernels over packed weights": the head runs as
+ * frequency-grouped row buckets; §3.4, "From discovery to a fixed recipe",
+ * for the tiers). tiers[0..count) are the head's row blocks in rank order,
+ * tier t holding the ranks s_t .. s_t + n_t - 1 (s_0 = 0, s_{t+1} = s_t +
+ * n_t; the blocks vbq_recipe_head_tiers describes, each usually declaring
+ * its width), all with the same k, count <= VBQ_MAX_MULTI. row_map: device
+ * uint32 [sum of n_t], the vocabulary row of each rank (the order_out of
+ * vbq_recipe_head_tiers). The call computes (tier x)[r] exactly as
+ * vbq_gemv_multi computes it for these tiers and stores it at
+ * y[row_map[s_t + r]]; map values >= y_rows are skipped, and rows of y that
+ * no rank maps to are left unchanged. Distinct ranks must map to distinct
+ * rows (two ranks on one row race). x: device binary16 [k]; y: device fp32
+ * [y_rows]; x, row_map and y 16-byte aligned, owned by the caller. k == 0
+ * stores 0 at every mapped row. Scratch as for vbq_gemv_multi.
+ * Asynchronous on `stream`. Errors: NULL, ABI, SHAPE (count, the k's
+ * differ, k > VBQ_MAX_K), ALIGN, OFFSETS, HIP. */
+VBQ_API vbq_status vbq_gemv_head_grouped(const vbq_matrix *const *tiers, uint32_t count, const uint16_t *x,
+                                         const uint32_t *row_map, float *y, uint32_t y_rows, void *stream);
+
 /* Export-time check of the padding contract (VBQ §6, "Granularity is
  * deployment-friendly": MLP intermediates are zero-padded so the contracted
  * dimension is a multiple of 512; padded channels are inert because

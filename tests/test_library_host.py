@@ -38,7 +38,8 @@ def test_header_declares_the_abi():
         "vbq_recipe_head_bits", "vbq_recipe_head_order", "vbq_recipe_head_tiers", "vbq_check_padding",
         "vbq_container_size", "vbq_container_write", "vbq_container_open", "vbq_gemv_swiglu", "vbq_uniform_width",
         "vbq_gemv_multi_f16", "vbq_soft_quantize", "vbq_status_string", "vbq_last_error",
-        "vbq_probe_stream_read", "vbq_probe_dense_gemv", "vbq_stream_index_bytes", "vbq_build_stream_index"])
+        "vbq_probe_stream_read", "vbq_probe_dense_gemv", "vbq_stream_index_bytes", "vbq_build_stream_index",
+        "vbq_gemv_head_grouped"])
 
 
 def declaration_comments():
