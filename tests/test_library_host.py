@@ -365,6 +365,34 @@ def test_gemv_swiglu_rejects_bad_arguments_without_launching(V):
     assert f(ctypes.byref(empty), ctypes.byref(empty), None, None, None) == V.OK   # n == 0: nothing to do
 
 
+def test_gemv_head_grouped_rejects_bad_arguments_without_launching(V):
+    h = V.vbq_pack(*(lambda b, c, s: (2, 128, b, c, s))(*W.draw_random_matrix(9, 2, 128)))
+    buf = np.zeros(4096, np.uint8)
+    base = (buf.ctypes.data + 255) // 256 * 256
+    t = V.VbqMatrix(V.ABI_VERSION, 2, 128, h.payload_bytes, base, base, base, base)
+    wide = V.VbqMatrix(V.ABI_VERSION, 2, 192, 2 * 3 * 8, base, base, base, base)
+    f = V.lib.vbq_gemv_head_grouped
+    over = V.MAX_MULTI + 1
+    Wo = (ctypes.POINTER(V.VbqMatrix) * over)(*([ctypes.pointer(t)] * over))
+    assert f(Wo, over, base, base, base, 8, None) == V.ERR_SHAPE
+    assert f(None, 2, base, base, base, 8, None) == V.ERR_NULL
+    assert f(Wo, 0, None, None, None, 0, None) == V.OK
+    W2 = (ctypes.POINTER(V.VbqMatrix) * 2)(ctypes.pointer(t), ctypes.pointer(wide))
+    assert f(W2, 2, base, base, base, 8, None) == V.ERR_SHAPE          # the tiers share x: one k
+    W1 = (ctypes.POINTER(V.VbqMatrix) * 1)(ctypes.pointer(t))
+    assert f(W1, 1, base, None, base, 8, None) == V.ERR_NULL            # no row map
+    assert f(W1, 1, None, base, base, 8, None) == V.ERR_NULL
+    assert f(W1, 1, base, base, None, 8, None) == V.ERR_NULL
+    assert f(W1, 1, base, base + 4, base, 8, None) == V.ERR_ALIGN
+    assert f(W1, 1, base, base, base + 4, 8, None) == V.ERR_ALIGN
+    bad = V.VbqMatrix(99, 2, 128, h.payload_bytes, base, base, base, base)
+    Wb = (ctypes.POINTER(V.VbqMatrix) * 1)(ctypes.pointer(bad))
+    assert f(Wb, 1, base, base, base, 8, None) == V.ERR_ABI
+    empty = V.VbqMatrix(V.ABI_VERSION, 0, 128, 0, None, None, None, None)
+    We = (ctypes.POINTER(V.VbqMatrix) * 1)(ctypes.pointer(empty))
+    assert f(We, 1, None, None, None, 0, None) == V.OK                  # no ranks: nothing to do
+
+
 @pytest.mark.parametrize("n, k", [(1, 64), (3, 192), (65, 320), (300, 4096)])
 def test_uniform_width_query_and_check(V, n, k):
     for b in (1, 2, 4, 8):
