@@ -307,6 +307,53 @@ def probe_summary(a) -> str:
     return "\n".join(lines) + "\n"
 
 
+# counters of the matrix-core GEMM (one rocprofv3 --pmc pass: eight SQ counters and the GPU's busy cycles)
+GEMM_PMC = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_VMEM_RD SQ_INSTS_SALU SQ_WAVES "
+            "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE")
+SIMD_NUM = 4 * CU_NUM
+
+
+def kernel_counters_summary(a) -> str:
+    """Per kernel and grid of the VBQ kernels in one --pmc pass: instructions by kind per wave, and the
+    mean time a SIMD spends per dispatch issuing VALU work (SQ_ACTIVE_INST_VALU quad-cycles x 4) and
+    with its matrix core busy (SQ_VALU_MFMA_BUSY_CYCLES), over all SIMDs at 2.4 GHz (compare with the
+    kernel-trace duration)."""
+    con = sqlite3.connect(a.db)
+    try:
+        rows = con.execute("select dispatch_id, kernel_name, grid_size_x, grid_size_y, counter_name, value "
+                           "from counters_collection order by dispatch_id").fetchall()
+    finally:
+        con.close()
+    per, disp = {}, {}
+    for did, kn, gx, gy, cn, val in rows:
+        if not any(k in kn for k in ("gemv_tiles", "gemv_uniform", "gemv_rows", "gemm_frag")):
+            continue
+        key = (kn, gx, gy)
+        per.setdefault(key, {})
+        per[key][cn] = per[key].get(cn, 0.0) + val
+        disp.setdefault(key, set()).add(did)
+    lines = [f"# Instruction counters per kernel and grid, {a.title}",
+             "# commands (repository root):",
+             f"#   rocprofv3 --pmc {GEMM_PMC} -d <dir> -o {a.name} -- {a.command}",
+             f"#   python bench_counters.py kcounters --db <dir>/{a.name}_results.db --out <this file>",
+             "# per wave: instructions issued by one wave; valu_us_per_simd / mfma_busy_us_per_simd: per "
+             f"dispatch, summed over the {SIMD_NUM} SIMDs and divided by them, at 2.4 GHz",
+             f"kernel_source_sha256: {kernel_source_sha()}"]
+    for key, t in per.items():
+        waves = t.get("SQ_WAVES", 0.0)
+        if not waves:
+            continue
+        nd = len(disp[key])
+        parts = [f"dispatches={nd}", f"waves_per_dispatch={waves / nd:.0f}"]
+        parts += [f"{k.replace('SQ_', '').lower()}={v / waves:.1f}" for k, v in sorted(t.items())
+                  if k.startswith("SQ_INSTS_")]
+        parts.append(f"valu_us_per_simd={4 * t.get('SQ_ACTIVE_INST_VALU', 0.0) / SIMD_NUM / nd / 2400.0:.2f}")
+        parts.append(f"mfma_busy_us_per_simd={t.get('SQ_VALU_MFMA_BUSY_CYCLES', 0.0) / SIMD_NUM / nd / 2400.0:.2f}")
+        lines.append(f"kernel: {key[0]} grid={key[1]}x{key[2]}")
+        lines.append("  " + " ".join(parts))
+    return "\n".join(lines) + "\n"
+
+
 def read_traffic(path: str) -> dict | None:
     """{launch: traffic bytes} from a traffic summary, or None if absent or taken on another kernel source."""
     if not os.path.exists(path):
@@ -358,9 +405,15 @@ def main():
     c.add_argument("--title", default="")
     c.add_argument("--kernel-sha", default="", help="sha256 of the kernel source the counters were taken on "
                                                      "(default: the current source)")
+    kc = sub.add_parser("kcounters")
+    kc.add_argument("--db", required=True)
+    kc.add_argument("--name", default="gemm")
+    kc.add_argument("--title", required=True)
+    kc.add_argument("--command", required=True)
+    kc.add_argument("--out", required=True)
     a = ap.parse_args()
     text = {"traffic": traffic_summary, "trace": trace_summary, "kernels": kernels_summary,
-            "counters": counters_summary, "probe": probe_summary}[a.cmd](a)
+            "counters": counters_summary, "probe": probe_summary, "kcounters": kernel_counters_summary}[a.cmd](a)
     with open(a.out, "w") as f:
         f.write(text)
     print(text, end="")
