@@ -7,7 +7,9 @@ one-width row block per tier in rank order (§6, "Fused kernels over packed
 weights": the head as frequency-grouped row buckets). One launch stores each
 rank's logit at its vocabulary row. Bars:
   (1) bit for bit the unmapped grouped launch (vbq_gemv_multi on the tiers),
-      gathered on the host;
+      gathered on the host, on one-width tiers (the per-matrix-width kernel)
+      and on mixed-width tiers (the mixed kernel, with and without stream
+      indexes);
   (2) within the GEMV tolerance of the CPU oracle on the same rows packed in
       vocabulary order;
   (3) rows no rank maps to, and ranks whose map value is at or past y_rows,
@@ -35,9 +37,10 @@ def print_case(**kw):
     print("CASE", " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
 
 
-def make_head(V, seed, rows, k):
+def make_head(V, seed, rows, k, mixed=False, index=True):
     """Tier blocks (DeviceMatrix, rank order), the rank -> row map, and the same rows in vocabulary order
-    as one oracle pack."""
+    as one oracle pack. mixed: every tier draws its widths per group from the standard mix (no declared
+    width: the mixed-width kernel runs, with or without stream indexes)."""
     freq = np.minimum(np.random.default_rng(seed).zipf(1.3, rows), 10 ** 6).astype(np.uint64)
     order, tiers = V.vbq_recipe_head_tiers(freq)
     G = k // 64
@@ -49,20 +52,23 @@ def make_head(V, seed, rows, k):
         cnt = int(cnt)
         if cnt == 0:
             continue
-        bb, bc, bs = W.draw_random_matrix((seed, t), cnt, k, {b: 1.0})
+        bb, bc, bs = W.draw_random_matrix((seed, t), cnt, k, W.STD_MIX if mixed else {b: 1.0})
         r = order[start:start + cnt]
         full_bits[r], full_codes[r], full_scales[r] = bb, bc, bs
-        blocks.append(V.DeviceMatrix(V.vbq_pack(cnt, k, bb, bc, bs)))
+        blocks.append(V.DeviceMatrix(V.vbq_pack(cnt, k, bb, bc, bs), stream_index=index))
         start += cnt
     ref_pack = oracle.pack(rows, k, full_bits, full_codes, full_scales) if k else None
     return blocks, order, ref_pack, full_scales
 
 
-@pytest.mark.parametrize("rows, k", [(4000, 1024), (32000, 4096), (777, 320)])
-def test_grouped_head_vocabulary_order(V, rows, k):
+@pytest.mark.parametrize("rows, k, mixed, index", [(4000, 1024, False, True), (32000, 4096, False, True),
+                                                   (777, 320, False, True), (3000, 2048, True, True),
+                                                   (1500, 448, True, False)])
+def test_grouped_head_vocabulary_order(V, rows, k, mixed, index):
     import torch
-    print_case(test="head_grouped", rows=rows, k=k)
-    blocks, order, ref_pack, scales = make_head(V, 97, rows, k)
+    print_case(test="head_grouped", rows=rows, k=k, mixed=mixed, index=index)
+    blocks, order, ref_pack, scales = make_head(V, 97, rows, k, mixed, index)
+    assert all(b.uniform_bits == 0 for b in blocks) if mixed else all(b.uniform_bits for b in blocks)
     x = W.draw_x((97, 1), k)
     xt = torch.from_numpy(x[0].view(np.float16)).cuda()
     row_map = torch.from_numpy(order.astype(np.int32)).cuda()
