@@ -314,9 +314,10 @@ VBQ_API vbq_status vbq_gemm_smallbatch_multi(const vbq_matrix *const *ws, const 
  * `stream`. Every call on one GPU shares that GPU's array: calls that
  * overlap on one GPU (on any streams, graph replays included) race and are
  * not allowed. Errors: those of vbq_gemv_multi, and CAPACITY when the
- * launch needs more than the array holds (more counter slots than
- * VBQ_NOALLOC_COUNTER_BYTES / 4, i.e. 64-row tiles, or more partial sums
- * than the rest of the array). */
+ * launch needs more than the array holds (more split 64-row tiles than
+ * VBQ_NOALLOC_COUNTER_BYTES / 128, each tile's arrival counter on a
+ * 128-byte line of its own, or more partial sums than the rest of the
+ * array). */
 #define VBQ_NOALLOC_SCRATCH_BYTES (4u << 20)
 #define VBQ_NOALLOC_COUNTER_BYTES (64u << 10)
 VBQ_API vbq_status vbq_gemv_multi_noalloc(const vbq_matrix *const *ws, const uint16_t *const *xs, float *const *ys,
