@@ -581,6 +581,87 @@ __device__ __forceinline__ void task8(WaveLds &L, uint32_t info, uint32_t qd, ui
     if (qd == 0) store_part(L, info, finish8bit(L, jl, a));
 }
 
+// A width that is rare in a tile (a few 2- or 4-bit groups among 1-bit
+// ones, as in a head tiered by frequency) leaves most lanes of its round
+// idle, and the round costs the same instructions whatever the number of
+// active lanes. Such a bucket is spread over more lanes per group: a 2-bit
+// group over 2 lanes (two words each) or 4 (one word each), a 4-bit group
+// over 4 (two words each), which cuts the round's instructions by about
+// the same factor. The per-lane partials are added across the lanes with
+// DPP quad permutes; the per-tile choice is uniform over the wave.
+
+// 2-bit: the partial u x sum of kWords consecutive words from word w0 of a group of column jl
+template <uint32_t kWords>
+__device__ __forceinline__ float part2bit(WaveLds &L, uint32_t jl, uint32_t w0, const uint32_t w[kWords]) {
+    const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride) + 2u * w0;
+    float a1 = 0.f, a4 = 0.f, a16 = 0.f, a64 = 0.f, a256 = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < kWords; ++q) {
+        uint32_t p[8];
+        unpack2(w[q], p);
+        const uint4 xa = xp[2 * q], xb = xp[2 * q + 1];
+        a1 = dot2(p[0], xa.x, a1);
+        a4 = dot2(p[1], xa.y, a4);
+        a16 = dot2(p[2], xa.z, a16);
+        a64 = dot2(p[3], xa.w, a64);
+        a256 = dot2(p[4], xb.x, a256);
+        a1 = dot2(p[5], xb.y, a1);
+        a4 = dot2(p[6], xb.z, a4);
+        a16 = dot2(p[7], xb.w, a16);
+    }
+    return fmaf(0x1p16f, a256, fmaf(0x1p18f, a64, fmaf(0x1p20f, a16, fmaf(0x1p22f, a4, 0x1p24f * a1))));
+}
+
+// 2-bit over two lanes: lane half h holds words 2h, 2h+1 (v)
+__device__ __forceinline__ void task2h(WaveLds &L, uint32_t info, uint32_t h, uint2 v) {
+    const uint32_t jl = info >> 6;
+    const uint32_t w[2] = {v.x, v.y};
+    float ux = part2bit<2>(L, jl, 2u * h, w);
+    ux += dpp<kQuadXor1>(ux);
+    if (h == 0) store_part(L, info, fmaf(-2.f, L.corr[jl], ux));
+}
+
+// 2-bit over four lanes: lane quarter qd holds word qd (v)
+__device__ __forceinline__ void task2q(WaveLds &L, uint32_t info, uint32_t qd, uint32_t v) {
+    const uint32_t jl = info >> 6;
+    const uint32_t w[1] = {v};
+    float ux = part2bit<1>(L, jl, qd, w);
+    ux += dpp<kQuadXor1>(ux);
+    ux += dpp<kQuadXor2>(ux);
+    if (qd == 0) store_part(L, info, fmaf(-2.f, L.corr[jl], ux));
+}
+
+// 4-bit over four lanes: lane quarter qd holds words 2qd, 2qd+1 (elements 16qd .. 16qd+15)
+__device__ __forceinline__ void task4q(WaveLds &L, uint32_t info, uint32_t qd, uint2 v) {
+    const uint32_t jl = info >> 6;
+    const uint32_t w[2] = {v.x, v.y};
+    const uint4 *xp = reinterpret_cast<const uint4 *>(L.xs + jl * kXStride + 8u * qd);
+    float a1 = 0.f, a16 = 0.f;
+#pragma unroll
+    for (uint32_t q = 0; q < 2; ++q) {
+        uint32_t p[4];
+        unpack4(w[q], p);
+        const uint4 xa = xp[q];
+        a1 = dot2(p[0], xa.x, a1);
+        a16 = dot2(p[1], xa.y, a16);
+        a1 = dot2(p[2], xa.z, a1);
+        a16 = dot2(p[3], xa.w, a16);
+    }
+    float part = fmaf(0.0625f, a16, a1);
+    part += dpp<kQuadXor1>(part);
+    part += dpp<kQuadXor2>(part);
+    if (qd == 0) store_part(L, info, finish4bit(L, jl, part));
+}
+
+// Lanes per group of a tile's 2-bit and 4-bit buckets, as shifts: 2 bits take 1, 2 or 4 lanes (s2 = 0,
+// 1, 2), 4 bits 2 or 4 (s4 = 0, 1); a bucket that fits one round at the wider spread takes it.
+struct Spread {
+    uint32_t s2, s4;
+};
+__device__ __forceinline__ Spread tile_spread(const uint32_t cnt[4]) {
+    return Spread{cnt[1] <= kWave / 4 ? 2u : cnt[1] <= kWave / 2 ? 1u : 0u, cnt[2] <= kWave / 4 ? 1u : 0u};
+}
+
 // Payload of the first 256 one-bit groups and of the first 64 slices of
 // each wider bucket, loaded before any of it is used. A tile has at most
 // 256 groups, so only the wider buckets can need more rounds. The addresses
@@ -607,10 +688,28 @@ __device__ __forceinline__ void stage_payload(rsrc_t tile, const uint32_t cnt[4]
     S.p8b = buf_load8(tile, o8 + 16u * lane + 8u);
 }
 
-// Staged work first, then the rounds that load their own bytes (rare: more
-// than 64 two-bit groups or 64 slices of a wider width in one tile).
+// stage_payload with the 2- and 4-bit buckets read at their spread (tile_spread): a lane's bytes of
+// a 2-bit bucket start at 16, 8 or 4 bytes per lane, of a 4-bit bucket at 16 or 8 (the same loads
+// every time; the second 8 bytes are used only at the one-lane and two-lane spreads)
+__device__ __forceinline__ void stage_payload_spread(rsrc_t tile, const uint32_t cnt[4], Spread sp, uint32_t lane,
+                                                     Staged &S) {
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) S.p1[i] = buf_load8(tile, 8u * lane + 8u * kWave * i);
+    const uint32_t o2 = 8u * cnt[0], o4 = o2 + 16u * cnt[1], o8 = o4 + 32u * cnt[2];
+    const uint32_t a2 = o2 + ((16u * lane) >> sp.s2), a4 = o4 + ((16u * lane) >> sp.s4);
+    S.p2a = buf_load8(tile, a2);
+    S.p2b = buf_load8(tile, a2 + 8u);
+    S.p4a = buf_load8(tile, a4);
+    S.p4b = buf_load8(tile, a4 + 8u);
+    S.p8a = buf_load8(tile, o8 + 16u * lane);
+    S.p8b = buf_load8(tile, o8 + 16u * lane + 8u);
+}
+
+// Staged work first, then the rounds that load their own bytes (rare: more than 64 two-bit groups or 64
+// slices of a wider width in one tile); the 2- and 4-bit rounds at the tile's spread (a spread bucket
+// fits its one staged round).
 __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, rsrc_t tile, const uint32_t cnt[4],
-                                              uint32_t lane, LutKeys keys) {
+                                              Spread sp, uint32_t lane, LutKeys keys) {
     // A lane without a group in a round parks its (unused) result in a spare
     // slot past L.part, so the deferred stores need no branches.
     uint32_t info1[4];
@@ -628,13 +727,23 @@ __device__ __forceinline__ void tile_products(WaveLds &L, const Staged &S, rsrc_
     for (uint32_t i = 0; i < 4; ++i) store_part(L, info1[i], v1[i]);
     const uint32_t o2 = 8u * cnt[0], o4 = o2 + 16u * cnt[1], o8 = o4 + 32u * cnt[2];
     const uint8_t *l2 = L.list + cnt[0], *l4 = l2 + cnt[1], *l8 = l4 + cnt[2];
-    if (lane < cnt[1]) group2(L, l2[lane], S.p2a, S.p2b);
-    if (lane < 2u * cnt[2]) task4(L, l4[lane >> 1], lane & 1u, S.p4a, S.p4b);
+    if (sp.s2 == 2) {
+        if (lane < 4u * cnt[1]) task2q(L, l2[lane >> 2], lane & 3u, S.p2a.x);
+    } else if (sp.s2 == 1) {
+        if (lane < 2u * cnt[1]) task2h(L, l2[lane >> 1], lane & 1u, S.p2a);
+    } else {
+        if (lane < cnt[1]) group2(L, l2[lane], S.p2a, S.p2b);
+        for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
+            group2(L, l2[e], buf_load8(tile, o2 + 16u * e), buf_load8(tile, o2 + 16u * e + 8u));
+    }
+    if (sp.s4 == 1) {
+        if (lane < 4u * cnt[2]) task4q(L, l4[lane >> 2], lane & 3u, S.p4a);
+    } else {
+        if (lane < 2u * cnt[2]) task4(L, l4[lane >> 1], lane & 1u, S.p4a, S.p4b);
+        for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
+            task4(L, l4[e >> 1], e & 1u, buf_load8(tile, o4 + 16u * e), buf_load8(tile, o4 + 16u * e + 8u));
+    }
     if (lane < 4u * cnt[3]) task8(L, l8[lane >> 2], lane & 3u, S.p8a, S.p8b);
-    for (uint32_t e = lane + kWave; e < cnt[1]; e += kWave)
-        group2(L, l2[e], buf_load8(tile, o2 + 16u * e), buf_load8(tile, o2 + 16u * e + 8u));
-    for (uint32_t e = lane + kWave; e < 2u * cnt[2]; e += kWave)
-        task4(L, l4[e >> 1], e & 1u, buf_load8(tile, o4 + 16u * e), buf_load8(tile, o4 + 16u * e + 8u));
     for (uint32_t e = lane + kWave; e < 4u * cnt[3]; e += kWave)
         task8(L, l8[e >> 2], e & 3u, buf_load8(tile, o8 + 16u * e), buf_load8(tile, o8 + 16u * e + 8u));
 }
@@ -798,8 +907,9 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         else
             P = tile_scan(cur, rows, cn, relane(lane0), cnt);
         const rsrc_t tp = tile_rsrc(M.payload, M.payload_bytes, cur.off);
+        const Spread sp = tile_spread(cnt);
         Staged S;
-        stage_payload(tp, cnt, relane(lane0), S);
+        stage_payload_spread(tp, cnt, sp, relane(lane0), S);
         // the next tile's metadata travels while this tile computes
         const uint32_t cnx = ct + kWaves < c_hi ? ct + kWaves : ct;
         const TileMeta nxt = load_meta<kAligned>(M, a, cnx, relane(lane0), true, !kIndexed);
@@ -811,7 +921,7 @@ __global__ __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(
         else
             build_lists(L, cur, P, cnt, rows, cn, relane(lane0));
         wave_lds_sync();
-        tile_products(L, S, tp, cnt, relane(lane0), keys);
+        tile_products(L, S, tp, cnt, sp, relane(lane0), keys);
         wave_lds_sync();
         const uint32_t lane = relane(lane0);
         if (lane < rows)
