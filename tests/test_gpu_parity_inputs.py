@@ -132,3 +132,43 @@ def test_negative_scales(V, mix):
                 continue
             print_case(test="negative_scales", mix=len(mix), m=m, kernel=name)
             assert_within_tolerance(run(V, dm, x), ref, x, scales, f"signed scales m={m} {name}")
+
+
+def spread_modes(bits: np.ndarray) -> set:
+    """The rare-width spreads the mixed kernel takes over this matrix's tiles (64 rows x 4 groups): per
+    tile, 2-bit groups at 4 lanes (at most 16 in the tile), 2 lanes (at most 32) or 1; 4-bit groups at 4
+    lanes (at most 16) or 2."""
+    n, G = bits.shape
+    modes = set()
+    for r0 in range(0, n, 64):
+        for j0 in range(0, G, 4):
+            t = bits[r0:r0 + 64, j0:j0 + 4]
+            c2, c4 = int((t == 2).sum()), int((t == 4).sum())
+            if c2:
+                modes.add("2bit-quarter" if c2 <= 16 else "2bit-half" if c2 <= 32 else "2bit-one")
+            if c4:
+                modes.add("4bit-quarter" if c4 <= 16 else "4bit-half")
+    return modes
+
+
+@pytest.mark.parametrize("mix, want", [
+    ({1: 0.95, 2: 0.05}, {"2bit-quarter"}),
+    ({1: 0.9, 2: 0.1}, {"2bit-quarter", "2bit-half", "2bit-one"}),
+    ({1: 0.95, 4: 0.05}, {"4bit-quarter"}),
+    ({1: 0.85, 4: 0.1, 2: 0.05}, {"4bit-quarter", "4bit-half", "2bit-quarter"}),
+    ({1: 0.97, 2: 0.02, 4: 0.01}, {"2bit-quarter", "4bit-quarter"}),
+])
+@pytest.mark.parametrize("mean", [0.0, 4.0])
+def test_rare_width_spreads(V, mix, want, mean):
+    """Tiles whose 2- or 4-bit bucket is small spread each such group over two or four lanes; every
+    spread (checked on the host from the widths) against the oracle, on a ragged shape, with plain and
+    offset activations."""
+    n, k = 300, 4160
+    bits, codes, scales = W.draw_random_matrix((120, len(mix), int(100 * min(mix.values()))), n, k, mix)
+    assert want <= spread_modes(bits), spread_modes(bits)
+    host = V.vbq_pack(n, k, bits, codes, scales)
+    p = oracle.pack(n, k, bits, codes, scales)
+    x = (W.draw_x_offset((121, int(mean)), k, 1, mean=mean, sigma=0.5) if mean else W.draw_x((121, 0), k))
+    print_case(test="rare_spread", mix=sorted(mix.items()), mean=mean)
+    got = run(V, V.DeviceMatrix(host), x)
+    assert_within_tolerance(got, oracle.gemm(p, x), x, scales, f"spread {sorted(mix.items())} mean={mean}")
