@@ -179,7 +179,7 @@ struct MatArgs {
     const uint16_t *x;
     float *y;
     float *partial;       // [splits][n] when splits > 1
-    uint32_t *counters;   // [row tiles] arrival counters when splits > 1 (self-resetting)
+    uint32_t *counters;   // [row tiles x kCounterStride] arrival counters when splits > 1 (self-resetting)
     uint32_t n, groups, col_tiles, splits, blocks;   // blocks = row tiles x splits
     uint32_t units;   // work units along K: column tiles, or groups of one chunk for uniform 8- and lean 4-bit
     uint32_t payload_bytes;
@@ -200,13 +200,14 @@ struct Batch {
     // (same n), and instead of y the launch writes h = fp16(silu(g) * u).
     uint16_t *h;
     float *pair;              // [2][n]: each row tile's finished g and u values
-    uint32_t *pair_counters;  // [row tiles] arrival counters (self-resetting)
+    uint32_t *pair_counters;  // [row tiles x kCounterStride] arrival counters (self-resetting)
     // Grouped head: when row_map is set, the matrices are row blocks of one head, matrix i holding the
     // ranks after those of matrices 0..i-1, and row r of matrix i is stored at y[row_map[rank]] (every
     // matrix's y is the head's y); map values at or past y_rows are not stored.
     const uint32_t *row_map;
     uint32_t y_rows;
 };
+static_assert(sizeof(Batch) <= 4096, "a launch's kernel arguments fit 4 KiB");
 
 // 4992 bytes per wave: eight 4-wave, four 8-wave or two 16-wave workgroups
 // fit one CU's 160 KiB. 64-byte aligned: the lookup table's addresses are
