@@ -1651,6 +1651,7 @@ struct FragCol {
 struct alignas(16) FragTables {
     uint32_t where[kTileGroups][kTileRows];   // group byte offset in the tile | width code (0 past the rows)
     float scale[kTileGroups][kTileRows];      // group scale as fp32 (0 past the rows)
+    uint32_t hscale[kTileGroups][kTileRows];  // 17 to 32 rows of X: the scale's fp16 bits in both halves (0 past the rows)
 };
 constexpr uint32_t kRedStride = kTileRows + 4;   // floats per parked activation row (spreads the banks)
 
@@ -1665,7 +1666,11 @@ union alignas(16) FragLds {
 };
 
 // Lane r = row r: the byte offset and width of each of its groups, and its scales as fp32. Returns
-// (uniform) bit 4 jl + rb set when every row of 16-row block rb is 1-bit in column jl.
+// (uniform) bit 4 jl + rb set when every row of 16-row block rb is 1-bit in column jl. kScaled: also
+// the scales' fp16 bits, and bit 16 + 4 jl + rb set when every row of the block is 1- or 2-bit in
+// column jl with a scale s that is zero or normal and below 2^15 (then s q is an exact fp16 value, normal
+// or zero, for each code q in [-2, 1]).
+template <bool kScaled>
 __device__ __forceinline__ uint32_t frag_tables(FragTables &T, const TileMeta &t, const TileScan &S,
                                                 const uint64_t colstart[kTileGroups + 1], const uint32_t cnt[4],
                                                 uint32_t rows, uint32_t cn, uint32_t lane) {
@@ -1686,6 +1691,15 @@ __device__ __forceinline__ uint32_t frag_tables(FragTables &T, const TileMeta &t
 #pragma unroll
         for (uint32_t rb = 0; rb < 4; ++rb)
             ones |= (((wide >> (16 * rb)) & 0xFFFFu) == 0 ? 1u : 0u) << (4 * jl + rb);
+        if constexpr (kScaled) {
+            T.hscale[jl][lane] = ok ? sb * 0x00010001u : 0u;
+            const uint32_t e = (sb >> 10) & 0x1Fu;
+            const bool fits = (e >= 1 && e <= 29) || (sb & 0x7FFFu) == 0;
+            const uint64_t unfit = __builtin_amdgcn_ballot_w64(ok && (c > 1 || !fits));
+#pragma unroll
+            for (uint32_t rb = 0; rb < 4; ++rb)
+                ones |= (((unfit >> (16 * rb)) & 0xFFFFu) == 0 ? 1u : 0u) << (16 + 4 * jl + rb);
+        }
     }
     return ones;
 }
@@ -1813,13 +1827,19 @@ __device__ __forceinline__ void frag_finish(FragLds<MB, kWaves> &S, const GemmAr
     if (threadIdx.x == 0) __hip_atomic_store(&G.counters[a * kCounterStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One 16-row block rb of column jl: decode the lane's A fragments (a block whose rows are all 1-bit by the
-// nibble table, any other by the width-generic decoder), multiply with the activations on the matrix
-// cores, scale each row by its group scale and add into acc (rows 16rb + 4q .. +3, activation row mr).
+// One 16-row block rb of column jl: decode the lane's A fragments (codes 8q..+7 and 32+8q..+7 of row
+// 16rb + i; a block whose rows are all 1-bit by the nibble table, any other by the width-generic
+// decoder), multiply with the activations on the matrix cores and add into acc (rows 16rb + 4q .. +3,
+// activation row mr). At 17 to 32 rows of X a scaled block (every row 1- or 2-bit, scales that keep s q
+// exact in fp16) carries s q in its fragments, so the matrix cores add straight into acc; any other
+// block's products are scaled by each row's fp32 group scale and then added. (Beyond 32 rows the
+// accumulators live in the matrix-core registers, and the other blocks' scaling then costs two moves per
+// accumulator: every block is scaled after the products there.)
 template <uint32_t MB>
 __device__ __forceinline__ void frag_block(const FragParams *params, const uint2 *nib, const FragTables &T,
-                                           uint32_t jl, uint32_t rb, bool one_bit, const uint2 w[2],
+                                           uint32_t jl, uint32_t rb, uint32_t kind, const uint2 w[2],
                                            const half8_t bx[2][MB], uint32_t q, uint32_t i, float4_t acc[MB]) {
+    const bool one_bit = (kind & 1u) != 0;
     half8_t a0, a1;
     if (one_bit) {
         const uint32_t w0 = w[0].x, w1 = w[0].y;
@@ -1831,6 +1851,26 @@ __device__ __forceinline__ void frag_block(const FragParams *params, const uint2
         const uint32_t c = T.where[jl][16 * rb + i] & 3u;
         frag_generic(w[0], w[1], params[4 * c + q], a0, a1);
     }
+    if constexpr (MB == 2) {
+        if (kind & 2u) {
+            const uint32_t hs = T.hscale[jl][16 * rb + i];
+            if (one_bit) {   // +-1 -> +-s: the codes' sign bits onto the scale's
+                const uint32_t k = hs ^ 0x3C003C00u;
+                const uint4 u0 = __builtin_bit_cast(uint4, a0), u1 = __builtin_bit_cast(uint4, a1);
+                a0 = frag_of(u0.x ^ k, u0.y ^ k, u0.z ^ k, u0.w ^ k);
+                a1 = frag_of(u1.x ^ k, u1.y ^ k, u1.z ^ k, u1.w ^ k);
+            } else {
+                const half8_t s8 = __builtin_bit_cast(half8_t, make_uint4(hs, hs, hs, hs));
+                a0 *= s8;
+                a1 *= s8;
+            }
+#pragma unroll
+            for (uint32_t mb = 0; mb < MB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, bx[0][mb], acc[mb], 0, 0, 0);
+#pragma unroll
+            for (uint32_t mb = 0; mb < MB; ++mb) acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, bx[1][mb], acc[mb], 0, 0, 0);
+            return;
+        }
+    }
     float4_t d[MB];
 #pragma unroll
     for (uint32_t mb = 0; mb < MB; ++mb)
@@ -1840,6 +1880,11 @@ __device__ __forceinline__ void frag_block(const FragParams *params, const uint2
     const float4_t s = *static_cast<const float4_t *>(__builtin_assume_aligned(&T.scale[jl][16 * rb + 4 * q], 16));
 #pragma unroll
     for (uint32_t mb = 0; mb < MB; ++mb) acc[mb] += s * d[mb];
+}
+
+// frag_block's kind from frag_tables' masks: bit 0 all 1-bit, bit 1 scaled
+__device__ __forceinline__ uint32_t block_kind(uint32_t masks, uint32_t jl, uint32_t rb) {
+    return ((masks >> (4 * jl + rb)) & 1u) | (((masks >> (16 + 4 * jl + rb)) & 1u) << 1);
 }
 
 template <uint32_t MB, uint32_t kWaves, bool kAligned, bool kMulti>
@@ -1883,7 +1928,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
         const TileScan sc = tile_scan(meta, rows, cn, lane_id(), cnt);
         uint64_t colstart[kTileGroups + 1];
         column_starts(sc, colstart);
-        const uint32_t ones = frag_tables(T, meta, sc, colstart, cnt, rows, cn, lane_id());
+        const uint32_t ones = frag_tables<(MB == 2)>(T, meta, sc, colstart, cnt, rows, cn, lane_id());
         const rsrc_t tile = tile_rsrc(G.payload, G.payload_bytes, meta.off);
         const uint16_t *xp[MB];
         frag_x_rows<MB>(G, j0, xp);
@@ -1902,7 +1947,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
                 frag_load_x<MB>(xp, jl, bx);
 #pragma unroll
                 for (uint32_t rb = 0; rb < 4; ++rb)
-                    frag_block<MB>(S.run.params, S.run.nib1, T, jl, rb, (ones >> (4 * jl + rb)) & 1u, col.w[rb], bx,
+                    frag_block<MB>(S.run.params, S.run.nib1, T, jl, rb, block_kind(ones, jl, rb), col.w[rb], bx,
                                    q, i, acc[rb]);
             }
             wave_lds_sync();
@@ -1924,7 +1969,7 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
             if (jl > 0) frag_load_x<MB>(xp, jl, bx);
 #pragma unroll
             for (uint32_t rb = 0; rb < 4; ++rb) {
-                frag_block<MB>(S.run.params, S.run.nib1, T, jl, rb, (ones >> (4 * jl + rb)) & 1u, cur.w[rb], bx, q, i,
+                frag_block<MB>(S.run.params, S.run.nib1, T, jl, rb, block_kind(ones, jl, rb), cur.w[rb], bx, q, i,
                                acc[rb]);
             }
             cur = nxt;

@@ -172,3 +172,76 @@ def test_rare_width_spreads(V, mix, want, mean):
     print_case(test="rare_spread", mix=sorted(mix.items()), mean=mean)
     got = run(V, V.DeviceMatrix(host), x)
     assert_within_tolerance(got, oracle.gemm(p, x), x, scales, f"spread {sorted(mix.items())} mean={mean}")
+
+
+def scaled_blocks(bits: np.ndarray, scales: np.ndarray) -> tuple:
+    """(scaled, other) counts of 16-row blocks per group column that the matrix-core kernel runs beyond 16
+    rows of X: a block is scaled (s q folded into its fp16 codes) when every row is 1- or 2-bit with a
+    scale that is zero or normal and below 2^15; rows past n do not count."""
+    e = (scales >> 10) & 0x1F
+    ok = (bits <= 2) & (((e >= 1) & (e <= 29)) | ((scales & 0x7FFF) == 0))
+    scaled = sum(int(ok[r:r + 16].all(axis=0).sum()) for r in range(0, bits.shape[0], 16))
+    return scaled, (-(-bits.shape[0] // 16)) * bits.shape[1] - scaled
+
+
+@pytest.mark.parametrize("key, mix", [(1, {1: 1.0}), (2, {2: 1.0}), (3, W.HEAD_MIX), (4, {1: 0.6, 2: 0.3, 4: 0.1})])
+def test_gemm_scaled_blocks(V, key, mix):
+    """Beyond 16 rows of X the matrix-core kernel multiplies a block of 1- and 2-bit rows by its scales in
+    fp16 before the matrix cores (exact for the scales it admits) and every other block in fp32 after
+    them. Scales here include zeros, subnormals, values of 2^15 and above and negatives, so both kinds of
+    block and each reason to fall back occur; rows with a scale of 2^15 or more are checked apart, so their
+    size does not loosen the bound on the others."""
+    n, k = 200, 1024 + 3 * 64
+    G = k // 64
+    bits, codes, _ = W.draw_random_matrix((118, key), n, k, mix)
+    scales = W.draw_signed_scales((119, key), n, G)
+    rng = np.random.default_rng(120 + key)
+    sign = rng.integers(0, 2, size=(n, G)).astype(np.uint16) << 15
+    pick = rng.random((n, G))
+    scales = np.where(pick < 0.01, sign, scales)                                            # +-0
+    scales = np.where((pick >= 0.01) & (pick < 0.02), sign | rng.integers(1, 0x400, size=(n, G)), scales)
+    big = (pick >= 0.02) & (pick < 0.025)
+    scales = np.where(big, sign | rng.integers(0x7800, 0x7C00, size=(n, G)), scales)        # 2^15 .. 65504
+    scales = np.where((pick >= 0.025) & (pick < 0.03), sign | rng.integers(0x7400, 0x7800, size=(n, G)), scales)
+    scales = scales.astype(np.uint16)
+    scaled, other = scaled_blocks(bits, scales)
+    assert scaled > 0 and other > 0, (scaled, other)
+    host = V.vbq_pack(n, k, bits, codes, scales)
+    p = oracle.pack(n, k, bits, codes, scales)
+    huge = big.any(axis=1)
+    rest = np.flatnonzero(~huge)
+    for name, dm in both_kernels(V, host).items():
+        if name == "declared" and len(mix) > 1:
+            continue
+        for m in (17, 32, 48, 64):
+            print_case(test="gemm_scaled", mix=key, m=m, kernel=name, scaled=scaled, other=other)
+            x = W.draw_x((121, key, m), k, m)
+            y, ref = run(V, dm, x), oracle.gemm(p, x)
+            assert_within_tolerance(y[:, rest], ref[:, rest], x, scales[rest], f"scaled m={m} {name}")
+            if huge.any():
+                rows = np.flatnonzero(huge)
+                assert_within_tolerance(y[:, rows], ref[:, rows], x, scales[rows], f"scaled, big scales m={m} {name}")
+
+
+def test_gemm_scaled_blocks_with_reserved_codes(V):
+    """A 2-bit payload that holds the reserved pattern (q = -2) next to scales near 2^15: 2 s stays finite
+    in fp16 only below 2^15, which is where the kernel stops folding the scale into the codes."""
+    import torch  # noqa: F401
+    n, k = 130, 1280
+    G = k // 64
+    bits, codes, _ = W.draw_random_matrix((122, 2), n, k, {2: 1.0})
+    rng = np.random.default_rng(123)
+    below = ((np.arange(n) // 16) % 2 == 0)[:, None]   # 16-row blocks alternate: below 2^15, then above
+    scales = np.where(below, rng.integers(0x7400, 0x7800, size=(n, G)),
+                      rng.integers(0x7800, 0x7C00, size=(n, G))).astype(np.uint16)
+    scaled, other = scaled_blocks(bits, scales)
+    assert scaled > 0 and other > 0, (scaled, other)
+    host = V.vbq_pack(n, k, bits, codes, scales)
+    p = oracle.pack(n, k, bits, codes, scales)
+    assert plant_reserved(host.payload, 2, np.random.default_rng(124)) > 0
+    p.payload[:] = host.payload
+    for m in (17, 64):
+        x = W.draw_x((125, m), k, m)
+        for name, dm in both_kernels(V, host).items():
+            print_case(test="gemm_scaled_reserved", m=m, kernel=name)
+            assert_within_tolerance(run(V, dm, x), oracle.gemm(p, x), x, scales, f"reserved, big scales m={m} {name}")
