@@ -1832,9 +1832,9 @@ __device__ __forceinline__ void frag_finish(FragLds<MB, kWaves> &S, const GemmAr
 // decoder), multiply with the activations on the matrix cores and add into acc (rows 16rb + 4q .. +3,
 // activation row mr). At 17 to 32 rows of X a scaled block (every row 1- or 2-bit, scales that keep s q
 // exact in fp16) carries s q in its fragments, so the matrix cores add straight into acc; any other
-// block's products are scaled by each row's fp32 group scale and then added. (Beyond 32 rows the
-// accumulators live in the matrix-core registers, and the other blocks' scaling then costs two moves per
-// accumulator: every block is scaled after the products there.)
+// block's products are scaled by each row's fp32 group scale and then added. (Beyond 32 rows the same
+// folding measured slower, with the accumulators in matrix-core registers or in VGPRs: every block is
+// scaled after its products there.)
 template <uint32_t MB>
 __device__ __forceinline__ void frag_block(const FragParams *params, const uint2 *nib, const FragTables &T,
                                            uint32_t jl, uint32_t rb, uint32_t kind, const uint2 w[2],
