@@ -18,7 +18,9 @@ Beside each line, the same pass on dense fp16 weights of the same shapes
 (torch F.linear, i.e. rocBLAS/hipBLASLt; random values, timed the same way)
 gives fp16_us_per_pass and speedup_vs_fp16.
 
-  python bench_configs.py [--configs 1,2,3,4,5] [--passes 50] [--warmup 10]
+  python bench_configs.py [--configs 1,2,3,4,5] [--passes 50] [--warmup 10] [--batches 24,32]
+
+--batches replaces each workload's own batch sizes (1 to 64 rows of X).
 """
 from __future__ import annotations
 
@@ -41,7 +43,12 @@ def parse():
     ap.add_argument("--rotate-mb", type=float, default=640.0)
     ap.add_argument("--graph-launches", type=int, default=4096)
     ap.add_argument("--no-fp16", action="store_true")
-    return ap.parse_args()
+    ap.add_argument("--batches", default="", help="comma-separated batch sizes instead of each workload's own")
+    a = ap.parse_args()
+    a.batches = tuple(int(m) for m in a.batches.split(",") if m)
+    if any(not 1 <= m <= 64 for m in a.batches):
+        ap.error("--batches: each batch size must be in 1..64")
+    return a
 
 
 def launch_groups(specs):
@@ -96,7 +103,7 @@ def main():
         copies = max(1, math.ceil(args.rotate_mb * 1e6 / packed))
         layers = [[V.DeviceMatrix(h, dev) for h in hosts] for _ in range(copies)]
         groups = launch_groups(specs)
-        for m in cfg.batches:
+        for m in args.batches or cfg.batches:
             xs, ys = {}, []
             for s in specs:
                 key = (W.x_seed(s), m)
