@@ -233,6 +233,35 @@ def test_edge_values(V, torch_mod):
             assert_within_tolerance(y, ref, xx, scales, "edge values")
 
 
+@pytest.mark.parametrize("m", [17, 24, 32, 64])
+def test_edge_values_small_batch(V, torch_mod, m):
+    # 1- and 2-bit rows, so the matrix-core kernel folds most blocks' scales into the fp16 codes at 17 to
+    # 32 rows: zero, subnormal and largest finite scales (the last two keep their blocks on the fp32
+    # scaling), with subnormal, zero and all-zero activations
+    n, k = 130, 640
+    bits, codes, scales = W.draw_random_matrix(11, n, k, {1: 0.5, 2: 0.5})
+    scales = scales.copy()
+    scales.reshape(-1)[::7] = 0
+    scales.reshape(-1)[2::9] = 0x8000         # negative zero
+    scales.reshape(-1)[3::97] = 0x0001
+    scales.reshape(-1)[5::101] = 0x03FF
+    scales.reshape(-1)[1::103] = 0x7BFF
+    p = oracle.pack(n, k, bits, codes, scales)
+    h, dm = upload(V, bits, codes, scales)
+    x = W.draw_x(12, k, m)
+    xs = x.copy()
+    xs.reshape(-1)[::5] = 0x0003
+    xs.reshape(-1)[2::9] = 0
+    for xx in (x, xs, np.zeros_like(x)):
+        print_case(test="edge_values_small_batch", m=m)
+        y = gpu_gemm(V, torch_mod, dm, xx)
+        ref = oracle.gemm(p, xx)
+        if not np.any(ref):
+            assert np.all(y == 0)
+        else:
+            assert_within_tolerance(y, ref, xx, scales, f"edge values m={m}")
+
+
 def test_empty_shapes(V, torch_mod):
     torch = torch_mod
     h, dm = upload(V, np.zeros((0, 2), np.uint8), np.zeros((0, 128), np.int8), np.zeros((0, 2), np.uint16))
