@@ -1934,11 +1934,12 @@ __global__ __launch_bounds__(kWaves * kWave) void gemm_frag(GemmBatch B) {
         frag_x_rows<MB>(G, j0, xp);
         const uint32_t lane = lane_id(), q = lane >> 4, i = lane & 15u;
         wave_lds_sync();
-        if constexpr (MB == 1) {
+        if constexpr (MB != 2) {
             // the next tile's metadata travels while this tile computes
             meta = load_meta<kAligned>(G, a, ct + kWaves < c_hi ? ct + kWaves : ct, lane_id(), false);
-            // one column at a time: with 82 VGPRs the other waves of the SIMD cover the loads' latency
-            // (LM head, head mix, m = 16: 22.9 -> 21.7 us against the two-stage pipeline below)
+            // one column at a time: the other waves of the SIMD cover the loads' latency (LM head, head
+            // mix, against the two-stage pipeline below: m = 16 22.9 -> 21.7 us, m = 48 42.2 -> 38.3,
+            // m = 64 alike; at m = 17..32 the pipeline is faster, 28.8 against 30.8 us at m = 24)
 #pragma unroll 1
             for (uint32_t jl = 0; jl < kTileGroups; ++jl) {
                 if (jl >= cn) break;
