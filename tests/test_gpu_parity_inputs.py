@@ -175,7 +175,7 @@ def test_rare_width_spreads(V, mix, want, mean):
 
 
 def scaled_blocks(bits: np.ndarray, scales: np.ndarray) -> tuple:
-    """(scaled, other) counts of 16-row blocks per group column that the matrix-core kernel runs beyond 16
+    """(scaled, other) counts of 16-row blocks per group column that the matrix-core kernel runs at 17 to 32
     rows of X: a block is scaled (s q folded into its fp16 codes) when every row is 1- or 2-bit with a
     scale that is zero or normal and below 2^15; rows past n do not count."""
     e = (scales >> 10) & 0x1F
@@ -186,9 +186,9 @@ def scaled_blocks(bits: np.ndarray, scales: np.ndarray) -> tuple:
 
 @pytest.mark.parametrize("key, mix", [(1, {1: 1.0}), (2, {2: 1.0}), (3, W.HEAD_MIX), (4, {1: 0.6, 2: 0.3, 4: 0.1})])
 def test_gemm_scaled_blocks(V, key, mix):
-    """Beyond 16 rows of X the matrix-core kernel multiplies a block of 1- and 2-bit rows by its scales in
+    """At 17 to 32 rows of X the matrix-core kernel multiplies a block of 1- and 2-bit rows by its scales in
     fp16 before the matrix cores (exact for the scales it admits) and every other block in fp32 after
-    them. Scales here include zeros, subnormals, values of 2^15 and above and negatives, so both kinds of
+    them (beyond 32 rows every block is scaled after, which m = 48 and 64 check). Scales here include zeros, subnormals, values of 2^15 and above and negatives, so both kinds of
     block and each reason to fall back occur; rows with a scale of 2^15 or more are checked apart, so their
     size does not loosen the bound on the others."""
     n, k = 200, 1024 + 3 * 64
